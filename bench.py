@@ -1,0 +1,286 @@
+#!/usr/bin/env python3
+"""Benchmark of the RankMixerBlock forward+backward on one MI355X.
+
+One step = rm_block_fwd + rm_block_bwd over one batch of synthetic input
+(every step of the block, both directions, all 15 gradient tensors).
+Default workload: B=1024, T=64, D=1280, k=2 (H=2560), bf16 storage, fp32
+accumulation, inputs resident in HBM before timing starts.
+
+Printed as the last stdout line: one JSON object with
+  value        tokens/s (B*T per step / seconds per step) over K timed steps
+  roofline     the kernel with the largest share of step time, its algorithmic
+               flops (or bytes) per launch / its mean launch time from HIP
+               events recorded on the library's stream during a timed pass
+  cpu_baseline the float64 oracle on a bounded sample, on the host's cores
+Also reported: the pages' timing protocol (flush, sync, event span per
+iteration, first sample dropped, mean/min/max in us), per-kernel times, % of
+MFMA peak for the whole step, peak device memory.
+
+Workload and protocol follow "Subgraph-fusion-based Mega-kernel Generation"
+(page 1): "Workload and interfaces", "Run the benchmark" (WARMUP=5,
+NUM_TESTS=20) and "Exact timing behavior".
+"""
+from __future__ import annotations
+
+import argparse
+import json
+import os
+import sys
+import time
+
+import numpy as np
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+from rankmixer_inputs import PRODUCTION, WORKLOADS, make_case  # noqa: E402
+
+# MI355X published peaks
+PEAK_TFLOPS = {"bf16": 2516.6, "f32": 157.3}   # dense MFMA: 256 CU x 2.4 GHz x (4096 | 256) flop/clk
+PEAK_HBM_GBS = 8000.0
+
+
+def log(msg):
+    print(msg, file=sys.stderr, flush=True)
+
+
+def gemm_flops(d):
+    """Algorithmic flops of each GEMM launch (one launch covers all T tokens)."""
+    B, T, D, H = d.B, d.T, d.D, d.k * d.D
+    return {"gemm_up": 2.0 * B * T * D * 2 * H, "gemm_down": 2.0 * B * T * H * D,
+            "gemm_dhid": 2.0 * B * T * D * H, "gemm_dwout": 2.0 * T * H * D * B,
+            "gemm_dw1": 2.0 * T * D * 2 * H * B, "gemm_dh1": 2.0 * B * T * 2 * H * D}
+
+
+def row_bytes(d, sz):
+    """Algorithmic HBM bytes of each row-kernel launch: its inputs read once, outputs written once."""
+    B, T, D, H = d.B, d.T, d.D, d.k * d.D
+    N = B * T
+    nb = (B + 63) // 64
+    return {
+        "prologue": N * D * sz * 2 + N * 16,                         # x -> out1, 4 stats
+        "gate_fwd": N * 2 * H * sz + N * H * sz + N * 16,            # Z -> hidden
+        "ln2_fwd": N * D * 4 + N * D * sz + N * 8,                   # r2 (fp32) -> y
+        "ln2_bwd": N * D * 4 + 2 * N * D * sz + 3 * nb * T * D * 4,  # r2, dy -> d(out2), partials
+        "gate_bwd": N * 2 * H * sz + N * H * sz + N * 2 * H * sz + 6 * nb * T * H * 4,  # Z, dhid -> dZ
+        "tail_bwd": N * D * sz + N * D * 4 + N * D * sz + 4 * B * D * 4,  # x, d(out1) -> dx, partials
+    }
+
+
+def step_flops(d):
+    return 18.0 * d.B * d.T * d.D * d.k * d.D
+
+
+def cpu_baseline(name, batch, min_seconds):
+    """The float64 oracle (unchanged) on the first `batch` samples of the workload."""
+    import oracle
+    from rankmixer_inputs import as_f64
+    try:
+        from threadpoolctl import threadpool_info
+        cores = max([int(i.get("num_threads", 1)) for i in threadpool_info()] or [1])
+    except Exception:
+        cores = os.cpu_count() or 1
+    case = make_case(name, batch=batch)
+    x, p, dy = as_f64(case)
+    d = case["dims"]
+    oracle.forward_backward(x, p, dy)   # untimed warm run
+    reps, t0 = 0, time.perf_counter()
+    while True:
+        oracle.forward_backward(x, p, dy)
+        reps += 1
+        el = time.perf_counter() - t0
+        if el >= min_seconds:
+            break
+    tokens = reps * d.B * d.T
+    return {"value": tokens / el, "unit": "tokens/s", "cores": cores, "kind": "oracle",
+            "sample": f"first {batch} of {WORKLOADS[name].dims.B} samples of {name} "
+                      f"(all parameters), float64 fwd+bwd x{reps} in {el:.1f} s"}
+
+
+def main():
+    ap = argparse.ArgumentParser(description=__doc__, formatter_class=argparse.RawDescriptionHelpFormatter)
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=20)
+    ap.add_argument("--warmup", type=int, default=5)
+    ap.add_argument("--workload", default=PRODUCTION, choices=sorted(WORKLOADS))
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--cpu-batch", type=int, default=8)
+    ap.add_argument("--cpu-seconds", type=float, default=10.0)
+    ap.add_argument("--no-protocol", action="store_true", help="skip the per-iteration flush protocol pass")
+    ap.add_argument("--no-kernel-times", action="store_true", help="skip the event-instrumented pass")
+    args = ap.parse_args()
+
+    if args.gpus != 1:
+        print(f"bench.py: this build runs on one GPU only (asked for --gpus {args.gpus}); "
+              "multi-GPU sharding is not built", file=sys.stderr)
+        sys.exit(2)
+
+    import torch
+    import transformer_block_norm0_amd as rb
+    if not torch.cuda.is_available():
+        print("bench.py: no GPU visible", file=sys.stderr)
+        sys.exit(1)
+    rb.library()
+
+    w = WORKLOADS[args.workload]
+    d = w.dims
+    log(f"generating {w.name} (seed {w.seed})")
+    case = make_case(w)
+    sys.path.insert(0, os.path.join(ROOT, "tests"))
+    from rm_gpu import DeviceCase  # noqa: E402  (moves the case to the device, calls the C ABI)
+    dc = DeviceCase(case)
+    del case
+    torch.cuda.synchronize()
+    stream = torch.cuda.current_stream()
+
+    def step():
+        dc.fwd(stream)
+        dc.bwd(stream)
+
+    # warmup (untimed), then exactly K timed steps bracketed by synchronisation
+    for _ in range(args.warmup):
+        step()
+    torch.cuda.synchronize()
+    torch.cuda.reset_peak_memory_stats()
+    ev0, ev1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    torch.cuda.synchronize()
+    h0 = time.perf_counter()
+    ev0.record(stream)
+    for _ in range(args.steps):
+        step()
+    ev1.record(stream)
+    torch.cuda.synchronize()
+    host_s = time.perf_counter() - h0
+    ms_total = ev0.elapsed_time(ev1)
+    ms_step = ms_total / args.steps
+    peak_mem = torch.cuda.max_memory_allocated()
+    tokens = d.B * d.T
+    value = tokens / (ms_step / 1e3)
+    tflops = step_flops(d) / (ms_step / 1e3) / 1e12
+    pct_peak = 100.0 * tflops / PEAK_TFLOPS[w.dtype]
+    log(f"B={d.B} T={d.T} D={d.D} k={d.k} H={d.H} T_local={d.T} a2a_bytes=0 mode=fwd+bwd")
+    log(f"{args.steps} steps: {ms_step:.3f} ms/step (host {1e3 * host_s / args.steps:.3f}), "
+        f"{value:.4g} tokens/s, {tflops:.1f} TFLOP/s = {pct_peak:.1f}% of {w.dtype} MFMA peak")
+
+    # per-kernel HIP events (library instrumentation) over a second timed pass
+    kernels = {}
+    roofline = None
+    if not args.no_kernel_times:
+        rb.prof_enable(True)
+        torch.cuda.synchronize()
+        for _ in range(args.steps):
+            step()
+        torch.cuda.synchronize()
+        rb.prof_enable(False)
+        prof = rb.prof_collect()
+        flops = gemm_flops(d)
+        sz = 2 if w.dtype == "bf16" else 4
+        rbytes = row_bytes(d, sz)
+        step_ms_sum = 0.0
+        for name, (ms, n) in prof.items():
+            if n == 0:
+                continue
+            avg = ms / n
+            step_ms_sum += ms / args.steps
+            ent = {"avg_ms": round(avg, 5), "launches": n}
+            if name in flops:
+                ent["tflops"] = round(flops[name] / (avg / 1e3) / 1e12, 2)
+                ent["frac_peak"] = round(ent["tflops"] / PEAK_TFLOPS[w.dtype], 4)
+            elif name in rbytes:
+                ent["gbs"] = round(rbytes[name] / (avg / 1e3) / 1e9, 1)
+                ent["frac_peak"] = round(ent["gbs"] / PEAK_HBM_GBS, 4)
+            kernels[name] = ent
+        for name, ent in sorted(kernels.items(), key=lambda kv: -kv[1]["avg_ms"]):
+            log(f"  {name:12s} {ent['avg_ms'] * 1e3:9.1f} us  " +
+                (f"{ent['tflops']:8.1f} TFLOP/s" if "tflops" in ent else f"{ent.get('gbs', 0):8.1f} GB/s"))
+        log(f"  sum of kernel means {step_ms_sum:.3f} ms/step (instrumented)")
+        dom = max(kernels.items(), key=lambda kv: kv[1]["avg_ms"])
+        name, ent = dom
+        if "tflops" in ent:
+            roofline = {"kernel": name, "bound": "mfma", "achieved": ent["tflops"], "peak": PEAK_TFLOPS[w.dtype],
+                        "unit": "TFLOP/s", "frac": round(ent["tflops"] / PEAK_TFLOPS[w.dtype], 4),
+                        "traffic": None, "avg_ms": ent["avg_ms"],
+                        "per_launch": f"{flops[name]:.4g} flop"}
+        else:
+            roofline = {"kernel": name, "bound": "hbm", "achieved": ent["gbs"], "peak": PEAK_HBM_GBS,
+                        "unit": "GB/s", "frac": round(ent["gbs"] / PEAK_HBM_GBS, 4), "traffic": None,
+                        "avg_ms": ent["avg_ms"], "per_launch": f"{rbytes[name]:.4g} B"}
+        traffic = load_traffic(name, w.name)
+        if traffic is not None:
+            roofline["traffic"] = traffic
+
+    # the pages' protocol: flush caches, sync, event span per iteration, drop the first sample
+    protocol = None
+    if not args.no_protocol:
+        flush = torch.empty(512 * 1024 * 1024 // 4, dtype=torch.float32, device="cuda")
+        samples = []
+        n_iter = max(2, args.steps)
+        for _ in range(n_iter):
+            flush.zero_()
+            torch.cuda.synchronize()
+            a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+            a.record(stream)
+            step()
+            b.record(stream)
+            torch.cuda.synchronize()
+            samples.append(a.elapsed_time(b) * 1e3)
+        kept = samples[1:]
+        protocol = {"mean_us": round(float(np.mean(kept)), 1), "min_us": round(float(np.min(kept)), 1),
+                    "max_us": round(float(np.max(kept)), 1), "iterations": len(kept),
+                    "flush": "512 MiB fill before each iteration (untimed)"}
+        log(f"pages' protocol: mean {protocol['mean_us']:.1f} us, min {protocol['min_us']:.1f}, "
+            f"max {protocol['max_us']:.1f} over {len(kept)} iterations")
+        del flush
+
+    cpu = None
+    if not args.no_cpu_baseline:
+        log(f"cpu baseline: oracle on {args.cpu_batch} samples for >= {args.cpu_seconds} s")
+        cpu = cpu_baseline(w.name, args.cpu_batch, args.cpu_seconds)
+        log(f"  {cpu['value']:.4g} tokens/s on {cpu['cores']} threads")
+
+    out = {
+        "metric": "fwd+bwd tokens/s and % MFMA peak, B1024 T64 D1280 k2 bf16, 1 GPU",
+        "value": round(value, 1),
+        "unit": "tokens/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": round(ms_step, 4),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": w.dtype,
+        "data": "synthetic (seeded N(0,1) inputs and upstream grad, he-uniform weights)",
+        "config": {"workload": w.name, "B": d.B, "T": d.T, "D": d.D, "k": d.k, "H": d.H,
+                   "tokens_per_step": tokens, "parallelism": "single GPU"},
+        "tflops": round(tflops, 2),
+        "pct_mfma_peak": round(pct_peak, 2),
+        "peak_device_bytes": int(peak_mem),
+        "roofline": roofline,
+        "cpu_baseline": cpu,
+        "pages_protocol": protocol,
+        "kernels": kernels,
+    }
+    print(json.dumps(out), flush=True)
+
+
+def load_traffic(kernel, workload):
+    """HBM bytes per launch measured with rocprofv3 counters, if recorded for this kernel build."""
+    path = os.path.join(ROOT, "profiles", "traffic.json")
+    if not os.path.exists(path):
+        return None
+    try:
+        rec = json.load(open(path))
+        ent = rec.get(workload, {}).get(kernel)
+        if not ent:
+            return None
+        from transformer_block_norm0_amd.build import source_digest
+        if ent.get("source_digest") != source_digest():
+            return None
+        return ent["bytes_per_launch"]
+    except Exception:
+        return None
+
+
+if __name__ == "__main__":
+    main()

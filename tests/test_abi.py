@@ -1,0 +1,131 @@
+"""The C-ABI library loads, exports every declared symbol, and rejects invalid
+arguments on the host before any launch (CPU only: no compute call is made)."""
+import ctypes
+import os
+import re
+
+import pytest
+
+from rankmixer_inputs import Dims, in_envelope
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+HEADER = os.path.join(ROOT, "include", "rmblock.h")
+
+
+def header_functions():
+    text = open(HEADER).read()
+    text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
+    return sorted(set(re.findall(r"\b(rm_[a-z_0-9]+)\s*\(", text)))
+
+
+@pytest.fixture(scope="module")
+def rb():
+    import transformer_block_norm0_amd as rb
+    rb.library()
+    return rb
+
+
+def test_header_declares_the_boundary():
+    names = header_functions()
+    for required in ("rm_workspace_bytes", "rm_block_fwd", "rm_block_bwd", "rm_token_mix",
+                     "rm_status_string", "rm_ws_region"):
+        assert required in names
+
+
+def test_library_exports_every_declared_symbol(rb):
+    lib = rb.library()
+    for name in header_functions():
+        assert hasattr(lib, name), f"{name} declared in rmblock.h but not exported"
+    assert lib.rm_abi_version() == 1
+
+
+def expected_workspace_bytes(B, T, D, k, dtype):
+    """The workspace layout restated from rmblock.h / the library's documented regions."""
+    al = lambda v: (v + 255) // 256 * 256
+    N, H = B * T, k * D
+    sz = 2 if dtype == "bf16" else 4
+    nb = (B + 63) // 64
+    sizes = [N * D * sz, N * 2 * H * sz, N * H * sz, N * D * 4, 10 * N * 4,      # saved by the forward
+             N * D * sz, N * H * sz, N * 2 * H * sz, N * D * 4, N * D * 4,       # backward scratch
+             3 * nb * T * D * 4, (4 * nb * T * H + nb * T * 2 * H) * 4, 4 * B * D * 4]  # partials
+    off = 0
+    for s in sizes:
+        off = al(off) + s
+    return al(off)
+
+
+@pytest.mark.parametrize("shape", [(1, 8, 64, 2), (4, 16, 128, 2), (999, 40, 1000, 3), (1024, 64, 1280, 2),
+                                   (3, 13, 65, 3)])
+@pytest.mark.parametrize("dtype", ["f32", "bf16"])
+def test_workspace_bytes_formula(rb, shape, dtype):
+    d = rb.dims(*shape, dtype)
+    assert rb.workspace_bytes(d) == expected_workspace_bytes(*shape, dtype)
+
+
+@pytest.mark.parametrize("shape", [(0, 8, 64, 2), (1025, 8, 64, 2), (2, 7, 63, 2), (2, 65, 130, 2),
+                                   (2, 8, 60, 2), (2, 8, 1288, 2), (2, 16, 120, 2), (2, 8, 64, 1),
+                                   (2, 8, 64, 4)])
+def test_out_of_envelope_dims_rejected(rb, shape):
+    assert not in_envelope(Dims(*shape))
+    d = rb.dims(*shape, "f32")
+    assert rb.workspace_bytes(d) == 0
+    lib = rb.library()
+    params = rb.rmblock.CParams(*([8] * 14))
+    st = lib.rm_block_fwd(ctypes.byref(d), ctypes.byref(params), 8, 8, 256, 1 << 40, None)
+    assert st == 1  # RM_E_DIMS
+    st = lib.rm_token_mix(ctypes.byref(d), 8, 16, None)
+    assert st == 1
+
+
+def _valid_call_args(rb, dtype="f32"):
+    d = rb.dims(4, 16, 128, 2, dtype)
+    params = rb.rmblock.CParams(*([256] * 14))
+    grads = rb.rmblock.CGrads(*([512] * 14))
+    return d, params, grads, rb.workspace_bytes(d)
+
+
+def test_bad_arguments_rejected_before_launch(rb):
+    lib = rb.library()
+    d, params, grads, wsb = _valid_call_args(rb)
+    by = ctypes.byref
+    # null pointers
+    assert lib.rm_block_fwd(by(d), by(params), None, 1024, 4096, wsb, None) == 2
+    assert lib.rm_block_fwd(by(d), by(params), 1024, 1024, None, wsb, None) == 2
+    p_null = rb.rmblock.CParams(*([256] * 13 + [0]))
+    assert lib.rm_block_fwd(by(d), by(p_null), 1024, 1024, 4096, wsb, None) == 2
+    g_null = rb.rmblock.CGrads(*([512] * 6 + [0] + [512] * 7))
+    assert lib.rm_block_bwd(by(d), by(params), 1024, 1024, 4096, wsb, 2048, by(g_null), None) == 2
+    # short workspace
+    assert lib.rm_block_fwd(by(d), by(params), 1024, 1024, 4096, wsb - 1, None) == 4
+    assert lib.rm_block_bwd(by(d), by(params), 1024, 1024, 4096, wsb - 256, 2048, by(grads), None) == 4
+    # misaligned: workspace needs 256 bytes, fp32 elements need 4
+    assert lib.rm_block_fwd(by(d), by(params), 1024, 1024, 4100, wsb, None) == 3
+    assert lib.rm_block_fwd(by(d), by(params), 1026, 1024, 4096, wsb, None) == 3
+    p_mis = rb.rmblock.CParams(*([256] * 5 + [258] + [256] * 8))
+    assert lib.rm_block_fwd(by(d), by(p_mis), 1024, 1024, 4096, wsb, None) == 3
+    # bf16 elements need only 2-byte alignment, but odd addresses fail
+    d16, p16, g16, wsb16 = _valid_call_args(rb, "bf16")
+    assert lib.rm_block_fwd(by(d16), by(p16), 1025, 1024, 4096, wsb16, None) == 3
+    # unknown dtype
+    dbad = rb.rmblock.CDims(4, 16, 128, 2, 7)
+    assert lib.rm_block_fwd(by(dbad), by(params), 1024, 1024, 4096, wsb, None) == 5
+    assert lib.rm_workspace_bytes(by(dbad)) == 0
+    # token mix in place is refused
+    assert lib.rm_token_mix(by(d), 1024, 1024, None) == 7
+    # region query
+    off, nb = ctypes.c_size_t(), ctypes.c_size_t()
+    assert lib.rm_ws_region(by(d), 99, by(off), by(nb)) == 7
+    assert lib.rm_ws_region(by(d), 0, by(off), by(nb)) == 0 and off.value == 0 and nb.value == 64 * 128 * 4
+    for code in range(8):
+        assert lib.rm_status_string(code)
+
+
+def test_no_oracle_or_fallback_in_product_path():
+    """The product package never imports the oracle and has no CPU compute path."""
+    pkg = os.path.join(ROOT, "transformer_block_norm0_amd")
+    for dirpath, _, files in os.walk(pkg):
+        for f in files:
+            if f.endswith((".py", ".hip", ".h", ".cpp")):
+                text = open(os.path.join(dirpath, f)).read()
+                assert "import oracle" not in text and "from oracle" not in text, f
+                assert "numpy" not in text, f

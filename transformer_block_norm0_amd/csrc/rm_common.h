@@ -1,0 +1,77 @@
+// Internal device helpers shared by the RankMixerBlock kernels (gfx950, wave64).
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+namespace rm {
+
+// ---------------------------------------------------------------------------
+// storage types.  bf16 is carried as its 16-bit pattern.
+
+struct bf16_t {
+  uint16_t u;
+};
+
+__device__ __forceinline__ float to_f32(float v) { return v; }
+__device__ __forceinline__ float to_f32(bf16_t v) { return __uint_as_float(((uint32_t)v.u) << 16); }
+
+// float -> bf16, round to nearest even; NaN stays a (quiet) NaN.
+__device__ __forceinline__ uint16_t f32_to_bf16_bits(float f) {
+  uint32_t u = __float_as_uint(f);
+  if ((u & 0x7fffffffu) > 0x7f800000u) return (uint16_t)((u >> 16) | 0x0040u);
+  u += 0x7fffu + ((u >> 16) & 1u);
+  return (uint16_t)(u >> 16);
+}
+
+template <typename ST> __device__ __forceinline__ ST from_f32(float f);
+template <> __device__ __forceinline__ float from_f32<float>(float f) { return f; }
+template <> __device__ __forceinline__ bf16_t from_f32<bf16_t>(float f) {
+  bf16_t r;
+  r.u = f32_to_bf16_bits(f);
+  return r;
+}
+
+template <typename ST> __device__ __forceinline__ float ld(const ST* p, long i) { return to_f32(p[i]); }
+template <typename ST> __device__ __forceinline__ void st(ST* p, long i, float v) { p[i] = from_f32<ST>(v); }
+
+// ---------------------------------------------------------------------------
+// token mixing index map (page 1, "Exact computation": view [B,T,D] as
+// [B,T,T,S] with S = D/T, swap the two T axes).  Output row i, column c reads
+// input row c / S, column i*S + c % S.  The map is an involution, so the same
+// function also gives the adjoint (the backward gather).
+__device__ __forceinline__ void tm_source(int i, int c, int S, int& src_row, int& src_col) {
+  const int j = c / S;
+  src_row = j;
+  src_col = i * S + (c - j * S);
+}
+
+// ---------------------------------------------------------------------------
+// reductions (fixed order: deterministic)
+
+__device__ __forceinline__ float wave_sum(float v) {
+#pragma unroll
+  for (int o = 32; o > 0; o >>= 1) v += __shfl_xor(v, o, 64);
+  return v;
+}
+
+// Sum NV values over a 256-thread block; every thread gets the totals.
+// scratch: at least 4*NV floats of LDS.  Contains two barriers.
+template <int NV>
+__device__ __forceinline__ void block_sum256(float (&v)[NV], float* scratch) {
+  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+#pragma unroll
+  for (int i = 0; i < NV; ++i) {
+    float s = wave_sum(v[i]);
+    if (lane == 0) scratch[i * 4 + wave] = s;
+  }
+  __syncthreads();
+#pragma unroll
+  for (int i = 0; i < NV; ++i)
+    v[i] = (scratch[i * 4 + 0] + scratch[i * 4 + 1]) + (scratch[i * 4 + 2] + scratch[i * 4 + 3]);
+  __syncthreads();
+}
+
+__device__ __forceinline__ float sigmoidf_(float v) { return 1.0f / (1.0f + expf(-v)); }
+
+}  // namespace rm

@@ -1,0 +1,90 @@
+// Internal host-side declarations: workspace layout, kernel ids, launchers.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stddef.h>
+#include <stdint.h>
+
+#include "rmblock.h"
+
+namespace rm {
+
+// Rows (b) per workgroup in the per-token row-group kernels of the backward.
+constexpr int ROWS_PER_GROUP = 64;
+
+enum KernelId {
+  KID_PROLOGUE = 0,   // norm0 -> token mix -> +x -> norm1
+  KID_GEMM_UP,        // Z = out1 @ w1[t] + b1[t]
+  KID_GATE_FWD,       // LN_x(U) * silu(LN_gate(G))
+  KID_GEMM_DOWN,      // out1 + hidden @ wout[t] + bout[t]
+  KID_LN2_FWD,        // norm2
+  KID_LN2_BWD,        // norm2 backward (+ dbout, dgamma2, dbeta2 partials)
+  KID_GEMM_DHID,      // d hidden = d(out2) @ wout[t]^T
+  KID_GATE_BWD,       // gate / SiLU / inner LayerNorm backward -> dZ
+  KID_GEMM_DWOUT,     // dwout[t] = hidden^T @ d(out2)
+  KID_GEMM_DW1,       // dw1[t] = out1^T @ dZ
+  KID_GEMM_DH1,       // d(out1) = dZ @ w1[t]^T + d(out2)
+  KID_TAIL_BWD,       // norm1 backward, inverse token mix, norm0 backward -> dx
+  KID_FINALIZE,       // fixed-order sums of parameter-gradient partials
+  KID_TOKEN_MIX,      // stand-alone token permutation
+  KID_COUNT
+};
+
+extern const char* const kKernelNames[KID_COUNT];
+
+// Byte offsets into the caller's workspace.
+struct WsLayout {
+  size_t h1, z, hid, r2, stats;            // written by the forward, read by the backward
+  size_t do2, dhid, dz, dh1, dr1;          // backward scratch
+  size_t p_ln2, p_gate, p_tail;            // backward partial sums (fp32)
+  size_t total;
+  int nb;                                  // row groups per token: ceil(B / ROWS_PER_GROUP)
+};
+
+bool dims_valid(const rm_dims& d);
+WsLayout ws_layout(const rm_dims& d);
+
+// stats block: 10 arrays of B*T floats in this order
+enum { ST_MU0 = 0, ST_RS0, ST_MU1, ST_RS1, ST_MUX, ST_RSX, ST_MUG, ST_RSG, ST_MU2, ST_RS2, ST_COUNT };
+
+// instrumentation hooks (no-ops unless enabled)
+void prof_begin(int kid, hipStream_t s);
+void prof_end(int kid, hipStream_t s);
+
+// ---------------------------------------------------------------------------
+// GEMM over T independent problems (one per token t):  C_t = A_t (MxK) . B_t (KxN)
+// A K-major: element (m,k) at A + t*a_bs + m*a_ld + k;  M-major: at A + t*a_bs + k*a_ld + m
+// B K-major: element (k,n) at B + t*b_bs + n*b_ld + k;  N-major: at B + t*b_bs + k*b_ld + n
+// epilogue: v = acc (+ bias[t*bias_bs + n]) (+ res[t*res_bs + m*res_ld + n]);
+//           C[t*c_bs + m*c_ld + n] = v  (storage dtype, or fp32 when c_f32)
+struct GemmArgs {
+  int M, N, K, batch;
+  const void* A; long a_bs, a_ld;
+  const void* B; long b_bs, b_ld;
+  void* C; long c_bs, c_ld; int c_f32;
+  const void* bias; long bias_bs;
+  const void* res; long res_bs, res_ld; int res_f32;
+};
+
+hipError_t launch_gemm(int dtype, bool a_kmajor, bool b_kmajor, const GemmArgs& g, int kid,
+                       hipStream_t s);
+
+// ---------------------------------------------------------------------------
+// row kernels
+hipError_t launch_prologue(const rm_dims& d, const rm_params& p, const void* x, void* ws,
+                           const WsLayout& L, hipStream_t s);
+hipError_t launch_gate_fwd(const rm_dims& d, const rm_params& p, void* ws, const WsLayout& L,
+                           hipStream_t s);
+hipError_t launch_ln2_fwd(const rm_dims& d, const rm_params& p, void* y, void* ws,
+                          const WsLayout& L, hipStream_t s);
+hipError_t launch_ln2_bwd(const rm_dims& d, const rm_params& p, const void* dy, void* ws,
+                          const WsLayout& L, hipStream_t s);
+hipError_t launch_gate_bwd(const rm_dims& d, const rm_params& p, void* ws, const WsLayout& L,
+                           hipStream_t s);
+hipError_t launch_tail_bwd(const rm_dims& d, const rm_params& p, const void* x, void* dx, void* ws,
+                           const WsLayout& L, hipStream_t s);
+hipError_t launch_finalize(const rm_dims& d, const rm_grads& g, void* ws, const WsLayout& L,
+                           hipStream_t s);
+hipError_t launch_token_mix(const rm_dims& d, const void* in, void* out, hipStream_t s);
+
+}  // namespace rm
