@@ -15,7 +15,8 @@
 //   gemm dwout dwout[t] = hidden^T @ d(out2)
 //   gemm dw1   dw1[t] = out1^T @ dZ
 //   gemm dh1   d(out1) = dZ @ w1[t]^T + d(out2)               (fp32)
-//   tail bwd   norm1 backward, token-mix adjoint, norm0 backward => dx (+ outer affine partials)
+//   ln1 bwd    norm1 backward (r1 recomputed via the token-mix gather) => dr1 (+ dgamma1, dbeta1)
+//   ln0 bwd    token-mix adjoint as a gather, norm0 backward, + dr1   => dx (+ dgamma0, dbeta0)
 //   finalize   fixed-order sums of every partial              => parameter gradients
 #include <mutex>
 #include <vector>
@@ -26,7 +27,7 @@ namespace rm {
 
 const char* const kKernelNames[KID_COUNT] = {
     "prologue", "gemm_up", "gate_fwd", "gemm_down", "ln2_fwd", "ln2_bwd", "gemm_dhid",
-    "gate_bwd", "gemm_dwout", "gemm_dw1", "gemm_dh1", "tail_bwd", "finalize", "token_mix"};
+    "gate_bwd", "gemm_dwout", "gemm_dw1", "gemm_dh1", "ln1_bwd", "ln0_bwd", "finalize", "token_mix"};
 
 bool dims_valid(const rm_dims& d) {
   if (d.dtype != RM_F32 && d.dtype != RM_BF16) return false;
@@ -65,7 +66,7 @@ WsLayout ws_layout(const rm_dims& d) {
   L.dr1 = take(N * D * 4);
   L.p_ln2 = take(3 * nb * T * D * 4);
   L.p_gate = take((4 * nb * T * H + nb * T * 2 * H) * 4);
-  L.p_tail = take(4 * (size_t)d.B * D * 4);
+  L.p_tail = take(4 * nb * T * D * 4);
   L.total = align256(off);
   return L;
 }

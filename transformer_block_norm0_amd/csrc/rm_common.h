@@ -72,6 +72,8 @@ __device__ __forceinline__ void block_sum256(float (&v)[NV], float* scratch) {
   __syncthreads();
 }
 
-__device__ __forceinline__ float sigmoidf_(float v) { return 1.0f / (1.0f + expf(-v)); }
+// sigmoid(v) = 1 / (1 + exp(-v)) with the hardware exp2 and reciprocal (about
+// 2 ulp); saturates cleanly to 0 and 1 for large |v|.
+__device__ __forceinline__ float sigmoidf_(float v) { return __builtin_amdgcn_rcpf(1.0f + __expf(-v)); }
 
 }  // namespace rm

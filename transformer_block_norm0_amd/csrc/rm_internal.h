@@ -24,7 +24,8 @@ enum KernelId {
   KID_GEMM_DWOUT,     // dwout[t] = hidden^T @ d(out2)
   KID_GEMM_DW1,       // dw1[t] = out1^T @ dZ
   KID_GEMM_DH1,       // d(out1) = dZ @ w1[t]^T + d(out2)
-  KID_TAIL_BWD,       // norm1 backward, inverse token mix, norm0 backward -> dx
+  KID_LN1_BWD,        // norm1 backward (r1 recomputed through the token-mix gather)
+  KID_LN0_BWD,        // token-mix adjoint (gather) + norm0 backward -> dx
   KID_FINALIZE,       // fixed-order sums of parameter-gradient partials
   KID_TOKEN_MIX,      // stand-alone token permutation
   KID_COUNT

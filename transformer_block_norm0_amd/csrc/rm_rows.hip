@@ -1,13 +1,23 @@
 // Row-wise kernels of the RankMixerBlock (LayerNorms, token mixing, gating,
 // and their backward), for gfx950 wave64.  All of them are HBM-bandwidth
-// bound: each reads and writes its rows once and keeps statistics in fp32.
+// bound: each reads and writes its rows once, in 16-byte (or 8-byte) vector
+// chunks, and keeps statistics in fp32.
 //
 // Page 1 of "Subgraph-fusion-based Mega-kernel Generation", section "Exact
 // computation", defines what they compute: outer LayerNorms (eps 1e-3),
 // token mixing (swap the two T axes of a [B,T,T,D/T] view), the residual
 // adds, and the gated inner LayerNorms (eps 1e-5) of the dense subgraph.
+//
+// Two shapes of kernel:
+//   * one wave per row (rows are independent, no parameter gradient): the
+//     forward prologue, gate forward, norm2 forward;
+//   * one thread per vector chunk of the row, a workgroup walking the rows
+//     (b, t) of one group of samples at one token t, with block reductions:
+//     the backward kernels, whose per-column parameter-gradient partial sums
+//     then stay in a few registers per thread.
 #include "rm_common.h"
 #include "rm_internal.h"
+#include "rm_vec.h"
 
 namespace rm {
 
@@ -15,477 +25,730 @@ namespace {
 
 constexpr float EPS_OUTER = 1e-3f;
 constexpr float EPS_INNER = 1e-5f;
-constexpr int QD = 1280 / 64;   // columns per lane when one wave owns a D-wide row (D <= 1280)
-constexpr int QH = 3840 / 256;  // columns per thread when 256 threads own an H-wide row (H <= 3840)
-constexpr int QG = 4096 / 512;  // columns per thread when 512 threads own an H-wide row
+constexpr int MAXD = 1280, MAXH = 3840;
 
 template <typename ST>
 __host__ __device__ __forceinline__ const ST* cptr(const void* p) { return reinterpret_cast<const ST*>(p); }
 
 // ---------------------------------------------------------------------------
-// Forward prologue, one workgroup per sample b:
+// Forward prologue, one workgroup (8 waves) per sample b, one wave per row:
 //   a0 = norm0(x[b]);  r1 = token_mix(a0) + x[b];  out1 = norm1(r1).
-// The token-mixed a0 is never stored: row i of token_mix(a0) gathers column
-// block i of every token j, recomputed from x and norm0's statistics.
-template <typename ST>
-__global__ __launch_bounds__(256) void k_prologue(const ST* __restrict__ x, const ST* __restrict__ g0,
+// Token mixing is a gather: output row i, column c reads token c/S, column
+// i*S + c%S of a0, recomputed from x and norm0's statistics (kept in LDS).
+// N = elements per lane chunk; N > 1 needs D % N == 0 and S % N == 0 so a
+// chunk's gather source is N contiguous, aligned elements.
+template <typename ST, int N>
+__global__ __launch_bounds__(512) void k_prologue(const ST* __restrict__ x, const ST* __restrict__ g0,
                                                   const ST* __restrict__ be0, const ST* __restrict__ g1,
                                                   const ST* __restrict__ be1, ST* __restrict__ h1,
                                                   float* __restrict__ stats, int B, int T, int D) {
+  constexpr int Q = (MAXD + 64 * N - 1) / (64 * N);
   __shared__ float s_mu0[64], s_rs0[64];
   const int b = blockIdx.x;
   const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
-  const long N = (long)B * T;
+  const long NR = (long)B * T;
   const long base = (long)b * T * D;
   const int S = D / T;
-  const float invD = 1.0f / (float)D;
+  const float invS = 1.0f / (float)S, invD = 1.0f / (float)D;
 
-  for (int j = wave; j < T; j += 4) {
-    float v[QD];
+  for (int j = wave; j < T; j += 8) {
+    float v[Q][N];
     float s = 0.f;
 #pragma unroll
-    for (int q = 0; q < QD; ++q) {
-      const int c = lane + 64 * q;
-      v[q] = (c < D) ? ld(x, base + (long)j * D + c) : 0.f;
-      s += v[q];
+    for (int q = 0; q < Q; ++q) {
+      const int c = (lane + 64 * q) * N;
+      if (c < D) {
+        ldv(x + base + (long)j * D + c, v[q]);
+      } else {
+#pragma unroll
+        for (int e = 0; e < N; ++e) v[q][e] = 0.f;
+      }
+#pragma unroll
+      for (int e = 0; e < N; ++e) s += v[q][e];
     }
     const float mean = wave_sum(s) * invD;
     float s2 = 0.f;
 #pragma unroll
-    for (int q = 0; q < QD; ++q) {
-      const int c = lane + 64 * q;
-      const float dd = (c < D) ? v[q] - mean : 0.f;
-      s2 += dd * dd;
+    for (int q = 0; q < Q; ++q) {
+      const int c = (lane + 64 * q) * N;
+      if (c < D) {
+#pragma unroll
+        for (int e = 0; e < N; ++e) {
+          const float dd = v[q][e] - mean;
+          s2 += dd * dd;
+        }
+      }
     }
     const float rstd = rsqrtf(wave_sum(s2) * invD + EPS_OUTER);
     if (lane == 0) {
       s_mu0[j] = mean;
       s_rs0[j] = rstd;
-      stats[ST_MU0 * N + (long)b * T + j] = mean;
-      stats[ST_RS0 * N + (long)b * T + j] = rstd;
+      stats[ST_MU0 * NR + (long)b * T + j] = mean;
+      stats[ST_RS0 * NR + (long)b * T + j] = rstd;
     }
   }
   __syncthreads();
 
-  for (int i = wave; i < T; i += 4) {
-    float r[QD];
+  for (int i = wave; i < T; i += 8) {
+    float r[Q][N];
     float s = 0.f;
 #pragma unroll
-    for (int q = 0; q < QD; ++q) {
-      const int c = lane + 64 * q;
-      float v = 0.f;
+    for (int q = 0; q < Q; ++q) {
+      const int c = (lane + 64 * q) * N;
       if (c < D) {
-        int j, sc;
-        tm_source(i, c, S, j, sc);
-        const float a0 = (ld(x, base + (long)j * D + sc) - s_mu0[j]) * s_rs0[j] * ld(g0, sc) + ld(be0, sc);
-        v = a0 + ld(x, base + (long)i * D + c);
+        const int j = div_small(c, invS);
+        const int sc = i * S + (c - j * S);
+        float a[N], gg[N], bb[N], xi[N];
+        ldv(x + base + (long)j * D + sc, a);
+        ldv(g0 + sc, gg);
+        ldv(be0 + sc, bb);
+        ldv(x + base + (long)i * D + c, xi);
+        const float mu = s_mu0[j], rs = s_rs0[j];
+#pragma unroll
+        for (int e = 0; e < N; ++e) r[q][e] = (a[e] - mu) * rs * gg[e] + bb[e] + xi[e];
+      } else {
+#pragma unroll
+        for (int e = 0; e < N; ++e) r[q][e] = 0.f;
       }
-      r[q] = v;
-      s += v;
+#pragma unroll
+      for (int e = 0; e < N; ++e) s += r[q][e];
     }
     const float mean = wave_sum(s) * invD;
     float s2 = 0.f;
 #pragma unroll
-    for (int q = 0; q < QD; ++q) {
-      const int c = lane + 64 * q;
-      const float dd = (c < D) ? r[q] - mean : 0.f;
-      s2 += dd * dd;
+    for (int q = 0; q < Q; ++q) {
+      const int c = (lane + 64 * q) * N;
+      if (c < D) {
+#pragma unroll
+        for (int e = 0; e < N; ++e) {
+          const float dd = r[q][e] - mean;
+          s2 += dd * dd;
+        }
+      }
     }
     const float rstd = rsqrtf(wave_sum(s2) * invD + EPS_OUTER);
 #pragma unroll
-    for (int q = 0; q < QD; ++q) {
-      const int c = lane + 64 * q;
-      if (c < D) st(h1, base + (long)i * D + c, (r[q] - mean) * rstd * ld(g1, c) + ld(be1, c));
+    for (int q = 0; q < Q; ++q) {
+      const int c = (lane + 64 * q) * N;
+      if (c < D) {
+        float gg[N], bb[N], o[N];
+        ldv(g1 + c, gg);
+        ldv(be1 + c, bb);
+#pragma unroll
+        for (int e = 0; e < N; ++e) o[e] = (r[q][e] - mean) * rstd * gg[e] + bb[e];
+        stv(h1 + base + (long)i * D + c, o);
+      }
     }
     if (lane == 0) {
-      stats[ST_MU1 * N + (long)b * T + i] = mean;
-      stats[ST_RS1 * N + (long)b * T + i] = rstd;
+      stats[ST_MU1 * NR + (long)b * T + i] = mean;
+      stats[ST_RS1 * NR + (long)b * T + i] = rstd;
     }
   }
 }
 
 // ---------------------------------------------------------------------------
-// hidden = LN_x(U) * silu(LN_gate(G)) for one row of Z per workgroup.
-// The statistics are taken from the stored (rounded) Z so that the backward,
-// which re-reads Z, sees the same normalised values.
-template <typename ST>
+// hidden = LN_x(U) * silu(LN_gate(G)).  One workgroup per GATE_ROWS rows of
+// Z, one thread per N-element chunk of U (and the matching chunk of G); the
+// next row's chunks are loaded while the current row is reduced.
+// The statistics come from the stored (rounded) Z, which the backward re-reads.
+// One wave per row; Q = chunks of N elements per lane (Q * 64 * N >= H).
+// Loads use clamped in-bounds addresses and masks instead of branches, so a
+// row's loads are all in flight together.
+template <typename ST, int N, int Q>
 __global__ __launch_bounds__(256) void k_gate_fwd(const ST* __restrict__ Z, const ST* __restrict__ gx,
                                                   const ST* __restrict__ bx, const ST* __restrict__ gg,
                                                   const ST* __restrict__ bg, ST* __restrict__ hid,
-                                                  float* __restrict__ stats, long N, int H) {
-  __shared__ float red[8];
-  const long row = blockIdx.x;
-  const int tid = threadIdx.x;
+                                                  float* __restrict__ stats, long NR, int H) {
+  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+  const long row = (long)blockIdx.x * 4 + wave;
+  if (row >= NR) return;
   const ST* z = Z + row * 2 * H;
   const float invH = 1.0f / (float)H;
-  float u[QH], g[QH];
-  float s[2] = {0.f, 0.f};
+  Raw<ST, N> ru[Q], rg[Q];
 #pragma unroll
-  for (int q = 0; q < QH; ++q) {
-    const int h = tid + 256 * q;
-    u[q] = (h < H) ? ld(z, h) : 0.f;
-    g[q] = (h < H) ? ld(z, H + h) : 0.f;
-    s[0] += u[q];
-    s[1] += g[q];
+  for (int q = 0; q < Q; ++q) {
+    const int c = min((lane + 64 * q) * N, H - N);
+    ldr(z + c, ru[q]);
+    ldr(z + H + c, rg[q]);
   }
-  block_sum256(s, red);
-  const float mu_u = s[0] * invH, mu_g = s[1] * invH;
-  float s2[2] = {0.f, 0.f};
+  float su = 0.f, sg = 0.f;
 #pragma unroll
-  for (int q = 0; q < QH; ++q) {
-    const int h = tid + 256 * q;
-    if (h < H) {
-      const float du = u[q] - mu_u, dg = g[q] - mu_g;
-      s2[0] += du * du;
-      s2[1] += dg * dg;
+  for (int q = 0; q < Q; ++q) {
+    const float m = ((lane + 64 * q) * N < H) ? 1.f : 0.f;
+    float u[N], g[N];
+    unpack(ru[q], u);
+    unpack(rg[q], g);
+#pragma unroll
+    for (int e = 0; e < N; ++e) {
+      su += m * u[e];
+      sg += m * g[e];
     }
   }
-  block_sum256(s2, red);
-  const float rs_u = rsqrtf(s2[0] * invH + EPS_INNER);
-  const float rs_g = rsqrtf(s2[1] * invH + EPS_INNER);
+  const float mu_u = wave_sum(su) * invH, mu_g = wave_sum(sg) * invH;
+  float vu = 0.f, vg = 0.f;
 #pragma unroll
-  for (int q = 0; q < QH; ++q) {
-    const int h = tid + 256 * q;
-    if (h < H) {
-      const float ux = (u[q] - mu_u) * rs_u * ld(gx, h) + ld(bx, h);
-      const float ug = (g[q] - mu_g) * rs_g * ld(gg, h) + ld(bg, h);
-      st(hid, row * H + h, ux * (ug * sigmoidf_(ug)));
+  for (int q = 0; q < Q; ++q) {
+    const float m = ((lane + 64 * q) * N < H) ? 1.f : 0.f;
+    float u[N], g[N];
+    unpack(ru[q], u);
+    unpack(rg[q], g);
+#pragma unroll
+    for (int e = 0; e < N; ++e) {
+      const float du = u[e] - mu_u, dg = g[e] - mu_g;
+      vu += m * du * du;
+      vg += m * dg * dg;
     }
   }
-  if (tid == 0) {
-    stats[ST_MUX * N + row] = mu_u;
-    stats[ST_RSX * N + row] = rs_u;
-    stats[ST_MUG * N + row] = mu_g;
-    stats[ST_RSG * N + row] = rs_g;
+  const float rs_u = rsqrtf(wave_sum(vu) * invH + EPS_INNER);
+  const float rs_g = rsqrtf(wave_sum(vg) * invH + EPS_INNER);
+#pragma unroll
+  for (int q = 0; q < Q; ++q) {
+    const int c = (lane + 64 * q) * N;
+    if (c < H) {
+      float u[N], g[N], cgx[N], cbx[N], cgg[N], cbg[N], o[N];
+      unpack(ru[q], u);
+      unpack(rg[q], g);
+      ldv(gx + c, cgx);
+      ldv(bx + c, cbx);
+      ldv(gg + c, cgg);
+      ldv(bg + c, cbg);
+#pragma unroll
+      for (int e = 0; e < N; ++e) {
+        const float ux = (u[e] - mu_u) * rs_u * cgx[e] + cbx[e];
+        const float ug = (g[e] - mu_g) * rs_g * cgg[e] + cbg[e];
+        o[e] = ux * (ug * sigmoidf_(ug));
+      }
+      stv(hid + row * H + c, o);
+    }
+  }
+  if (lane == 0) {
+    stats[ST_MUX * NR + row] = mu_u;
+    stats[ST_RSX * NR + row] = rs_u;
+    stats[ST_MUG * NR + row] = mu_g;
+    stats[ST_RSG * NR + row] = rs_g;
   }
 }
 
 // ---------------------------------------------------------------------------
 // y = norm2(r2), r2 = out1 + out2 kept in fp32.  One wave per row.
-template <typename ST>
+template <typename ST, int N>
 __global__ __launch_bounds__(256) void k_ln2_fwd(const float* __restrict__ r2, const ST* __restrict__ g2,
                                                  const ST* __restrict__ be2, ST* __restrict__ y,
-                                                 float* __restrict__ stats, long N, int D) {
+                                                 float* __restrict__ stats, long NR, int D) {
+  constexpr int Q = (MAXD + 64 * N - 1) / (64 * N);
   const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
   const long row = (long)blockIdx.x * 4 + wave;
-  if (row >= N) return;
+  if (row >= NR) return;
   const float invD = 1.0f / (float)D;
   const float* r = r2 + row * D;
-  float v[QD];
+  float v[Q][N];
   float s = 0.f;
 #pragma unroll
-  for (int q = 0; q < QD; ++q) {
-    const int c = lane + 64 * q;
-    v[q] = (c < D) ? r[c] : 0.f;
-    s += v[q];
+  for (int q = 0; q < Q; ++q) {
+    const int c = (lane + 64 * q) * N;
+    if (c < D) {
+      ldv(r + c, v[q]);
+    } else {
+#pragma unroll
+      for (int e = 0; e < N; ++e) v[q][e] = 0.f;
+    }
+#pragma unroll
+    for (int e = 0; e < N; ++e) s += v[q][e];
   }
   const float mean = wave_sum(s) * invD;
   float s2 = 0.f;
 #pragma unroll
-  for (int q = 0; q < QD; ++q) {
-    const int c = lane + 64 * q;
-    const float dd = (c < D) ? v[q] - mean : 0.f;
-    s2 += dd * dd;
+  for (int q = 0; q < Q; ++q) {
+    const int c = (lane + 64 * q) * N;
+    if (c < D) {
+#pragma unroll
+      for (int e = 0; e < N; ++e) {
+        const float dd = v[q][e] - mean;
+        s2 += dd * dd;
+      }
+    }
   }
   const float rstd = rsqrtf(wave_sum(s2) * invD + EPS_OUTER);
 #pragma unroll
-  for (int q = 0; q < QD; ++q) {
-    const int c = lane + 64 * q;
-    if (c < D) st(y, row * D + c, (v[q] - mean) * rstd * ld(g2, c) + ld(be2, c));
+  for (int q = 0; q < Q; ++q) {
+    const int c = (lane + 64 * q) * N;
+    if (c < D) {
+      float gg[N], bb[N], o[N];
+      ldv(g2 + c, gg);
+      ldv(be2 + c, bb);
+#pragma unroll
+      for (int e = 0; e < N; ++e) o[e] = (v[q][e] - mean) * rstd * gg[e] + bb[e];
+      stv(y + row * D + c, o);
+    }
   }
   if (lane == 0) {
-    stats[ST_MU2 * N + row] = mean;
-    stats[ST_RS2 * N + row] = rstd;
+    stats[ST_MU2 * NR + row] = mean;
+    stats[ST_RS2 * NR + row] = rstd;
   }
-}
-
-// Adds the four waves' per-column partials (lane-owned columns lane + 64*q)
-// in a fixed order through LDS (4 x D floats) and writes them to out[0, D).
-__device__ __forceinline__ void combine_waves_store(const float (&acc)[QD], float* lds, float* __restrict__ out,
-                                                    int D) {
-  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
-#pragma unroll
-  for (int q = 0; q < QD; ++q) {
-    const int c = lane + 64 * q;
-    if (c < D) lds[wave * D + c] = acc[q];
-  }
-  __syncthreads();
-  for (int c = threadIdx.x; c < D; c += 256)
-    out[c] = (lds[c] + lds[D + c]) + (lds[2 * D + c] + lds[3 * D + c]);
-  __syncthreads();
 }
 
 // ---------------------------------------------------------------------------
-// norm2 backward for the rows (b, t), b in one group of ROWS_PER_GROUP, t fixed:
-//   do2 = rstd2 * (dn - mean(dn) - n2 * mean(dn * n2)),  dn = dy * gamma2.
-// Per-group partial sums: dgamma2 += dy * n2, dbeta2 += dy, dbout[t] += do2.
-template <typename ST>
+// Backward row-group kernels: blockIdx.x = token t, blockIdx.y = group of
+// ROWS_PER_GROUP samples; thread k owns the N-element chunks k, k + blockDim,
+// ... (QC of them) of every row it visits.  Partial sums of parameter
+// gradients over the group's rows are written to part[.][group][t][col].
+
+// The three D-wide backward kernels below use one wave per row: a workgroup
+// of 4 waves walks the rows (b, t) of one group of samples at one token t,
+// wave w taking b = first + w, first + w + 4, ...  Lane l owns the columns
+// (l + 64q) * N; its parameter-gradient partial sums stay in registers and
+// the 4 waves' sums are added in a fixed order through LDS at the end.
+
+// Adds the four waves' per-column partials (lane-owned columns (l + 64q) * N)
+// in a fixed order through LDS (4 x D floats) and writes them to out[0, D).
+template <int N, int Q>
+__device__ __forceinline__ void combine_waves_store(const float (&acc)[Q][N], float* lds, float* __restrict__ out,
+                                                    int D) {
+  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+  __syncthreads();
+#pragma unroll
+  for (int q = 0; q < Q; ++q) {
+    const int c = (lane + 64 * q) * N;
+    if (c < D) stv(lds + wave * D + c, acc[q]);
+  }
+  __syncthreads();
+  for (int c = threadIdx.x; c < D; c += 256) out[c] = (lds[c] + lds[D + c]) + (lds[2 * D + c] + lds[3 * D + c]);
+}
+
+// norm2 backward:  do2 = rstd2 * (dn - mean(dn) - n2 * mean(dn * n2)),  dn = dy * gamma2.
+// Partials: dgamma2 (dy * n2), dbeta2 (dy), dbout[t] (do2).
+template <typename ST, int N, int Q>
 __global__ __launch_bounds__(256) void k_ln2_bwd(const float* __restrict__ r2, const ST* __restrict__ dy,
                                                  const ST* __restrict__ g2, const float* __restrict__ stats,
-                                                 ST* __restrict__ do2, float* __restrict__ part, int B,
-                                                 int T, int D, int nb) {
-  __shared__ float lds[4 * 1280];
+                                                 ST* __restrict__ do2, float* __restrict__ part, int B, int T,
+                                                 int D, int nb) {
+  __shared__ float lds[4 * MAXD];
   const int t = blockIdx.x, grp = blockIdx.y;
   const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
-  const long N = (long)B * T;
+  const long NR = (long)B * T;
   const float invD = 1.0f / (float)D;
-  float pg[QD], pb[QD], po[QD];
+  float pg[Q][N], pb[Q][N], po[Q][N];
 #pragma unroll
-  for (int q = 0; q < QD; ++q) pg[q] = pb[q] = po[q] = 0.f;
+  for (int q = 0; q < Q; ++q)
+#pragma unroll
+    for (int e = 0; e < N; ++e) pg[q][e] = pb[q][e] = po[q][e] = 0.f;
   const int b_end = min(B, (grp + 1) * ROWS_PER_GROUP);
   for (int b = grp * ROWS_PER_GROUP + wave; b < b_end; b += 4) {
     const long row = (long)b * T + t;
-    const float mu = stats[ST_MU2 * N + row], rs = stats[ST_RS2 * N + row];
-    float n2[QD], dn[QD], dyv[QD];
+    const float mu = stats[ST_MU2 * NR + row], rs = stats[ST_RS2 * NR + row];
+    Raw<float, N> rr[Q];
+    Raw<ST, N> rdy[Q], rgm[Q];
+#pragma unroll
+    for (int q = 0; q < Q; ++q) {
+      const int c = min((lane + 64 * q) * N, D - N);
+      ldr(r2 + row * D + c, rr[q]);
+      ldr(dy + row * D + c, rdy[q]);
+      ldr(g2 + c, rgm[q]);
+    }
     float s1 = 0.f, s2 = 0.f;
 #pragma unroll
-    for (int q = 0; q < QD; ++q) {
-      const int c = lane + 64 * q;
-      if (c < D) {
-        n2[q] = (r2[row * D + c] - mu) * rs;
-        dyv[q] = ld(dy, row * D + c);
-        dn[q] = dyv[q] * ld(g2, c);
-      } else {
-        n2[q] = dn[q] = dyv[q] = 0.f;
+    for (int q = 0; q < Q; ++q) {
+      const float m = ((lane + 64 * q) * N < D) ? 1.f : 0.f;
+      float r[N], d[N], gm[N];
+      unpack(rr[q], r);
+      unpack(rdy[q], d);
+      unpack(rgm[q], gm);
+#pragma unroll
+      for (int e = 0; e < N; ++e) {
+        const float n2 = (r[e] - mu) * rs, dn = m * d[e] * gm[e];
+        s1 += dn;
+        s2 += dn * n2;
       }
-      s1 += dn[q];
-      s2 += dn[q] * n2[q];
     }
     const float m1 = wave_sum(s1) * invD, m2 = wave_sum(s2) * invD;
 #pragma unroll
-    for (int q = 0; q < QD; ++q) {
-      const int c = lane + 64 * q;
+    for (int q = 0; q < Q; ++q) {
+      const int c = (lane + 64 * q) * N;
       if (c < D) {
-        const float v = rs * (dn[q] - m1 - n2[q] * m2);
-        st(do2, row * D + c, v);
-        pg[q] += dyv[q] * n2[q];
-        pb[q] += dyv[q];
-        po[q] += v;
+        float r[N], d[N], gm[N], o[N];
+        unpack(rr[q], r);
+        unpack(rdy[q], d);
+        unpack(rgm[q], gm);
+#pragma unroll
+        for (int e = 0; e < N; ++e) {
+          const float n2 = (r[e] - mu) * rs;
+          o[e] = rs * (d[e] * gm[e] - m1 - n2 * m2);
+          pg[q][e] += d[e] * n2;
+          pb[q][e] += d[e];
+          po[q][e] += o[e];
+        }
+        stv(do2 + row * D + c, o);
       }
     }
   }
-  // partial layout: [3][nb][T][D]
   const long blk = (long)nb * T * D;
   float* out = part + ((long)grp * T + t) * D;
-  combine_waves_store(pg, lds, out + 0 * blk, D);
-  combine_waves_store(pb, lds, out + 1 * blk, D);
+  combine_waves_store(pg, lds, out, D);
+  combine_waves_store(pb, lds, out + blk, D);
   combine_waves_store(po, lds, out + 2 * blk, D);
 }
 
-// ---------------------------------------------------------------------------
-// Backward of hidden = LN_x(U) * silu(LN_gate(G)) for the rows (b, t) of one
-// group, t fixed.  512 threads; thread h owns columns h, h+512, ...
+// Backward of hidden = LN_x(U) * silu(LN_gate(G)):
 //   ux = LN_x(U), ug = LN_gate(G), s = sigmoid(ug)
 //   d ux = dh * ug * s,  d ug = dh * ux * s * (1 + ug * (1 - s))
 //   dU = rstd_x * (dnx - mean(dnx) - nx * mean(dnx * nx)),  dnx = d ux * gamma_x   (same for G)
-// Per-group partials: dgamma_x, dbeta_x, dgamma_g, dbeta_g and db1[t] (= sum of dZ).
-template <typename ST>
-__global__ __launch_bounds__(512) void k_gate_bwd(const ST* __restrict__ Z, const ST* __restrict__ dhid,
-                                                  const ST* __restrict__ gx, const ST* __restrict__ bx,
-                                                  const ST* __restrict__ gg, const ST* __restrict__ bg,
-                                                  const float* __restrict__ stats, ST* __restrict__ dZ,
-                                                  float* __restrict__ pgate, float* __restrict__ pb1,
-                                                  int B, int T, int H, int nb) {
-  __shared__ float red[32];
+// Partials: dgamma_x, dbeta_x, dgamma_g, dbeta_g, and db1[t] (the sum of dZ).
+// Rows and affine constants stay packed in registers; the cheap elementwise
+// terms are recomputed after the row reduction instead of being kept live,
+// which keeps occupancy (and loads in flight) high.
+template <typename ST, int N>
+struct GateTerms {
+  float nx[N], ng[N], dux[N], dug[N];
+};
+
+template <typename ST, int N>
+__device__ __forceinline__ void gate_terms(const Raw<ST, N>& ru, const Raw<ST, N>& rg, const Raw<ST, N>& rdh,
+                                           const Raw<ST, N>& rgx, const Raw<ST, N>& rbx, const Raw<ST, N>& rgg,
+                                           const Raw<ST, N>& rbg, float mux, float rsx, float mug, float rsg,
+                                           GateTerms<ST, N>& o) {
+  float u[N], g[N], dh[N], cgx[N], cbx[N], cgg[N], cbg[N];
+  unpack(ru, u);
+  unpack(rg, g);
+  unpack(rdh, dh);
+  unpack(rgx, cgx);
+  unpack(rbx, cbx);
+  unpack(rgg, cgg);
+  unpack(rbg, cbg);
+#pragma unroll
+  for (int e = 0; e < N; ++e) {
+    o.nx[e] = (u[e] - mux) * rsx;
+    o.ng[e] = (g[e] - mug) * rsg;
+    const float ux = o.nx[e] * cgx[e] + cbx[e];
+    const float ug = o.ng[e] * cgg[e] + cbg[e];
+    const float sgm = sigmoidf_(ug);
+    o.dux[e] = dh[e] * ug * sgm;
+    o.dug[e] = dh[e] * ux * sgm * (1.f + ug * (1.f - sgm));
+  }
+}
+
+template <typename ST, int N, int QC>
+struct GateBwdSlot {
+  float st[4];
+  Raw<ST, N> u[QC], g[QC], dh[QC];
+};
+
+// One thread per N-element chunk; RPI rows per iteration are loaded together
+// (straight-line code, clamped in-bounds addresses) and share one block
+// reduction, so several rows' loads are in flight per workgroup.
+template <typename ST, int N, int QC, int MAXT, int RPI>
+__global__ __launch_bounds__(MAXT) void k_gate_bwd(const ST* __restrict__ Z, const ST* __restrict__ dhid,
+                                                   const ST* __restrict__ gx, const ST* __restrict__ bx,
+                                                   const ST* __restrict__ gg, const ST* __restrict__ bg,
+                                                   const float* __restrict__ stats, ST* __restrict__ dZ,
+                                                   float* __restrict__ pgate, float* __restrict__ pb1, int B,
+                                                   int T, int H, int nb) {
+  __shared__ float red[2 * 4 * RPI * 16];
   const int t = blockIdx.x, grp = blockIdx.y;
-  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
-  const long N = (long)B * T;
+  const int nw = blockDim.x >> 6;
+  const long NR = (long)B * T;
   const float invH = 1.0f / (float)H;
-  float agx[QG], abx[QG], agg[QG], abg[QG], au[QG], ag[QG];
-  float cgx[QG], cbx[QG], cgg[QG], cbg[QG];
+  Raw<ST, N> rgx[QC], rbx[QC], rgg[QC], rbg[QC];
+  float agx[QC][N], abx[QC][N], agg[QC][N], abg[QC][N], au[QC][N], ag[QC][N];
+  float msk[QC];
 #pragma unroll
-  for (int q = 0; q < QG; ++q) {
-    agx[q] = abx[q] = agg[q] = abg[q] = au[q] = ag[q] = 0.f;
-    const int h = tid + 512 * q;
-    cgx[q] = (h < H) ? ld(gx, h) : 0.f;
-    cbx[q] = (h < H) ? ld(bx, h) : 0.f;
-    cgg[q] = (h < H) ? ld(gg, h) : 0.f;
-    cbg[q] = (h < H) ? ld(bg, h) : 0.f;
+  for (int k = 0; k < QC; ++k) {
+    const int craw = (threadIdx.x + k * blockDim.x) * N;
+    const int c = min(craw, H - N);
+    msk[k] = craw < H ? 1.f : 0.f;
+#pragma unroll
+    for (int e = 0; e < N; ++e) agx[k][e] = abx[k][e] = agg[k][e] = abg[k][e] = au[k][e] = ag[k][e] = 0.f;
+    ldr(gx + c, rgx[k]);
+    ldr(bx + c, rbx[k]);
+    ldr(gg + c, rgg[k]);
+    ldr(bg + c, rbg[k]);
   }
-  const int b_end = min(B, (grp + 1) * ROWS_PER_GROUP);
-  for (int b = grp * ROWS_PER_GROUP; b < b_end; ++b) {
-    const long row = (long)b * T + t;
-    const float mux = stats[ST_MUX * N + row], rsx = stats[ST_RSX * N + row];
-    const float mug = stats[ST_MUG * N + row], rsg = stats[ST_RSG * N + row];
-    const ST* z = Z + row * 2 * H;
-    float nx[QG], ng[QG], dnx[QG], dng[QG];
-    float s[4] = {0.f, 0.f, 0.f, 0.f};
+  const int b_begin = grp * ROWS_PER_GROUP, b_end = min(B, (grp + 1) * ROWS_PER_GROUP);
+  int parity = 0;
+  for (int b0 = b_begin; b0 < b_end; b0 += RPI) {
+    GateBwdSlot<ST, N, QC> cur[RPI];
+    float valid[RPI];
 #pragma unroll
-    for (int q = 0; q < QG; ++q) {
-      const int h = tid + 512 * q;
-      if (h < H) {
-        nx[q] = (ld(z, h) - mux) * rsx;
-        ng[q] = (ld(z, H + h) - mug) * rsg;
-        const float dh = ld(dhid, row * H + h);
-        const float ux = nx[q] * cgx[q] + cbx[q];
-        const float ug = ng[q] * cgg[q] + cbg[q];
-        const float sg = sigmoidf_(ug);
-        const float dux = dh * ug * sg;
-        const float dug = dh * ux * sg * (1.f + ug * (1.f - sg));
-        agx[q] += dux * nx[q];
-        abx[q] += dux;
-        agg[q] += dug * ng[q];
-        abg[q] += dug;
-        dnx[q] = dux * cgx[q];
-        dng[q] = dug * cgg[q];
-      } else {
-        nx[q] = ng[q] = dnx[q] = dng[q] = 0.f;
-      }
-      s[0] += dnx[q];
-      s[1] += dnx[q] * nx[q];
-      s[2] += dng[q];
-      s[3] += dng[q] * ng[q];
-    }
-    // block reduction over 8 waves, fixed order
+    for (int r = 0; r < RPI; ++r) {
+      const int b = min(b0 + r, b_end - 1);
+      valid[r] = (b0 + r < b_end) ? 1.f : 0.f;
+      const long row = (long)b * T + t;
+      cur[r].st[0] = stats[ST_MUX * NR + row];
+      cur[r].st[1] = stats[ST_RSX * NR + row];
+      cur[r].st[2] = stats[ST_MUG * NR + row];
+      cur[r].st[3] = stats[ST_RSG * NR + row];
 #pragma unroll
-    for (int i = 0; i < 4; ++i) {
-      const float w = wave_sum(s[i]);
-      if (lane == 0) red[i * 8 + wave] = w;
-    }
-    __syncthreads();
-#pragma unroll
-    for (int i = 0; i < 4; ++i) {
-      const float* r = red + i * 8;
-      s[i] = ((r[0] + r[1]) + (r[2] + r[3])) + ((r[4] + r[5]) + (r[6] + r[7]));
-    }
-    __syncthreads();
-    const float m1 = s[0] * invH, m2 = s[1] * invH, m3 = s[2] * invH, m4 = s[3] * invH;
-#pragma unroll
-    for (int q = 0; q < QG; ++q) {
-      const int h = tid + 512 * q;
-      if (h < H) {
-        const float du = rsx * (dnx[q] - m1 - nx[q] * m2);
-        const float dg = rsg * (dng[q] - m3 - ng[q] * m4);
-        st(dZ, row * 2 * H + h, du);
-        st(dZ, row * 2 * H + H + h, dg);
-        au[q] += du;
-        ag[q] += dg;
+      for (int k = 0; k < QC; ++k) {
+        const int c = min((int)((threadIdx.x + k * blockDim.x) * N), H - N);
+        ldr(Z + row * 2 * H + c, cur[r].u[k]);
+        ldr(Z + row * 2 * H + H + c, cur[r].g[k]);
+        ldr(dhid + row * H + c, cur[r].dh[k]);
       }
     }
+    float sm[4 * RPI];
+#pragma unroll
+    for (int r = 0; r < RPI; ++r) {
+      const float mux = cur[r].st[0], rsx = cur[r].st[1], mug = cur[r].st[2], rsg = cur[r].st[3];
+      float s0 = 0.f, s1 = 0.f, s2 = 0.f, s3 = 0.f;
+#pragma unroll
+      for (int k = 0; k < QC; ++k) {
+        GateTerms<ST, N> gt;
+        gate_terms(cur[r].u[k], cur[r].g[k], cur[r].dh[k], rgx[k], rbx[k], rgg[k], rbg[k], mux, rsx, mug, rsg, gt);
+        float cgx[N], cgg[N];
+        unpack(rgx[k], cgx);
+        unpack(rgg[k], cgg);
+        const float w = msk[k] * valid[r];
+#pragma unroll
+        for (int e = 0; e < N; ++e) {
+          const float dux = w * gt.dux[e], dug = w * gt.dug[e];
+          agx[k][e] += dux * gt.nx[e];
+          abx[k][e] += dux;
+          agg[k][e] += dug * gt.ng[e];
+          abg[k][e] += dug;
+          const float dnx = dux * cgx[e], dng = dug * cgg[e];
+          s0 += dnx;
+          s1 += dnx * gt.nx[e];
+          s2 += dng;
+          s3 += dng * gt.ng[e];
+        }
+      }
+      sm[4 * r + 0] = s0;
+      sm[4 * r + 1] = s1;
+      sm[4 * r + 2] = s2;
+      sm[4 * r + 3] = s3;
+    }
+    block_sum(sm, red, nw, parity);
+    parity ^= 1;
+#pragma unroll
+    for (int r = 0; r < RPI; ++r)
+#pragma unroll
+      for (int k = 0; k < QC; ++k) {
+        opaque(cur[r].u[k]);
+        opaque(cur[r].g[k]);
+        opaque(cur[r].dh[k]);
+      }
+#pragma unroll
+    for (int r = 0; r < RPI; ++r) {
+      if (b0 + r < b_end) {
+        const long row = (long)(b0 + r) * T + t;
+        const float mux = cur[r].st[0], rsx = cur[r].st[1], mug = cur[r].st[2], rsg = cur[r].st[3];
+        const float m1 = sm[4 * r] * invH, m2 = sm[4 * r + 1] * invH;
+        const float m3 = sm[4 * r + 2] * invH, m4 = sm[4 * r + 3] * invH;
+#pragma unroll
+        for (int k = 0; k < QC; ++k) {
+          const int c = (threadIdx.x + k * blockDim.x) * N;
+          if (c < H) {
+            GateTerms<ST, N> gt;
+            gate_terms(cur[r].u[k], cur[r].g[k], cur[r].dh[k], rgx[k], rbx[k], rgg[k], rbg[k], mux, rsx, mug, rsg,
+                       gt);
+            float cgx[N], cgg[N], du[N], dg[N];
+            unpack(rgx[k], cgx);
+            unpack(rgg[k], cgg);
+#pragma unroll
+            for (int e = 0; e < N; ++e) {
+              du[e] = rsx * (gt.dux[e] * cgx[e] - m1 - gt.nx[e] * m2);
+              dg[e] = rsg * (gt.dug[e] * cgg[e] - m3 - gt.ng[e] * m4);
+              au[k][e] += du[e];
+              ag[k][e] += dg[e];
+            }
+            stv(dZ + row * 2 * H + c, du);
+            stv(dZ + row * 2 * H + H + c, dg);
+          }
+        }
+      }
+    }
   }
-  // partial layouts: pgate [4][nb][T][H], pb1 [nb][T][2H]
   const long blk = (long)nb * T * H;
   const long o = ((long)grp * T + t) * H;
   const long o1 = ((long)grp * T + t) * 2 * H;
 #pragma unroll
-  for (int q = 0; q < QG; ++q) {
-    const int h = tid + 512 * q;
-    if (h < H) {
-      pgate[0 * blk + o + h] = agx[q];
-      pgate[1 * blk + o + h] = abx[q];
-      pgate[2 * blk + o + h] = agg[q];
-      pgate[3 * blk + o + h] = abg[q];
-      pb1[o1 + h] = au[q];
-      pb1[o1 + H + h] = ag[q];
+  for (int k = 0; k < QC; ++k) {
+    const int c = (threadIdx.x + k * blockDim.x) * N;
+    if (c < H) {
+      stv(pgate + o + c, agx[k]);
+      stv(pgate + blk + o + c, abx[k]);
+      stv(pgate + 2 * blk + o + c, agg[k]);
+      stv(pgate + 3 * blk + o + c, abg[k]);
+      stv(pb1 + o1 + c, au[k]);
+      stv(pb1 + o1 + H + c, ag[k]);
     }
   }
 }
 
-// ---------------------------------------------------------------------------
-// Backward tail, one workgroup per sample b:
-//   phase 1 (rows i): dr1 = norm1 backward of d(out1), with r1 recomputed from x
-//                     through the token-mix gather and norm0's statistics;
-//   phase 2 (rows j): da0 = token_mix(dr1) (the permutation is its own adjoint,
-//                     applied as a gather, never as a copy);
-//                     dx = dr1 + norm0 backward of da0.
-// Per-sample partials: dgamma1, dbeta1, dgamma0, dbeta0.
-template <typename ST>
-__global__ __launch_bounds__(256) void k_tail_bwd(const ST* __restrict__ x, const float* __restrict__ dh1,
-                                                  const ST* __restrict__ g0, const ST* __restrict__ be0,
-                                                  const ST* __restrict__ g1, const float* __restrict__ stats,
-                                                  float* __restrict__ dr1, ST* __restrict__ dx,
-                                                  float* __restrict__ ptail, int B, int T, int D) {
-  __shared__ float s_mu0[64], s_rs0[64];
-  __shared__ float lds[4 * 1280];
-  const int b = blockIdx.x;
-  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
-  const long N = (long)B * T;
-  const long base = (long)b * T * D;
+// norm1 backward:  dr1 = rstd1 * (dn - mean(dn) - n1 * mean(dn * n1)),  dn = d(out1) * gamma1,
+// with r1 = token_mix(norm0(x)) + x recomputed through the token-mix gather.
+// Partials: dgamma1 (d(out1) * n1), dbeta1 (d(out1)).  Row (b, i) with i = t.
+// N > 1 needs S % N == 0 (a chunk's gather source is contiguous).
+template <typename ST, int N, int Q>
+__global__ __launch_bounds__(256) void k_ln1_bwd(const ST* __restrict__ x, const float* __restrict__ dh1,
+                                                 const ST* __restrict__ g0, const ST* __restrict__ be0,
+                                                 const ST* __restrict__ g1, const float* __restrict__ stats,
+                                                 float* __restrict__ dr1, float* __restrict__ part, int B, int T,
+                                                 int D, int nb) {
+  __shared__ float lds[4 * MAXD];
+  const int i = blockIdx.x, grp = blockIdx.y;
+  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+  const long NR = (long)B * T;
   const int S = D / T;
-  const float invD = 1.0f / (float)D;
-  for (int j = tid; j < T; j += 256) {
-    s_mu0[j] = stats[ST_MU0 * N + (long)b * T + j];
-    s_rs0[j] = stats[ST_RS0 * N + (long)b * T + j];
-  }
-  __syncthreads();
-
-  float pg1[QD], pb1[QD], pg0[QD], pb0[QD];
+  const float invS = 1.0f / (float)S, invD = 1.0f / (float)D;
+  float pg[Q][N], pb[Q][N];
+  int src_j[Q], src_c[Q];
 #pragma unroll
-  for (int q = 0; q < QD; ++q) pg1[q] = pb1[q] = pg0[q] = pb0[q] = 0.f;
-
-  for (int i = wave; i < T; i += 4) {
-    const float mu1 = stats[ST_MU1 * N + (long)b * T + i], rs1 = stats[ST_RS1 * N + (long)b * T + i];
-    float n1[QD], dn[QD];
+  for (int q = 0; q < Q; ++q) {
+    const int c = min((lane + 64 * q) * N, D - N);
+    const int j = div_small(c, invS);
+    src_j[q] = j;
+    src_c[q] = i * S + (c - j * S);
+#pragma unroll
+    for (int e = 0; e < N; ++e) pg[q][e] = pb[q][e] = 0.f;
+  }
+  const int b_end = min(B, (grp + 1) * ROWS_PER_GROUP);
+  for (int b = grp * ROWS_PER_GROUP + wave; b < b_end; b += 4) {
+    const long row = (long)b * T + i;
+    const long base = (long)b * T * D;
+    const float mu1 = stats[ST_MU1 * NR + row], rs1 = stats[ST_RS1 * NR + row];
+    Raw<ST, N> ra[Q], rxi[Q];
+    Raw<float, N> rg[Q];
+    float mu0[Q], rs0[Q];
+#pragma unroll
+    for (int q = 0; q < Q; ++q) {
+      const int c = min((lane + 64 * q) * N, D - N);
+      ldr(x + base + (long)src_j[q] * D + src_c[q], ra[q]);
+      ldr(x + base + (long)i * D + c, rxi[q]);
+      ldr(dh1 + row * D + c, rg[q]);
+      mu0[q] = stats[ST_MU0 * NR + (long)b * T + src_j[q]];
+      rs0[q] = stats[ST_RS0 * NR + (long)b * T + src_j[q]];
+    }
+    float n1[Q][N], dn[Q][N];
     float s1 = 0.f, s2 = 0.f;
 #pragma unroll
-    for (int q = 0; q < QD; ++q) {
-      const int c = lane + 64 * q;
-      if (c < D) {
-        int j, sc;
-        tm_source(i, c, S, j, sc);
-        const float a0 = (ld(x, base + (long)j * D + sc) - s_mu0[j]) * s_rs0[j] * ld(g0, sc) + ld(be0, sc);
-        const float r1 = a0 + ld(x, base + (long)i * D + c);
-        n1[q] = (r1 - mu1) * rs1;
-        const float g = dh1[base + (long)i * D + c];
-        dn[q] = g * ld(g1, c);
-        pg1[q] += g * n1[q];
-        pb1[q] += g;
-      } else {
-        n1[q] = dn[q] = 0.f;
+    for (int q = 0; q < Q; ++q) {
+      const int c = min((lane + 64 * q) * N, D - N);
+      const float m = ((lane + 64 * q) * N < D) ? 1.f : 0.f;
+      float a[N], xi[N], gv[N], cg0[N], cb0[N], cg1[N];
+      unpack(ra[q], a);
+      unpack(rxi[q], xi);
+      unpack(rg[q], gv);
+      ldv(g0 + src_c[q], cg0);
+      ldv(be0 + src_c[q], cb0);
+      ldv(g1 + c, cg1);
+#pragma unroll
+      for (int e = 0; e < N; ++e) {
+        const float r1 = (a[e] - mu0[q]) * rs0[q] * cg0[e] + cb0[e] + xi[e];
+        n1[q][e] = (r1 - mu1) * rs1;
+        dn[q][e] = m * gv[e] * cg1[e];
+        s1 += dn[q][e];
+        s2 += dn[q][e] * n1[q][e];
       }
-      s1 += dn[q];
-      s2 += dn[q] * n1[q];
     }
     const float m1 = wave_sum(s1) * invD, m2 = wave_sum(s2) * invD;
 #pragma unroll
-    for (int q = 0; q < QD; ++q) {
-      const int c = lane + 64 * q;
-      if (c < D) dr1[base + (long)i * D + c] = rs1 * (dn[q] - m1 - n1[q] * m2);
+    for (int q = 0; q < Q; ++q) {
+      const int c = (lane + 64 * q) * N;
+      if (c < D) {
+        float gv[N], o[N];
+        unpack(rg[q], gv);
+#pragma unroll
+        for (int e = 0; e < N; ++e) {
+          o[e] = rs1 * (dn[q][e] - m1 - n1[q][e] * m2);
+          pg[q][e] += gv[e] * n1[q][e];
+          pb[q][e] += gv[e];
+        }
+        stv(dr1 + row * D + c, o);
+      }
     }
   }
-  __threadfence();
-  __syncthreads();
+  const long blk = (long)nb * T * D;
+  float* out = part + ((long)grp * T + i) * D;
+  combine_waves_store(pg, lds, out + 2 * blk, D);
+  combine_waves_store(pb, lds, out + 3 * blk, D);
+}
 
-  for (int j = wave; j < T; j += 4) {
-    const float mu0 = s_mu0[j], rs0 = s_rs0[j];
-    float n0[QD], dn[QD];
+// Token-mix adjoint and norm0 backward, row (b, j) with j = t:
+//   da0 = token_mix(dr1)  (a gather: row j, column c reads row c/S, column j*S + c%S)
+//   dx = dr1 + rstd0 * (dn - mean(dn) - n0 * mean(dn * n0)),  dn = da0 * gamma0.
+// Partials: dgamma0 (da0 * n0), dbeta0 (da0).
+template <typename ST, int N, int Q>
+__global__ __launch_bounds__(256) void k_ln0_bwd(const ST* __restrict__ x, const float* __restrict__ dr1,
+                                                 const ST* __restrict__ g0, const float* __restrict__ stats,
+                                                 ST* __restrict__ dx, float* __restrict__ part, int B, int T, int D,
+                                                 int nb) {
+  __shared__ float lds[4 * MAXD];
+  const int j = blockIdx.x, grp = blockIdx.y;
+  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+  const long NR = (long)B * T;
+  const int S = D / T;
+  const float invS = 1.0f / (float)S, invD = 1.0f / (float)D;
+  float pg[Q][N], pb[Q][N];
+  int src_i[Q], src_c[Q];
+#pragma unroll
+  for (int q = 0; q < Q; ++q) {
+    const int c = min((lane + 64 * q) * N, D - N);
+    const int ii = div_small(c, invS);
+    src_i[q] = ii;
+    src_c[q] = j * S + (c - ii * S);
+#pragma unroll
+    for (int e = 0; e < N; ++e) pg[q][e] = pb[q][e] = 0.f;
+  }
+  const int b_end = min(B, (grp + 1) * ROWS_PER_GROUP);
+  for (int b = grp * ROWS_PER_GROUP + wave; b < b_end; b += 4) {
+    const long row = (long)b * T + j;
+    const long base = (long)b * T * D;
+    const float mu0 = stats[ST_MU0 * NR + row], rs0 = stats[ST_RS0 * NR + row];
+    Raw<float, N> rda[Q], rown[Q];
+    Raw<ST, N> rx[Q];
+#pragma unroll
+    for (int q = 0; q < Q; ++q) {
+      const int c = min((lane + 64 * q) * N, D - N);
+      ldr(dr1 + base + (long)src_i[q] * D + src_c[q], rda[q]);
+      ldr(x + row * D + c, rx[q]);
+      ldr(dr1 + row * D + c, rown[q]);
+    }
+    float n0[Q][N], dn[Q][N];
     float s1 = 0.f, s2 = 0.f;
 #pragma unroll
-    for (int q = 0; q < QD; ++q) {
-      const int c = lane + 64 * q;
-      if (c < D) {
-        int i, sc;
-        tm_source(j, c, S, i, sc);
-        const float da0 = dr1[base + (long)i * D + sc];
-        n0[q] = (ld(x, base + (long)j * D + c) - mu0) * rs0;
-        dn[q] = da0 * ld(g0, c);
-        pg0[q] += da0 * n0[q];
-        pb0[q] += da0;
-      } else {
-        n0[q] = dn[q] = 0.f;
+    for (int q = 0; q < Q; ++q) {
+      const int c = min((lane + 64 * q) * N, D - N);
+      const float m = ((lane + 64 * q) * N < D) ? 1.f : 0.f;
+      float da[N], xv[N], cg0[N];
+      unpack(rda[q], da);
+      unpack(rx[q], xv);
+      ldv(g0 + c, cg0);
+#pragma unroll
+      for (int e = 0; e < N; ++e) {
+        n0[q][e] = (xv[e] - mu0) * rs0;
+        dn[q][e] = m * da[e] * cg0[e];
+        s1 += dn[q][e];
+        s2 += dn[q][e] * n0[q][e];
       }
-      s1 += dn[q];
-      s2 += dn[q] * n0[q];
     }
     const float m1 = wave_sum(s1) * invD, m2 = wave_sum(s2) * invD;
 #pragma unroll
-    for (int q = 0; q < QD; ++q) {
-      const int c = lane + 64 * q;
-      if (c < D) st(dx, base + (long)j * D + c, dr1[base + (long)j * D + c] + rs0 * (dn[q] - m1 - n0[q] * m2));
+    for (int q = 0; q < Q; ++q) {
+      const int c = (lane + 64 * q) * N;
+      if (c < D) {
+        float da[N], own[N], o[N];
+        unpack(rda[q], da);
+        unpack(rown[q], own);
+#pragma unroll
+        for (int e = 0; e < N; ++e) {
+          o[e] = own[e] + rs0 * (dn[q][e] - m1 - n0[q][e] * m2);
+          pg[q][e] += da[e] * n0[q][e];
+          pb[q][e] += da[e];
+        }
+        stv(dx + row * D + c, o);
+      }
     }
   }
-
-  // partial layout: [4][B][D]: dgamma0, dbeta0, dgamma1, dbeta1
-  const long blk = (long)B * D;
-  float* out = ptail + (long)b * D;
-  combine_waves_store(pg0, lds, out + 0 * blk, D);
-  combine_waves_store(pb0, lds, out + 1 * blk, D);
-  combine_waves_store(pg1, lds, out + 2 * blk, D);
-  combine_waves_store(pb1, lds, out + 3 * blk, D);
+  const long blk = (long)nb * T * D;
+  float* out = part + ((long)grp * T + j) * D;
+  combine_waves_store(pg, lds, out, D);
+  combine_waves_store(pb, lds, out + blk, D);
 }
 
 // ---------------------------------------------------------------------------
 // Fixed-order column sums of partial rows: out[c] = sum_p part[p * pstride + c].
+// 1024 threads = 16 row lanes x 64 columns; lane r sums rows r, r+16, ... in
+// order, then the 16 lane sums are added in order.
 struct RedJob {
   const float* part;
   long pstride;
@@ -498,18 +761,31 @@ struct RedJobs {
 };
 
 template <typename ST>
-__global__ __launch_bounds__(256) void k_finalize(RedJobs jobs) {
+__global__ __launch_bounds__(1024) void k_finalize(RedJobs jobs) {
+  __shared__ float red[16][64];
   const RedJob job = jobs.j[blockIdx.y];
-  const long c = (long)blockIdx.x * 256 + threadIdx.x;
-  if (c >= job.ncols) return;
-  float total = 0.f;
-  for (int p0 = 0; p0 < job.P; p0 += 16) {
-    float s = 0.f;
-    const int p1 = min(job.P, p0 + 16);
-    for (int p = p0; p < p1; ++p) s += job.part[(long)p * job.pstride + c];
-    total += s;
+  const int cx = threadIdx.x & 63, ry = threadIdx.x >> 6;
+  if ((long)blockIdx.x * 64 >= job.ncols) return;  // whole block leaves together
+  const long c = (long)blockIdx.x * 64 + cx;
+  float s = 0.f;
+  if (c < job.ncols) {
+    const float* p = job.part + c;
+    int r = ry;
+    for (; r + 48 < job.P; r += 64) {
+      const float a = p[(long)r * job.pstride], b = p[(long)(r + 16) * job.pstride];
+      const float d = p[(long)(r + 32) * job.pstride], e = p[(long)(r + 48) * job.pstride];
+      s += (a + b) + (d + e);
+    }
+    for (; r < job.P; r += 16) s += p[(long)r * job.pstride];
   }
-  st(reinterpret_cast<ST*>(job.out), c, total);
+  red[ry][cx] = s;
+  __syncthreads();
+  if (ry == 0 && c < job.ncols) {
+    float t = 0.f;
+#pragma unroll
+    for (int k = 0; k < 16; ++k) t += red[k][cx];
+    st(reinterpret_cast<ST*>(job.out), c, t);
+  }
 }
 
 // ---------------------------------------------------------------------------
@@ -531,35 +807,71 @@ inline ST* wsp(void* ws, size_t off) {
   return reinterpret_cast<ST*>(reinterpret_cast<char*>(ws) + off);
 }
 
+inline unsigned round64(long n) { return (unsigned)((n + 63) / 64 * 64); }
+
+// chunk width of a D-wide row: 4 elements when rows, and (for the token-mix
+// gathers) the S-wide runs, are multiples of 4; else 1.
+inline bool vec4_rows(const rm_dims& d) { return d.D % 4 == 0 && (d.D / d.T) % 4 == 0; }
+
 template <typename ST>
 hipError_t prologue_t(const rm_dims& d, const rm_params& p, const void* x, void* ws, const WsLayout& L,
                       hipStream_t s) {
   prof_begin(KID_PROLOGUE, s);
-  hipLaunchKernelGGL(k_prologue<ST>, dim3(d.B), dim3(256), 0, s, cptr<ST>(x), cptr<ST>(p.ln0_g),
-                     cptr<ST>(p.ln0_b), cptr<ST>(p.ln1_g), cptr<ST>(p.ln1_b), wsp<ST>(ws, L.h1),
-                     wsp<float>(ws, L.stats), d.B, d.T, d.D);
+  if (vec4_rows(d))
+    hipLaunchKernelGGL((k_prologue<ST, 4>), dim3(d.B), dim3(512), 0, s, cptr<ST>(x), cptr<ST>(p.ln0_g),
+                       cptr<ST>(p.ln0_b), cptr<ST>(p.ln1_g), cptr<ST>(p.ln1_b), wsp<ST>(ws, L.h1),
+                       wsp<float>(ws, L.stats), d.B, d.T, d.D);
+  else
+    hipLaunchKernelGGL((k_prologue<ST, 1>), dim3(d.B), dim3(512), 0, s, cptr<ST>(x), cptr<ST>(p.ln0_g),
+                       cptr<ST>(p.ln0_b), cptr<ST>(p.ln1_g), cptr<ST>(p.ln1_b), wsp<ST>(ws, L.h1),
+                       wsp<float>(ws, L.stats), d.B, d.T, d.D);
   prof_end(KID_PROLOGUE, s);
   return hipGetLastError();
 }
 
+template <typename ST, int N, int Q>
+void gate_fwd_launch(const rm_dims& d, const rm_params& p, void* ws, const WsLayout& L, hipStream_t s) {
+  const long NR = (long)d.B * d.T;
+  hipLaunchKernelGGL((k_gate_fwd<ST, N, Q>), dim3((unsigned)((NR + 3) / 4)), dim3(256), 0, s, wsp<ST>(ws, L.z),
+                     cptr<ST>(p.lnx_g), cptr<ST>(p.lnx_b), cptr<ST>(p.lng_g), cptr<ST>(p.lng_b), wsp<ST>(ws, L.hid),
+                     wsp<float>(ws, L.stats), NR, d.k * d.D);
+}
+
 template <typename ST>
 hipError_t gate_fwd_t(const rm_dims& d, const rm_params& p, void* ws, const WsLayout& L, hipStream_t s) {
-  const long N = (long)d.B * d.T;
+  const int H = d.k * d.D;
+  constexpr int NV = 16 / sizeof(ST);
   prof_begin(KID_GATE_FWD, s);
-  hipLaunchKernelGGL(k_gate_fwd<ST>, dim3((unsigned)N), dim3(256), 0, s, wsp<ST>(ws, L.z), cptr<ST>(p.lnx_g),
-                     cptr<ST>(p.lnx_b), cptr<ST>(p.lng_g), cptr<ST>(p.lng_b), wsp<ST>(ws, L.hid),
-                     wsp<float>(ws, L.stats), N, d.k * d.D);
+  if (H % NV == 0) {
+    // the smallest instantiated lane-chunk count covering H
+    const int q = (H + 64 * NV - 1) / (64 * NV);
+    if (q <= 1) gate_fwd_launch<ST, NV, 1>(d, p, ws, L, s);
+    else if (q <= 2) gate_fwd_launch<ST, NV, 2>(d, p, ws, L, s);
+    else if (q <= 3) gate_fwd_launch<ST, NV, 3>(d, p, ws, L, s);
+    else if (q <= 4) gate_fwd_launch<ST, NV, 4>(d, p, ws, L, s);
+    else if (q <= 5) gate_fwd_launch<ST, NV, 5>(d, p, ws, L, s);
+    else if (q <= 6) gate_fwd_launch<ST, NV, 6>(d, p, ws, L, s);
+    else if (q <= 8) gate_fwd_launch<ST, NV, 8>(d, p, ws, L, s);
+    else if (q <= 12) gate_fwd_launch<ST, NV, 12>(d, p, ws, L, s);
+    else gate_fwd_launch<ST, NV, 15>(d, p, ws, L, s);
+  } else {
+    gate_fwd_launch<ST, 1, (MAXH + 63) / 64>(d, p, ws, L, s);
+  }
   prof_end(KID_GATE_FWD, s);
   return hipGetLastError();
 }
 
 template <typename ST>
 hipError_t ln2_fwd_t(const rm_dims& d, const rm_params& p, void* y, void* ws, const WsLayout& L, hipStream_t s) {
-  const long N = (long)d.B * d.T;
+  const long NR = (long)d.B * d.T;
+  const dim3 grid((unsigned)((NR + 3) / 4));
   prof_begin(KID_LN2_FWD, s);
-  hipLaunchKernelGGL(k_ln2_fwd<ST>, dim3((unsigned)((N + 3) / 4)), dim3(256), 0, s, wsp<float>(ws, L.r2),
-                     cptr<ST>(p.ln2_g), cptr<ST>(p.ln2_b), reinterpret_cast<ST*>(y), wsp<float>(ws, L.stats), N,
-                     d.D);
+  if (d.D % 4 == 0)
+    hipLaunchKernelGGL((k_ln2_fwd<ST, 4>), grid, dim3(256), 0, s, wsp<float>(ws, L.r2), cptr<ST>(p.ln2_g),
+                       cptr<ST>(p.ln2_b), reinterpret_cast<ST*>(y), wsp<float>(ws, L.stats), NR, d.D);
+  else
+    hipLaunchKernelGGL((k_ln2_fwd<ST, 1>), grid, dim3(256), 0, s, wsp<float>(ws, L.r2), cptr<ST>(p.ln2_g),
+                       cptr<ST>(p.ln2_b), reinterpret_cast<ST*>(y), wsp<float>(ws, L.stats), NR, d.D);
   prof_end(KID_LN2_FWD, s);
   return hipGetLastError();
 }
@@ -567,10 +879,16 @@ hipError_t ln2_fwd_t(const rm_dims& d, const rm_params& p, void* y, void* ws, co
 template <typename ST>
 hipError_t ln2_bwd_t(const rm_dims& d, const rm_params& p, const void* dy, void* ws, const WsLayout& L,
                      hipStream_t s) {
+  const dim3 grid(d.T, L.nb);
   prof_begin(KID_LN2_BWD, s);
-  hipLaunchKernelGGL(k_ln2_bwd<ST>, dim3(d.T, L.nb), dim3(256), 0, s, wsp<float>(ws, L.r2), cptr<ST>(dy),
-                     cptr<ST>(p.ln2_g), wsp<float>(ws, L.stats), wsp<ST>(ws, L.do2), wsp<float>(ws, L.p_ln2),
-                     d.B, d.T, d.D, L.nb);
+  if (d.D % 4 == 0)
+    hipLaunchKernelGGL((k_ln2_bwd<ST, 4, MAXD / 256>), grid, dim3(256), 0, s, wsp<float>(ws, L.r2), cptr<ST>(dy),
+                       cptr<ST>(p.ln2_g), wsp<float>(ws, L.stats), wsp<ST>(ws, L.do2), wsp<float>(ws, L.p_ln2), d.B,
+                       d.T, d.D, L.nb);
+  else
+    hipLaunchKernelGGL((k_ln2_bwd<ST, 1, MAXD / 64>), grid, dim3(256), 0, s, wsp<float>(ws, L.r2), cptr<ST>(dy),
+                       cptr<ST>(p.ln2_g), wsp<float>(ws, L.stats), wsp<ST>(ws, L.do2), wsp<float>(ws, L.p_ln2), d.B,
+                       d.T, d.D, L.nb);
   prof_end(KID_LN2_BWD, s);
   return hipGetLastError();
 }
@@ -578,12 +896,20 @@ hipError_t ln2_bwd_t(const rm_dims& d, const rm_params& p, const void* dy, void*
 template <typename ST>
 hipError_t gate_bwd_t(const rm_dims& d, const rm_params& p, void* ws, const WsLayout& L, hipStream_t s) {
   const int H = d.k * d.D;
+  constexpr int NV = 16 / sizeof(ST);
   float* pg = wsp<float>(ws, L.p_gate);
   float* pb1 = pg + 4L * L.nb * d.T * H;
+  const dim3 grid(d.T, L.nb);
   prof_begin(KID_GATE_BWD, s);
-  hipLaunchKernelGGL(k_gate_bwd<ST>, dim3(d.T, L.nb), dim3(512), 0, s, wsp<ST>(ws, L.z), wsp<ST>(ws, L.dhid),
-                     cptr<ST>(p.lnx_g), cptr<ST>(p.lnx_b), cptr<ST>(p.lng_g), cptr<ST>(p.lng_b),
-                     wsp<float>(ws, L.stats), wsp<ST>(ws, L.dz), pg, pb1, d.B, d.T, H, L.nb);
+  // 8-byte chunks (4 elements) keep the per-thread partial sums small
+  if (H % 4 == 0)
+    hipLaunchKernelGGL((k_gate_bwd<ST, 4, 1, 1024, 2>), grid, dim3(round64(H / 4)), 0, s, wsp<ST>(ws, L.z),
+                       wsp<ST>(ws, L.dhid), cptr<ST>(p.lnx_g), cptr<ST>(p.lnx_b), cptr<ST>(p.lng_g),
+                       cptr<ST>(p.lng_b), wsp<float>(ws, L.stats), wsp<ST>(ws, L.dz), pg, pb1, d.B, d.T, H, L.nb);
+  else
+    hipLaunchKernelGGL((k_gate_bwd<ST, 1, 8, 512, 1>), grid, dim3(round64((H + 7) / 8)), 0, s, wsp<ST>(ws, L.z),
+                       wsp<ST>(ws, L.dhid), cptr<ST>(p.lnx_g), cptr<ST>(p.lnx_b), cptr<ST>(p.lng_g),
+                       cptr<ST>(p.lng_b), wsp<float>(ws, L.stats), wsp<ST>(ws, L.dz), pg, pb1, d.B, d.T, H, L.nb);
   prof_end(KID_GATE_BWD, s);
   return hipGetLastError();
 }
@@ -591,11 +917,29 @@ hipError_t gate_bwd_t(const rm_dims& d, const rm_params& p, void* ws, const WsLa
 template <typename ST>
 hipError_t tail_bwd_t(const rm_dims& d, const rm_params& p, const void* x, void* dx, void* ws, const WsLayout& L,
                       hipStream_t s) {
-  prof_begin(KID_TAIL_BWD, s);
-  hipLaunchKernelGGL(k_tail_bwd<ST>, dim3(d.B), dim3(256), 0, s, cptr<ST>(x), wsp<float>(ws, L.dh1),
-                     cptr<ST>(p.ln0_g), cptr<ST>(p.ln0_b), cptr<ST>(p.ln1_g), wsp<float>(ws, L.stats),
-                     wsp<float>(ws, L.dr1), reinterpret_cast<ST*>(dx), wsp<float>(ws, L.p_tail), d.B, d.T, d.D);
-  prof_end(KID_TAIL_BWD, s);
+  const dim3 grid(d.T, L.nb);
+  hipError_t e;
+  prof_begin(KID_LN1_BWD, s);
+  if (vec4_rows(d))
+    hipLaunchKernelGGL((k_ln1_bwd<ST, 4, MAXD / 256>), grid, dim3(256), 0, s, cptr<ST>(x), wsp<float>(ws, L.dh1),
+                       cptr<ST>(p.ln0_g), cptr<ST>(p.ln0_b), cptr<ST>(p.ln1_g), wsp<float>(ws, L.stats),
+                       wsp<float>(ws, L.dr1), wsp<float>(ws, L.p_tail), d.B, d.T, d.D, L.nb);
+  else
+    hipLaunchKernelGGL((k_ln1_bwd<ST, 1, MAXD / 64>), grid, dim3(256), 0, s, cptr<ST>(x), wsp<float>(ws, L.dh1),
+                       cptr<ST>(p.ln0_g), cptr<ST>(p.ln0_b), cptr<ST>(p.ln1_g), wsp<float>(ws, L.stats),
+                       wsp<float>(ws, L.dr1), wsp<float>(ws, L.p_tail), d.B, d.T, d.D, L.nb);
+  prof_end(KID_LN1_BWD, s);
+  if ((e = hipGetLastError()) != hipSuccess) return e;
+  prof_begin(KID_LN0_BWD, s);
+  if (vec4_rows(d))
+    hipLaunchKernelGGL((k_ln0_bwd<ST, 4, MAXD / 256>), grid, dim3(256), 0, s, cptr<ST>(x), wsp<float>(ws, L.dr1),
+                       cptr<ST>(p.ln0_g), wsp<float>(ws, L.stats), reinterpret_cast<ST*>(dx),
+                       wsp<float>(ws, L.p_tail), d.B, d.T, d.D, L.nb);
+  else
+    hipLaunchKernelGGL((k_ln0_bwd<ST, 1, MAXD / 64>), grid, dim3(256), 0, s, cptr<ST>(x), wsp<float>(ws, L.dr1),
+                       cptr<ST>(p.ln0_g), wsp<float>(ws, L.stats), reinterpret_cast<ST*>(dx),
+                       wsp<float>(ws, L.p_tail), d.B, d.T, d.D, L.nb);
+  prof_end(KID_LN0_BWD, s);
   return hipGetLastError();
 }
 
@@ -605,7 +949,7 @@ hipError_t finalize_t(const rm_dims& d, const rm_grads& g, void* ws, const WsLay
   const float* pl = wsp<float>(ws, L.p_ln2);
   const float* pg = wsp<float>(ws, L.p_gate);
   const float* pt = wsp<float>(ws, L.p_tail);
-  const long bl = (long)nb * T * D, bg = (long)nb * T * H, bt = (long)d.B * D;
+  const long bl = (long)nb * T * D, bg = (long)nb * T * H;
   RedJobs J;
   J.j[0] = {pl + 0 * bl, D, nb * T, D, g.ln2_g};
   J.j[1] = {pl + 1 * bl, D, nb * T, D, g.ln2_b};
@@ -615,13 +959,13 @@ hipError_t finalize_t(const rm_dims& d, const rm_grads& g, void* ws, const WsLay
   J.j[5] = {pg + 2 * bg, H, nb * T, H, g.lng_g};
   J.j[6] = {pg + 3 * bg, H, nb * T, H, g.lng_b};
   J.j[7] = {pg + 4 * bg, (long)T * 2 * H, nb, T * 2 * H, g.b1};
-  J.j[8] = {pt + 0 * bt, D, d.B, D, g.ln0_g};
-  J.j[9] = {pt + 1 * bt, D, d.B, D, g.ln0_b};
-  J.j[10] = {pt + 2 * bt, D, d.B, D, g.ln1_g};
-  J.j[11] = {pt + 3 * bt, D, d.B, D, g.ln1_b};
+  J.j[8] = {pt + 0 * bl, D, nb * T, D, g.ln0_g};
+  J.j[9] = {pt + 1 * bl, D, nb * T, D, g.ln0_b};
+  J.j[10] = {pt + 2 * bl, D, nb * T, D, g.ln1_g};
+  J.j[11] = {pt + 3 * bl, D, nb * T, D, g.ln1_b};
   const int maxc = T * 2 * H;
   prof_begin(KID_FINALIZE, s);
-  hipLaunchKernelGGL(k_finalize<ST>, dim3((maxc + 255) / 256, 12), dim3(256), 0, s, J);
+  hipLaunchKernelGGL(k_finalize<ST>, dim3((maxc + 63) / 64, 12), dim3(1024), 0, s, J);
   prof_end(KID_FINALIZE, s);
   return hipGetLastError();
 }

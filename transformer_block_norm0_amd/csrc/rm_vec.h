@@ -1,0 +1,176 @@
+// Vector load/store of N consecutive storage elements as fp32 (16-, 8- or
+// 4-byte accesses), plus block reductions for row kernels.
+#pragma once
+
+#include "rm_common.h"
+
+namespace rm {
+
+__device__ __forceinline__ float bf_lo(uint32_t w) { return __uint_as_float(w << 16); }
+__device__ __forceinline__ float bf_hi(uint32_t w) { return __uint_as_float(w & 0xffff0000u); }
+__device__ __forceinline__ uint32_t bf_pack(float a, float b) {
+  return (uint32_t)f32_to_bf16_bits(a) | ((uint32_t)f32_to_bf16_bits(b) << 16);
+}
+
+// p must be aligned to N elements.
+template <int N>
+__device__ __forceinline__ void ldv(const float* __restrict__ p, float (&v)[N]) {
+  if constexpr (N == 1) {
+    v[0] = p[0];
+  } else if constexpr (N == 2) {
+    const float2 a = *reinterpret_cast<const float2*>(p);
+    v[0] = a.x; v[1] = a.y;
+  } else {
+#pragma unroll
+    for (int i = 0; i < N; i += 4) {
+      const float4 a = *reinterpret_cast<const float4*>(p + i);
+      v[i] = a.x; v[i + 1] = a.y; v[i + 2] = a.z; v[i + 3] = a.w;
+    }
+  }
+}
+
+template <int N>
+__device__ __forceinline__ void ldv(const bf16_t* __restrict__ p, float (&v)[N]) {
+  if constexpr (N == 1) {
+    v[0] = to_f32(p[0]);
+  } else if constexpr (N == 2) {
+    const uint32_t a = *reinterpret_cast<const uint32_t*>(p);
+    v[0] = bf_lo(a); v[1] = bf_hi(a);
+  } else if constexpr (N == 4) {
+    const uint2 a = *reinterpret_cast<const uint2*>(p);
+    v[0] = bf_lo(a.x); v[1] = bf_hi(a.x); v[2] = bf_lo(a.y); v[3] = bf_hi(a.y);
+  } else {
+    static_assert(N % 8 == 0, "bf16 vector width");
+#pragma unroll
+    for (int i = 0; i < N; i += 8) {
+      const uint4 a = *reinterpret_cast<const uint4*>(p + i);
+      v[i] = bf_lo(a.x); v[i + 1] = bf_hi(a.x); v[i + 2] = bf_lo(a.y); v[i + 3] = bf_hi(a.y);
+      v[i + 4] = bf_lo(a.z); v[i + 5] = bf_hi(a.z); v[i + 6] = bf_lo(a.w); v[i + 7] = bf_hi(a.w);
+    }
+  }
+}
+
+template <int N>
+__device__ __forceinline__ void stv(float* __restrict__ p, const float (&v)[N]) {
+  if constexpr (N == 1) {
+    p[0] = v[0];
+  } else if constexpr (N == 2) {
+    *reinterpret_cast<float2*>(p) = make_float2(v[0], v[1]);
+  } else {
+#pragma unroll
+    for (int i = 0; i < N; i += 4) *reinterpret_cast<float4*>(p + i) = make_float4(v[i], v[i + 1], v[i + 2], v[i + 3]);
+  }
+}
+
+template <int N>
+__device__ __forceinline__ void stv(bf16_t* __restrict__ p, const float (&v)[N]) {
+  if constexpr (N == 1) {
+    p[0].u = f32_to_bf16_bits(v[0]);
+  } else if constexpr (N == 2) {
+    *reinterpret_cast<uint32_t*>(p) = bf_pack(v[0], v[1]);
+  } else if constexpr (N == 4) {
+    *reinterpret_cast<uint2*>(p) = make_uint2(bf_pack(v[0], v[1]), bf_pack(v[2], v[3]));
+  } else {
+#pragma unroll
+    for (int i = 0; i < N; i += 8)
+      *reinterpret_cast<uint4*>(p + i) = make_uint4(bf_pack(v[i], v[i + 1]), bf_pack(v[i + 2], v[i + 3]),
+                                                    bf_pack(v[i + 4], v[i + 5]), bf_pack(v[i + 6], v[i + 7]));
+  }
+}
+
+// Raw (still packed) storage words of N elements, for prefetching a row
+// without unpacking it into N fp32 registers.
+template <typename ST, int N>
+struct Raw {
+  static constexpr int BYTES = N * (int)sizeof(ST);
+  static constexpr int W = BYTES >= 4 ? BYTES / 4 : 1;
+  uint32_t w[W];
+};
+
+template <typename ST, int N>
+__device__ __forceinline__ void ldr(const ST* __restrict__ p, Raw<ST, N>& r) {
+  constexpr int BYTES = Raw<ST, N>::BYTES;
+  if constexpr (BYTES == 2) {
+    r.w[0] = *reinterpret_cast<const uint16_t*>(p);
+  } else if constexpr (BYTES == 4) {
+    r.w[0] = *reinterpret_cast<const uint32_t*>(p);
+  } else if constexpr (BYTES == 8) {
+    const uint2 a = *reinterpret_cast<const uint2*>(p);
+    r.w[0] = a.x; r.w[1] = a.y;
+  } else {
+#pragma unroll
+    for (int i = 0; i < BYTES / 16; ++i) {
+      const uint4 a = *reinterpret_cast<const uint4*>(reinterpret_cast<const char*>(p) + 16 * i);
+      r.w[4 * i] = a.x; r.w[4 * i + 1] = a.y; r.w[4 * i + 2] = a.z; r.w[4 * i + 3] = a.w;
+    }
+  }
+}
+
+template <typename ST, int N>
+__device__ __forceinline__ void zero_raw(Raw<ST, N>& r) {
+#pragma unroll
+  for (int i = 0; i < Raw<ST, N>::W; ++i) r.w[i] = 0u;
+}
+
+// Hide a value from the optimiser (no code emitted): forces a recomputation
+// after a barrier instead of keeping earlier results alive across it.
+template <typename ST, int N>
+__device__ __forceinline__ void opaque(Raw<ST, N>& r) {
+#pragma unroll
+  for (int i = 0; i < Raw<ST, N>::W; ++i) asm volatile("" : "+v"(r.w[i]));
+}
+
+template <int N>
+__device__ __forceinline__ void unpack(const Raw<float, N>& r, float (&v)[N]) {
+#pragma unroll
+  for (int e = 0; e < N; ++e) v[e] = __uint_as_float(r.w[e]);
+}
+
+template <int N>
+__device__ __forceinline__ void unpack(const Raw<bf16_t, N>& r, float (&v)[N]) {
+  if constexpr (N == 1) {
+    v[0] = bf_lo(r.w[0]);
+  } else {
+#pragma unroll
+    for (int e = 0; e < N; e += 2) {
+      v[e] = bf_lo(r.w[e / 2]);
+      v[e + 1] = bf_hi(r.w[e / 2]);
+    }
+  }
+}
+
+// Workgroup barrier for LDS-only communication: waits for this wave's LDS
+// operations (lgkmcnt(0); gfx9 s_waitcnt encoding with vmcnt/expcnt at their
+// maxima) but not for its outstanding global loads, so row prefetches stay in
+// flight across it.  Not a fence for global memory.
+__device__ __forceinline__ void lds_barrier() {
+  __builtin_amdgcn_s_waitcnt(0xC07F);
+  __builtin_amdgcn_s_barrier();
+}
+
+// Sum NV values over the whole block (nw waves, nw <= 16), fixed order.
+// red: 2 * NV * 16 floats of LDS, used as two alternating halves selected by
+// `parity`, so consecutive calls need only one barrier each.
+template <int NV>
+__device__ __forceinline__ void block_sum(float (&v)[NV], float* red, int nw, int parity) {
+  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+  float* r = red + parity * NV * 16;
+#pragma unroll
+  for (int i = 0; i < NV; ++i) {
+    const float s = wave_sum(v[i]);
+    if (lane == 0) r[i * 16 + wave] = s;
+  }
+  lds_barrier();
+#pragma unroll
+  for (int i = 0; i < NV; ++i) {
+    float t = 0.f;
+    for (int w = 0; w < nw; ++w) t += r[i * 16 + w];
+    v[i] = t;
+  }
+}
+
+// floor(c / S) for 0 <= c < 2^16, 1 <= S <= 1280 (exact: the quotient's
+// fractional part is at least 0.5/S away from an integer).
+__device__ __forceinline__ int div_small(int c, float invS) { return (int)(((float)c + 0.5f) * invS); }
+
+}  // namespace rm
