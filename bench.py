@@ -108,6 +108,8 @@ def main():
     ap.add_argument("--cpu-seconds", type=float, default=10.0)
     ap.add_argument("--no-protocol", action="store_true", help="skip the per-iteration flush protocol pass")
     ap.add_argument("--no-kernel-times", action="store_true", help="skip the event-instrumented pass")
+    ap.add_argument("--copy-calibration-mib", type=int, default=0,
+                    help="run one plain device-to-device copy of this many MiB first (reference for HBM counters)")
     args = ap.parse_args()
 
     if args.gpus != 1:
@@ -132,6 +134,15 @@ def main():
     del case
     torch.cuda.synchronize()
     stream = torch.cuda.current_stream()
+    if args.copy_calibration_mib:
+        n = args.copy_calibration_mib * 1024 * 1024 // 4
+        src = torch.ones(n, dtype=torch.float32, device="cuda")
+        dst = torch.empty_like(src)
+        torch.cuda.synchronize()
+        dst.copy_(src)
+        torch.cuda.synchronize()
+        log(f"calibration copy: {args.copy_calibration_mib} MiB read + {args.copy_calibration_mib} MiB written")
+        del src, dst
 
     def step():
         dc.fwd(stream)

@@ -334,8 +334,12 @@ hipError_t launch_gemm(int dtype, bool a_kmajor, bool b_kmajor, const GemmArgs& 
   const bool vec = (a_cont % vw == 0) && (b_cont % vw == 0) && (g.a_ld % vw == 0) && (g.b_ld % vw == 0) &&
                    (g.a_bs % vw == 0) && (g.b_bs % vw == 0) && aligned16(g.A) && aligned16(g.B);
   prof_begin(kid, s);
-  hipError_t e = dtype == RM_BF16 ? dispatch<bf16_t>(a_kmajor, b_kmajor, g, vec, s)
-                                  : dispatch<float>(a_kmajor, b_kmajor, g, vec, s);
+  hipError_t e;
+  if (gemm256_supported(dtype, a_kmajor, b_kmajor, g))
+    e = launch_gemm256(a_kmajor, b_kmajor, g, s);
+  else
+    e = dtype == RM_BF16 ? dispatch<bf16_t>(a_kmajor, b_kmajor, g, vec, s)
+                         : dispatch<float>(a_kmajor, b_kmajor, g, vec, s);
   prof_end(kid, s);
   return e;
 }

@@ -144,8 +144,10 @@ __device__ __forceinline__ void unpack(const Raw<bf16_t, N>& r, float (&v)[N]) {
 // maxima) but not for its outstanding global loads, so row prefetches stay in
 // flight across it.  Not a fence for global memory.
 __device__ __forceinline__ void lds_barrier() {
+  asm volatile("" ::: "memory");
   __builtin_amdgcn_s_waitcnt(0xC07F);
   __builtin_amdgcn_s_barrier();
+  asm volatile("" ::: "memory");
 }
 
 // Sum NV values over the whole block (nw waves, nw <= 16), fixed order.
