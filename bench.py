@@ -138,7 +138,10 @@ def main():
         n = args.copy_calibration_mib * 1024 * 1024 // 4
         src = torch.ones(n, dtype=torch.float32, device="cuda")
         dst = torch.empty_like(src)
+        evict = torch.empty(1024 * 1024 * 1024 // 4, dtype=torch.float32, device="cuda")
+        evict.fill_(0.0)   # 1 GiB written after src: src is no longer cache-resident when copied
         torch.cuda.synchronize()
+        del evict
         dst.copy_(src)
         torch.cuda.synchronize()
         log(f"calibration copy: {args.copy_calibration_mib} MiB read + {args.copy_calibration_mib} MiB written")

@@ -2,25 +2,32 @@
 //
 // Same contract as the general kernel (GemmArgs; page 1 of "Subgraph-fusion-
 // based Mega-kernel Generation", section "Exact computation": one independent
-// GEMM per token t), for the common case K % 64 == 0 with 16-byte aligned,
-// 8-element-multiple rows.
+// GEMM per token t), for the common case K % 128 == 0, K >= 256, with 16-byte
+// aligned, 8-element-multiple rows.
 //
 //   * 4 waves (2 x 2), each owning a 128 x 128 output tile: 4 x 4 MFMA
 //     v_mfma_f32_32x32x16_bf16 tiles, 256 fp32 accumulators per lane (AGPRs,
 //     one wave per SIMD).  Per 16-deep k step a wave reads 8 KB of operand
 //     fragments from LDS for 16 MFMAs (64 bytes of LDS per clock per CU at
 //     full MFMA rate).
-//   * Operand slabs (64 deep in K) are copied global -> LDS with the gfx950
-//     16-byte direct loads (no register staging), double buffered: the copy of
-//     slab k+1 is issued before the MFMAs of slab k and awaited at the one
-//     barrier per slab.  The two stages are separate LDS objects named
-//     directly (the K loop is unrolled by two), which lets the compiler see
-//     that the copies cannot alias the fragment reads of the other stage.
-//   * K-major operands (row = m or n, 128 contiguous bytes of K) live in LDS
-//     as 128-byte rows whose 16-byte chunks are XOR-swizzled by (row/2)%8; an
+//   * Operand slabs (32 deep in K, 16 KB per operand) are copied global ->
+//     LDS with the gfx950 16-byte direct loads (no register staging) through
+//     four stages, three slabs in flight.  The copies are inline assembly with
+//     explicit wait counts, so the compiler neither waits for them at every
+//     LDS read nor reorders them.
+//   * One barrier per slab, in the middle of it: the second k step's
+//     fragments are read during the first k step's MFMAs, then the barrier
+//     (next slab landed, this slab fully read), the copy into the stage just
+//     freed, and the next slab's first fragments are read during the second
+//     k step's MFMAs.  No LDS latency is exposed inside a tile.
+//   * Persistent: one workgroup per CU walks a range of tiles; the copy
+//     stream continues into the next tile and a tile's results are stored
+//     straight from the accumulators while the next tile's copies land.
+//   * K-major operands (row = m or n, 64 contiguous bytes of K) live in LDS
+//     as 64-byte rows whose 16-byte chunks are XOR-swizzled by (row/4)%4; an
 //     MFMA fragment is one 16-byte read per lane.
 //   * M/N-major operands (the forward weights and both weight-gradient
-//     operands) live in LDS as 64 rows of k, each 256 contiguous m/n values
+//     operands) live in LDS as 32 rows of k, each 256 contiguous m/n values
 //     (512 bytes, 16-byte chunks XOR-swizzled by 4*(k%4), so the 4 k-rows x
 //     4 chunks one half-wave reads cover all 64 banks); a fragment is built by
 //     two ds_read_b64_tr_b16 transposing reads (in each 16-lane group, lane j
@@ -28,11 +35,9 @@
 //     nbase + i for four consecutive k).  No transposed copy of any operand is
 //     ever made.
 //   * Rows past M or N are loaded from a clamped valid address and their
-//     results discarded; K must be a multiple of 128.
+//     results dropped at the store.
 #include "rm_common.h"
 #include "rm_internal.h"
-
-#include <type_traits>
 
 namespace rm {
 namespace {
@@ -41,12 +46,24 @@ typedef __attribute__((__vector_size__(8 * sizeof(__bf16)))) __bf16 bf16x8_t;
 typedef __attribute__((__vector_size__(16 * sizeof(float)))) float f32x16_t;
 typedef short short4_t __attribute__((ext_vector_type(4)));
 typedef short short8_t __attribute__((ext_vector_type(8)));
+typedef uint32_t v2u32 __attribute__((ext_vector_type(2)));
+typedef uint32_t v4u32 __attribute__((ext_vector_type(4)));
+typedef __attribute__((address_space(3))) short4_t lds_short4;
 
 constexpr int BM = 256, BN = 256, BK = 32;
 constexpr int STAGES = 4;
 constexpr int TILE_BYTES = 256 * BK * 2;  // one operand slab: 256 x 32 bf16 = 16 KB
-typedef __attribute__((address_space(3))) short4_t lds_short4;
-typedef __attribute__((address_space(3))) void lds_void;
+constexpr int DMA_PER_SLAB = 8;           // direct loads per slab per wave (A and B pieces)
+// Buffer stores the epilogue issues per tile per wave, unconditionally (lanes
+// outside C get an out-of-range offset, which the buffer unit drops).
+constexpr int EPI_STORES = 64;
+static_assert(EPI_STORES >= 63, "the waits at a tile's start rely on >= 63 newer operations");
+
+// Two fp32 values as packed bf16 (round to nearest even: v_cvt_pk_bf16_f32).
+__device__ __forceinline__ uint32_t bf16_pair(float a, float b) {
+  return (uint32_t)__builtin_bit_cast(unsigned short, (__bf16)a) |
+         ((uint32_t)__builtin_bit_cast(unsigned short, (__bf16)b) << 16);
+}
 
 // K-major slab: 256 rows x 64 bytes (4 chunks of 16 B); chunk swizzled by (row/4)%4
 // so the 16 rows of a fragment read hit 16 distinct 4-bank groups.
@@ -54,12 +71,12 @@ __device__ __forceinline__ int kswz(int row, int chunk) { return row * 64 + ((ch
 // M/N-major slab: 32 k-rows x 512 bytes (32 chunks); chunk swizzled by 4*(k%4).
 __device__ __forceinline__ int mswz(int krow, int chunk) { return krow * 512 + ((chunk ^ ((krow & 3) << 2)) << 4); }
 
-// Loop-invariant element offsets of this thread's four 16-byte pieces of a
-// slab (32-bit: every operand here is far below 2^31 elements).  Instruction
-// i of wave w writes 1 KB of LDS: K-major rows 64w + 16i .. +15 (lane l ->
-// row +l/4, physical chunk l%4), M/N-major k-rows 8w + 2i, +1 (lane l -> k-row
-// +l/32, physical chunk l%32); each lane fetches the logical chunk that the
-// swizzle places there.
+// Loop-invariant byte offsets of this thread's four 16-byte pieces of a slab
+// (32-bit: every operand here spans far less than 4 GB per token).
+// Instruction i of wave w writes 1 KB of LDS: K-major rows 64w + 16i .. +15
+// (lane l -> row +l/4, physical chunk l%4), M/N-major k-rows 8w + 2i, +1
+// (lane l -> k-row +l/32, physical chunk l%32); each lane fetches the logical
+// chunk that the swizzle places there.
 template <bool KMAJ>
 __device__ __forceinline__ void slab_offsets(uint32_t (&off)[4], long ld, int mn0, int MN, int wave, int lane) {
 #pragma unroll
@@ -68,31 +85,32 @@ __device__ __forceinline__ void slab_offsets(uint32_t (&off)[4], long ld, int mn
       const int row = 64 * wave + 16 * i + (lane >> 2);
       const int chunk = (lane & 3) ^ ((row >> 2) & 3);
       const int mn = min(mn0 + row, MN - 1);
-      off[i] = (uint32_t)((long)mn * ld + chunk * 8);
+      off[i] = (uint32_t)(((long)mn * ld + chunk * 8) * 2);
     } else {
       const int krow = 8 * wave + 2 * i + (lane >> 5);
       const int chunk = (lane & 31) ^ ((krow & 3) << 2);
       const int mn = min(mn0 + chunk * 8, MN - 8);
-      off[i] = (uint32_t)((long)krow * ld + mn);
+      off[i] = (uint32_t)(((long)krow * ld + mn) * 2);
     }
   }
 }
 
-// One 16-byte direct global -> LDS load per lane: lane l's bytes land at
-// LDS address lds + 16*l.  Issued through inline assembly so that the
-// compiler's own wait-count bookkeeping ignores it; the pipeline below waits
-// for these loads explicitly (vm_barrier) before any LDS read of their data,
-// and no other vector-memory instruction is in flight meanwhile.
-__device__ __forceinline__ void dma16(const void* gptr, uint32_t lds_addr) {
-  asm volatile("s_mov_b32 m0, %1\n\tglobal_load_lds_dwordx4 %0, off" ::"v"(gptr), "s"(lds_addr) : "memory", "m0");
+// One 16-byte direct global -> LDS load per lane from the uniform base plus
+// this lane's byte offset: lane l's bytes land at LDS address lds + 16*l.
+// Issued through inline assembly so that the compiler's own wait-count
+// bookkeeping ignores it; the pipeline waits for these loads explicitly
+// (sync_slab) before any LDS read of their data.
+__device__ __forceinline__ void dma16(uint32_t voff, const void* sbase, uint32_t lds) {
+  asm volatile("global_load_lds_dwordx4 %0, %1" ::"v"(voff), "s"(sbase), "{m0}"(lds) : "memory");
 }
 
+// LDS byte address of a pointer into a __shared__ object.
 __device__ __forceinline__ uint32_t lds_addr(const char* p) {
-  // low 32 bits of a flat pointer into the LDS aperture are the LDS address
-  return __builtin_amdgcn_readfirstlane((uint32_t)reinterpret_cast<uintptr_t>(p));
+  return (uint32_t)(uintptr_t)((__attribute__((address_space(3))) const char*)p);
 }
 
-// Copy the slab starting at k0 into LDS with 16-byte direct loads.
+// Copy the slab starting at k0 into LDS with 16-byte direct loads (wave is
+// uniform, so the LDS addresses are scalar).
 template <bool KMAJ>
 __device__ __forceinline__ void dma_slab(char* lds, const bf16_t* __restrict__ base, const uint32_t (&off)[4], long ld,
                                          int k0, int wave) {
@@ -100,7 +118,7 @@ __device__ __forceinline__ void dma_slab(char* lds, const bf16_t* __restrict__ b
 #pragma unroll
   for (int i = 0; i < 4; ++i) {
     const int dst = KMAJ ? (64 * wave + 16 * i) * 64 : (8 * wave + 2 * i) * 512;
-    dma16(b + off[i], lds_addr(lds + dst));
+    dma16(off[i], b, lds_addr(lds + dst));
   }
 }
 
@@ -124,218 +142,369 @@ __device__ __forceinline__ bf16x8_t read_frag(const char* lds, int row0, int ks,
   }
 }
 
+// Operand fragments of one 16-deep k step: 4 of A (m blocks), 4 of B (n blocks).
+struct Frags {
+  bf16x8_t a[4], b[4];
+};
+
 template <bool AK, bool BKM>
-__device__ __forceinline__ void read_frags(bf16x8_t (&a)[4], bf16x8_t (&b)[4], const char* a_s, const char* b_s,
-                                           int wm, int wn, int ks, int lane) {
+__device__ __forceinline__ void read_frags(Frags& f, const char* a_s, const char* b_s, int wm, int wn, int ks,
+                                           int lane) {
 #pragma unroll
-  for (int i = 0; i < 4; ++i) a[i] = read_frag<AK>(a_s, wm * 128 + 32 * i, ks, lane);
+  for (int i = 0; i < 4; ++i) f.a[i] = read_frag<AK>(a_s, wm * 128 + 32 * i, ks, lane);
 #pragma unroll
-  for (int j = 0; j < 4; ++j) b[j] = read_frag<BKM>(b_s, wn * 128 + 32 * j, ks, lane);
+  for (int j = 0; j < 4; ++j) f.b[j] = read_frag<BKM>(b_s, wn * 128 + 32 * j, ks, lane);
 }
 
-// MFMAs over one 32-deep slab (2 k steps x 16 MFMAs).  The fragments of the
-// second step are read while the MFMAs of the first issue (one MFMA, one LDS
-// read, alternately).
-template <bool AK, bool BKM>
-__device__ __forceinline__ void slab_mfma(f32x16_t (&acc)[4][4], const char* a_s, const char* b_s, int wm, int wn,
-                                          int lane) {
-  constexpr int NREAD = (AK ? 4 : 8) + (BKM ? 4 : 8);
-  bf16x8_t a0[4], b0[4], a1[4], b1[4];
-  read_frags<AK, BKM>(a0, b0, a_s, b_s, wm, wn, 0, lane);
-  read_frags<AK, BKM>(a1, b1, a_s, b_s, wm, wn, 1, lane);
+// 16 MFMAs of one k step.  The B fragment is the MFMA's first operand, so
+// each 32 x 32 accumulator block holds C transposed: element v of lane l is
+// C[m = l%32][n = 8*(v/4) + 4*(l/32) + v%4], four consecutive n per lane.
+// ZERO: the tile's first k step starts from zero accumulators.
+template <bool ZERO>
+__device__ __forceinline__ void mfma16(f32x16_t (&acc)[4][4], const Frags& f) {
+  const f32x16_t zero = {};
 #pragma unroll
   for (int i = 0; i < 4; ++i)
 #pragma unroll
-    for (int j = 0; j < 4; ++j) acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a0[i], b0[j], acc[i][j], 0, 0, 0);
+    for (int j = 0; j < 4; ++j)
+      acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(f.b[j], f.a[i], ZERO ? zero : acc[i][j], 0, 0, 0);
+}
+
+// Scheduling pattern for 16 MFMAs whose fragments are already in registers,
+// issued together with NREAD LDS reads for a later k step: one MFMA, one
+// read, alternately, then the remaining MFMAs.
+template <int NREAD>
+__device__ __forceinline__ void interleave() {
 #pragma unroll
   for (int k = 0; k < 16; ++k) {
     __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
     if (k < NREAD) __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);
   }
-#pragma unroll
-  for (int i = 0; i < 4; ++i)
-#pragma unroll
-    for (int j = 0; j < 4; ++j) acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a1[i], b1[j], acc[i][j], 0, 0, 0);
 }
 
-// Wait until at most N of this wave's direct loads are outstanding (gfx9
-// s_waitcnt encoding: vmcnt in bits 3:0 and 15:14; expcnt and lgkmcnt left
-// at their maxima), then a workgroup barrier.  After it, every wave's copies
-// older than the newest N are in LDS.
+// Wait until this wave's LDS reads are done and at most N of its
+// vector-memory operations are outstanding (gfx9 s_waitcnt encoding: vmcnt
+// in bits 3:0 and 15:14, expcnt 6:4 left at its maximum, lgkmcnt 11:8 = 0),
+// then a workgroup barrier.  Vector-memory operations complete in issue
+// order, so afterwards every wave's operations older than its newest N are
+// done, and no wave still reads LDS data from before the barrier.
 template <int N>
-__device__ __forceinline__ void vm_barrier() {
+__device__ __forceinline__ void sync_slab() {
+  static_assert(N >= 0 && N <= 63, "vmcnt range");
+  __builtin_amdgcn_sched_barrier(0);
   asm volatile("" ::: "memory");
-  __builtin_amdgcn_s_waitcnt((N & 15) | ((N >> 4) << 14) | 0x0F70);
+  __builtin_amdgcn_s_waitcnt((N & 15) | ((N >> 4) << 14) | 0x0070);
   __builtin_amdgcn_s_barrier();
   asm volatile("" ::: "memory");
-}
-
-// Directly-loaded copies per slab per wave (A and B pieces).
-constexpr int DMA_PER_SLAB = 8;
-
-// One pipeline step: slab k sits in stage s (LDS objects sa, sb); wait for
-// it, then start the copy of slab k + 3 into the stage read one step ago
-// (sa3, sb3), then run its MFMAs.
-template <bool AK, bool BKM>
-__device__ __forceinline__ void pipe_step(f32x16_t (&acc)[4][4], const char* sa, const char* sb, char* sa3, char* sb3,
-                                          int k, int nk, const bf16_t* A, const bf16_t* B, const GemmArgs& g,
-                                          const uint32_t (&offa)[4], const uint32_t (&offb)[4], int wm, int wn,
-                                          int wave, int lane) {
-  // copies still allowed in flight: those of slabs k+1 and k+2 that exist
-  if (k + 2 < nk) vm_barrier<2 * DMA_PER_SLAB>();
-  else if (k + 1 < nk) vm_barrier<DMA_PER_SLAB>();
-  else vm_barrier<0>();
-  if (k + 3 < nk) {
-    dma_slab<AK>(sa3, A, offa, g.a_ld, (k + 3) * BK, wave);
-    dma_slab<BKM>(sb3, B, offb, g.b_ld, (k + 3) * BK, wave);
-  }
   __builtin_amdgcn_sched_barrier(0);
-  slab_mfma<AK, BKM>(acc, sa, sb, wm, wn, lane);
+}
+
+// Raw buffer resource: base, byte extent, gfx9 word 3 with a 32-bit data
+// format (a zero format would disable the access).  Offsets at or beyond the
+// extent read zero / write nothing.
+constexpr int RSRC_WORD3 = 0x00020000;
+constexpr uint32_t OUT_OF_RANGE = 0x80000000u;
+__device__ __forceinline__ __amdgpu_buffer_rsrc_t make_rsrc(const void* base, long bytes) {
+  const int n = (int)min(bytes, 0x7fffffffL);
+  return __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(base), (short)0, n, RSRC_WORD3);
+}
+
+// One tile of the persistent schedule: token, first row, first column.
+struct Tile {
+  int t, m0, n0;
+};
+__device__ __forceinline__ Tile tile_of(int logical, int tiles_m, int per_t) {
+  Tile c;
+  c.t = logical / per_t;
+  const int in_t = logical - c.t * per_t;
+  const int tn = in_t / tiles_m;
+  c.m0 = (in_t - tn * tiles_m) * BM;
+  c.n0 = tn * BN;
+  return c;
+}
+
+// Operand source of one tile: per-token base pointers and this thread's
+// four slab offsets for A and B.
+struct Src {
+  const bf16_t* A;
+  const bf16_t* B;
+  uint32_t offa[4], offb[4];
+};
+template <bool AK, bool BKM>
+__device__ __forceinline__ void tile_src(Src& s, const GemmArgs& g, const Tile& c, int wave, int lane) {
+  s.A = reinterpret_cast<const bf16_t*>(g.A) + (long)c.t * g.a_bs;
+  s.B = reinterpret_cast<const bf16_t*>(g.B) + (long)c.t * g.b_bs;
+  slab_offsets<AK>(s.offa, g.a_ld, c.m0, g.M, wave, lane);
+  slab_offsets<BKM>(s.offb, g.b_ld, c.n0, g.N, wave, lane);
+}
+
+// The tile's 256 bias values (bf16, 512 bytes) copied by wave 0 into a 1 KB
+// LDS area (lanes 32..63 write a second copy); issued just before the tile's
+// first slab, so the wait for that slab covers it.
+__device__ __forceinline__ void dma_bias(char* dst, const GemmArgs& g, const Tile& c, int lane) {
+  const bf16_t* b = reinterpret_cast<const bf16_t*>(g.bias) + (long)c.t * g.bias_bs;
+  const int n = min(c.n0 + 8 * (lane & 31), g.N - 8);
+  dma16((uint32_t)n * 2, b, lds_addr(dst));
 }
 
 template <bool AK, bool BKM>
-__global__ __launch_bounds__(256, 1) void k_gemm256(GemmArgs g) {
-  // four stages, each in LDS objects of their own that are always named
-  // directly (the k loop is unrolled by four), so the compiler can tell which
-  // direct loads feed which fragment reads
-  // stage s = one LDS object holding the A slab then the B slab
-  __shared__ __attribute__((aligned(1024))) char s0[2 * TILE_BYTES];
-  __shared__ __attribute__((aligned(1024))) char s1[2 * TILE_BYTES];
-  __shared__ __attribute__((aligned(1024))) char s2[2 * TILE_BYTES];
-  __shared__ __attribute__((aligned(1024))) char s3[2 * TILE_BYTES];
-  char* const a0 = s0;
-  char* const b0 = s0 + TILE_BYTES;
-  char* const a1 = s1;
-  char* const b1 = s1 + TILE_BYTES;
-  char* const a2 = s2;
-  char* const b2 = s2 + TILE_BYTES;
-  char* const a3 = s3;
-  char* const b3 = s3 + TILE_BYTES;
+__device__ __forceinline__ void dma_pair(char* sa, char* sb, const Src& s, const GemmArgs& g, int kslab, int wave) {
+  dma_slab<AK>(sa, s.A, s.offa, g.a_ld, kslab * BK, wave);
+  dma_slab<BKM>(sb, s.B, s.offb, g.b_ld, kslab * BK, wave);
+}
 
-  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
-  const int wm = wave >> 1, wn = wave & 1;
-
-  // XCD-aware tile numbering (workgroup w runs on XCD w % 8): each XCD gets a
-  // contiguous range of logical tiles, token-major, then N tile, then M tile.
-  const int tiles_m = (g.M + BM - 1) / BM, tiles_n = (g.N + BN - 1) / BN;
-  const int total = tiles_m * tiles_n * g.batch;
-  const int w = blockIdx.x;
-  const int xcd = w & 7, q = total >> 3, rem = total & 7;
-  const int logical = xcd * q + min(xcd, rem) + (w >> 3);
-  const int per_t = tiles_m * tiles_n;
-  const int t = logical / per_t;
-  const int in_t = logical - t * per_t;
-  const int tn = in_t / tiles_m, tm = in_t - tn * tiles_m;
-  const int m0 = tm * BM, n0 = tn * BN;
-
-  const bf16_t* A = reinterpret_cast<const bf16_t*>(g.A) + (long)t * g.a_bs;
-  const bf16_t* B = reinterpret_cast<const bf16_t*>(g.B) + (long)t * g.b_bs;
-
-  f32x16_t acc[4][4];
-#pragma unroll
-  for (int i = 0; i < 4; ++i)
-#pragma unroll
-    for (int j = 0; j < 4; ++j)
-#pragma unroll
-      for (int v = 0; v < 16; ++v) acc[i][j][v] = 0.f;
-
-  uint32_t offa[4], offb[4];
-  slab_offsets<AK>(offa, g.a_ld, m0, g.M, wave, lane);
-  slab_offsets<BKM>(offb, g.b_ld, n0, g.N, wave, lane);
-  const int nk = g.K / BK;  // a multiple of 4: K % 128 == 0
-  dma_slab<AK>(a0, A, offa, g.a_ld, 0, wave);
-  dma_slab<BKM>(b0, B, offb, g.b_ld, 0, wave);
-  dma_slab<AK>(a1, A, offa, g.a_ld, BK, wave);
-  dma_slab<BKM>(b1, B, offb, g.b_ld, BK, wave);
-  dma_slab<AK>(a2, A, offa, g.a_ld, 2 * BK, wave);
-  dma_slab<BKM>(b2, B, offb, g.b_ld, 2 * BK, wave);
-  for (int k = 0; k < nk; k += 4) {
-    pipe_step<AK, BKM>(acc, a0, b0, a3, b3, k, nk, A, B, g, offa, offb, wm, wn, wave, lane);
-    pipe_step<AK, BKM>(acc, a1, b1, a0, b0, k + 1, nk, A, B, g, offa, offb, wm, wn, wave, lane);
-    pipe_step<AK, BKM>(acc, a2, b2, a1, b1, k + 2, nk, A, B, g, offa, offb, wm, wn, wave, lane);
-    pipe_step<AK, BKM>(acc, a3, b3, a2, b2, k + 3, nk, A, B, g, offa, offb, wm, wn, wave, lane);
-  }
-
-  // ---- epilogue ------------------------------------------------------
-  // Each wave stages its 128 x 128 tile through its own LDS area 32 rows at a
-  // time (fp32, rows padded to 136 floats so the two half-waves of an MFMA
-  // output write land in disjoint banks), then writes whole 256-byte row
-  // segments with 16-byte vector stores, adding bias[t] and the residual.
-  // MFMA 32x32 output layout: element v of lane l is (row 8*(v/4) + 4*(l/32) + v%4, column l%32).
-  __syncthreads();  // every wave is done reading the operand stages
-  constexpr int PITCH = 136;
-  float* stage = reinterpret_cast<float*>(wave == 0 ? s0 : wave == 1 ? s1 : wave == 2 ? s2 : s3);
-  const int r32 = lane & 31, hl = lane >> 5;
-  const bf16_t* bias = reinterpret_cast<const bf16_t*>(g.bias);
-  float bv[4];
-#pragma unroll
-  for (int j = 0; j < 4; ++j) {
-    const int col = min(n0 + wn * 128 + 32 * j + r32, g.N - 1);
-    bv[j] = bias ? to_f32(bias[(long)t * g.bias_bs + col]) : 0.f;
-  }
-  const int rsub = lane >> 4;        // write phase: 4 rows per pass
-  const int csub = (lane & 15) * 8;  // 8 consecutive columns per lane
-  const int col0 = n0 + wn * 128 + csub;
+// Tile epilogue straight from the accumulators: v = acc (+ bias) (+ residual),
+// stored as 4 consecutive columns per lane and per (m block, n block, v/4):
+// 8-byte bf16 or 16-byte fp32 buffer stores, EPI_STORES per wave, every one
+// issued (rows past M or columns past N get an out-of-range offset).  One m
+// block at a time (scheduling barriers between blocks), so at most 16
+// residual loads are live at once.
+__device__ __forceinline__ void epilogue(const f32x16_t (&acc)[4][4], const GemmArgs& g, const Tile& c,
+                                         const char* sbias, int wm, int wn, int lane) {
+  const int r = lane & 31, h = lane >> 5;
+  const int mb = c.m0 + wm * 128 + r;  // + 32 i
+  const int nb = wn * 128 + 4 * h;     // + 32 j + 8 q (tile-local)
+  const int esz = g.c_f32 ? 4 : 2;
+  char* cbase = reinterpret_cast<char*>(g.C) + (long)c.t * g.c_bs * esz;
+  const __amdgpu_buffer_rsrc_t crs = make_rsrc(cbase, (long)g.M * g.c_ld * esz);
+  const int rsz = g.res_f32 ? 4 : 2;
+  const char* rbase = g.res ? reinterpret_cast<const char*>(g.res) + (long)c.t * g.res_bs * rsz : cbase;
+  const __amdgpu_buffer_rsrc_t rrs = make_rsrc(rbase, g.res ? (long)g.M * g.res_ld * rsz : 0L);
+  // byte strides (uniform; every per-token offset is below 2^31)
+  const uint32_t cld = (uint32_t)(g.c_ld * esz), rld = (uint32_t)(g.res_ld * rsz);
+  uint32_t boff = lds_addr(sbias) + 2 * nb;
 #pragma unroll
   for (int i = 0; i < 4; ++i) {
+    __builtin_amdgcn_sched_barrier(0);
+    asm volatile("" : "+v"(boff));  // re-read the bias per m block instead of keeping 64 values live
+    const int m = mb + 32 * i;
+    const bool mok = m < g.M;
 #pragma unroll
     for (int j = 0; j < 4; ++j)
 #pragma unroll
-      for (int v = 0; v < 16; ++v) {
-        const int rr = 8 * (v >> 2) + 4 * hl + (v & 3);
-        stage[rr * PITCH + 32 * j + r32] = acc[i][j][v] + bv[j];
-      }
-    __builtin_amdgcn_s_waitcnt(0xC07F);  // lgkmcnt(0): this wave's staging writes are in LDS
+      for (int q = 0; q < 4; ++q) {
+        const int n = c.n0 + nb + 32 * j + 8 * q;
+        const bool ok = mok && n < g.N;  // N % 8 == 0: the 4 columns are all in or all out
+        float v[4];
 #pragma unroll
-    for (int pass = 0; pass < 8; ++pass) {
-      const int rr = 4 * pass + rsub;
-      const int row = m0 + wm * 128 + 32 * i + rr;
-      float vals[8];
-      const float4 lo = *reinterpret_cast<const float4*>(stage + rr * PITCH + csub);
-      const float4 hi = *reinterpret_cast<const float4*>(stage + rr * PITCH + csub + 4);
-      vals[0] = lo.x; vals[1] = lo.y; vals[2] = lo.z; vals[3] = lo.w;
-      vals[4] = hi.x; vals[5] = hi.y; vals[6] = hi.z; vals[7] = hi.w;
-      if (row < g.M && col0 < g.N) {
+        for (int e = 0; e < 4; ++e) v[e] = acc[i][j][4 * q + e];
+        if (g.bias) {
+          const v2u32 w = *reinterpret_cast<const __attribute__((address_space(3))) v2u32*>(
+              (uintptr_t)(boff + 2 * (32 * j + 8 * q)));
+          v[0] += __uint_as_float(w.x << 16);
+          v[1] += __uint_as_float(w.x & 0xffff0000u);
+          v[2] += __uint_as_float(w.y << 16);
+          v[3] += __uint_as_float(w.y & 0xffff0000u);
+        }
         if (g.res) {
-          const long ri = (long)t * g.res_bs + (long)row * g.res_ld + col0;
+          const uint32_t ro = ok ? (uint32_t)m * rld + (uint32_t)n * rsz : OUT_OF_RANGE;
           if (g.res_f32) {
-            const float4 a = *reinterpret_cast<const float4*>(reinterpret_cast<const float*>(g.res) + ri);
-            const float4 b = *reinterpret_cast<const float4*>(reinterpret_cast<const float*>(g.res) + ri + 4);
-            vals[0] += a.x; vals[1] += a.y; vals[2] += a.z; vals[3] += a.w;
-            vals[4] += b.x; vals[5] += b.y; vals[6] += b.z; vals[7] += b.w;
+            const v4u32 a = __builtin_bit_cast(v4u32, __builtin_amdgcn_raw_buffer_load_b128(rrs, ro, 0, 0));
+            v[0] += __uint_as_float(a.x); v[1] += __uint_as_float(a.y);
+            v[2] += __uint_as_float(a.z); v[3] += __uint_as_float(a.w);
           } else {
-            const uint4 a = *reinterpret_cast<const uint4*>(reinterpret_cast<const bf16_t*>(g.res) + ri);
-            const uint32_t w4[4] = {a.x, a.y, a.z, a.w};
-#pragma unroll
-            for (int e = 0; e < 4; ++e) {
-              vals[2 * e] += __uint_as_float(w4[e] << 16);
-              vals[2 * e + 1] += __uint_as_float(w4[e] & 0xffff0000u);
-            }
+            const v2u32 a = __builtin_bit_cast(v2u32, __builtin_amdgcn_raw_buffer_load_b64(rrs, ro, 0, 0));
+            v[0] += __uint_as_float(a.x << 16);
+            v[1] += __uint_as_float(a.x & 0xffff0000u);
+            v[2] += __uint_as_float(a.y << 16);
+            v[3] += __uint_as_float(a.y & 0xffff0000u);
           }
         }
-        const long o = (long)t * g.c_bs + (long)row * g.c_ld + col0;
+        const uint32_t co = ok ? (uint32_t)m * cld + (uint32_t)n * esz : OUT_OF_RANGE;
         if (g.c_f32) {
-          float* c = reinterpret_cast<float*>(g.C) + o;
-          *reinterpret_cast<float4*>(c) = make_float4(vals[0], vals[1], vals[2], vals[3]);
-          *reinterpret_cast<float4*>(c + 4) = make_float4(vals[4], vals[5], vals[6], vals[7]);
+          const v4u32 d = {__float_as_uint(v[0]), __float_as_uint(v[1]), __float_as_uint(v[2]), __float_as_uint(v[3])};
+          __builtin_amdgcn_raw_buffer_store_b128(d, crs, co, 0, 0);
         } else {
-          uint4 pk;
-          pk.x = (uint32_t)f32_to_bf16_bits(vals[0]) | ((uint32_t)f32_to_bf16_bits(vals[1]) << 16);
-          pk.y = (uint32_t)f32_to_bf16_bits(vals[2]) | ((uint32_t)f32_to_bf16_bits(vals[3]) << 16);
-          pk.z = (uint32_t)f32_to_bf16_bits(vals[4]) | ((uint32_t)f32_to_bf16_bits(vals[5]) << 16);
-          pk.w = (uint32_t)f32_to_bf16_bits(vals[6]) | ((uint32_t)f32_to_bf16_bits(vals[7]) << 16);
-          *reinterpret_cast<uint4*>(reinterpret_cast<bf16_t*>(g.C) + o) = pk;
+          const v2u32 d = {bf16_pair(v[0], v[1]), bf16_pair(v[2], v[3])};
+          __builtin_amdgcn_raw_buffer_store_b64(d, crs, co, 0, 0);
         }
       }
-    }
-    __builtin_amdgcn_s_waitcnt(0xC07F);  // staging reads done before the next block overwrites it
   }
+  __builtin_amdgcn_sched_barrier(0);
+}
+
+// Per-step wait selections (operations newer than the awaited slab's
+// copies; see the pipeline description at the kernel).
+enum WaitKind {
+  W_STEADY,  // two later slabs in flight: 2 * DMA_PER_SLAB
+  W_START,   // steps 0..2 of a tile: the previous tile's stores too, unless it is the first tile
+  W_TAIL1,   // awaiting slab nk-2: one later slab of this tile, plus the next tile's first if any
+  W_TAIL2,   // awaiting slab nk-1: the next tile's first two slabs if any
+};
+
+template <int KIND>
+__device__ __forceinline__ void wait_slab(bool first, bool has_next) {
+  if constexpr (KIND == W_STEADY) {
+    sync_slab<2 * DMA_PER_SLAB>();
+  } else if constexpr (KIND == W_START) {
+    if (first) sync_slab<2 * DMA_PER_SLAB>();
+    else sync_slab<63>();
+  } else if constexpr (KIND == W_TAIL1) {
+    if (has_next) sync_slab<2 * DMA_PER_SLAB>();
+    else sync_slab<DMA_PER_SLAB>();
+  } else {
+    if (has_next) sync_slab<2 * DMA_PER_SLAB>();
+    else sync_slab<0>();
+  }
+}
+
+// One slab step.  On entry f0 holds slab k's first-k-step fragments (stage
+// sa/sb).  Reads slab k's second k step into f1 during the first k step's
+// MFMAs; waits for slab k+1 (stage na/nb) and the workgroup; copies slab
+// k+4 (this tile's, DMA == 1, or the next tile's, DMA == 2, when there is
+// one; that tile's bias first) into the stage just freed; reads slab k+1's
+// first k step into f0 during the second k step's MFMAs.
+template <bool AK, bool BKM, bool ZERO, int WAIT, int DMA>
+__device__ __forceinline__ void slab_step(f32x16_t (&acc)[4][4], Frags& f0, Frags& f1, char* sa, char* sb,
+                                          const char* na, const char* nb, int kdma, bool first, bool has_next,
+                                          const GemmArgs& g, const Src& src, const Tile& nt, char* nbias, int wm,
+                                          int wn, int wave, int lane) {
+  constexpr int NR = (AK ? 4 : 8) + (BKM ? 4 : 8);
+  read_frags<AK, BKM>(f1, sa, sb, wm, wn, 1, lane);
+  mfma16<ZERO>(acc, f0);
+  interleave<NR>();
+  wait_slab<WAIT>(first, has_next);
+  if constexpr (DMA == 1) {
+    dma_pair<AK, BKM>(sa, sb, src, g, kdma, wave);
+  } else {
+    if (has_next) {
+      if (kdma == 0 && g.bias && wave == 0) dma_bias(nbias, g, nt, lane);
+      dma_pair<AK, BKM>(sa, sb, src, g, kdma, wave);
+    }
+  }
+  __builtin_amdgcn_sched_barrier(0);
+  read_frags<AK, BKM>(f0, na, nb, wm, wn, 0, lane);
+  mfma16<false>(acc, f1);
+  interleave<NR>();
+}
+
+// Persistent kernel: one workgroup per CU.  Workgroup w runs on XCD w % 8;
+// each XCD owns a contiguous range of logical tiles (token-major, then N
+// tile, then M tile) and its workgroups take every (grid/8)-th tile of it, so
+// the tiles in flight on one XCD share operands in that XCD's L2.
+//
+// Pipeline (slab index s runs on across tiles, stage s % 4; nk % 4 == 0):
+// step k copies slab k+4 after its barrier, so slabs k+2, k+3 are in flight
+// at the wait for slab k+1 (2 * DMA_PER_SLAB newer operations).  The last
+// four steps of a tile copy the next tile's slabs 0..3; the tile's
+// EPI_STORES stores follow, so at the waits of the next tile's steps 0..2
+// at least 64 operations are newer than the awaited slab: vmcnt(63).
+template <bool AK, bool BKM>
+__global__ __launch_bounds__(256, 1) void k_gemm256(GemmArgs g) {
+  // stage s: A slab at sA + s * TILE_BYTES, B slab at sB + s * TILE_BYTES
+  // (one base address per fragment serves all four stages through the
+  // instruction's 16-bit offset); bias tiles double buffered
+  __shared__ __attribute__((aligned(1024))) char sA[STAGES * TILE_BYTES];
+  __shared__ __attribute__((aligned(1024))) char sB[STAGES * TILE_BYTES];
+  __shared__ __attribute__((aligned(1024))) char sbias[2][1024];
+  char* const a0 = sA;
+  char* const b0 = sB;
+  char* const a1 = sA + TILE_BYTES;
+  char* const b1 = sB + TILE_BYTES;
+  char* const a2 = sA + 2 * TILE_BYTES;
+  char* const b2 = sB + 2 * TILE_BYTES;
+  char* const a3 = sA + 3 * TILE_BYTES;
+  char* const b3 = sB + 3 * TILE_BYTES;
+
+  const int tid = threadIdx.x, lane = tid & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);  // uniform per wave: scalar address arithmetic
+  const int wm = wave >> 1, wn = wave & 1;
+
+  const int tiles_m = (g.M + BM - 1) / BM, tiles_n = (g.N + BN - 1) / BN;
+  const int per_t = tiles_m * tiles_n;
+  const int total = per_t * g.batch;
+  const int xcd = blockIdx.x & 7, slot = blockIdx.x >> 3, nslots = gridDim.x >> 3;
+  const int q = total >> 3, rem = total & 7;
+  const int lo = xcd * q + min(xcd, rem), hi = lo + q + (xcd < rem ? 1 : 0);
+  int tile = lo + slot;
+  if (tile >= hi) return;
+
+  Tile ct = tile_of(tile, tiles_m, per_t);
+  Src cur;
+  tile_src<AK, BKM>(cur, g, ct, wave, lane);
+  const int nk = g.K / BK;  // a multiple of 4, at least 8
+  if (g.bias && wave == 0) dma_bias(sbias[0], g, ct, lane);
+  dma_pair<AK, BKM>(a0, b0, cur, g, 0, wave);
+  dma_pair<AK, BKM>(a1, b1, cur, g, 1, wave);
+  dma_pair<AK, BKM>(a2, b2, cur, g, 2, wave);
+  dma_pair<AK, BKM>(a3, b3, cur, g, 3, wave);
+  sync_slab<3 * DMA_PER_SLAB>();
+  Frags f0, f1;
+  read_frags<AK, BKM>(f0, a0, b0, wm, wn, 0, lane);
+
+  f32x16_t acc[4][4];
+  bool first = true;
+  for (int it = 0;; ++it) {
+    const int next = tile + nslots;
+    const bool has_next = next < hi;
+    const Tile nt = tile_of(has_next ? next : tile, tiles_m, per_t);
+    Src nxt;
+    tile_src<AK, BKM>(nxt, g, nt, wave, lane);
+    char* nbias = sbias[(it + 1) & 1];
+
+    // steps 0..3 copy this tile's slabs 4..7 (nk >= 8)
+    slab_step<AK, BKM, true, W_START, 1>(acc, f0, f1, a0, b0, a1, b1, 4, first, has_next, g, cur, nt, nbias, wm, wn,
+                                         wave, lane);
+    slab_step<AK, BKM, false, W_START, 1>(acc, f0, f1, a1, b1, a2, b2, 5, first, has_next, g, cur, nt, nbias, wm, wn,
+                                          wave, lane);
+    slab_step<AK, BKM, false, W_START, 1>(acc, f0, f1, a2, b2, a3, b3, 6, first, has_next, g, cur, nt, nbias, wm, wn,
+                                          wave, lane);
+    slab_step<AK, BKM, false, W_STEADY, 1>(acc, f0, f1, a3, b3, a0, b0, 7, first, has_next, g, cur, nt, nbias, wm,
+                                           wn, wave, lane);
+    // steps 4 .. nk-5 copy slabs 8 .. nk-1
+    for (int k = 4; k < nk - 4; k += 4) {
+      slab_step<AK, BKM, false, W_STEADY, 1>(acc, f0, f1, a0, b0, a1, b1, k + 4, first, has_next, g, cur, nt, nbias,
+                                             wm, wn, wave, lane);
+      slab_step<AK, BKM, false, W_STEADY, 1>(acc, f0, f1, a1, b1, a2, b2, k + 5, first, has_next, g, cur, nt, nbias,
+                                             wm, wn, wave, lane);
+      slab_step<AK, BKM, false, W_STEADY, 1>(acc, f0, f1, a2, b2, a3, b3, k + 6, first, has_next, g, cur, nt, nbias,
+                                             wm, wn, wave, lane);
+      slab_step<AK, BKM, false, W_STEADY, 1>(acc, f0, f1, a3, b3, a0, b0, k + 7, first, has_next, g, cur, nt, nbias,
+                                             wm, wn, wave, lane);
+    }
+    // steps nk-4 .. nk-1 copy the next tile's slabs 0..3 (if any)
+    slab_step<AK, BKM, false, W_STEADY, 2>(acc, f0, f1, a0, b0, a1, b1, 0, first, has_next, g, nxt, nt, nbias, wm, wn,
+                                           wave, lane);
+    slab_step<AK, BKM, false, W_TAIL1, 2>(acc, f0, f1, a1, b1, a2, b2, 1, first, has_next, g, nxt, nt, nbias, wm, wn,
+                                          wave, lane);
+    slab_step<AK, BKM, false, W_TAIL2, 2>(acc, f0, f1, a2, b2, a3, b3, 2, first, has_next, g, nxt, nt, nbias, wm, wn,
+                                          wave, lane);
+    // (without a next tile this step copies nothing and its fragment reads
+    // of stage 0 are stale and unused; the same code on both paths keeps the
+    // accumulators in AGPRs)
+    slab_step<AK, BKM, false, W_STEADY, 2>(acc, f0, f1, a3, b3, a0, b0, 3, first, has_next, g, nxt, nt, nbias, wm, wn,
+                                           wave, lane);
+
+    epilogue(acc, g, ct, sbias[it & 1], wm, wn, lane);
+    if (!has_next) break;
+    tile = next;
+    ct = nt;
+    cur = nxt;
+    first = false;
+  }
+}
+
+int cu_count() {
+  static int cached[64] = {0};
+  int dev = 0;
+  if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= 64) return 256;
+  if (cached[dev] == 0) {
+    int n = 0;
+    if (hipDeviceGetAttribute(&n, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess || n <= 0) n = 256;
+    cached[dev] = n;
+  }
+  return cached[dev];
 }
 
 template <bool AK, bool BKM>
 hipError_t run256(const GemmArgs& g, hipStream_t s) {
   const int tiles = ((g.M + BM - 1) / BM) * ((g.N + BN - 1) / BN) * g.batch;
-  hipLaunchKernelGGL((k_gemm256<AK, BKM>), dim3(tiles), dim3(256), 0, s, g);
+  // one workgroup per CU (its LDS use allows no more), a multiple of 8 (XCDs)
+  int grid = cu_count() & ~7;
+  if (grid < 8) grid = 8;
+  const int need = (tiles + 7) & ~7;
+  if (grid > need) grid = need;
+  hipLaunchKernelGGL((k_gemm256<AK, BKM>), dim3(grid), dim3(256), 0, s, g);
   return hipGetLastError();
 }
 
@@ -344,15 +513,23 @@ hipError_t run256(const GemmArgs& g, hipStream_t s) {
 bool gemm256_supported(int dtype, bool a_kmajor, bool b_kmajor, const GemmArgs& g) {
   if (dtype != RM_BF16) return false;
   if (a_kmajor == false && b_kmajor == true) return false;
-  if (g.K % (STAGES * BK) != 0) return false;
+  if (g.K % (STAGES * BK) != 0 || g.K < 2 * STAGES * BK) return false;
   const long a_cont = a_kmajor ? g.K : g.M, b_cont = b_kmajor ? g.K : g.N;
   if (a_cont % 8 || b_cont % 8 || g.a_ld % 8 || g.b_ld % 8 || g.a_bs % 8 || g.b_bs % 8) return false;
   if ((reinterpret_cast<uintptr_t>(g.A) & 15) || (reinterpret_cast<uintptr_t>(g.B) & 15)) return false;
   if (!a_kmajor && g.M < 8) return false;
   if (!b_kmajor && g.N < 8) return false;
-  // the epilogue writes 8-column vectors
-  if (g.N % 8 || g.c_ld % 8 || g.c_bs % 8 || (reinterpret_cast<uintptr_t>(g.C) & 15)) return false;
-  if (g.res && (g.res_ld % 8 || g.res_bs % 8 || (reinterpret_cast<uintptr_t>(g.res) & 15))) return false;
+  // per-token operand byte offsets fit the 32-bit copy offsets
+  const long a_rows = a_kmajor ? g.M : g.K, b_rows = b_kmajor ? g.N : g.K;
+  if (a_rows * g.a_ld * 2 > 0xffffffffL || b_rows * g.b_ld * 2 > 0xffffffffL) return false;
+  // the epilogue stores 4 columns per lane; a bias tile is copied in 16-byte pieces
+  if (g.N % 8 || g.c_ld % 4 || g.c_bs % 4 || (reinterpret_cast<uintptr_t>(g.C) & 15)) return false;
+  if (g.bias && (g.bias_bs % 8 || (reinterpret_cast<uintptr_t>(g.bias) & 15))) return false;
+  if (g.res && (g.res_ld % 4 || g.res_bs % 4 || (reinterpret_cast<uintptr_t>(g.res) & 15))) return false;
+  // per-token byte offsets of C and the residual fit the 31-bit buffer range
+  const long csz = g.c_f32 ? 4 : 2, rsz = g.res_f32 ? 4 : 2;
+  if ((long)g.M * g.c_ld * csz > 0x7fffffffL) return false;
+  if (g.res && (long)g.M * g.res_ld * rsz > 0x7fffffffL) return false;
   return true;
 }
 
