@@ -19,6 +19,8 @@
 #include "rm_internal.h"
 #include "rm_vec.h"
 
+#include <type_traits>
+
 namespace rm {
 
 namespace {
@@ -574,6 +576,174 @@ __global__ __launch_bounds__(MAXT) void k_gate_bwd(const ST* __restrict__ Z, con
   }
 }
 
+// Gate / SiLU / inner LayerNorm backward for H % 4 == 0: one thread per
+// 4-column chunk of U (and the matching chunk of G and d hidden), one
+// workgroup walking the ROWS_PER_GROUP rows (b, t) of one sample group at one
+// token t.  Rows are prefetched P ahead into a register ring (u, g, d hidden,
+// the row's four inner-LN statistics) with unconditional loads from clamped
+// rows, so they stay in flight across the LDS-only barrier of each row's
+// block reduction.  The per-element terms are kept in registers between the
+// reduction and the dZ computation.  Rows past B get zero weight and
+// out-of-range (dropped) buffer stores.
+//   dux = dh * ug * sigmoid(ug)                  (d of the LN_x output)
+//   dug = dh * ux * sigmoid(ug) * (1 + ug (1 - sigmoid(ug)))
+//   dU  = rsx (dux gx - mean(dux gx) - nx mean(dux gx nx)), same for dG.
+constexpr int RING = 2;
+
+// Raw buffer resource over `bytes` bytes at p (gfx9 word 3: 32-bit data
+// format).  Range checks apply to the per-lane offset only (not the scalar
+// one): a lane offset of 0x80000000 reads zero / drops the store.
+__device__ __forceinline__ __amdgpu_buffer_rsrc_t row_rsrc(const void* p, long bytes) {
+  return __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(p), (short)0, (int)min(bytes, 0x7fffffffL), 0x00020000);
+}
+
+template <typename ST>
+__device__ __forceinline__ void bld4(__amdgpu_buffer_rsrc_t rs, uint32_t voff, uint32_t soff, Raw<ST, 4>& r) {
+  if constexpr (sizeof(ST) == 2) {
+    typedef uint32_t v2u __attribute__((ext_vector_type(2)));
+    const v2u a = __builtin_bit_cast(v2u, __builtin_amdgcn_raw_buffer_load_b64(rs, voff, soff, 0));
+    r.w[0] = a.x; r.w[1] = a.y;
+  } else {
+    typedef uint32_t v4u __attribute__((ext_vector_type(4)));
+    const v4u a = __builtin_bit_cast(v4u, __builtin_amdgcn_raw_buffer_load_b128(rs, voff, soff, 0));
+    r.w[0] = a.x; r.w[1] = a.y; r.w[2] = a.z; r.w[3] = a.w;
+  }
+}
+
+template <typename ST>
+__device__ __forceinline__ void bst4(__amdgpu_buffer_rsrc_t rs, uint32_t voff, uint32_t soff, const float (&v)[4]) {
+  if constexpr (sizeof(ST) == 2) {
+    typedef uint32_t v2u __attribute__((ext_vector_type(2)));
+    const v2u a = {bf_pack(v[0], v[1]), bf_pack(v[2], v[3])};
+    __builtin_amdgcn_raw_buffer_store_b64(a, rs, voff, soff, 0);
+  } else {
+    typedef uint32_t v4u __attribute__((ext_vector_type(4)));
+    const v4u a = {__float_as_uint(v[0]), __float_as_uint(v[1]), __float_as_uint(v[2]), __float_as_uint(v[3])};
+    __builtin_amdgcn_raw_buffer_store_b128(a, rs, voff, soff, 0);
+  }
+}
+
+template <typename ST, int MAXT>
+__global__ __launch_bounds__(MAXT) void k_gate_bwd_ring(const ST* __restrict__ Z, const ST* __restrict__ dhid,
+                                                        const ST* __restrict__ gx, const ST* __restrict__ bx,
+                                                        const ST* __restrict__ gg, const ST* __restrict__ bg,
+                                                        const float* __restrict__ stats, ST* __restrict__ dZ,
+                                                        float* __restrict__ pgate, float* __restrict__ pb1, int B,
+                                                        int T, int H, int nb) {
+  __shared__ float4 red4[2 * 16];
+  __shared__ float4 sst[ROWS_PER_GROUP];
+  constexpr int SZ = (int)sizeof(ST);
+  const int t = blockIdx.x, grp = blockIdx.y;
+  const int nw = blockDim.x >> 6;
+  const long NR = (long)B * T;
+  const float invH = 1.0f / (float)H;
+  const int craw = threadIdx.x * 4;
+  const int c = min(craw, H - 4);
+  const float cm = craw < H ? 1.f : 0.f;
+  float cgx[4], cbx[4], cgg[4], cbg[4];
+  ldv(gx + c, cgx);
+  ldv(bx + c, cbx);
+  ldv(gg + c, cgg);
+  ldv(bg + c, cbg);
+  float agx[4], abx[4], agg[4], abg[4], au[4], ag[4];
+#pragma unroll
+  for (int e = 0; e < 4; ++e) agx[e] = abx[e] = agg[e] = abg[e] = au[e] = ag[e] = 0.f;
+
+  const int b0 = grp * ROWS_PER_GROUP, bl = min(B, b0 + ROWS_PER_GROUP) - 1;
+  // every row access: uniform row offset (scalar) + this thread's column offset
+  const __amdgpu_buffer_rsrc_t zrs = row_rsrc(Z, NR * 2 * H * SZ);
+  const __amdgpu_buffer_rsrc_t hrs = row_rsrc(dhid, NR * H * SZ);
+  const __amdgpu_buffer_rsrc_t drs = row_rsrc(dZ, NR * 2 * H * SZ);
+  const uint32_t vu = (uint32_t)(c * SZ), vg = (uint32_t)((H + c) * SZ);
+  const uint32_t zrow = (uint32_t)(2 * H * SZ), hrow = (uint32_t)(H * SZ);
+
+  // the group's inner-LN statistics (mux, rsx, mug, rsg per row) staged in LDS once
+  for (int i = threadIdx.x; i < 4 * ROWS_PER_GROUP; i += blockDim.x) {
+    const int r = i >> 2, q = i & 3;
+    const long row = (long)min(b0 + r, bl) * T + t;
+    reinterpret_cast<float*>(sst)[i] = stats[(ST_MUX + q) * NR + row];
+  }
+  Raw<ST, 4> ru[RING], rg[RING], rd[RING];
+  auto load_row = [&](int slot, int r) {
+    const uint32_t row = (uint32_t)(min(b0 + r, bl) * T + t);
+    bld4<ST>(zrs, vu, row * zrow, ru[slot]);
+    bld4<ST>(zrs, vg, row * zrow, rg[slot]);
+    bld4<ST>(hrs, vu, row * hrow, rd[slot]);
+  };
+#pragma unroll
+  for (int p = 0; p < RING; ++p) load_row(p, p);
+  __syncthreads();
+
+  // one row: consume ring slot p, refill it with row r + RING (PREFETCH), reduce, store dZ
+  int parity = 0;
+  auto row_step = [&](int p, int r, auto prefetch) {
+    const bool valid = b0 + r <= bl;
+    const float w = valid ? cm : 0.f;
+    const float4 sr = sst[r];
+    const float mux = sr.x, rsx = sr.y, mug = sr.z, rsg = sr.w;
+    float u[4], g[4], dh[4];
+    unpack(ru[p], u);
+    unpack(rg[p], g);
+    unpack(rd[p], dh);
+    const uint32_t row = (uint32_t)(min(b0 + r, bl) * T + t);
+    if constexpr (decltype(prefetch)::value) load_row(p, r + RING);
+    float nx[4], ng[4], dux[4], dug[4];
+    float sm[4] = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+    for (int e = 0; e < 4; ++e) {
+      nx[e] = (u[e] - mux) * rsx;
+      ng[e] = (g[e] - mug) * rsg;
+      const float ux = nx[e] * cgx[e] + cbx[e];
+      const float ug = ng[e] * cgg[e] + cbg[e];
+      const float sgm = sigmoidf_(ug);
+      dux[e] = w * (dh[e] * ug * sgm);
+      dug[e] = w * (dh[e] * ux * sgm * (1.f + ug * (1.f - sgm)));
+      const float dnx = dux[e] * cgx[e], dng = dug[e] * cgg[e];
+      sm[0] += dnx;
+      sm[1] += dnx * nx[e];
+      sm[2] += dng;
+      sm[3] += dng * ng[e];
+      agx[e] += dux[e] * nx[e];
+      abx[e] += dux[e];
+      agg[e] += dug[e] * ng[e];
+      abg[e] += dug[e];
+    }
+    block_sum4(sm, red4, nw, parity);
+    parity ^= 1;
+    const float m1 = sm[0] * invH, m2 = sm[1] * invH, m3 = sm[2] * invH, m4 = sm[3] * invH;
+    float du[4], dg[4];
+#pragma unroll
+    for (int e = 0; e < 4; ++e) {
+      du[e] = rsx * (dux[e] * cgx[e] - m1 - nx[e] * m2);
+      dg[e] = rsg * (dug[e] * cgg[e] - m3 - ng[e] * m4);
+      au[e] += w * du[e];
+      ag[e] += w * dg[e];
+    }
+    const bool sok = valid && craw < H;
+    bst4<ST>(drs, sok ? vu : 0x80000000u, row * zrow, du);
+    bst4<ST>(drs, sok ? vg : 0x80000000u, row * zrow, dg);
+  };
+  static_assert(ROWS_PER_GROUP % RING == 0, "ring divides the row group");
+#pragma unroll 1
+  for (int r0 = 0; r0 < ROWS_PER_GROUP - RING; r0 += RING) {
+#pragma unroll
+    for (int p = 0; p < RING; ++p) row_step(p, r0 + p, std::true_type{});
+  }
+#pragma unroll
+  for (int p = 0; p < RING; ++p) row_step(p, ROWS_PER_GROUP - RING + p, std::false_type{});
+  if (craw < H) {
+    const long blk = (long)nb * T * H;
+    const long o = ((long)grp * T + t) * H;
+    const long o1 = ((long)grp * T + t) * 2 * H;
+    stv(pgate + o + c, agx);
+    stv(pgate + blk + o + c, abx);
+    stv(pgate + 2 * blk + o + c, agg);
+    stv(pgate + 3 * blk + o + c, abg);
+    stv(pb1 + o1 + c, au);
+    stv(pb1 + o1 + H + c, ag);
+  }
+}
+
 // norm1 backward:  dr1 = rstd1 * (dn - mean(dn) - n1 * mean(dn * n1)),  dn = d(out1) * gamma1,
 // with r1 = token_mix(norm0(x)) + x recomputed through the token-mix gather.
 // Partials: dgamma1 (d(out1) * n1), dbeta1 (d(out1)).  Row (b, i) with i = t.
@@ -902,7 +1072,12 @@ hipError_t gate_bwd_t(const rm_dims& d, const rm_params& p, void* ws, const WsLa
   const dim3 grid(d.T, L.nb);
   prof_begin(KID_GATE_BWD, s);
   // 8-byte chunks (4 elements) keep the per-thread partial sums small
-  if (H % 4 == 0)
+  // one workgroup of H/4 threads per row group (up to 640: 10 waves, room for the prefetch ring)
+  if (H % 4 == 0 && H <= 2560 && 2L * d.B * d.T * H * (long)sizeof(ST) <= 0x7fffffffL)
+    hipLaunchKernelGGL((k_gate_bwd_ring<ST, 640>), grid, dim3(round64(H / 4)), 0, s, wsp<ST>(ws, L.z),
+                       wsp<ST>(ws, L.dhid), cptr<ST>(p.lnx_g), cptr<ST>(p.lnx_b), cptr<ST>(p.lng_g),
+                       cptr<ST>(p.lng_b), wsp<float>(ws, L.stats), wsp<ST>(ws, L.dz), pg, pb1, d.B, d.T, H, L.nb);
+  else if (H % 4 == 0)
     hipLaunchKernelGGL((k_gate_bwd<ST, 4, 1, 1024, 2>), grid, dim3(round64(H / 4)), 0, s, wsp<ST>(ws, L.z),
                        wsp<ST>(ws, L.dhid), cptr<ST>(p.lnx_g), cptr<ST>(p.lnx_b), cptr<ST>(p.lng_g),
                        cptr<ST>(p.lng_b), wsp<float>(ws, L.stats), wsp<ST>(ws, L.dz), pg, pb1, d.B, d.T, H, L.nb);

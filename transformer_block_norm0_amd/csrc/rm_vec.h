@@ -171,6 +171,54 @@ __device__ __forceinline__ void block_sum(float (&v)[NV], float* red, int nw, in
   }
 }
 
+// Sum over the 64 lanes of a wave, result in every lane, without LDS: DPP
+// butterflies inside each 16-lane row (pairs, quads, half-row mirror, row
+// mirror), then the four row sums read from lanes 0, 16, 32, 48.  Fixed order.
+template <int CTRL>
+__device__ __forceinline__ float dpp_mov(float v) {
+  return __builtin_bit_cast(float, __builtin_amdgcn_update_dpp(0, __builtin_bit_cast(int, v), CTRL, 0xF, 0xF, false));
+}
+__device__ __forceinline__ float lane_f(float v, int l) {
+  return __builtin_bit_cast(float, __builtin_amdgcn_readlane(__builtin_bit_cast(int, v), l));
+}
+__device__ __forceinline__ float wave_sum_dpp(float v) {
+  v += dpp_mov<0xB1>(v);   // quad_perm [1,0,3,2]
+  v += dpp_mov<0x4E>(v);   // quad_perm [2,3,0,1]
+  v += dpp_mov<0x141>(v);  // row_half_mirror
+  v += dpp_mov<0x140>(v);  // row_mirror
+  return (lane_f(v, 0) + lane_f(v, 16)) + (lane_f(v, 32) + lane_f(v, 48));
+}
+
+// Sum 4 values over the whole block (nw waves, nw <= 16), fixed order.
+// red: 2 * 16 float4 of LDS, two halves alternating with `parity`, so
+// consecutive calls need one barrier each.  The barrier waits for LDS only.
+__device__ __forceinline__ void block_sum4(float (&v)[4], float4* red, int nw, int parity) {
+  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+  float4 s;
+  s.x = wave_sum_dpp(v[0]);
+  s.y = wave_sum_dpp(v[1]);
+  s.z = wave_sum_dpp(v[2]);
+  s.w = wave_sum_dpp(v[3]);
+  float4* r = red + parity * 16;
+  if (lane == 0) r[wave] = s;
+  // scheduling barriers: no arithmetic of the next row moves above the
+  // barrier (it would keep two rows' temporaries live at once)
+  __builtin_amdgcn_sched_barrier(0);
+  lds_barrier();
+  __builtin_amdgcn_sched_barrier(0);
+  float4 a = r[0];
+  // fully unrolled with a uniform guard: a loop here would keep the caller's
+  // whole row of temporaries live through it
+#pragma unroll
+  for (int w = 1; w < 16; ++w) {
+    if (w < nw) {
+      const float4 b = r[w];
+      a.x += b.x; a.y += b.y; a.z += b.z; a.w += b.w;
+    }
+  }
+  v[0] = a.x; v[1] = a.y; v[2] = a.z; v[3] = a.w;
+}
+
 // floor(c / S) for 0 <= c < 2^16, 1 <= S <= 1280 (exact: the quotient's
 // fractional part is at least 0.5/S away from an integer).
 __device__ __forceinline__ int div_small(int c, float invS) { return (int)(((float)c + 0.5f) * invS); }
