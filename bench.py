@@ -57,13 +57,16 @@ def row_bytes(d, sz):
     B, T, D, H = d.B, d.T, d.D, d.k * d.D
     N = B * T
     nb = (B + 63) // 64
+    p_ln2, p_gate, p_tail = 3 * nb * T * D * 4, (4 * nb * T * H + nb * T * 2 * H) * 4, 4 * nb * T * D * 4
     return {
-        "prologue": N * D * sz * 2 + N * 16,                         # x -> out1, 4 stats
-        "gate_fwd": N * 2 * H * sz + N * H * sz + N * 16,            # Z -> hidden
-        "ln2_fwd": N * D * 4 + N * D * sz + N * 8,                   # r2 (fp32) -> y
-        "ln2_bwd": N * D * 4 + 2 * N * D * sz + 3 * nb * T * D * 4,  # r2, dy -> d(out2), partials
-        "gate_bwd": N * 2 * H * sz + N * H * sz + N * 2 * H * sz + 6 * nb * T * H * 4,  # Z, dhid -> dZ
-        "tail_bwd": N * D * sz + N * D * 4 + N * D * sz + 4 * B * D * 4,  # x, d(out1) -> dx, partials
+        "prologue": N * D * sz * 2 + N * 16,                              # x -> out1, 4 stats
+        "gate_fwd": N * 2 * H * sz + N * H * sz + N * 16,                 # Z -> hidden, 4 stats
+        "ln2_fwd": N * D * 4 + N * D * sz + N * 8,                        # r2 (fp32) -> y
+        "ln2_bwd": N * D * 4 + 2 * N * D * sz + p_ln2,                    # r2, dy -> d(out2), partials
+        "gate_bwd": N * 2 * H * sz + N * H * sz + N * 2 * H * sz + p_gate,  # Z, dhid -> dZ, partials
+        "ln1_bwd": N * D * sz + 2 * N * D * 4 + p_tail // 2,              # x, d(out1) -> dr1, partials
+        "ln0_bwd": N * D * sz + N * D * 4 + N * D * sz + p_tail // 2,     # x, dr1 -> dx, partials
+        "finalize": p_ln2 + p_gate + p_tail,                              # partials -> 14 small gradients
     }
 
 
@@ -279,21 +282,26 @@ def main():
 
 
 def load_traffic(kernel, workload):
-    """HBM bytes per launch measured with rocprofv3 counters, if recorded for this kernel build."""
-    path = os.path.join(ROOT, "profiles", "traffic.json")
+    """HBM bytes per launch of `kernel`, from the rocprofv3 counter summary in profiles/ (FETCH_SIZE and
+    WRITE_SIZE scaled by a calibration copy), or None when there is none or it predates the current kernel
+    sources (source digest mismatch)."""
+    path = os.path.join(ROOT, "profiles", f"hbm_traffic_{workload}.md")
     if not os.path.exists(path):
         return None
-    try:
-        rec = json.load(open(path))
-        ent = rec.get(workload, {}).get(kernel)
-        if not ent:
-            return None
-        from transformer_block_norm0_amd.build import source_digest
-        if ent.get("source_digest") != source_digest():
-            return None
-        return ent["bytes_per_launch"]
-    except Exception:
+    from transformer_block_norm0_amd.build import source_digest
+    digest, total = None, None
+    for line in open(path):
+        if line.startswith("source_digest:"):
+            digest = line.split(":", 1)[1].strip()
+        cells = [c.strip() for c in line.strip().strip("|").split("|")]
+        if len(cells) == 7 and cells[0] == kernel:
+            try:
+                total = int(float(cells[6]))
+            except ValueError:
+                total = None
+    if digest != source_digest():
         return None
+    return total
 
 
 if __name__ == "__main__":

@@ -336,7 +336,7 @@ hipError_t launch_gemm(int dtype, bool a_kmajor, bool b_kmajor, const GemmArgs& 
   prof_begin(kid, s);
   hipError_t e;
   if (gemm256_supported(dtype, a_kmajor, b_kmajor, g))
-    e = launch_gemm256(a_kmajor, b_kmajor, g, s);
+    e = launch_gemm256(a_kmajor, b_kmajor, g, kid, s);
   else
     e = dtype == RM_BF16 ? dispatch<bf16_t>(a_kmajor, b_kmajor, g, vec, s)
                          : dispatch<float>(a_kmajor, b_kmajor, g, vec, s);

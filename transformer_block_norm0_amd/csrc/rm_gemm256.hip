@@ -390,7 +390,7 @@ __device__ __forceinline__ void slab_step(f32x16_t (&acc)[4][4], Frags& f0, Frag
 // EPI_STORES stores follow, so at the waits of the next tile's steps 0..2
 // at least 64 operations are newer than the awaited slab: vmcnt(63).
 template <bool AK, bool BKM>
-__global__ __launch_bounds__(256, 1) void k_gemm256(GemmArgs g) {
+__device__ __forceinline__ void gemm256_body(const GemmArgs& g) {
   // stage s: A slab at sA + s * TILE_BYTES, B slab at sB + s * TILE_BYTES
   // (one base address per fragment serves all four stages through the
   // instruction's 16-bit offset); bias tiles double buffered
@@ -496,15 +496,28 @@ int cu_count() {
   return cached[dev];
 }
 
-template <bool AK, bool BKM>
-hipError_t run256(const GemmArgs& g, hipStream_t s) {
+// One kernel symbol per GEMM of the block, so that profiles name them.
+__global__ __launch_bounds__(256, 1) void gemm_up_bf16(GemmArgs g) { gemm256_body<true, false>(g); }
+__global__ __launch_bounds__(256, 1) void gemm_down_bf16(GemmArgs g) { gemm256_body<true, false>(g); }
+__global__ __launch_bounds__(256, 1) void gemm_dhid_bf16(GemmArgs g) { gemm256_body<true, true>(g); }
+__global__ __launch_bounds__(256, 1) void gemm_dh1_bf16(GemmArgs g) { gemm256_body<true, true>(g); }
+__global__ __launch_bounds__(256, 1) void gemm_dwout_bf16(GemmArgs g) { gemm256_body<false, false>(g); }
+__global__ __launch_bounds__(256, 1) void gemm_dw1_bf16(GemmArgs g) { gemm256_body<false, false>(g); }
+// other callers of the same operand layouts
+__global__ __launch_bounds__(256, 1) void gemm_kn_bf16(GemmArgs g) { gemm256_body<true, false>(g); }
+__global__ __launch_bounds__(256, 1) void gemm_kk_bf16(GemmArgs g) { gemm256_body<true, true>(g); }
+__global__ __launch_bounds__(256, 1) void gemm_mn_bf16(GemmArgs g) { gemm256_body<false, false>(g); }
+
+typedef void (*Gemm256Kernel)(GemmArgs);
+
+hipError_t run256(Gemm256Kernel k, const GemmArgs& g, hipStream_t s) {
   const int tiles = ((g.M + BM - 1) / BM) * ((g.N + BN - 1) / BN) * g.batch;
   // one workgroup per CU (its LDS use allows no more), a multiple of 8 (XCDs)
   int grid = cu_count() & ~7;
   if (grid < 8) grid = 8;
   const int need = (tiles + 7) & ~7;
   if (grid > need) grid = need;
-  hipLaunchKernelGGL((k_gemm256<AK, BKM>), dim3(grid), dim3(256), 0, s, g);
+  hipLaunchKernelGGL(k, dim3(grid), dim3(256), 0, s, g);
   return hipGetLastError();
 }
 
@@ -533,10 +546,12 @@ bool gemm256_supported(int dtype, bool a_kmajor, bool b_kmajor, const GemmArgs& 
   return true;
 }
 
-hipError_t launch_gemm256(bool a_kmajor, bool b_kmajor, const GemmArgs& g, hipStream_t s) {
-  if (a_kmajor && !b_kmajor) return run256<true, false>(g, s);
-  if (a_kmajor && b_kmajor) return run256<true, true>(g, s);
-  return run256<false, false>(g, s);
+hipError_t launch_gemm256(bool a_kmajor, bool b_kmajor, const GemmArgs& g, int kid, hipStream_t s) {
+  if (a_kmajor && !b_kmajor)
+    return run256(kid == KID_GEMM_UP ? gemm_up_bf16 : kid == KID_GEMM_DOWN ? gemm_down_bf16 : gemm_kn_bf16, g, s);
+  if (a_kmajor && b_kmajor)
+    return run256(kid == KID_GEMM_DHID ? gemm_dhid_bf16 : kid == KID_GEMM_DH1 ? gemm_dh1_bf16 : gemm_kk_bf16, g, s);
+  return run256(kid == KID_GEMM_DWOUT ? gemm_dwout_bf16 : kid == KID_GEMM_DW1 ? gemm_dw1_bf16 : gemm_mn_bf16, g, s);
 }
 
 }  // namespace rm

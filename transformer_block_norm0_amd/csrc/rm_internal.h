@@ -71,7 +71,7 @@ hipError_t launch_gemm(int dtype, bool a_kmajor, bool b_kmajor, const GemmArgs& 
                        hipStream_t s);
 // 256x256-tile bf16 kernel (direct-to-LDS loads, transposing LDS reads): shapes it takes
 bool gemm256_supported(int dtype, bool a_kmajor, bool b_kmajor, const GemmArgs& g);
-hipError_t launch_gemm256(bool a_kmajor, bool b_kmajor, const GemmArgs& g, hipStream_t s);
+hipError_t launch_gemm256(bool a_kmajor, bool b_kmajor, const GemmArgs& g, int kid, hipStream_t s);
 
 // ---------------------------------------------------------------------------
 // row kernels
