@@ -50,14 +50,14 @@ typedef uint32_t v2u32 __attribute__((ext_vector_type(2)));
 typedef uint32_t v4u32 __attribute__((ext_vector_type(4)));
 typedef __attribute__((address_space(3))) short4_t lds_short4;
 
-constexpr int BM = 256, BN = 256, BK = 32;
-constexpr int STAGES = 4;
-constexpr int TILE_BYTES = 256 * BK * 2;  // one operand slab: 256 x 32 bf16 = 16 KB
-constexpr int DMA_PER_SLAB = 8;           // direct loads per slab per wave (A and B pieces)
+constexpr int BM = 256, BN = 256, BK = 64;
+constexpr int STAGES = 2;
+constexpr int TILE_BYTES = 256 * BK * 2;  // one operand slab: 256 x 64 bf16 = 32 KB
+constexpr int KSTEPS = BK / 16;           // MFMA k steps per slab
 // Buffer stores the epilogue issues per tile per wave, unconditionally (lanes
 // outside C get an out-of-range offset, which the buffer unit drops).
 constexpr int EPI_STORES = 64;
-static_assert(EPI_STORES >= 63, "the waits at a tile's start rely on >= 63 newer operations");
+static_assert(EPI_STORES >= 63, "the wait at a tile's start relies on >= 63 newer operations");
 
 // Two fp32 values as packed bf16 (round to nearest even: v_cvt_pk_bf16_f32).
 __device__ __forceinline__ uint32_t bf16_pair(float a, float b) {
@@ -65,29 +65,33 @@ __device__ __forceinline__ uint32_t bf16_pair(float a, float b) {
          ((uint32_t)__builtin_bit_cast(unsigned short, (__bf16)b) << 16);
 }
 
-// K-major slab: 256 rows x 64 bytes (4 chunks of 16 B); chunk swizzled by (row/4)%4
-// so the 16 rows of a fragment read hit 16 distinct 4-bank groups.
-__device__ __forceinline__ int kswz(int row, int chunk) { return row * 64 + ((chunk ^ ((row >> 2) & 3)) << 4); }
-// M/N-major slab: 32 k-rows x 512 bytes (32 chunks); chunk swizzled by 4*(k%4).
+// K-major slab: 256 rows x 128 bytes (8 chunks of 16 B, one cache line per
+// row); chunk swizzled by row%8 so the 8 rows one LDS cycle serves hit 8
+// distinct 4-bank groups.
+__device__ __forceinline__ int kswz(int row, int chunk) { return row * 128 + ((chunk ^ (row & 7)) << 4); }
+// M/N-major slab: 64 k-rows x 512 bytes (32 chunks); chunk swizzled by 4*(k%4).
 __device__ __forceinline__ int mswz(int krow, int chunk) { return krow * 512 + ((chunk ^ ((krow & 3) << 2)) << 4); }
 
-// Loop-invariant byte offsets of this thread's four 16-byte pieces of a slab
-// (32-bit: every operand here spans far less than 4 GB per token).
-// Instruction i of wave w writes 1 KB of LDS: K-major rows 64w + 16i .. +15
-// (lane l -> row +l/4, physical chunk l%4), M/N-major k-rows 8w + 2i, +1
-// (lane l -> k-row +l/32, physical chunk l%32); each lane fetches the logical
-// chunk that the swizzle places there.
+// Loop-invariant byte offsets of this thread's eight 16-byte pieces of a
+// slab (32-bit: every operand here spans far less than 4 GB per token).
+// Instruction i of wave w writes 1 KB of LDS: K-major rows 64w + 8i .. +7,
+// whole 128-byte lines (lane l -> row +l/8, physical chunk l%8), M/N-major
+// k-rows 16w + 2i, +1 (lane l -> k-row +l/32, physical chunk l%32); each lane
+// fetches the logical chunk that the swizzle places there.
+constexpr int DMA_PER_OPERAND = 8;
+constexpr int DMA_PER_SLAB = 2 * DMA_PER_OPERAND;  // per wave, A and B
 template <bool KMAJ>
-__device__ __forceinline__ void slab_offsets(uint32_t (&off)[4], long ld, int mn0, int MN, int wave, int lane) {
+__device__ __forceinline__ void slab_offsets(uint32_t (&off)[DMA_PER_OPERAND], long ld, int mn0, int MN, int wave,
+                                             int lane) {
 #pragma unroll
-  for (int i = 0; i < 4; ++i) {
+  for (int i = 0; i < DMA_PER_OPERAND; ++i) {
     if constexpr (KMAJ) {
-      const int row = 64 * wave + 16 * i + (lane >> 2);
-      const int chunk = (lane & 3) ^ ((row >> 2) & 3);
+      const int row = 64 * wave + 8 * i + (lane >> 3);
+      const int chunk = (lane & 7) ^ (row & 7);
       const int mn = min(mn0 + row, MN - 1);
       off[i] = (uint32_t)(((long)mn * ld + chunk * 8) * 2);
     } else {
-      const int krow = 8 * wave + 2 * i + (lane >> 5);
+      const int krow = 16 * wave + 2 * i + (lane >> 5);
       const int chunk = (lane & 31) ^ ((krow & 3) << 2);
       const int mn = min(mn0 + chunk * 8, MN - 8);
       off[i] = (uint32_t)(((long)krow * ld + mn) * 2);
@@ -112,12 +116,12 @@ __device__ __forceinline__ uint32_t lds_addr(const char* p) {
 // Copy the slab starting at k0 into LDS with 16-byte direct loads (wave is
 // uniform, so the LDS addresses are scalar).
 template <bool KMAJ>
-__device__ __forceinline__ void dma_slab(char* lds, const bf16_t* __restrict__ base, const uint32_t (&off)[4], long ld,
-                                         int k0, int wave) {
+__device__ __forceinline__ void dma_slab(char* lds, const bf16_t* __restrict__ base,
+                                         const uint32_t (&off)[DMA_PER_OPERAND], long ld, int k0, int wave) {
   const bf16_t* b = base + (KMAJ ? (long)k0 : (long)k0 * ld);
 #pragma unroll
-  for (int i = 0; i < 4; ++i) {
-    const int dst = KMAJ ? (64 * wave + 16 * i) * 64 : (8 * wave + 2 * i) * 512;
+  for (int i = 0; i < DMA_PER_OPERAND; ++i) {
+    const int dst = KMAJ ? (64 * wave + 8 * i) * 128 : (16 * wave + 2 * i) * 512;
     dma16(off[i], b, lds_addr(lds + dst));
   }
 }
@@ -228,7 +232,7 @@ __device__ __forceinline__ Tile tile_of(int logical, int tiles_m, int per_t) {
 struct Src {
   const bf16_t* A;
   const bf16_t* B;
-  uint32_t offa[4], offb[4];
+  uint32_t offa[DMA_PER_OPERAND], offb[DMA_PER_OPERAND];
 };
 template <bool AK, bool BKM>
 __device__ __forceinline__ void tile_src(Src& s, const GemmArgs& g, const Tile& c, int wave, int lane) {
@@ -323,47 +327,34 @@ __device__ __forceinline__ void epilogue(const f32x16_t (&acc)[4][4], const Gemm
   __builtin_amdgcn_sched_barrier(0);
 }
 
-// Per-step wait selections (operations newer than the awaited slab's
-// copies; see the pipeline description at the kernel).
-enum WaitKind {
-  W_STEADY,  // two later slabs in flight: 2 * DMA_PER_SLAB
-  W_START,   // steps 0..2 of a tile: the previous tile's stores too, unless it is the first tile
-  W_TAIL1,   // awaiting slab nk-2: one later slab of this tile, plus the next tile's first if any
-  W_TAIL2,   // awaiting slab nk-1: the next tile's first two slabs if any
-};
-
-template <int KIND>
-__device__ __forceinline__ void wait_slab(bool first, bool has_next) {
-  if constexpr (KIND == W_STEADY) {
-    sync_slab<2 * DMA_PER_SLAB>();
-  } else if constexpr (KIND == W_START) {
-    if (first) sync_slab<2 * DMA_PER_SLAB>();
-    else sync_slab<63>();
-  } else if constexpr (KIND == W_TAIL1) {
-    if (has_next) sync_slab<2 * DMA_PER_SLAB>();
-    else sync_slab<DMA_PER_SLAB>();
-  } else {
-    if (has_next) sync_slab<2 * DMA_PER_SLAB>();
-    else sync_slab<0>();
-  }
-}
-
 // One slab step.  On entry f0 holds slab k's first-k-step fragments (stage
-// sa/sb).  Reads slab k's second k step into f1 during the first k step's
-// MFMAs; waits for slab k+1 (stage na/nb) and the workgroup; copies slab
-// k+4 (this tile's, DMA == 1, or the next tile's, DMA == 2, when there is
-// one; that tile's bias first) into the stage just freed; reads slab k+1's
-// first k step into f0 during the second k step's MFMAs.
-template <bool AK, bool BKM, bool ZERO, int WAIT, int DMA>
+// sa/sb).  The second, third and fourth k steps' fragments are read while
+// the previous k step's MFMAs issue; then this wave waits for its LDS reads
+// and for slab k+1 (stage na/nb): at most WAIT newer vector-memory
+// operations (the previous tile's stores at a tile's first step, none
+// otherwise), and the workgroup barrier; the stage just freed receives slab
+// k+2 (this tile's, DMA == 1, or the next tile's, DMA == 2, when there is one;
+// that tile's bias first); the next slab's first fragments are read during
+// the last k step's MFMAs.
+template <bool AK, bool BKM, bool ZERO, int DMA>
 __device__ __forceinline__ void slab_step(f32x16_t (&acc)[4][4], Frags& f0, Frags& f1, char* sa, char* sb,
-                                          const char* na, const char* nb, int kdma, bool first, bool has_next,
+                                          const char* na, const char* nb, int kdma, bool tile_start, bool has_next,
                                           const GemmArgs& g, const Src& src, const Tile& nt, char* nbias, int wm,
                                           int wn, int wave, int lane) {
   constexpr int NR = (AK ? 4 : 8) + (BKM ? 4 : 8);
   read_frags<AK, BKM>(f1, sa, sb, wm, wn, 1, lane);
   mfma16<ZERO>(acc, f0);
   interleave<NR>();
-  wait_slab<WAIT>(first, has_next);
+  __builtin_amdgcn_sched_barrier(0);
+  read_frags<AK, BKM>(f0, sa, sb, wm, wn, 2, lane);
+  mfma16<false>(acc, f1);
+  interleave<NR>();
+  __builtin_amdgcn_sched_barrier(0);
+  read_frags<AK, BKM>(f1, sa, sb, wm, wn, 3, lane);
+  mfma16<false>(acc, f0);
+  interleave<NR>();
+  if (tile_start) sync_slab<63>();  // >= EPI_STORES stores are newer than slab k+1's copies
+  else sync_slab<0>();
   if constexpr (DMA == 1) {
     dma_pair<AK, BKM>(sa, sb, src, g, kdma, wave);
   } else {
@@ -383,17 +374,16 @@ __device__ __forceinline__ void slab_step(f32x16_t (&acc)[4][4], Frags& f0, Frag
 // tile, then M tile) and its workgroups take every (grid/8)-th tile of it, so
 // the tiles in flight on one XCD share operands in that XCD's L2.
 //
-// Pipeline (slab index s runs on across tiles, stage s % 4; nk % 4 == 0):
-// step k copies slab k+4 after its barrier, so slabs k+2, k+3 are in flight
-// at the wait for slab k+1 (2 * DMA_PER_SLAB newer operations).  The last
-// four steps of a tile copy the next tile's slabs 0..3; the tile's
-// EPI_STORES stores follow, so at the waits of the next tile's steps 0..2
-// at least 64 operations are newer than the awaited slab: vmcnt(63).
+// Pipeline (slab index s runs on across tiles, stage s % 2; nk is even): step
+// k copies slab k+2 into the stage freed by slab k, after the barrier that
+// waits for slab k+1, the only copy then in flight.  The last two steps of a
+// tile copy the next tile's slabs 0 and 1; the tile's EPI_STORES stores follow,
+// so at the next tile's first wait at least 64 operations are newer than the
+// awaited slab: vmcnt(63).
 template <bool AK, bool BKM>
 __device__ __forceinline__ void gemm256_body(const GemmArgs& g) {
-  // stage s: A slab at sA + s * TILE_BYTES, B slab at sB + s * TILE_BYTES
-  // (one base address per fragment serves all four stages through the
-  // instruction's 16-bit offset); bias tiles double buffered
+  // stage s: A slab at sA + s * TILE_BYTES, B slab at sB + s * TILE_BYTES;
+  // bias tiles double buffered
   __shared__ __attribute__((aligned(1024))) char sA[STAGES * TILE_BYTES];
   __shared__ __attribute__((aligned(1024))) char sB[STAGES * TILE_BYTES];
   __shared__ __attribute__((aligned(1024))) char sbias[2][1024];
@@ -401,10 +391,6 @@ __device__ __forceinline__ void gemm256_body(const GemmArgs& g) {
   char* const b0 = sB;
   char* const a1 = sA + TILE_BYTES;
   char* const b1 = sB + TILE_BYTES;
-  char* const a2 = sA + 2 * TILE_BYTES;
-  char* const b2 = sB + 2 * TILE_BYTES;
-  char* const a3 = sA + 3 * TILE_BYTES;
-  char* const b3 = sB + 3 * TILE_BYTES;
 
   const int tid = threadIdx.x, lane = tid & 63;
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);  // uniform per wave: scalar address arithmetic
@@ -422,13 +408,11 @@ __device__ __forceinline__ void gemm256_body(const GemmArgs& g) {
   Tile ct = tile_of(tile, tiles_m, per_t);
   Src cur;
   tile_src<AK, BKM>(cur, g, ct, wave, lane);
-  const int nk = g.K / BK;  // a multiple of 4, at least 8
+  const int nk = g.K / BK;  // even, at least 2
   if (g.bias && wave == 0) dma_bias(sbias[0], g, ct, lane);
   dma_pair<AK, BKM>(a0, b0, cur, g, 0, wave);
   dma_pair<AK, BKM>(a1, b1, cur, g, 1, wave);
-  dma_pair<AK, BKM>(a2, b2, cur, g, 2, wave);
-  dma_pair<AK, BKM>(a3, b3, cur, g, 3, wave);
-  sync_slab<3 * DMA_PER_SLAB>();
+  sync_slab<DMA_PER_SLAB>();
   Frags f0, f1;
   read_frags<AK, BKM>(f0, a0, b0, wm, wn, 0, lane);
 
@@ -442,38 +426,25 @@ __device__ __forceinline__ void gemm256_body(const GemmArgs& g) {
     tile_src<AK, BKM>(nxt, g, nt, wave, lane);
     char* nbias = sbias[(it + 1) & 1];
 
-    // steps 0..3 copy this tile's slabs 4..7 (nk >= 8)
-    slab_step<AK, BKM, true, W_START, 1>(acc, f0, f1, a0, b0, a1, b1, 4, first, has_next, g, cur, nt, nbias, wm, wn,
-                                         wave, lane);
-    slab_step<AK, BKM, false, W_START, 1>(acc, f0, f1, a1, b1, a2, b2, 5, first, has_next, g, cur, nt, nbias, wm, wn,
-                                          wave, lane);
-    slab_step<AK, BKM, false, W_START, 1>(acc, f0, f1, a2, b2, a3, b3, 6, first, has_next, g, cur, nt, nbias, wm, wn,
-                                          wave, lane);
-    slab_step<AK, BKM, false, W_STEADY, 1>(acc, f0, f1, a3, b3, a0, b0, 7, first, has_next, g, cur, nt, nbias, wm,
-                                           wn, wave, lane);
-    // steps 4 .. nk-5 copy slabs 8 .. nk-1
-    for (int k = 4; k < nk - 4; k += 4) {
-      slab_step<AK, BKM, false, W_STEADY, 1>(acc, f0, f1, a0, b0, a1, b1, k + 4, first, has_next, g, cur, nt, nbias,
-                                             wm, wn, wave, lane);
-      slab_step<AK, BKM, false, W_STEADY, 1>(acc, f0, f1, a1, b1, a2, b2, k + 5, first, has_next, g, cur, nt, nbias,
-                                             wm, wn, wave, lane);
-      slab_step<AK, BKM, false, W_STEADY, 1>(acc, f0, f1, a2, b2, a3, b3, k + 6, first, has_next, g, cur, nt, nbias,
-                                             wm, wn, wave, lane);
-      slab_step<AK, BKM, false, W_STEADY, 1>(acc, f0, f1, a3, b3, a0, b0, k + 7, first, has_next, g, cur, nt, nbias,
-                                             wm, wn, wave, lane);
+    // steps 0 .. nk-3 copy this tile's slabs 2 .. nk-1
+    slab_step<AK, BKM, true, 1>(acc, f0, f1, a0, b0, a1, b1, 2, !first, has_next, g, cur, nt, nbias, wm, wn, wave,
+                                lane);
+    slab_step<AK, BKM, false, 1>(acc, f0, f1, a1, b1, a0, b0, 3, false, has_next, g, cur, nt, nbias, wm, wn, wave,
+                                 lane);
+    for (int k = 2; k < nk - 2; k += 2) {
+      slab_step<AK, BKM, false, 1>(acc, f0, f1, a0, b0, a1, b1, k + 2, false, has_next, g, cur, nt, nbias, wm, wn,
+                                   wave, lane);
+      slab_step<AK, BKM, false, 1>(acc, f0, f1, a1, b1, a0, b0, k + 3, false, has_next, g, cur, nt, nbias, wm, wn,
+                                   wave, lane);
     }
-    // steps nk-4 .. nk-1 copy the next tile's slabs 0..3 (if any)
-    slab_step<AK, BKM, false, W_STEADY, 2>(acc, f0, f1, a0, b0, a1, b1, 0, first, has_next, g, nxt, nt, nbias, wm, wn,
-                                           wave, lane);
-    slab_step<AK, BKM, false, W_TAIL1, 2>(acc, f0, f1, a1, b1, a2, b2, 1, first, has_next, g, nxt, nt, nbias, wm, wn,
-                                          wave, lane);
-    slab_step<AK, BKM, false, W_TAIL2, 2>(acc, f0, f1, a2, b2, a3, b3, 2, first, has_next, g, nxt, nt, nbias, wm, wn,
-                                          wave, lane);
-    // (without a next tile this step copies nothing and its fragment reads
-    // of stage 0 are stale and unused; the same code on both paths keeps the
-    // accumulators in AGPRs)
-    slab_step<AK, BKM, false, W_STEADY, 2>(acc, f0, f1, a3, b3, a0, b0, 3, first, has_next, g, nxt, nt, nbias, wm, wn,
-                                           wave, lane);
+    // steps nk-2, nk-1 copy the next tile's slabs 0, 1 (if any; without a next
+    // tile the last step copies nothing and its fragment reads of stage 0 are
+    // stale and unused: the same code on both paths keeps the accumulators in
+    // AGPRs)
+    slab_step<AK, BKM, false, 2>(acc, f0, f1, a0, b0, a1, b1, 0, false, has_next, g, nxt, nt, nbias, wm, wn, wave,
+                                 lane);
+    slab_step<AK, BKM, false, 2>(acc, f0, f1, a1, b1, a0, b0, 1, false, has_next, g, nxt, nt, nbias, wm, wn, wave,
+                                 lane);
 
     epilogue(acc, g, ct, sbias[it & 1], wm, wn, lane);
     if (!has_next) break;
@@ -526,7 +497,7 @@ hipError_t run256(Gemm256Kernel k, const GemmArgs& g, hipStream_t s) {
 bool gemm256_supported(int dtype, bool a_kmajor, bool b_kmajor, const GemmArgs& g) {
   if (dtype != RM_BF16) return false;
   if (a_kmajor == false && b_kmajor == true) return false;
-  if (g.K % (STAGES * BK) != 0 || g.K < 2 * STAGES * BK) return false;
+  if (g.K % (2 * BK) != 0 || g.K < 4 * BK) return false;  // nk even, at least 4
   const long a_cont = a_kmajor ? g.K : g.M, b_cont = b_kmajor ? g.K : g.N;
   if (a_cont % 8 || b_cont % 8 || g.a_ld % 8 || g.b_ld % 8 || g.a_bs % 8 || g.b_bs % 8) return false;
   if ((reinterpret_cast<uintptr_t>(g.A) & 15) || (reinterpret_cast<uintptr_t>(g.B) & 15)) return false;
