@@ -10,24 +10,25 @@
 //     one wave per SIMD).  Per 16-deep k step a wave reads 8 KB of operand
 //     fragments from LDS for 16 MFMAs (64 bytes of LDS per clock per CU at
 //     full MFMA rate).
-//   * Operand slabs (32 deep in K, 16 KB per operand) are copied global ->
+//   * Operand slabs (64 deep in K, 32 KB per operand) are copied global ->
 //     LDS with the gfx950 16-byte direct loads (no register staging) through
-//     four stages, three slabs in flight.  The copies are inline assembly with
-//     explicit wait counts, so the compiler neither waits for them at every
-//     LDS read nor reorders them.
-//   * One barrier per slab, in the middle of it: the second k step's
-//     fragments are read during the first k step's MFMAs, then the barrier
-//     (next slab landed, this slab fully read), the copy into the stage just
-//     freed, and the next slab's first fragments are read during the second
-//     k step's MFMAs.  No LDS latency is exposed inside a tile.
+//     two stages.  The copies are inline assembly with explicit wait counts,
+//     so the compiler neither waits for them at every LDS read nor reorders
+//     them.
+//   * One barrier per slab, before its last k step: the fragments of k steps
+//     2..4 are read during the MFMAs of the step before, then the barrier
+//     (next slab landed, this slab fully read), the copy of slab k+2 into the
+//     stage just freed, and the next slab's first fragments are read during
+//     the last k step's MFMAs.  No LDS latency is exposed inside a tile.
 //   * Persistent: one workgroup per CU walks a range of tiles; the copy
 //     stream continues into the next tile and a tile's results are stored
 //     straight from the accumulators while the next tile's copies land.
-//   * K-major operands (row = m or n, 64 contiguous bytes of K) live in LDS
-//     as 64-byte rows whose 16-byte chunks are XOR-swizzled by (row/4)%4; an
-//     MFMA fragment is one 16-byte read per lane.
+//   * K-major operands (row = m or n, 128 contiguous bytes of K: one whole
+//     cache line per row and slab) live in LDS as 128-byte rows whose 16-byte
+//     chunks are XOR-swizzled by row%8; an MFMA fragment is one 16-byte read
+//     per lane.
 //   * M/N-major operands (the forward weights and both weight-gradient
-//     operands) live in LDS as 32 rows of k, each 256 contiguous m/n values
+//     operands) live in LDS as 64 rows of k, each 256 contiguous m/n values
 //     (512 bytes, 16-byte chunks XOR-swizzled by 4*(k%4), so the 4 k-rows x
 //     4 chunks one half-wave reads cover all 64 banks); a fragment is built by
 //     two ds_read_b64_tr_b16 transposing reads (in each 16-lane group, lane j

@@ -149,6 +149,146 @@ __global__ __launch_bounds__(512) void k_prologue(const ST* __restrict__ x, cons
 }
 
 // ---------------------------------------------------------------------------
+// Forward prologue for bf16 with the whole sample staged in LDS (T*D*2 bytes,
+// at most 160 KB), so x is read from HBM once.  One workgroup (16 waves) per
+// sample b, one wave per row, 4-element chunks (D % 4 == 0, S % 4 == 0):
+//   1. each wave loads its rows of x[b] once, computes norm0's statistics in
+//      registers, writes the raw row to LDS and the statistics to `stats`;
+//   2. after the barrier each lane fetches the statistics of the (at most
+//      MAXD / 256) source rows its columns gather from -- the same rows for
+//      every output row -- with L1-bypassing loads;
+//   3. output row i: the token-mix gather and the residual read LDS, then
+//      norm1 in registers and one store of out1.
+constexpr int PRO_LDS_BYTES = 64 * MAXD * 2;  // 160 KB: T*D bf16 for T <= 64, D <= 1280
+
+__device__ __forceinline__ float load_bypass_l1(const float* p) {
+  return __hip_atomic_load(p, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+}
+
+__global__ __launch_bounds__(1024) void k_prologue_lds(const bf16_t* __restrict__ x, const bf16_t* __restrict__ g0,
+                                                       const bf16_t* __restrict__ be0, const bf16_t* __restrict__ g1,
+                                                       const bf16_t* __restrict__ be1, bf16_t* __restrict__ h1,
+                                                       float* __restrict__ stats, int B, int T, int D) {
+  constexpr int N = 4;
+  constexpr int Q = MAXD / (64 * N);
+  __shared__ __attribute__((aligned(16))) char sx[PRO_LDS_BYTES];
+  const int b = blockIdx.x;
+  const int lane = threadIdx.x & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+  const int nw = blockDim.x >> 6;
+  const long NR = (long)B * T;
+  const long base = (long)b * T * D;
+  const int S = D / T;
+  const float invS = 1.0f / (float)S, invD = 1.0f / (float)D;
+
+  // 1. statistics of norm0, raw rows into LDS
+  for (int j = wave; j < T; j += nw) {
+    Raw<bf16_t, N> rr[Q];
+    float v[Q][N];
+    float s = 0.f;
+#pragma unroll
+    for (int q = 0; q < Q; ++q) {
+      const int c = (lane + 64 * q) * N;
+      ldr(x + base + (long)j * D + min(c, D - N), rr[q]);
+      unpack(rr[q], v[q]);
+      const float m = c < D ? 1.f : 0.f;
+#pragma unroll
+      for (int e = 0; e < N; ++e) s += m * v[q][e];
+    }
+    const float mean = wave_sum_dpp(s) * invD;
+    float s2 = 0.f;
+#pragma unroll
+    for (int q = 0; q < Q; ++q) {
+      const int c = (lane + 64 * q) * N;
+      const float m = c < D ? 1.f : 0.f;
+#pragma unroll
+      for (int e = 0; e < N; ++e) {
+        const float dd = v[q][e] - mean;
+        s2 += m * dd * dd;
+      }
+      if (c < D) *reinterpret_cast<uint2*>(sx + ((long)j * D + c) * 2) = make_uint2(rr[q].w[0], rr[q].w[1]);
+    }
+    const float rstd = rsqrtf(wave_sum_dpp(s2) * invD + EPS_OUTER);
+    if (lane == 0) {
+      stats[ST_MU0 * NR + (long)b * T + j] = mean;
+      stats[ST_RS0 * NR + (long)b * T + j] = rstd;
+    }
+  }
+  __syncthreads();
+
+  // 2. per-lane source rows and their statistics; out1's affine for this lane's columns
+  float mu[Q], rs[Q];
+  int jq[Q];
+  Raw<bf16_t, N> rg1[Q], rb1[Q];
+#pragma unroll
+  for (int q = 0; q < Q; ++q) {
+    const int c = (lane + 64 * q) * N;
+    const int cc = min(c, D - N);
+    const int j = div_small(cc, invS);
+    jq[q] = j;
+    mu[q] = load_bypass_l1(stats + ST_MU0 * NR + (long)b * T + j);
+    rs[q] = load_bypass_l1(stats + ST_RS0 * NR + (long)b * T + j);
+    ldr(g1 + cc, rg1[q]);
+    ldr(be1 + cc, rb1[q]);
+  }
+
+  // 3. out1 rows
+  for (int i = wave; i < T; i += nw) {
+    float r[Q][N];
+    float s = 0.f;
+#pragma unroll
+    for (int q = 0; q < Q; ++q) {
+      const int c = (lane + 64 * q) * N;
+      const int cc = min(c, D - N);
+      const int j = jq[q];
+      const int sc = i * S + (cc - j * S);
+      float a[N], gg[N], bb[N], xi[N];
+      const uint2 ra = *reinterpret_cast<const uint2*>(sx + ((long)j * D + sc) * 2);
+      const uint2 rx = *reinterpret_cast<const uint2*>(sx + ((long)i * D + cc) * 2);
+      a[0] = bf_lo(ra.x); a[1] = bf_hi(ra.x); a[2] = bf_lo(ra.y); a[3] = bf_hi(ra.y);
+      xi[0] = bf_lo(rx.x); xi[1] = bf_hi(rx.x); xi[2] = bf_lo(rx.y); xi[3] = bf_hi(rx.y);
+      ldv(g0 + sc, gg);
+      ldv(be0 + sc, bb);
+      const float m = c < D ? 1.f : 0.f;
+#pragma unroll
+      for (int e = 0; e < N; ++e) {
+        r[q][e] = (a[e] - mu[q]) * rs[q] * gg[e] + bb[e] + xi[e];
+        s += m * r[q][e];
+      }
+    }
+    const float mean = wave_sum_dpp(s) * invD;
+    float s2 = 0.f;
+#pragma unroll
+    for (int q = 0; q < Q; ++q) {
+      const int c = (lane + 64 * q) * N;
+      const float m = c < D ? 1.f : 0.f;
+#pragma unroll
+      for (int e = 0; e < N; ++e) {
+        const float dd = r[q][e] - mean;
+        s2 += m * dd * dd;
+      }
+    }
+    const float rstd = rsqrtf(wave_sum_dpp(s2) * invD + EPS_OUTER);
+#pragma unroll
+    for (int q = 0; q < Q; ++q) {
+      const int c = (lane + 64 * q) * N;
+      if (c < D) {
+        float gg[N], bb[N], o[N];
+        unpack(rg1[q], gg);
+        unpack(rb1[q], bb);
+#pragma unroll
+        for (int e = 0; e < N; ++e) o[e] = (r[q][e] - mean) * rstd * gg[e] + bb[e];
+        stv(h1 + base + (long)i * D + c, o);
+      }
+    }
+    if (lane == 0) {
+      stats[ST_MU1 * NR + (long)b * T + i] = mean;
+      stats[ST_RS1 * NR + (long)b * T + i] = rstd;
+    }
+  }
+}
+
+// ---------------------------------------------------------------------------
 // hidden = LN_x(U) * silu(LN_gate(G)).  One workgroup per GATE_ROWS rows of
 // Z, one thread per N-element chunk of U (and the matching chunk of G); the
 // next row's chunks are loaded while the current row is reduced.
@@ -987,7 +1127,11 @@ template <typename ST>
 hipError_t prologue_t(const rm_dims& d, const rm_params& p, const void* x, void* ws, const WsLayout& L,
                       hipStream_t s) {
   prof_begin(KID_PROLOGUE, s);
-  if (vec4_rows(d))
+  if (std::is_same<ST, bf16_t>::value && vec4_rows(d) && (long)d.T * d.D * 2 <= PRO_LDS_BYTES)
+    hipLaunchKernelGGL(k_prologue_lds, dim3(d.B), dim3(1024), 0, s, cptr<bf16_t>(x), cptr<bf16_t>(p.ln0_g),
+                       cptr<bf16_t>(p.ln0_b), cptr<bf16_t>(p.ln1_g), cptr<bf16_t>(p.ln1_b), wsp<bf16_t>(ws, L.h1),
+                       wsp<float>(ws, L.stats), d.B, d.T, d.D);
+  else if (vec4_rows(d))
     hipLaunchKernelGGL((k_prologue<ST, 4>), dim3(d.B), dim3(512), 0, s, cptr<ST>(x), cptr<ST>(p.ln0_g),
                        cptr<ST>(p.ln0_b), cptr<ST>(p.ln1_g), cptr<ST>(p.ln1_b), wsp<ST>(ws, L.h1),
                        wsp<float>(ws, L.stats), d.B, d.T, d.D);
