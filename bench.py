@@ -61,11 +61,11 @@ def row_bytes(d, sz):
     return {
         "prologue": N * D * sz * 2 + N * 16,                              # x -> out1, 4 stats
         "gate_fwd": N * 2 * H * sz + N * H * sz + N * 16,                 # Z -> hidden, 4 stats
-        "ln2_fwd": N * D * 4 + N * D * sz + N * 8,                        # r2 (fp32) -> y
-        "ln2_bwd": N * D * 4 + 2 * N * D * sz + p_ln2,                    # r2, dy -> d(out2), partials
+        "ln2_fwd": 2 * N * D * sz + N * 8,                                # r2 -> y
+        "ln2_bwd": 3 * N * D * sz + p_ln2,                                # r2, dy -> d(out2), partials
         "gate_bwd": N * 2 * H * sz + N * H * sz + N * 2 * H * sz + p_gate,  # Z, dhid -> dZ, partials
-        "ln1_bwd": N * D * sz + 2 * N * D * 4 + p_tail // 2,              # x, d(out1) -> dr1, partials
-        "ln0_bwd": N * D * sz + N * D * 4 + N * D * sz + p_tail // 2,     # x, dr1 -> dx, partials
+        "ln1_bwd": 3 * N * D * sz + p_tail // 2,                          # x, d(out1) -> dr1, partials
+        "ln0_bwd": 3 * N * D * sz + p_tail // 2,                          # x, dr1 -> dx, partials
         "finalize": p_ln2 + p_gate + p_tail,                              # partials -> 14 small gradients
     }
 

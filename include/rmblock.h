@@ -28,8 +28,9 @@
  *   - Validation (dims, dtype, null pointers, alignment, workspace size) runs
  *     on the host before anything is enqueued; on failure nothing is launched
  *     and the status says why.  RM_E_HIP means a launch failed.
- *   - Arithmetic: bf16 storage, fp32 accumulation and statistics, round to
- *     nearest even on every store.  Results are bitwise repeatable for
+ *   - Arithmetic: storage dtype (bf16 or fp32) for inputs, parameters,
+ *     outputs, gradients and every saved or intermediate tensor; fp32
+ *     accumulation and statistics; round to nearest even on every store.  Results are bitwise repeatable for
  *     identical inputs (fixed-order reductions, no floating-point atomics).
  */
 #ifndef RMBLOCK_H
@@ -87,7 +88,7 @@ size_t rm_workspace_bytes(const rm_dims* dims);
 
 /* Forward.  x, y: [B,T,D].  ws: at least rm_workspace_bytes(dims) bytes,
  * 256-byte aligned; the forward writes into it everything the backward needs
- * (out1, Z, hidden, out1+out2 in fp32 and the per-row LayerNorm mean/rstd).
+ * (out1, Z, hidden, out1+out2 and the per-row LayerNorm mean/rstd).
  * x, the parameters and ws must stay unchanged until rm_block_bwd is done. */
 rm_status rm_block_fwd(const rm_dims* dims, const rm_params* p, const void* x, void* y,
                        void* ws, size_t ws_bytes, void* stream);
@@ -111,7 +112,7 @@ enum {
   RM_WS_H1 = 0,     /* out1 [B,T,D] storage dtype                         */
   RM_WS_Z = 1,      /* Z [B,T,2H] storage dtype                           */
   RM_WS_HID = 2,    /* hidden [B,T,H] storage dtype                       */
-  RM_WS_R2 = 3,     /* out1 + out2 [B,T,D] fp32                           */
+  RM_WS_R2 = 3,     /* out1 + out2 [B,T,D] storage dtype                  */
   RM_WS_STATS = 4,  /* 10 x [B*T] fp32: mean,rstd of norm0, norm1, norm_x, norm_gate, norm2 */
   RM_WS_NREGIONS = 5
 };

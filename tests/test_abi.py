@@ -45,8 +45,8 @@ def expected_workspace_bytes(B, T, D, k, dtype):
     N, H = B * T, k * D
     sz = 2 if dtype == "bf16" else 4
     nb = (B + 63) // 64
-    sizes = [N * D * sz, N * 2 * H * sz, N * H * sz, N * D * 4, 10 * N * 4,      # saved by the forward
-             N * D * sz, N * H * sz, N * 2 * H * sz, N * D * 4, N * D * 4,       # backward scratch
+    sizes = [N * D * sz, N * 2 * H * sz, N * H * sz, N * D * sz, 10 * N * 4,     # saved by the forward
+             N * D * sz, N * H * sz, N * 2 * H * sz, N * D * sz, N * D * sz,     # backward scratch
              3 * nb * T * D * 4, (4 * nb * T * H + nb * T * 2 * H) * 4, 4 * nb * T * D * 4]  # partials
     off = 0
     for s in sizes:

@@ -6,7 +6,7 @@
 //   prologue   norm0 -> token mix -> + x -> norm1            => out1, stats
 //   gemm up    Z = out1 @ w1[t] + b1[t]                       => Z
 //   gate fwd   hidden = LN_x(U) * silu(LN_gate(G))            => hidden, stats
-//   gemm down  r2 = out1 + hidden @ wout[t] + bout[t]         => r2 (fp32)
+//   gemm down  r2 = out1 + hidden @ wout[t] + bout[t]         => r2
 //   ln2 fwd    y = norm2(r2)                                  => y, stats
 // Backward (the same steps in reverse):
 //   ln2 bwd    d(out2) = norm2 backward of dy                 (+ dgamma2, dbeta2, dbout partials)
@@ -14,7 +14,7 @@
 //   gate bwd   dZ = gate / SiLU / inner-LayerNorm backward    (+ inner affine, db1 partials)
 //   gemm dwout dwout[t] = hidden^T @ d(out2)
 //   gemm dw1   dw1[t] = out1^T @ dZ
-//   gemm dh1   d(out1) = dZ @ w1[t]^T + d(out2)               (fp32)
+//   gemm dh1   d(out1) = dZ @ w1[t]^T + d(out2)
 //   ln1 bwd    norm1 backward (r1 recomputed via the token-mix gather) => dr1 (+ dgamma1, dbeta1)
 //   ln0 bwd    token-mix adjoint as a gather, norm0 backward, + dr1   => dx (+ dgamma0, dbeta0)
 //   finalize   fixed-order sums of every partial              => parameter gradients
@@ -57,13 +57,13 @@ WsLayout ws_layout(const rm_dims& d) {
   L.h1 = take(N * D * sz);
   L.z = take(N * 2 * H * sz);
   L.hid = take(N * H * sz);
-  L.r2 = take(N * D * 4);
+  L.r2 = take(N * D * sz);
   L.stats = take(ST_COUNT * N * 4);
   L.do2 = take(N * D * sz);
   L.dhid = take(N * H * sz);
   L.dz = take(N * 2 * H * sz);
-  L.dh1 = take(N * D * 4);
-  L.dr1 = take(N * D * 4);
+  L.dh1 = take(N * D * sz);
+  L.dr1 = take(N * D * sz);
   L.p_ln2 = take(3 * nb * T * D * 4);
   L.p_gate = take((4 * nb * T * H + nb * T * 2 * H) * 4);
   L.p_tail = take(4 * nb * T * D * 4);
@@ -179,7 +179,7 @@ rm_status rm_ws_region(const rm_dims* dims, int region, size_t* offset, size_t* 
     case RM_WS_H1: *offset = L.h1; *bytes = N * D * sz; return RM_OK;
     case RM_WS_Z: *offset = L.z; *bytes = N * 2 * H * sz; return RM_OK;
     case RM_WS_HID: *offset = L.hid; *bytes = N * H * sz; return RM_OK;
-    case RM_WS_R2: *offset = L.r2; *bytes = N * D * 4; return RM_OK;
+    case RM_WS_R2: *offset = L.r2; *bytes = N * D * sz; return RM_OK;
     case RM_WS_STATS: *offset = L.stats; *bytes = ST_COUNT * N * 4; return RM_OK;
     default: return RM_E_ARG;
   }
@@ -215,7 +215,7 @@ rm_status rm_block_fwd(const rm_dims* dims, const rm_params* p, const void* x, v
   dn.M = d.B; dn.N = D; dn.K = H; dn.batch = T;
   dn.A = w + L.hid; dn.a_bs = H; dn.a_ld = T * H;
   dn.B = p->wout; dn.b_bs = H * D; dn.b_ld = D;
-  dn.C = w + L.r2; dn.c_bs = D; dn.c_ld = T * D; dn.c_f32 = 1;
+  dn.C = w + L.r2; dn.c_bs = D; dn.c_ld = T * D; dn.c_f32 = d.dtype == RM_F32;
   dn.bias = p->bout; dn.bias_bs = D;
   dn.res = w + L.h1; dn.res_bs = D; dn.res_ld = T * D; dn.res_f32 = 0;
   if ((e = launch_gemm(d.dtype, true, false, dn, KID_GEMM_DOWN, s)) != hipSuccess) return hip_status(e);
@@ -273,7 +273,7 @@ rm_status rm_block_bwd(const rm_dims* dims, const rm_params* p, const void* x, c
   dh.M = d.B; dh.N = D; dh.K = 2 * H; dh.batch = T;
   dh.A = w + L.dz; dh.a_bs = 2 * H; dh.a_ld = T * 2 * H;
   dh.B = p->w1; dh.b_bs = D * 2 * H; dh.b_ld = 2 * H;
-  dh.C = w + L.dh1; dh.c_bs = D; dh.c_ld = T * D; dh.c_f32 = 1;
+  dh.C = w + L.dh1; dh.c_bs = D; dh.c_ld = T * D; dh.c_f32 = d.dtype == RM_F32;
   dh.res = w + L.do2; dh.res_bs = D; dh.res_ld = T * D; dh.res_f32 = 0;
   if ((e = launch_gemm(d.dtype, true, true, dh, KID_GEMM_DH1, s)) != hipSuccess) return hip_status(e);
 

@@ -372,9 +372,9 @@ __global__ __launch_bounds__(256) void k_gate_fwd(const ST* __restrict__ Z, cons
 }
 
 // ---------------------------------------------------------------------------
-// y = norm2(r2), r2 = out1 + out2 kept in fp32.  One wave per row.
+// y = norm2(r2), r2 = out1 + out2 in the storage dtype.  One wave per row.
 template <typename ST, int N>
-__global__ __launch_bounds__(256) void k_ln2_fwd(const float* __restrict__ r2, const ST* __restrict__ g2,
+__global__ __launch_bounds__(256) void k_ln2_fwd(const ST* __restrict__ r2, const ST* __restrict__ g2,
                                                  const ST* __restrict__ be2, ST* __restrict__ y,
                                                  float* __restrict__ stats, long NR, int D) {
   constexpr int Q = (MAXD + 64 * N - 1) / (64 * N);
@@ -382,7 +382,7 @@ __global__ __launch_bounds__(256) void k_ln2_fwd(const float* __restrict__ r2, c
   const long row = (long)blockIdx.x * 4 + wave;
   if (row >= NR) return;
   const float invD = 1.0f / (float)D;
-  const float* r = r2 + row * D;
+  const ST* r = r2 + row * D;
   float v[Q][N];
   float s = 0.f;
 #pragma unroll
@@ -460,7 +460,7 @@ __device__ __forceinline__ void combine_waves_store(const float (&acc)[Q][N], fl
 // norm2 backward:  do2 = rstd2 * (dn - mean(dn) - n2 * mean(dn * n2)),  dn = dy * gamma2.
 // Partials: dgamma2 (dy * n2), dbeta2 (dy), dbout[t] (do2).
 template <typename ST, int N, int Q>
-__global__ __launch_bounds__(256) void k_ln2_bwd(const float* __restrict__ r2, const ST* __restrict__ dy,
+__global__ __launch_bounds__(256) void k_ln2_bwd(const ST* __restrict__ r2, const ST* __restrict__ dy,
                                                  const ST* __restrict__ g2, const float* __restrict__ stats,
                                                  ST* __restrict__ do2, float* __restrict__ part, int B, int T,
                                                  int D, int nb) {
@@ -478,7 +478,7 @@ __global__ __launch_bounds__(256) void k_ln2_bwd(const float* __restrict__ r2, c
   for (int b = grp * ROWS_PER_GROUP + wave; b < b_end; b += 4) {
     const long row = (long)b * T + t;
     const float mu = stats[ST_MU2 * NR + row], rs = stats[ST_RS2 * NR + row];
-    Raw<float, N> rr[Q];
+    Raw<ST, N> rr[Q];
     Raw<ST, N> rdy[Q], rgm[Q];
 #pragma unroll
     for (int q = 0; q < Q; ++q) {
@@ -889,10 +889,10 @@ __global__ __launch_bounds__(MAXT) void k_gate_bwd_ring(const ST* __restrict__ Z
 // Partials: dgamma1 (d(out1) * n1), dbeta1 (d(out1)).  Row (b, i) with i = t.
 // N > 1 needs S % N == 0 (a chunk's gather source is contiguous).
 template <typename ST, int N, int Q>
-__global__ __launch_bounds__(256) void k_ln1_bwd(const ST* __restrict__ x, const float* __restrict__ dh1,
+__global__ __launch_bounds__(256) void k_ln1_bwd(const ST* __restrict__ x, const ST* __restrict__ dh1,
                                                  const ST* __restrict__ g0, const ST* __restrict__ be0,
                                                  const ST* __restrict__ g1, const float* __restrict__ stats,
-                                                 float* __restrict__ dr1, float* __restrict__ part, int B, int T,
+                                                 ST* __restrict__ dr1, float* __restrict__ part, int B, int T,
                                                  int D, int nb) {
   __shared__ float lds[4 * MAXD];
   const int i = blockIdx.x, grp = blockIdx.y;
@@ -917,7 +917,7 @@ __global__ __launch_bounds__(256) void k_ln1_bwd(const ST* __restrict__ x, const
     const long base = (long)b * T * D;
     const float mu1 = stats[ST_MU1 * NR + row], rs1 = stats[ST_RS1 * NR + row];
     Raw<ST, N> ra[Q], rxi[Q];
-    Raw<float, N> rg[Q];
+    Raw<ST, N> rg[Q];
     float mu0[Q], rs0[Q];
 #pragma unroll
     for (int q = 0; q < Q; ++q) {
@@ -978,7 +978,7 @@ __global__ __launch_bounds__(256) void k_ln1_bwd(const ST* __restrict__ x, const
 //   dx = dr1 + rstd0 * (dn - mean(dn) - n0 * mean(dn * n0)),  dn = da0 * gamma0.
 // Partials: dgamma0 (da0 * n0), dbeta0 (da0).
 template <typename ST, int N, int Q>
-__global__ __launch_bounds__(256) void k_ln0_bwd(const ST* __restrict__ x, const float* __restrict__ dr1,
+__global__ __launch_bounds__(256) void k_ln0_bwd(const ST* __restrict__ x, const ST* __restrict__ dr1,
                                                  const ST* __restrict__ g0, const float* __restrict__ stats,
                                                  ST* __restrict__ dx, float* __restrict__ part, int B, int T, int D,
                                                  int nb) {
@@ -1004,7 +1004,7 @@ __global__ __launch_bounds__(256) void k_ln0_bwd(const ST* __restrict__ x, const
     const long row = (long)b * T + j;
     const long base = (long)b * T * D;
     const float mu0 = stats[ST_MU0 * NR + row], rs0 = stats[ST_RS0 * NR + row];
-    Raw<float, N> rda[Q], rown[Q];
+    Raw<ST, N> rda[Q], rown[Q];
     Raw<ST, N> rx[Q];
 #pragma unroll
     for (int q = 0; q < Q; ++q) {
@@ -1181,10 +1181,10 @@ hipError_t ln2_fwd_t(const rm_dims& d, const rm_params& p, void* y, void* ws, co
   const dim3 grid((unsigned)((NR + 3) / 4));
   prof_begin(KID_LN2_FWD, s);
   if (d.D % 4 == 0)
-    hipLaunchKernelGGL((k_ln2_fwd<ST, 4>), grid, dim3(256), 0, s, wsp<float>(ws, L.r2), cptr<ST>(p.ln2_g),
+    hipLaunchKernelGGL((k_ln2_fwd<ST, 4>), grid, dim3(256), 0, s, wsp<ST>(ws, L.r2), cptr<ST>(p.ln2_g),
                        cptr<ST>(p.ln2_b), reinterpret_cast<ST*>(y), wsp<float>(ws, L.stats), NR, d.D);
   else
-    hipLaunchKernelGGL((k_ln2_fwd<ST, 1>), grid, dim3(256), 0, s, wsp<float>(ws, L.r2), cptr<ST>(p.ln2_g),
+    hipLaunchKernelGGL((k_ln2_fwd<ST, 1>), grid, dim3(256), 0, s, wsp<ST>(ws, L.r2), cptr<ST>(p.ln2_g),
                        cptr<ST>(p.ln2_b), reinterpret_cast<ST*>(y), wsp<float>(ws, L.stats), NR, d.D);
   prof_end(KID_LN2_FWD, s);
   return hipGetLastError();
@@ -1196,11 +1196,11 @@ hipError_t ln2_bwd_t(const rm_dims& d, const rm_params& p, const void* dy, void*
   const dim3 grid(d.T, L.nb);
   prof_begin(KID_LN2_BWD, s);
   if (d.D % 4 == 0)
-    hipLaunchKernelGGL((k_ln2_bwd<ST, 4, MAXD / 256>), grid, dim3(256), 0, s, wsp<float>(ws, L.r2), cptr<ST>(dy),
+    hipLaunchKernelGGL((k_ln2_bwd<ST, 4, MAXD / 256>), grid, dim3(256), 0, s, wsp<ST>(ws, L.r2), cptr<ST>(dy),
                        cptr<ST>(p.ln2_g), wsp<float>(ws, L.stats), wsp<ST>(ws, L.do2), wsp<float>(ws, L.p_ln2), d.B,
                        d.T, d.D, L.nb);
   else
-    hipLaunchKernelGGL((k_ln2_bwd<ST, 1, MAXD / 64>), grid, dim3(256), 0, s, wsp<float>(ws, L.r2), cptr<ST>(dy),
+    hipLaunchKernelGGL((k_ln2_bwd<ST, 1, MAXD / 64>), grid, dim3(256), 0, s, wsp<ST>(ws, L.r2), cptr<ST>(dy),
                        cptr<ST>(p.ln2_g), wsp<float>(ws, L.stats), wsp<ST>(ws, L.do2), wsp<float>(ws, L.p_ln2), d.B,
                        d.T, d.D, L.nb);
   prof_end(KID_LN2_BWD, s);
@@ -1240,22 +1240,22 @@ hipError_t tail_bwd_t(const rm_dims& d, const rm_params& p, const void* x, void*
   hipError_t e;
   prof_begin(KID_LN1_BWD, s);
   if (vec4_rows(d))
-    hipLaunchKernelGGL((k_ln1_bwd<ST, 4, MAXD / 256>), grid, dim3(256), 0, s, cptr<ST>(x), wsp<float>(ws, L.dh1),
+    hipLaunchKernelGGL((k_ln1_bwd<ST, 4, MAXD / 256>), grid, dim3(256), 0, s, cptr<ST>(x), wsp<ST>(ws, L.dh1),
                        cptr<ST>(p.ln0_g), cptr<ST>(p.ln0_b), cptr<ST>(p.ln1_g), wsp<float>(ws, L.stats),
-                       wsp<float>(ws, L.dr1), wsp<float>(ws, L.p_tail), d.B, d.T, d.D, L.nb);
+                       wsp<ST>(ws, L.dr1), wsp<float>(ws, L.p_tail), d.B, d.T, d.D, L.nb);
   else
-    hipLaunchKernelGGL((k_ln1_bwd<ST, 1, MAXD / 64>), grid, dim3(256), 0, s, cptr<ST>(x), wsp<float>(ws, L.dh1),
+    hipLaunchKernelGGL((k_ln1_bwd<ST, 1, MAXD / 64>), grid, dim3(256), 0, s, cptr<ST>(x), wsp<ST>(ws, L.dh1),
                        cptr<ST>(p.ln0_g), cptr<ST>(p.ln0_b), cptr<ST>(p.ln1_g), wsp<float>(ws, L.stats),
-                       wsp<float>(ws, L.dr1), wsp<float>(ws, L.p_tail), d.B, d.T, d.D, L.nb);
+                       wsp<ST>(ws, L.dr1), wsp<float>(ws, L.p_tail), d.B, d.T, d.D, L.nb);
   prof_end(KID_LN1_BWD, s);
   if ((e = hipGetLastError()) != hipSuccess) return e;
   prof_begin(KID_LN0_BWD, s);
   if (vec4_rows(d))
-    hipLaunchKernelGGL((k_ln0_bwd<ST, 4, MAXD / 256>), grid, dim3(256), 0, s, cptr<ST>(x), wsp<float>(ws, L.dr1),
+    hipLaunchKernelGGL((k_ln0_bwd<ST, 4, MAXD / 256>), grid, dim3(256), 0, s, cptr<ST>(x), wsp<ST>(ws, L.dr1),
                        cptr<ST>(p.ln0_g), wsp<float>(ws, L.stats), reinterpret_cast<ST*>(dx),
                        wsp<float>(ws, L.p_tail), d.B, d.T, d.D, L.nb);
   else
-    hipLaunchKernelGGL((k_ln0_bwd<ST, 1, MAXD / 64>), grid, dim3(256), 0, s, cptr<ST>(x), wsp<float>(ws, L.dr1),
+    hipLaunchKernelGGL((k_ln0_bwd<ST, 1, MAXD / 64>), grid, dim3(256), 0, s, cptr<ST>(x), wsp<ST>(ws, L.dr1),
                        cptr<ST>(p.ln0_g), wsp<float>(ws, L.stats), reinterpret_cast<ST*>(dx),
                        wsp<float>(ws, L.p_tail), d.B, d.T, d.D, L.nb);
   prof_end(KID_LN0_BWD, s);
