@@ -25,8 +25,8 @@
 //     straight from the accumulators while the next tile's copies land.
 //   * K-major operands (row = m or n, 128 contiguous bytes of K: one whole
 //     cache line per row and slab) live in LDS as 128-byte rows whose 16-byte
-//     chunks are XOR-swizzled by row%8; an MFMA fragment is one 16-byte read
-//     per lane.
+//     chunks are XOR-swizzled by (row/2)%8; an MFMA fragment is one 16-byte
+//     read per lane.
 //   * M/N-major operands (the forward weights and both weight-gradient
 //     operands) live in LDS as 64 rows of k, each 256 contiguous m/n values
 //     (512 bytes, 16-byte chunks XOR-swizzled by 4*(k%4), so the 4 k-rows x
@@ -67,9 +67,11 @@ __device__ __forceinline__ uint32_t bf16_pair(float a, float b) {
 }
 
 // K-major slab: 256 rows x 128 bytes (8 chunks of 16 B, one cache line per
-// row); chunk swizzled by row%8 so the 8 rows one LDS cycle serves hit 8
-// distinct 4-bank groups.
-__device__ __forceinline__ int kswz(int row, int chunk) { return row * 128 + ((chunk ^ (row & 7)) << 4); }
+// row); chunk swizzled by (row/2)%8.  A 16-byte read serves 16 lanes (16
+// consecutive rows, one chunk) per LDS cycle: rows 2r and 2r+1 fall in the two
+// 128-byte halves of the 256-byte bank space and the swizzle gives the 8 row
+// pairs 8 distinct chunks, so the 16 reads hit 16 distinct 4-bank groups.
+__device__ __forceinline__ int kswz(int row, int chunk) { return row * 128 + ((chunk ^ ((row >> 1) & 7)) << 4); }
 // M/N-major slab: 64 k-rows x 512 bytes (32 chunks); chunk swizzled by 4*(k%4).
 __device__ __forceinline__ int mswz(int krow, int chunk) { return krow * 512 + ((chunk ^ ((krow & 3) << 2)) << 4); }
 
@@ -88,7 +90,7 @@ __device__ __forceinline__ void slab_offsets(uint32_t (&off)[DMA_PER_OPERAND], l
   for (int i = 0; i < DMA_PER_OPERAND; ++i) {
     if constexpr (KMAJ) {
       const int row = 64 * wave + 8 * i + (lane >> 3);
-      const int chunk = (lane & 7) ^ (row & 7);
+      const int chunk = (lane & 7) ^ ((row >> 1) & 7);
       const int mn = min(mn0 + row, MN - 1);
       off[i] = (uint32_t)(((long)mn * ld + chunk * 8) * 2);
     } else {
