@@ -55,10 +55,10 @@ constexpr int BM = 256, BN = 256, BK = 64;
 constexpr int STAGES = 2;
 constexpr int TILE_BYTES = 256 * BK * 2;  // one operand slab: 256 x 64 bf16 = 32 KB
 constexpr int KSTEPS = BK / 16;           // MFMA k steps per slab
-// Buffer stores the epilogue issues per tile per wave, unconditionally (lanes
-// outside C get an out-of-range offset, which the buffer unit drops).
-constexpr int EPI_STORES = 64;
-static_assert(EPI_STORES >= 63, "the wait at a tile's start relies on >= 63 newer operations");
+// Buffer stores the epilogue issues per tile per wave at least (32 for bf16
+// output, 64 for fp32), unconditionally (lanes outside C get an out-of-range
+// offset, which the buffer unit drops).
+constexpr int EPI_STORES = 32;
 
 // Two fp32 values as packed bf16 (round to nearest even: v_cvt_pk_bf16_f32).
 __device__ __forceinline__ uint32_t bf16_pair(float a, float b) {
@@ -260,10 +260,47 @@ __device__ __forceinline__ void dma_pair(char* sa, char* sb, const Src& s, const
   dma_slab<BKM>(sb, s.B, s.offb, g.b_ld, kslab * BK, wave);
 }
 
-// Tile epilogue straight from the accumulators: v = acc (+ bias) (+ residual),
-// stored as 4 consecutive columns per lane and per (m block, n block, v/4):
-// 8-byte bf16 or 16-byte fp32 buffer stores, EPI_STORES per wave, every one
-// issued (rows past M or columns past N get an out-of-range offset).  One m
+// v = acc (+ bias) (+ residual) for the 4 consecutive columns n..n+3 of row m
+// that this lane holds in accumulator block (i, j), v/4 group q.
+__device__ __forceinline__ void epi_values(float (&v)[4], const f32x16_t (&acc)[4][4], int i, int j, int q,
+                                           const GemmArgs& g, uint32_t boff, __amdgpu_buffer_rsrc_t rrs,
+                                           uint32_t rld, int rsz, int m, int n, bool ok) {
+#pragma unroll
+  for (int e = 0; e < 4; ++e) v[e] = acc[i][j][4 * q + e];
+  if (g.bias) {
+    const v2u32 w = *reinterpret_cast<const __attribute__((address_space(3))) v2u32*>(
+        (uintptr_t)(boff + 2 * (32 * j + 8 * q)));
+    v[0] += __uint_as_float(w.x << 16);
+    v[1] += __uint_as_float(w.x & 0xffff0000u);
+    v[2] += __uint_as_float(w.y << 16);
+    v[3] += __uint_as_float(w.y & 0xffff0000u);
+  }
+  if (g.res) {
+    const uint32_t ro = ok ? (uint32_t)m * rld + (uint32_t)n * rsz : OUT_OF_RANGE;
+    if (g.res_f32) {
+      const v4u32 a = __builtin_bit_cast(v4u32, __builtin_amdgcn_raw_buffer_load_b128(rrs, ro, 0, 0));
+      v[0] += __uint_as_float(a.x); v[1] += __uint_as_float(a.y);
+      v[2] += __uint_as_float(a.z); v[3] += __uint_as_float(a.w);
+    } else {
+      const v2u32 a = __builtin_bit_cast(v2u32, __builtin_amdgcn_raw_buffer_load_b64(rrs, ro, 0, 0));
+      v[0] += __uint_as_float(a.x << 16);
+      v[1] += __uint_as_float(a.x & 0xffff0000u);
+      v[2] += __uint_as_float(a.y << 16);
+      v[3] += __uint_as_float(a.y & 0xffff0000u);
+    }
+  }
+}
+
+// Tile epilogue straight from the accumulators: v = acc (+ bias) (+ residual).
+// Lane l holds, per (m block i, n block j, v/4 group q), 4 consecutive
+// columns n = 32j + 8q + 4(l/32) of row m = 32i + l%32.
+//   * bf16 output: lanes l and l+32 exchange halves (v_permlane32_swap) so
+//     that each lane holds 8 consecutive columns: lane l < 32 columns
+//     8q..8q+7, lane l+32 columns 8(q+1)..8(q+1)+7 for q = 0, 2; one 16-byte
+//     buffer store each, 32 per wave.
+//   * fp32 output: one 16-byte store per (i, j, q), 64 per wave.
+// Every store is issued (rows past M or columns past N get an out-of-range
+// offset that the buffer unit drops): at least EPI_STORES per wave.  One m
 // block at a time (scheduling barriers between blocks), so at most 16
 // residual loads are live at once.
 __device__ __forceinline__ void epilogue(const f32x16_t (&acc)[4][4], const GemmArgs& g, const Tile& c,
@@ -287,45 +324,41 @@ __device__ __forceinline__ void epilogue(const f32x16_t (&acc)[4][4], const Gemm
     const int m = mb + 32 * i;
     const bool mok = m < g.M;
 #pragma unroll
-    for (int j = 0; j < 4; ++j)
+    for (int j = 0; j < 4; ++j) {
+      if (g.c_f32) {
 #pragma unroll
-      for (int q = 0; q < 4; ++q) {
-        const int n = c.n0 + nb + 32 * j + 8 * q;
-        const bool ok = mok && n < g.N;  // N % 8 == 0: the 4 columns are all in or all out
-        float v[4];
-#pragma unroll
-        for (int e = 0; e < 4; ++e) v[e] = acc[i][j][4 * q + e];
-        if (g.bias) {
-          const v2u32 w = *reinterpret_cast<const __attribute__((address_space(3))) v2u32*>(
-              (uintptr_t)(boff + 2 * (32 * j + 8 * q)));
-          v[0] += __uint_as_float(w.x << 16);
-          v[1] += __uint_as_float(w.x & 0xffff0000u);
-          v[2] += __uint_as_float(w.y << 16);
-          v[3] += __uint_as_float(w.y & 0xffff0000u);
-        }
-        if (g.res) {
-          const uint32_t ro = ok ? (uint32_t)m * rld + (uint32_t)n * rsz : OUT_OF_RANGE;
-          if (g.res_f32) {
-            const v4u32 a = __builtin_bit_cast(v4u32, __builtin_amdgcn_raw_buffer_load_b128(rrs, ro, 0, 0));
-            v[0] += __uint_as_float(a.x); v[1] += __uint_as_float(a.y);
-            v[2] += __uint_as_float(a.z); v[3] += __uint_as_float(a.w);
-          } else {
-            const v2u32 a = __builtin_bit_cast(v2u32, __builtin_amdgcn_raw_buffer_load_b64(rrs, ro, 0, 0));
-            v[0] += __uint_as_float(a.x << 16);
-            v[1] += __uint_as_float(a.x & 0xffff0000u);
-            v[2] += __uint_as_float(a.y << 16);
-            v[3] += __uint_as_float(a.y & 0xffff0000u);
-          }
-        }
-        const uint32_t co = ok ? (uint32_t)m * cld + (uint32_t)n * esz : OUT_OF_RANGE;
-        if (g.c_f32) {
+        for (int q = 0; q < 4; ++q) {
+          const int n = c.n0 + nb + 32 * j + 8 * q;
+          const bool ok = mok && n < g.N;  // N % 8 == 0: the 4 columns are all in or all out
+          float v[4];
+          epi_values(v, acc, i, j, q, g, boff, rrs, rld, rsz, m, n, ok);
+          const uint32_t co = ok ? (uint32_t)m * cld + (uint32_t)n * 4 : OUT_OF_RANGE;
           const v4u32 d = {__float_as_uint(v[0]), __float_as_uint(v[1]), __float_as_uint(v[2]), __float_as_uint(v[3])};
           __builtin_amdgcn_raw_buffer_store_b128(d, crs, co, 0, 0);
-        } else {
-          const v2u32 d = {bf16_pair(v[0], v[1]), bf16_pair(v[2], v[3])};
-          __builtin_amdgcn_raw_buffer_store_b64(d, crs, co, 0, 0);
+        }
+      } else {
+#pragma unroll
+        for (int q = 0; q < 4; q += 2) {
+          const int n0 = c.n0 + nb + 32 * j + 8 * q, n1 = n0 + 8;
+          float v0[4], v1[4];
+          epi_values(v0, acc, i, j, q, g, boff, rrs, rld, rsz, m, n0, mok && n0 < g.N);
+          epi_values(v1, acc, i, j, q + 1, g, boff, rrs, rld, rsz, m, n1, mok && n1 < g.N);
+          // lane < 32: (v0 | partner's v0) = columns 8q..8q+7;  lane >= 32: (partner's v1 | v1) = 8(q+1)..
+          uint32_t a0 = bf16_pair(v0[0], v0[1]), a1 = bf16_pair(v0[2], v0[3]);
+          uint32_t b0 = bf16_pair(v1[0], v1[1]), b1 = bf16_pair(v1[2], v1[3]);
+          const auto s0 = __builtin_amdgcn_permlane32_swap(a0, b0, false, false);
+          const auto s1 = __builtin_amdgcn_permlane32_swap(a1, b1, false, false);
+          a0 = s0[0]; b0 = s0[1];
+          a1 = s1[0]; b1 = s1[1];
+          // now lane < 32 holds (a0 a1 | b0 b1) = columns 8q..8q+7, lane >= 32 (a0 a1 | b0 b1) = 8(q+1)..
+          const int ns = c.n0 + wn * 128 + 32 * j + 8 * (q + h);
+          const bool ok = mok && ns < g.N;
+          const uint32_t co = ok ? (uint32_t)m * cld + (uint32_t)ns * 2 : OUT_OF_RANGE;
+          const v4u32 d = {a0, a1, b0, b1};
+          __builtin_amdgcn_raw_buffer_store_b128(d, crs, co, 0, 0);
         }
       }
+    }
   }
   __builtin_amdgcn_sched_barrier(0);
 }
@@ -356,7 +389,7 @@ __device__ __forceinline__ void slab_step(f32x16_t (&acc)[4][4], Frags& f0, Frag
   read_frags<AK, BKM>(f1, sa, sb, wm, wn, 3, lane);
   mfma16<false>(acc, f0);
   interleave<NR>();
-  if (tile_start) sync_slab<63>();  // >= EPI_STORES stores are newer than slab k+1's copies
+  if (tile_start) sync_slab<EPI_STORES>();  // >= EPI_STORES stores are newer than slab k+1's copies
   else sync_slab<0>();
   if constexpr (DMA == 1) {
     dma_pair<AK, BKM>(sa, sb, src, g, kdma, wave);
@@ -381,8 +414,8 @@ __device__ __forceinline__ void slab_step(f32x16_t (&acc)[4][4], Frags& f0, Frag
 // k copies slab k+2 into the stage freed by slab k, after the barrier that
 // waits for slab k+1, the only copy then in flight.  The last two steps of a
 // tile copy the next tile's slabs 0 and 1; the tile's EPI_STORES stores follow,
-// so at the next tile's first wait at least 64 operations are newer than the
-// awaited slab: vmcnt(63).
+// so at the next tile's first wait at least EPI_STORES operations are newer
+// than the awaited slab: vmcnt(EPI_STORES).
 template <bool AK, bool BKM>
 __device__ __forceinline__ void gemm256_body(const GemmArgs& g) {
   // stage s: A slab at sA + s * TILE_BYTES, B slab at sB + s * TILE_BYTES;

@@ -829,15 +829,17 @@ __global__ __launch_bounds__(MAXT) void k_gate_bwd_ring(const ST* __restrict__ Z
     if constexpr (decltype(prefetch)::value) load_row(p, r + RING);
     float nx[4], ng[4], dux[4], dug[4];
     float sm[4] = {0.f, 0.f, 0.f, 0.f};
+    const float ox = -mux * rsx, og = -mug * rsg;
 #pragma unroll
     for (int e = 0; e < 4; ++e) {
-      nx[e] = (u[e] - mux) * rsx;
-      ng[e] = (g[e] - mug) * rsg;
+      nx[e] = u[e] * rsx + ox;
+      ng[e] = g[e] * rsg + og;
       const float ux = nx[e] * cgx[e] + cbx[e];
       const float ug = ng[e] * cgg[e] + cbg[e];
       const float sgm = sigmoidf_(ug);
-      dux[e] = w * (dh[e] * ug * sgm);
-      dug[e] = w * (dh[e] * ux * sgm * (1.f + ug * (1.f - sgm)));
+      const float dhw = w * dh[e];  // rows past B and columns past H contribute nothing
+      dux[e] = dhw * ug * sgm;
+      dug[e] = dhw * ux * sgm * (1.f + ug * (1.f - sgm));
       const float dnx = dux[e] * cgx[e], dng = dug[e] * cgg[e];
       sm[0] += dnx;
       sm[1] += dnx * nx[e];
@@ -856,8 +858,10 @@ __global__ __launch_bounds__(MAXT) void k_gate_bwd_ring(const ST* __restrict__ Z
     for (int e = 0; e < 4; ++e) {
       du[e] = rsx * (dux[e] * cgx[e] - m1 - nx[e] * m2);
       dg[e] = rsg * (dug[e] * cgg[e] - m3 - ng[e] * m4);
-      au[e] += w * du[e];
-      ag[e] += w * dg[e];
+      // a row past B has all four sums zero, so du = dg = 0 there; columns
+      // past H are never stored
+      au[e] += du[e];
+      ag[e] += dg[e];
     }
     const bool sok = valid && craw < H;
     bst4<ST>(drs, sok ? vu : 0x80000000u, row * zrow, du);
@@ -1081,10 +1085,12 @@ __global__ __launch_bounds__(1024) void k_finalize(RedJobs jobs) {
   if (c < job.ncols) {
     const float* p = job.part + c;
     int r = ry;
-    for (; r + 48 < job.P; r += 64) {
-      const float a = p[(long)r * job.pstride], b = p[(long)(r + 16) * job.pstride];
-      const float d = p[(long)(r + 32) * job.pstride], e = p[(long)(r + 48) * job.pstride];
-      s += (a + b) + (d + e);
+    // eight independent loads in flight per thread (the long reductions are latency-bound)
+    for (; r + 112 < job.P; r += 128) {
+      float v[8];
+#pragma unroll
+      for (int u = 0; u < 8; ++u) v[u] = p[(long)(r + 16 * u) * job.pstride];
+      s += ((v[0] + v[1]) + (v[2] + v[3])) + ((v[4] + v[5]) + (v[6] + v[7]));
     }
     for (; r < job.P; r += 16) s += p[(long)r * job.pstride];
   }
