@@ -66,6 +66,7 @@ def row_bytes(d, sz):
         "gate_bwd": N * 2 * H * sz + N * H * sz + N * 2 * H * sz + p_gate,  # Z, dhid -> dZ, partials
         "ln1_bwd": 3 * N * D * sz + p_tail // 2,                          # x, d(out1) -> dr1, partials
         "ln0_bwd": 3 * N * D * sz + p_tail // 2,                          # x, dr1 -> dx, partials
+        "tail_bwd": 3 * N * D * sz + 4 * B * D * 4,                       # x, d(out1) -> dx, per-sample partials
         "finalize": p_ln2 + p_gate + p_tail,                              # partials -> 14 small gradients
     }
 

@@ -39,6 +39,11 @@ def test_library_exports_every_declared_symbol(rb):
     assert lib.rm_abi_version() == 1
 
 
+def tail_per_sample(B, T, D, dtype):
+    """bf16 samples of at most 160 KB with 4-element token-mix chunks: backward tail one sample per workgroup."""
+    return dtype == "bf16" and D % 4 == 0 and (D // T) % 4 == 0 and T * D * 2 <= 64 * 1280 * 2
+
+
 def expected_workspace_bytes(B, T, D, k, dtype):
     """The workspace layout restated from rmblock.h / the library's documented regions."""
     al = lambda v: (v + 255) // 256 * 256
@@ -47,7 +52,8 @@ def expected_workspace_bytes(B, T, D, k, dtype):
     nb = (B + 63) // 64
     sizes = [N * D * sz, N * 2 * H * sz, N * H * sz, N * D * sz, 10 * N * 4,     # saved by the forward
              N * D * sz, N * H * sz, N * 2 * H * sz, N * D * sz, N * D * sz,     # backward scratch
-             3 * nb * T * D * 4, (4 * nb * T * H + nb * T * 2 * H) * 4, 4 * nb * T * D * 4]  # partials
+             3 * nb * T * D * 4, (4 * nb * T * H + nb * T * 2 * H) * 4,                        # partials
+             4 * (B if tail_per_sample(B, T, D, dtype) else nb * T) * D * 4]
     off = 0
     for s in sizes:
         off = al(off) + s

@@ -27,7 +27,8 @@ namespace rm {
 
 const char* const kKernelNames[KID_COUNT] = {
     "prologue", "gemm_up", "gate_fwd", "gemm_down", "ln2_fwd", "ln2_bwd", "gemm_dhid",
-    "gate_bwd", "gemm_dwout", "gemm_dw1", "gemm_dh1", "ln1_bwd", "ln0_bwd", "finalize", "token_mix"};
+    "gate_bwd", "gemm_dwout", "gemm_dw1", "gemm_dh1", "ln1_bwd", "ln0_bwd", "finalize", "token_mix",
+    "tail_bwd"};
 
 bool dims_valid(const rm_dims& d) {
   if (d.dtype != RM_F32 && d.dtype != RM_BF16) return false;
@@ -66,7 +67,8 @@ WsLayout ws_layout(const rm_dims& d) {
   L.dr1 = take(N * D * sz);
   L.p_ln2 = take(3 * nb * T * D * 4);
   L.p_gate = take((4 * nb * T * H + nb * T * 2 * H) * 4);
-  L.p_tail = take(4 * nb * T * D * 4);
+  // tail partials per (row group, token), or per sample when the tail runs one sample per workgroup
+  L.p_tail = take(4 * (sample_in_lds(d) ? (size_t)d.B : nb * T) * D * 4);
   L.total = align256(off);
   return L;
 }

@@ -28,6 +28,7 @@ enum KernelId {
   KID_LN0_BWD,        // token-mix adjoint (gather) + norm0 backward -> dx
   KID_FINALIZE,       // fixed-order sums of parameter-gradient partials
   KID_TOKEN_MIX,      // stand-alone token permutation
+  KID_TAIL_BWD,       // norm1 + token-mix adjoint + norm0 backward, one sample per workgroup
   KID_COUNT
 };
 
@@ -43,6 +44,14 @@ struct WsLayout {
 };
 
 bool dims_valid(const rm_dims& d);
+
+// One bf16 sample (T x D) fits the 160 KB LDS of a workgroup, with rows in
+// 4-element chunks whose token-mix sources are contiguous: the prologue and
+// the backward tail then run one sample per workgroup, staged in LDS.
+constexpr long SAMPLE_LDS_BYTES = 64L * 1280 * 2;
+inline bool sample_in_lds(const rm_dims& d) {
+  return d.dtype == RM_BF16 && d.D % 4 == 0 && (d.D / d.T) % 4 == 0 && (long)d.T * d.D * 2 <= SAMPLE_LDS_BYTES;
+}
 WsLayout ws_layout(const rm_dims& d);
 
 // stats block: 10 arrays of B*T floats in this order

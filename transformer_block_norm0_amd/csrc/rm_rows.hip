@@ -159,7 +159,7 @@ __global__ __launch_bounds__(512) void k_prologue(const ST* __restrict__ x, cons
 //      every output row -- with L1-bypassing loads;
 //   3. output row i: the token-mix gather and the residual read LDS, then
 //      norm1 in registers and one store of out1.
-constexpr int PRO_LDS_BYTES = 64 * MAXD * 2;  // 160 KB: T*D bf16 for T <= 64, D <= 1280
+constexpr int PRO_LDS_BYTES = (int)SAMPLE_LDS_BYTES;  // 160 KB: T*D bf16 for T <= 64, D <= 1280
 
 __device__ __forceinline__ float load_bypass_l1(const float* p) {
   return __hip_atomic_load(p, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
@@ -888,6 +888,232 @@ __global__ __launch_bounds__(MAXT) void k_gate_bwd_ring(const ST* __restrict__ Z
   }
 }
 
+// Backward tail for bf16, one workgroup (8 waves) per sample b with the
+// sample staged in LDS (at most 160 KB), so the two token-mix gathers read
+// LDS instead of re-fetching 40-byte pieces of HBM lines:
+//   1. x[b] -> LDS;
+//   2. norm1 backward, one wave per row i: r1 = token_mix(norm0(x)) + x is
+//      rebuilt from LDS (norm0 statistics saved by the forward),
+//      dr1 = rstd1 (dn - mean(dn) - n1 mean(dn n1)), dn = d(out1) gamma1,
+//      written to `dr1` (each wave later re-reads only its own rows);
+//      partial sums d(out1) n1 and d(out1) per column;
+//   3. the 8 waves' column partials added through LDS (fixed order) and
+//      stored; each wave's own dr1 rows -> LDS (over x);
+//   4. norm0 backward, one wave per row j: da0 = token_mix(dr1) gathered from
+//      LDS, dx = dr1 + rstd0 (dn - mean(dn) - n0 mean(dn n0)), dn = da0 gamma0,
+//      n0 from x (global, the rows read in step 1) and the saved statistics;
+//      column partials da0 n0 and da0 added through LDS at the end.
+// Partials: part[k][b][col], k = 0..3: dgamma0, dbeta0, dgamma1, dbeta1.
+__device__ __forceinline__ void wave_partials_to_lds(const float (&acc)[MAXD / 256][4], float* lds, int wave,
+                                                     int lane, int D) {
+#pragma unroll
+  for (int q = 0; q < MAXD / 256; ++q) {
+    const int c = (lane + 64 * q) * 4;
+    if (c < D) *reinterpret_cast<float4*>(lds + wave * D + c) = make_float4(acc[q][0], acc[q][1], acc[q][2], acc[q][3]);
+  }
+}
+// out[c] = sum over the nw waves' rows of lds (fixed order), c < D.
+__device__ __forceinline__ void sum_wave_rows(const float* lds, float* __restrict__ out, int nw, int D) {
+  for (int c = threadIdx.x; c < D; c += blockDim.x) {
+    float t = 0.f;
+    for (int w = 0; w < nw; ++w) t += lds[w * D + c];
+    out[c] = t;
+  }
+}
+
+__global__ __launch_bounds__(512) void k_tail_bwd_lds(const bf16_t* __restrict__ x, const bf16_t* __restrict__ dh1,
+                                                       const bf16_t* __restrict__ g0, const bf16_t* __restrict__ be0,
+                                                       const bf16_t* __restrict__ g1, const float* __restrict__ stats,
+                                                       bf16_t* __restrict__ dr1, bf16_t* __restrict__ dx,
+                                                       float* __restrict__ part, int B, int T, int D) {
+  constexpr int N = 4;
+  constexpr int Q = MAXD / (64 * N);
+  __shared__ __attribute__((aligned(16))) char sx[PRO_LDS_BYTES];
+  float* const lf = reinterpret_cast<float*>(sx);
+  const int b = blockIdx.x;
+  const int lane = threadIdx.x & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+  const int nw = blockDim.x >> 6;
+  const long NR = (long)B * T;
+  const long base = (long)b * T * D;
+  const int S = D / T;
+  const float invS = 1.0f / (float)S, invD = 1.0f / (float)D;
+  const long pblk = (long)B * D;
+
+  // 1. x[b] -> LDS
+  for (int j = wave; j < T; j += nw) {
+#pragma unroll
+    for (int q = 0; q < Q; ++q) {
+      const int c = (lane + 64 * q) * N;
+      if (c < D) *reinterpret_cast<uint2*>(sx + ((long)j * D + c) * 2) = *reinterpret_cast<const uint2*>(x + base + (long)j * D + c);
+    }
+  }
+  // gather sources of this lane's columns: row c/S (same for every row of the sample)
+  int jq[Q];
+  float mu0[Q], rs0[Q];
+  Raw<bf16_t, N> rg1[Q], rgg0[Q];
+#pragma unroll
+  for (int q = 0; q < Q; ++q) {
+    const int cc = min((lane + 64 * q) * N, D - N);
+    const int j = div_small(cc, invS);
+    jq[q] = j;
+    mu0[q] = stats[ST_MU0 * NR + (long)b * T + j];
+    rs0[q] = stats[ST_RS0 * NR + (long)b * T + j];
+    ldr(g1 + cc, rg1[q]);
+    ldr(g0 + cc, rgg0[q]);
+  }
+  __syncthreads();
+
+  // 2. norm1 backward
+  float pa[Q][N], pbb[Q][N];
+#pragma unroll
+  for (int q = 0; q < Q; ++q)
+#pragma unroll
+    for (int e = 0; e < N; ++e) pa[q][e] = pbb[q][e] = 0.f;
+  // d(out1) rows are prefetched one row ahead (the next row of this wave)
+  Raw<bf16_t, N> pdh[Q];
+#pragma unroll
+  for (int q = 0; q < Q; ++q) ldr(dh1 + ((long)b * T + min(wave, T - 1)) * D + min((lane + 64 * q) * N, D - N), pdh[q]);
+  for (int i = wave; i < T; i += nw) {
+    const long row = (long)b * T + i;
+    const float mu1 = stats[ST_MU1 * NR + row], rs1 = stats[ST_RS1 * NR + row];
+    Raw<bf16_t, N> cdh[Q];
+#pragma unroll
+    for (int q = 0; q < Q; ++q) {
+      cdh[q] = pdh[q];
+      ldr(dh1 + ((long)b * T + min(i + nw, T - 1)) * D + min((lane + 64 * q) * N, D - N), pdh[q]);
+    }
+    float n1[Q][N], dn[Q][N], gv[Q][N];
+    float s1 = 0.f, s2 = 0.f;
+#pragma unroll
+    for (int q = 0; q < Q; ++q) {
+      const int c = (lane + 64 * q) * N;
+      const int cc = min(c, D - N);
+      const float m = c < D ? 1.f : 0.f;
+      const int sc = i * S + (cc - jq[q] * S);
+      const uint2 ra = *reinterpret_cast<const uint2*>(sx + ((long)jq[q] * D + sc) * 2);
+      const uint2 rx = *reinterpret_cast<const uint2*>(sx + ((long)i * D + cc) * 2);
+      const Raw<bf16_t, N>& rdh = cdh[q];
+      float a[N], xi[N], cg0[N], cb0[N], cg1[N];
+      a[0] = bf_lo(ra.x); a[1] = bf_hi(ra.x); a[2] = bf_lo(ra.y); a[3] = bf_hi(ra.y);
+      xi[0] = bf_lo(rx.x); xi[1] = bf_hi(rx.x); xi[2] = bf_lo(rx.y); xi[3] = bf_hi(rx.y);
+      unpack(rdh, gv[q]);
+      ldv(g0 + sc, cg0);
+      ldv(be0 + sc, cb0);
+      unpack(rg1[q], cg1);
+#pragma unroll
+      for (int e = 0; e < N; ++e) {
+        const float r1 = (a[e] - mu0[q]) * rs0[q] * cg0[e] + cb0[e] + xi[e];
+        n1[q][e] = (r1 - mu1) * rs1;
+        dn[q][e] = m * gv[q][e] * cg1[e];
+        s1 += dn[q][e];
+        s2 += dn[q][e] * n1[q][e];
+      }
+    }
+    const float m1 = wave_sum_dpp(s1) * invD, m2 = wave_sum_dpp(s2) * invD;
+#pragma unroll
+    for (int q = 0; q < Q; ++q) {
+      const int c = (lane + 64 * q) * N;
+      if (c < D) {
+        float o[N];
+#pragma unroll
+        for (int e = 0; e < N; ++e) {
+          o[e] = rs1 * (dn[q][e] - m1 - n1[q][e] * m2);
+          pa[q][e] += gv[q][e] * n1[q][e];
+          pbb[q][e] += gv[q][e];
+        }
+        stv(dr1 + row * D + c, o);
+      }
+    }
+  }
+  __syncthreads();  // every wave is done with x in LDS (and its dr1 stores have completed)
+
+  // 3. norm1 partials; each wave's own dr1 rows -> LDS
+  wave_partials_to_lds(pa, lf, wave, lane, D);
+  __syncthreads();
+  sum_wave_rows(lf, part + 2 * pblk + (long)b * D, nw, D);
+  __syncthreads();
+  wave_partials_to_lds(pbb, lf, wave, lane, D);
+  __syncthreads();
+  sum_wave_rows(lf, part + 3 * pblk + (long)b * D, nw, D);
+  __syncthreads();
+  for (int i = wave; i < T; i += nw) {
+    const long row = (long)b * T + i;
+#pragma unroll
+    for (int q = 0; q < Q; ++q) {
+      const int c = (lane + 64 * q) * N;
+      if (c < D) *reinterpret_cast<uint2*>(sx + ((long)i * D + c) * 2) = *reinterpret_cast<const uint2*>(dr1 + row * D + c);
+    }
+  }
+  __syncthreads();
+
+  // 4. norm0 backward
+#pragma unroll
+  for (int q = 0; q < Q; ++q)
+#pragma unroll
+    for (int e = 0; e < N; ++e) pa[q][e] = pbb[q][e] = 0.f;
+  Raw<bf16_t, N> px[Q];
+#pragma unroll
+  for (int q = 0; q < Q; ++q) ldr(x + base + (long)min(wave, T - 1) * D + min((lane + 64 * q) * N, D - N), px[q]);
+  for (int j = wave; j < T; j += nw) {
+    const long row = (long)b * T + j;
+    const float mu = stats[ST_MU0 * NR + row], rs = stats[ST_RS0 * NR + row];
+    Raw<bf16_t, N> cx[Q];
+#pragma unroll
+    for (int q = 0; q < Q; ++q) {
+      cx[q] = px[q];
+      ldr(x + base + (long)min(j + nw, T - 1) * D + min((lane + 64 * q) * N, D - N), px[q]);
+    }
+    float n0[Q][N], dn[Q][N], da[Q][N];
+    float s1 = 0.f, s2 = 0.f;
+#pragma unroll
+    for (int q = 0; q < Q; ++q) {
+      const int c = (lane + 64 * q) * N;
+      const int cc = min(c, D - N);
+      const float m = c < D ? 1.f : 0.f;
+      // da0[j, c] = dr1[c/S, j*S + c%S]
+      const int sc = j * S + (cc - jq[q] * S);
+      const uint2 rd = *reinterpret_cast<const uint2*>(sx + ((long)jq[q] * D + sc) * 2);
+      da[q][0] = bf_lo(rd.x); da[q][1] = bf_hi(rd.x); da[q][2] = bf_lo(rd.y); da[q][3] = bf_hi(rd.y);
+      float xv[N], cg0[N];
+      unpack(cx[q], xv);
+      unpack(rgg0[q], cg0);
+#pragma unroll
+      for (int e = 0; e < N; ++e) {
+        n0[q][e] = (xv[e] - mu) * rs;
+        dn[q][e] = m * da[q][e] * cg0[e];
+        s1 += dn[q][e];
+        s2 += dn[q][e] * n0[q][e];
+      }
+    }
+    const float m1 = wave_sum_dpp(s1) * invD, m2 = wave_sum_dpp(s2) * invD;
+#pragma unroll
+    for (int q = 0; q < Q; ++q) {
+      const int c = (lane + 64 * q) * N;
+      if (c < D) {
+        const uint2 ro = *reinterpret_cast<const uint2*>(sx + ((long)j * D + c) * 2);
+        float own[N], o[N];
+        own[0] = bf_lo(ro.x); own[1] = bf_hi(ro.x); own[2] = bf_lo(ro.y); own[3] = bf_hi(ro.y);
+#pragma unroll
+        for (int e = 0; e < N; ++e) {
+          o[e] = own[e] + rs * (dn[q][e] - m1 - n0[q][e] * m2);
+          pa[q][e] += da[q][e] * n0[q][e];
+          pbb[q][e] += da[q][e];
+        }
+        stv(dx + row * D + c, o);
+      }
+    }
+  }
+  __syncthreads();
+  wave_partials_to_lds(pa, lf, wave, lane, D);
+  __syncthreads();
+  sum_wave_rows(lf, part + (long)b * D, nw, D);
+  __syncthreads();
+  wave_partials_to_lds(pbb, lf, wave, lane, D);
+  __syncthreads();
+  sum_wave_rows(lf, part + pblk + (long)b * D, nw, D);
+}
+
 // norm1 backward:  dr1 = rstd1 * (dn - mean(dn) - n1 * mean(dn * n1)),  dn = d(out1) * gamma1,
 // with r1 = token_mix(norm0(x)) + x recomputed through the token-mix gather.
 // Partials: dgamma1 (d(out1) * n1), dbeta1 (d(out1)).  Row (b, i) with i = t.
@@ -1133,7 +1359,7 @@ template <typename ST>
 hipError_t prologue_t(const rm_dims& d, const rm_params& p, const void* x, void* ws, const WsLayout& L,
                       hipStream_t s) {
   prof_begin(KID_PROLOGUE, s);
-  if (std::is_same<ST, bf16_t>::value && vec4_rows(d) && (long)d.T * d.D * 2 <= PRO_LDS_BYTES)
+  if (sample_in_lds(d))
     hipLaunchKernelGGL(k_prologue_lds, dim3(d.B), dim3(1024), 0, s, cptr<bf16_t>(x), cptr<bf16_t>(p.ln0_g),
                        cptr<bf16_t>(p.ln0_b), cptr<bf16_t>(p.ln1_g), cptr<bf16_t>(p.ln1_b), wsp<bf16_t>(ws, L.h1),
                        wsp<float>(ws, L.stats), d.B, d.T, d.D);
@@ -1244,6 +1470,15 @@ hipError_t tail_bwd_t(const rm_dims& d, const rm_params& p, const void* x, void*
                       hipStream_t s) {
   const dim3 grid(d.T, L.nb);
   hipError_t e;
+  if (sample_in_lds(d)) {
+    prof_begin(KID_TAIL_BWD, s);
+    hipLaunchKernelGGL(k_tail_bwd_lds, dim3(d.B), dim3(512), 0, s, cptr<bf16_t>(x), wsp<bf16_t>(ws, L.dh1),
+                       cptr<bf16_t>(p.ln0_g), cptr<bf16_t>(p.ln0_b), cptr<bf16_t>(p.ln1_g), wsp<float>(ws, L.stats),
+                       wsp<bf16_t>(ws, L.dr1), reinterpret_cast<bf16_t*>(dx), wsp<float>(ws, L.p_tail), d.B, d.T,
+                       d.D);
+    prof_end(KID_TAIL_BWD, s);
+    return hipGetLastError();
+  }
   prof_begin(KID_LN1_BWD, s);
   if (vec4_rows(d))
     hipLaunchKernelGGL((k_ln1_bwd<ST, 4, MAXD / 256>), grid, dim3(256), 0, s, cptr<ST>(x), wsp<ST>(ws, L.dh1),
@@ -1284,10 +1519,13 @@ hipError_t finalize_t(const rm_dims& d, const rm_grads& g, void* ws, const WsLay
   J.j[5] = {pg + 2 * bg, H, nb * T, H, g.lng_g};
   J.j[6] = {pg + 3 * bg, H, nb * T, H, g.lng_b};
   J.j[7] = {pg + 4 * bg, (long)T * 2 * H, nb, T * 2 * H, g.b1};
-  J.j[8] = {pt + 0 * bl, D, nb * T, D, g.ln0_g};
-  J.j[9] = {pt + 1 * bl, D, nb * T, D, g.ln0_b};
-  J.j[10] = {pt + 2 * bl, D, nb * T, D, g.ln1_g};
-  J.j[11] = {pt + 3 * bl, D, nb * T, D, g.ln1_b};
+  // tail partials: [4][row groups * T][D], or [4][B][D] when the tail ran one sample per workgroup
+  const int pt_rows = sample_in_lds(d) ? d.B : nb * T;
+  const long bt = (long)pt_rows * D;
+  J.j[8] = {pt + 0 * bt, D, pt_rows, D, g.ln0_g};
+  J.j[9] = {pt + 1 * bt, D, pt_rows, D, g.ln0_b};
+  J.j[10] = {pt + 2 * bt, D, pt_rows, D, g.ln1_g};
+  J.j[11] = {pt + 3 * bt, D, pt_rows, D, g.ln1_b};
   const int maxc = T * 2 * H;
   prof_begin(KID_FINALIZE, s);
   hipLaunchKernelGGL(k_finalize<ST>, dim3((maxc + 63) / 64, 12), dim3(1024), 0, s, J);
