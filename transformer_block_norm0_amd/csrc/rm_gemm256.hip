@@ -260,11 +260,10 @@ __device__ __forceinline__ void dma_pair(char* sa, char* sb, const Src& s, const
   dma_slab<BKM>(sb, s.B, s.offb, g.b_ld, kslab * BK, wave);
 }
 
-// v = acc (+ bias) (+ residual) for the 4 consecutive columns n..n+3 of row m
-// that this lane holds in accumulator block (i, j), v/4 group q.
+// v = acc (+ bias) (+ residual, already loaded) for the 4 consecutive
+// columns of accumulator block (i, j), v/4 group q held by this lane.
 __device__ __forceinline__ void epi_values(float (&v)[4], const f32x16_t (&acc)[4][4], int i, int j, int q,
-                                           const GemmArgs& g, uint32_t boff, __amdgpu_buffer_rsrc_t rrs,
-                                           uint32_t rld, int rsz, int m, int n, bool ok) {
+                                           const GemmArgs& g, uint32_t boff, v2u32 res) {
 #pragma unroll
   for (int e = 0; e < 4; ++e) v[e] = acc[i][j][4 * q + e];
   if (g.bias) {
@@ -276,19 +275,24 @@ __device__ __forceinline__ void epi_values(float (&v)[4], const f32x16_t (&acc)[
     v[3] += __uint_as_float(w.y & 0xffff0000u);
   }
   if (g.res) {
-    const uint32_t ro = ok ? (uint32_t)m * rld + (uint32_t)n * rsz : OUT_OF_RANGE;
-    if (g.res_f32) {
-      const v4u32 a = __builtin_bit_cast(v4u32, __builtin_amdgcn_raw_buffer_load_b128(rrs, ro, 0, 0));
-      v[0] += __uint_as_float(a.x); v[1] += __uint_as_float(a.y);
-      v[2] += __uint_as_float(a.z); v[3] += __uint_as_float(a.w);
-    } else {
-      const v2u32 a = __builtin_bit_cast(v2u32, __builtin_amdgcn_raw_buffer_load_b64(rrs, ro, 0, 0));
-      v[0] += __uint_as_float(a.x << 16);
-      v[1] += __uint_as_float(a.x & 0xffff0000u);
-      v[2] += __uint_as_float(a.y << 16);
-      v[3] += __uint_as_float(a.y & 0xffff0000u);
-    }
+    v[0] += __uint_as_float(res.x << 16);
+    v[1] += __uint_as_float(res.x & 0xffff0000u);
+    v[2] += __uint_as_float(res.y << 16);
+    v[3] += __uint_as_float(res.y & 0xffff0000u);
   }
+}
+
+// The bf16 residual of m block i: 16 loads of 4 columns (zero where out of range).
+__device__ __forceinline__ void load_residual(v2u32 (&r)[16], const GemmArgs& g, __amdgpu_buffer_rsrc_t rrs,
+                                              uint32_t rld, int m, int nbase, bool mok) {
+#pragma unroll
+  for (int j = 0; j < 4; ++j)
+#pragma unroll
+    for (int q = 0; q < 4; ++q) {
+      const int n = nbase + 32 * j + 8 * q;
+      const uint32_t ro = (mok && n < g.N) ? (uint32_t)m * rld + (uint32_t)n * 2 : OUT_OF_RANGE;
+      r[4 * j + q] = __builtin_bit_cast(v2u32, __builtin_amdgcn_raw_buffer_load_b64(rrs, ro, 0, 0));
+    }
 }
 
 // Tile epilogue straight from the accumulators: v = acc (+ bias) (+ residual).
@@ -301,8 +305,8 @@ __device__ __forceinline__ void epi_values(float (&v)[4], const f32x16_t (&acc)[
 //   * fp32 output: one 16-byte store per (i, j, q), 64 per wave.
 // Every store is issued (rows past M or columns past N get an out-of-range
 // offset that the buffer unit drops): at least EPI_STORES per wave.  One m
-// block at a time (scheduling barriers between blocks), so at most 16
-// residual loads are live at once.
+// block at a time (scheduling barriers between blocks); the residual (bf16)
+// of m block i+1 is loaded while block i is computed and stored.
 __device__ __forceinline__ void epilogue(const f32x16_t (&acc)[4][4], const GemmArgs& g, const Tile& c,
                                          const char* sbias, int wm, int wn, int lane) {
   const int r = lane & 31, h = lane >> 5;
@@ -311,18 +315,21 @@ __device__ __forceinline__ void epilogue(const f32x16_t (&acc)[4][4], const Gemm
   const int esz = g.c_f32 ? 4 : 2;
   char* cbase = reinterpret_cast<char*>(g.C) + (long)c.t * g.c_bs * esz;
   const __amdgpu_buffer_rsrc_t crs = make_rsrc(cbase, (long)g.M * g.c_ld * esz);
-  const int rsz = g.res_f32 ? 4 : 2;
-  const char* rbase = g.res ? reinterpret_cast<const char*>(g.res) + (long)c.t * g.res_bs * rsz : cbase;
-  const __amdgpu_buffer_rsrc_t rrs = make_rsrc(rbase, g.res ? (long)g.M * g.res_ld * rsz : 0L);
+  const char* rbase = g.res ? reinterpret_cast<const char*>(g.res) + (long)c.t * g.res_bs * 2 : cbase;
+  const __amdgpu_buffer_rsrc_t rrs = make_rsrc(rbase, g.res ? (long)g.M * g.res_ld * 2 : 0L);
   // byte strides (uniform; every per-token offset is below 2^31)
-  const uint32_t cld = (uint32_t)(g.c_ld * esz), rld = (uint32_t)(g.res_ld * rsz);
+  const uint32_t cld = (uint32_t)(g.c_ld * esz), rld = (uint32_t)(g.res_ld * 2);
   uint32_t boff = lds_addr(sbias) + 2 * nb;
+  v2u32 res[2][16];
+  if (g.res) load_residual(res[0], g, rrs, rld, mb, c.n0 + nb, mb < g.M);
 #pragma unroll
   for (int i = 0; i < 4; ++i) {
     __builtin_amdgcn_sched_barrier(0);
     asm volatile("" : "+v"(boff));  // re-read the bias per m block instead of keeping 64 values live
     const int m = mb + 32 * i;
     const bool mok = m < g.M;
+    if (g.res && i < 3) load_residual(res[(i + 1) & 1], g, rrs, rld, m + 32, c.n0 + nb, m + 32 < g.M);
+    const v2u32(&rc)[16] = res[i & 1];
 #pragma unroll
     for (int j = 0; j < 4; ++j) {
       if (g.c_f32) {
@@ -331,7 +338,7 @@ __device__ __forceinline__ void epilogue(const f32x16_t (&acc)[4][4], const Gemm
           const int n = c.n0 + nb + 32 * j + 8 * q;
           const bool ok = mok && n < g.N;  // N % 8 == 0: the 4 columns are all in or all out
           float v[4];
-          epi_values(v, acc, i, j, q, g, boff, rrs, rld, rsz, m, n, ok);
+          epi_values(v, acc, i, j, q, g, boff, rc[4 * j + q]);
           const uint32_t co = ok ? (uint32_t)m * cld + (uint32_t)n * 4 : OUT_OF_RANGE;
           const v4u32 d = {__float_as_uint(v[0]), __float_as_uint(v[1]), __float_as_uint(v[2]), __float_as_uint(v[3])};
           __builtin_amdgcn_raw_buffer_store_b128(d, crs, co, 0, 0);
@@ -339,11 +346,9 @@ __device__ __forceinline__ void epilogue(const f32x16_t (&acc)[4][4], const Gemm
       } else {
 #pragma unroll
         for (int q = 0; q < 4; q += 2) {
-          const int n0 = c.n0 + nb + 32 * j + 8 * q, n1 = n0 + 8;
           float v0[4], v1[4];
-          epi_values(v0, acc, i, j, q, g, boff, rrs, rld, rsz, m, n0, mok && n0 < g.N);
-          epi_values(v1, acc, i, j, q + 1, g, boff, rrs, rld, rsz, m, n1, mok && n1 < g.N);
-          // lane < 32: (v0 | partner's v0) = columns 8q..8q+7;  lane >= 32: (partner's v1 | v1) = 8(q+1)..
+          epi_values(v0, acc, i, j, q, g, boff, rc[4 * j + q]);
+          epi_values(v1, acc, i, j, q + 1, g, boff, rc[4 * j + q + 1]);
           uint32_t a0 = bf16_pair(v0[0], v0[1]), a1 = bf16_pair(v0[2], v0[3]);
           uint32_t b0 = bf16_pair(v1[0], v1[1]), b1 = bf16_pair(v1[2], v1[3]);
           const auto s0 = __builtin_amdgcn_permlane32_swap(a0, b0, false, false);
@@ -545,9 +550,10 @@ bool gemm256_supported(int dtype, bool a_kmajor, bool b_kmajor, const GemmArgs& 
   // the epilogue stores 4 columns per lane; a bias tile is copied in 16-byte pieces
   if (g.N % 8 || g.c_ld % 4 || g.c_bs % 4 || (reinterpret_cast<uintptr_t>(g.C) & 15)) return false;
   if (g.bias && (g.bias_bs % 8 || (reinterpret_cast<uintptr_t>(g.bias) & 15))) return false;
-  if (g.res && (g.res_ld % 4 || g.res_bs % 4 || (reinterpret_cast<uintptr_t>(g.res) & 15))) return false;
+  if (g.res && (g.res_f32 || g.res_ld % 4 || g.res_bs % 4 || (reinterpret_cast<uintptr_t>(g.res) & 15)))
+    return false;  // the residual is bf16
   // per-token byte offsets of C and the residual fit the 31-bit buffer range
-  const long csz = g.c_f32 ? 4 : 2, rsz = g.res_f32 ? 4 : 2;
+  const long csz = g.c_f32 ? 4 : 2, rsz = 2;
   if ((long)g.M * g.c_ld * csz > 0x7fffffffL) return false;
   if (g.res && (long)g.M * g.res_ld * rsz > 0x7fffffffL) return false;
   return true;
