@@ -52,6 +52,18 @@ class DeviceCase:
         self.grads = {n: torch.empty_like(v) for n, v in self.params.items()}
         self.ws = rb.alloc_workspace(self.cd, device)
 
+    def misalign(self):
+        """Move x, dy, y and dx to buffers that start 2 bytes past a 16-byte boundary
+        (element-aligned only, as the interface allows)."""
+        import torch
+        for name in ("x", "dy", "y", "dx"):
+            t = getattr(self, name)
+            buf = torch.empty(t.numel() + 8, dtype=t.dtype, device=t.device)
+            v = buf[1:1 + t.numel()].view(t.shape)
+            v.copy_(t)
+            assert v.data_ptr() % 16 != 0
+            setattr(self, name, v)
+
     def fwd(self, stream=None):
         import transformer_block_norm0_amd as rb
         rb.block_fwd(self.cd, self.params, self.x, self.y, self.ws, stream=stream)

@@ -40,8 +40,8 @@ def test_library_exports_every_declared_symbol(rb):
 
 
 def tail_per_sample(B, T, D, dtype):
-    """bf16 samples of at most 160 KB with 4-element token-mix chunks: backward tail one sample per workgroup."""
-    return dtype == "bf16" and D % 4 == 0 and (D // T) % 4 == 0 and T * D * 2 <= 64 * 1280 * 2
+    """bf16 samples of at most 160 KB, 16-byte rows, 4-element token-mix chunks: backward tail one sample per workgroup."""
+    return dtype == "bf16" and D % 8 == 0 and (D // T) % 4 == 0 and T * D * 2 <= 64 * 1280 * 2
 
 
 def expected_workspace_bytes(B, T, D, k, dtype):

@@ -137,6 +137,24 @@ def test_bitwise_repeatable():
         assert np.array_equal(a[k], b[k]), k
 
 
+@pytest.mark.parametrize("shape", [(67, 16, 256, 2), (5, 8, 1280, 3)])
+def test_misaligned_io_same_bits(shape):
+    """Element-aligned (not 16-byte aligned) x, dy, y, dx give the same bits as aligned buffers:
+    the kernels that stage a sample in LDS by 16-byte copies take their plain-load path."""
+    B, T, D, k = shape
+    say(f"misaligned io {shape} bf16")
+    case = make_custom(B, T, D, k, "bf16", seed=5, ln_affine="random")
+    a = DeviceCase(case)
+    a.run()
+    ra = a.raw_bits()
+    m = DeviceCase(case)
+    m.misalign()
+    m.run()
+    rm = m.raw_bits()
+    for key in ra:
+        assert np.array_equal(ra[key], rm[key]), key
+
+
 def test_backward_repeatable_on_same_workspace():
     """The backward leaves the forward's saved state intact: a second call agrees bitwise."""
     import torch

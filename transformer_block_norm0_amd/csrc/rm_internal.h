@@ -45,12 +45,14 @@ struct WsLayout {
 
 bool dims_valid(const rm_dims& d);
 
-// One bf16 sample (T x D) fits the 160 KB LDS of a workgroup, with rows in
-// 4-element chunks whose token-mix sources are contiguous: the prologue and
-// the backward tail then run one sample per workgroup, staged in LDS.
+// One bf16 sample (T x D) fits the 160 KB LDS of a workgroup, rows are whole
+// 16-byte pieces (D % 8 == 0) and 4-element chunks have contiguous token-mix
+// sources: the prologue and the backward tail then run one sample per
+// workgroup, staged in LDS by direct copies (which also need a 16-byte
+// aligned x).
 constexpr long SAMPLE_LDS_BYTES = 64L * 1280 * 2;
 inline bool sample_in_lds(const rm_dims& d) {
-  return d.dtype == RM_BF16 && d.D % 4 == 0 && (d.D / d.T) % 4 == 0 && (long)d.T * d.D * 2 <= SAMPLE_LDS_BYTES;
+  return d.dtype == RM_BF16 && d.D % 8 == 0 && (d.D / d.T) % 4 == 0 && (long)d.T * d.D * 2 <= SAMPLE_LDS_BYTES;
 }
 WsLayout ws_layout(const rm_dims& d);
 

@@ -890,20 +890,24 @@ __global__ __launch_bounds__(MAXT) void k_gate_bwd_ring(const ST* __restrict__ Z
 
 // Backward tail for bf16, one workgroup (8 waves) per sample b with the
 // sample staged in LDS (at most 160 KB), so the two token-mix gathers read
-// LDS instead of re-fetching 40-byte pieces of HBM lines:
-//   1. x[b] -> LDS;
-//   2. norm1 backward, one wave per row i: r1 = token_mix(norm0(x)) + x is
-//      rebuilt from LDS (norm0 statistics saved by the forward),
+// LDS instead of re-fetching 40-byte pieces of HBM lines.  Wave w owns the
+// contiguous rows R*w .. R*w+R-1 (R = ceil(T / 8)) in both row phases.
+//   1. x[b] -> LDS by direct 16-byte copies, all in flight together (plain
+//      loads when x is not 16-byte aligned);
+//   2. norm1 backward per row i: r1 = token_mix(norm0(x)) + x is rebuilt
+//      from LDS (norm0 statistics saved by the forward),
 //      dr1 = rstd1 (dn - mean(dn) - n1 mean(dn n1)), dn = d(out1) gamma1,
-//      written to `dr1` (each wave later re-reads only its own rows);
-//      partial sums d(out1) n1 and d(out1) per column;
+//      written to `dr1`; partial sums d(out1) n1 and d(out1) per column.
+//      The next row's d(out1), gathered gamma0/beta0 and statistics are
+//      loaded while the current row is computed;
 //   3. the 8 waves' column partials added through LDS (fixed order) and
-//      stored; each wave's own dr1 rows -> LDS (over x);
-//   4. norm0 backward, one wave per row j: da0 = token_mix(dr1) gathered from
-//      LDS, dx = dr1 + rstd0 (dn - mean(dn) - n0 mean(dn n0)), dn = da0 gamma0,
-//      n0 from x (global, the rows read in step 1) and the saved statistics;
+//      stored; each wave's own dr1 rows copied back into LDS (over x);
+//   4. norm0 backward per row j: da0 = token_mix(dr1) gathered from LDS,
+//      dx = dr1 + rstd0 (dn - mean(dn) - n0 mean(dn n0)), dn = da0 gamma0,
+//      n0 from x (global, next row prefetched) and the saved statistics;
 //      column partials da0 n0 and da0 added through LDS at the end.
 // Partials: part[k][b][col], k = 0..3: dgamma0, dbeta0, dgamma1, dbeta1.
+// Needs D % 8 == 0 (16-byte rows), S % 4 == 0, T * D * 2 <= 160 KB.
 __device__ __forceinline__ void wave_partials_to_lds(const float (&acc)[MAXD / 256][4], float* lds, int wave,
                                                      int lane, int D) {
 #pragma unroll
@@ -936,32 +940,48 @@ __global__ __launch_bounds__(512) void k_tail_bwd_lds(const bf16_t* __restrict__
   const int nw = blockDim.x >> 6;
   const long NR = (long)B * T;
   const long base = (long)b * T * D;
+  const long srow = (long)b * T;  // first row of the sample
   const int S = D / T;
   const float invS = 1.0f / (float)S, invD = 1.0f / (float)D;
   const long pblk = (long)B * D;
+  const int R = (T + nw - 1) / nw;
+  const int r0 = min(wave * R, T), r1 = min(r0 + R, T);  // this wave's rows (none if r0 == T)
+  const int i0 = min(r0, T - 1);
 
   // 1. x[b] -> LDS
-  for (int j = wave; j < T; j += nw) {
+  if ((reinterpret_cast<uintptr_t>(x) & 15) == 0) {
+    copy_to_lds(x + base, sx, T * D * 2, wave * 64, nw * 64, lane);
+  } else {
+    for (int j = wave; j < T; j += nw) {
 #pragma unroll
-    for (int q = 0; q < Q; ++q) {
-      const int c = (lane + 64 * q) * N;
-      if (c < D) *reinterpret_cast<uint2*>(sx + ((long)j * D + c) * 2) = *reinterpret_cast<const uint2*>(x + base + (long)j * D + c);
+      for (int q = 0; q < Q; ++q) {
+        const int c = (lane + 64 * q) * N;
+        if (c < D)
+          *reinterpret_cast<uint2*>(sx + ((long)j * D + c) * 2) = *reinterpret_cast<const uint2*>(x + base + (long)j * D + c);
+      }
     }
   }
-  // gather sources of this lane's columns: row c/S (same for every row of the sample)
+  // gather sources of this lane's columns: row c/S (same for every row of the sample);
+  // the first row's d(out1), gathered gamma0 / beta0 and statistics
   int jq[Q];
   float mu0[Q], rs0[Q];
-  Raw<bf16_t, N> rg1[Q], rgg0[Q];
+  Raw<bf16_t, N> rg1[Q], rgg0[Q], pdh[Q], pg0[Q], pb0[Q];
 #pragma unroll
   for (int q = 0; q < Q; ++q) {
     const int cc = min((lane + 64 * q) * N, D - N);
     const int j = div_small(cc, invS);
     jq[q] = j;
-    mu0[q] = stats[ST_MU0 * NR + (long)b * T + j];
-    rs0[q] = stats[ST_RS0 * NR + (long)b * T + j];
+    mu0[q] = stats[ST_MU0 * NR + srow + j];
+    rs0[q] = stats[ST_RS0 * NR + srow + j];
     ldr(g1 + cc, rg1[q]);
     ldr(g0 + cc, rgg0[q]);
+    ldr(dh1 + (srow + i0) * D + cc, pdh[q]);
+    const int sc = i0 * S + (cc - j * S);
+    ldr(g0 + sc, pg0[q]);
+    ldr(be0 + sc, pb0[q]);
   }
+  float pmu = stats[ST_MU1 * NR + srow + i0], prs = stats[ST_RS1 * NR + srow + i0];
+  wait_vm_all();
   __syncthreads();
 
   // 2. norm1 backward
@@ -970,19 +990,24 @@ __global__ __launch_bounds__(512) void k_tail_bwd_lds(const bf16_t* __restrict__
   for (int q = 0; q < Q; ++q)
 #pragma unroll
     for (int e = 0; e < N; ++e) pa[q][e] = pbb[q][e] = 0.f;
-  // d(out1) rows are prefetched one row ahead (the next row of this wave)
-  Raw<bf16_t, N> pdh[Q];
-#pragma unroll
-  for (int q = 0; q < Q; ++q) ldr(dh1 + ((long)b * T + min(wave, T - 1)) * D + min((lane + 64 * q) * N, D - N), pdh[q]);
-  for (int i = wave; i < T; i += nw) {
-    const long row = (long)b * T + i;
-    const float mu1 = stats[ST_MU1 * NR + row], rs1 = stats[ST_RS1 * NR + row];
-    Raw<bf16_t, N> cdh[Q];
+  for (int i = r0; i < r1; ++i) {
+    const long row = srow + i;
+    const float mu1 = pmu, rs1 = prs;
+    const int in = min(i + 1, T - 1);
+    Raw<bf16_t, N> cdh[Q], cg0[Q], cb0[Q];
 #pragma unroll
     for (int q = 0; q < Q; ++q) {
+      const int cc = min((lane + 64 * q) * N, D - N);
       cdh[q] = pdh[q];
-      ldr(dh1 + ((long)b * T + min(i + nw, T - 1)) * D + min((lane + 64 * q) * N, D - N), pdh[q]);
+      cg0[q] = pg0[q];
+      cb0[q] = pb0[q];
+      ldr(dh1 + (srow + in) * D + cc, pdh[q]);
+      const int scn = in * S + (cc - jq[q] * S);
+      ldr(g0 + scn, pg0[q]);
+      ldr(be0 + scn, pb0[q]);
     }
+    pmu = stats[ST_MU1 * NR + srow + in];
+    prs = stats[ST_RS1 * NR + srow + in];
     float n1[Q][N], dn[Q][N], gv[Q][N];
     float s1 = 0.f, s2 = 0.f;
 #pragma unroll
@@ -993,19 +1018,18 @@ __global__ __launch_bounds__(512) void k_tail_bwd_lds(const bf16_t* __restrict__
       const int sc = i * S + (cc - jq[q] * S);
       const uint2 ra = *reinterpret_cast<const uint2*>(sx + ((long)jq[q] * D + sc) * 2);
       const uint2 rx = *reinterpret_cast<const uint2*>(sx + ((long)i * D + cc) * 2);
-      const Raw<bf16_t, N>& rdh = cdh[q];
-      float a[N], xi[N], cg0[N], cb0[N], cg1[N];
+      float a[N], xi[N], gg0[N], bb0[N], gg1[N];
       a[0] = bf_lo(ra.x); a[1] = bf_hi(ra.x); a[2] = bf_lo(ra.y); a[3] = bf_hi(ra.y);
       xi[0] = bf_lo(rx.x); xi[1] = bf_hi(rx.x); xi[2] = bf_lo(rx.y); xi[3] = bf_hi(rx.y);
-      unpack(rdh, gv[q]);
-      ldv(g0 + sc, cg0);
-      ldv(be0 + sc, cb0);
-      unpack(rg1[q], cg1);
+      unpack(cdh[q], gv[q]);
+      unpack(cg0[q], gg0);
+      unpack(cb0[q], bb0);
+      unpack(rg1[q], gg1);
 #pragma unroll
       for (int e = 0; e < N; ++e) {
-        const float r1 = (a[e] - mu0[q]) * rs0[q] * cg0[e] + cb0[e] + xi[e];
-        n1[q][e] = (r1 - mu1) * rs1;
-        dn[q][e] = m * gv[q][e] * cg1[e];
+        const float r1v = (a[e] - mu0[q]) * rs0[q] * gg0[e] + bb0[e] + xi[e];
+        n1[q][e] = (r1v - mu1) * rs1;
+        dn[q][e] = m * gv[q][e] * gg1[e];
         s1 += dn[q][e];
         s2 += dn[q][e] * n1[q][e];
       }
@@ -1026,7 +1050,8 @@ __global__ __launch_bounds__(512) void k_tail_bwd_lds(const bf16_t* __restrict__
       }
     }
   }
-  __syncthreads();  // every wave is done with x in LDS (and its dr1 stores have completed)
+  wait_vm_all();    // this wave's dr1 stores have completed
+  __syncthreads();  // every wave is done with x in LDS
 
   // 3. norm1 partials; each wave's own dr1 rows -> LDS
   wave_partials_to_lds(pa, lf, wave, lane, D);
@@ -1037,14 +1062,14 @@ __global__ __launch_bounds__(512) void k_tail_bwd_lds(const bf16_t* __restrict__
   __syncthreads();
   sum_wave_rows(lf, part + 3 * pblk + (long)b * D, nw, D);
   __syncthreads();
-  for (int i = wave; i < T; i += nw) {
-    const long row = (long)b * T + i;
+  if (r1 > r0) copy_to_lds(dr1 + (srow + r0) * D, sx + (long)r0 * D * 2, (r1 - r0) * D * 2, 0, 64, lane);
+  // the first row's x and statistics
+  Raw<bf16_t, N> px[Q];
 #pragma unroll
-    for (int q = 0; q < Q; ++q) {
-      const int c = (lane + 64 * q) * N;
-      if (c < D) *reinterpret_cast<uint2*>(sx + ((long)i * D + c) * 2) = *reinterpret_cast<const uint2*>(dr1 + row * D + c);
-    }
-  }
+  for (int q = 0; q < Q; ++q) ldr(x + base + (long)i0 * D + min((lane + 64 * q) * N, D - N), px[q]);
+  pmu = stats[ST_MU0 * NR + srow + i0];
+  prs = stats[ST_RS0 * NR + srow + i0];
+  wait_vm_all();
   __syncthreads();
 
   // 4. norm0 backward
@@ -1052,18 +1077,18 @@ __global__ __launch_bounds__(512) void k_tail_bwd_lds(const bf16_t* __restrict__
   for (int q = 0; q < Q; ++q)
 #pragma unroll
     for (int e = 0; e < N; ++e) pa[q][e] = pbb[q][e] = 0.f;
-  Raw<bf16_t, N> px[Q];
-#pragma unroll
-  for (int q = 0; q < Q; ++q) ldr(x + base + (long)min(wave, T - 1) * D + min((lane + 64 * q) * N, D - N), px[q]);
-  for (int j = wave; j < T; j += nw) {
-    const long row = (long)b * T + j;
-    const float mu = stats[ST_MU0 * NR + row], rs = stats[ST_RS0 * NR + row];
+  for (int j = r0; j < r1; ++j) {
+    const long row = srow + j;
+    const float mu = pmu, rs = prs;
+    const int jn = min(j + 1, T - 1);
     Raw<bf16_t, N> cx[Q];
 #pragma unroll
     for (int q = 0; q < Q; ++q) {
       cx[q] = px[q];
-      ldr(x + base + (long)min(j + nw, T - 1) * D + min((lane + 64 * q) * N, D - N), px[q]);
+      ldr(x + base + (long)jn * D + min((lane + 64 * q) * N, D - N), px[q]);
     }
+    pmu = stats[ST_MU0 * NR + srow + jn];
+    prs = stats[ST_RS0 * NR + srow + jn];
     float n0[Q][N], dn[Q][N], da[Q][N];
     float s1 = 0.f, s2 = 0.f;
 #pragma unroll
