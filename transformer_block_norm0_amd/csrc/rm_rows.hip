@@ -148,6 +148,39 @@ __global__ __launch_bounds__(512) void k_prologue(const ST* __restrict__ x, cons
   }
 }
 
+// Raw buffer resource over `bytes` bytes at p (gfx9 word 3: 32-bit data
+// format).  Range checks apply to the per-lane offset only (not the scalar
+// one): a lane offset of 0x80000000 reads zero / drops the store.
+__device__ __forceinline__ __amdgpu_buffer_rsrc_t row_rsrc(const void* p, long bytes) {
+  return __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(p), (short)0, (int)min(bytes, 0x7fffffffL), 0x00020000);
+}
+
+template <typename ST>
+__device__ __forceinline__ void bld4(__amdgpu_buffer_rsrc_t rs, uint32_t voff, uint32_t soff, Raw<ST, 4>& r) {
+  if constexpr (sizeof(ST) == 2) {
+    typedef uint32_t v2u __attribute__((ext_vector_type(2)));
+    const v2u a = __builtin_bit_cast(v2u, __builtin_amdgcn_raw_buffer_load_b64(rs, voff, soff, 0));
+    r.w[0] = a.x; r.w[1] = a.y;
+  } else {
+    typedef uint32_t v4u __attribute__((ext_vector_type(4)));
+    const v4u a = __builtin_bit_cast(v4u, __builtin_amdgcn_raw_buffer_load_b128(rs, voff, soff, 0));
+    r.w[0] = a.x; r.w[1] = a.y; r.w[2] = a.z; r.w[3] = a.w;
+  }
+}
+
+template <typename ST>
+__device__ __forceinline__ void bst4(__amdgpu_buffer_rsrc_t rs, uint32_t voff, uint32_t soff, const float (&v)[4]) {
+  if constexpr (sizeof(ST) == 2) {
+    typedef uint32_t v2u __attribute__((ext_vector_type(2)));
+    const v2u a = {bf_pack(v[0], v[1]), bf_pack(v[2], v[3])};
+    __builtin_amdgcn_raw_buffer_store_b64(a, rs, voff, soff, 0);
+  } else {
+    typedef uint32_t v4u __attribute__((ext_vector_type(4)));
+    const v4u a = {__float_as_uint(v[0]), __float_as_uint(v[1]), __float_as_uint(v[2]), __float_as_uint(v[3])};
+    __builtin_amdgcn_raw_buffer_store_b128(a, rs, voff, soff, 0);
+  }
+}
+
 // ---------------------------------------------------------------------------
 // Forward prologue for bf16 with the whole sample staged in LDS (T*D*2 bytes,
 // at most 160 KB), so x is read from HBM once.  One workgroup (16 waves) per
@@ -730,39 +763,6 @@ __global__ __launch_bounds__(MAXT) void k_gate_bwd(const ST* __restrict__ Z, con
 //   dU  = rsx (dux gx - mean(dux gx) - nx mean(dux gx nx)), same for dG.
 constexpr int RING = 2;
 
-// Raw buffer resource over `bytes` bytes at p (gfx9 word 3: 32-bit data
-// format).  Range checks apply to the per-lane offset only (not the scalar
-// one): a lane offset of 0x80000000 reads zero / drops the store.
-__device__ __forceinline__ __amdgpu_buffer_rsrc_t row_rsrc(const void* p, long bytes) {
-  return __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(p), (short)0, (int)min(bytes, 0x7fffffffL), 0x00020000);
-}
-
-template <typename ST>
-__device__ __forceinline__ void bld4(__amdgpu_buffer_rsrc_t rs, uint32_t voff, uint32_t soff, Raw<ST, 4>& r) {
-  if constexpr (sizeof(ST) == 2) {
-    typedef uint32_t v2u __attribute__((ext_vector_type(2)));
-    const v2u a = __builtin_bit_cast(v2u, __builtin_amdgcn_raw_buffer_load_b64(rs, voff, soff, 0));
-    r.w[0] = a.x; r.w[1] = a.y;
-  } else {
-    typedef uint32_t v4u __attribute__((ext_vector_type(4)));
-    const v4u a = __builtin_bit_cast(v4u, __builtin_amdgcn_raw_buffer_load_b128(rs, voff, soff, 0));
-    r.w[0] = a.x; r.w[1] = a.y; r.w[2] = a.z; r.w[3] = a.w;
-  }
-}
-
-template <typename ST>
-__device__ __forceinline__ void bst4(__amdgpu_buffer_rsrc_t rs, uint32_t voff, uint32_t soff, const float (&v)[4]) {
-  if constexpr (sizeof(ST) == 2) {
-    typedef uint32_t v2u __attribute__((ext_vector_type(2)));
-    const v2u a = {bf_pack(v[0], v[1]), bf_pack(v[2], v[3])};
-    __builtin_amdgcn_raw_buffer_store_b64(a, rs, voff, soff, 0);
-  } else {
-    typedef uint32_t v4u __attribute__((ext_vector_type(4)));
-    const v4u a = {__float_as_uint(v[0]), __float_as_uint(v[1]), __float_as_uint(v[2]), __float_as_uint(v[3])};
-    __builtin_amdgcn_raw_buffer_store_b128(a, rs, voff, soff, 0);
-  }
-}
-
 template <typename ST, int MAXT>
 __global__ __launch_bounds__(MAXT) void k_gate_bwd_ring(const ST* __restrict__ Z, const ST* __restrict__ dhid,
                                                         const ST* __restrict__ gx, const ST* __restrict__ bx,
@@ -898,8 +898,9 @@ __global__ __launch_bounds__(MAXT) void k_gate_bwd_ring(const ST* __restrict__ Z
 //      from LDS (norm0 statistics saved by the forward),
 //      dr1 = rstd1 (dn - mean(dn) - n1 mean(dn n1)), dn = d(out1) gamma1,
 //      written to `dr1`; partial sums d(out1) n1 and d(out1) per column.
-//      The next row's d(out1), gathered gamma0/beta0 and statistics are
-//      loaded while the current row is computed;
+//      The next row's d(out1) and gathered gamma0/beta0 are loaded while the
+//      current row is computed; row statistics are read once per wave, one
+//      row per lane;
 //   3. the 8 waves' column partials added through LDS (fixed order) and
 //      stored; each wave's own dr1 rows copied back into LDS (over x);
 //   4. norm0 backward per row j: da0 = token_mix(dr1) gathered from LDS,
@@ -947,6 +948,12 @@ __global__ __launch_bounds__(512) void k_tail_bwd_lds(const bf16_t* __restrict__
   const int R = (T + nw - 1) / nw;
   const int r0 = min(wave * R, T), r1 = min(r0 + R, T);  // this wave's rows (none if r0 == T)
   const int i0 = min(r0, T - 1);
+  // the sample's dr1 and dx rows as buffers: every store is issued (columns
+  // past D get an out-of-range offset and are dropped), so the compiler's
+  // wait counts stay exact across the row loops
+  const uint32_t rowb = (uint32_t)D * 2;
+  const __amdgpu_buffer_rsrc_t drs = row_rsrc(dr1 + srow * D, (long)T * D * 2);
+  const __amdgpu_buffer_rsrc_t dxs = row_rsrc(dx + srow * D, (long)T * D * 2);
 
   // 1. x[b] -> LDS
   if ((reinterpret_cast<uintptr_t>(x) & 15) == 0) {
@@ -980,7 +987,11 @@ __global__ __launch_bounds__(512) void k_tail_bwd_lds(const bf16_t* __restrict__
     ldr(g0 + sc, pg0[q]);
     ldr(be0 + sc, pb0[q]);
   }
-  float pmu = stats[ST_MU1 * NR + srow + i0], prs = stats[ST_RS1 * NR + srow + i0];
+  // statistics of this wave's rows, lane l holding row r0 + l (vector loads:
+  // scalar ones would share the LDS reads' wait counter inside the row loops)
+  const int ri = min(r0 + lane, T - 1);
+  const float lmu1 = stats[ST_MU1 * NR + srow + ri], lrs1 = stats[ST_RS1 * NR + srow + ri];
+  const float lmu0 = stats[ST_MU0 * NR + srow + ri], lrs0 = stats[ST_RS0 * NR + srow + ri];
   wait_vm_all();
   __syncthreads();
 
@@ -992,7 +1003,7 @@ __global__ __launch_bounds__(512) void k_tail_bwd_lds(const bf16_t* __restrict__
     for (int e = 0; e < N; ++e) pa[q][e] = pbb[q][e] = 0.f;
   for (int i = r0; i < r1; ++i) {
     const long row = srow + i;
-    const float mu1 = pmu, rs1 = prs;
+    const float mu1 = lane_f(lmu1, i - r0), rs1 = lane_f(lrs1, i - r0);
     const int in = min(i + 1, T - 1);
     Raw<bf16_t, N> cdh[Q], cg0[Q], cb0[Q];
 #pragma unroll
@@ -1006,8 +1017,6 @@ __global__ __launch_bounds__(512) void k_tail_bwd_lds(const bf16_t* __restrict__
       ldr(g0 + scn, pg0[q]);
       ldr(be0 + scn, pb0[q]);
     }
-    pmu = stats[ST_MU1 * NR + srow + in];
-    prs = stats[ST_RS1 * NR + srow + in];
     float n1[Q][N], dn[Q][N], gv[Q][N];
     float s1 = 0.f, s2 = 0.f;
 #pragma unroll
@@ -1038,16 +1047,14 @@ __global__ __launch_bounds__(512) void k_tail_bwd_lds(const bf16_t* __restrict__
 #pragma unroll
     for (int q = 0; q < Q; ++q) {
       const int c = (lane + 64 * q) * N;
-      if (c < D) {
-        float o[N];
+      float o[N];
 #pragma unroll
-        for (int e = 0; e < N; ++e) {
-          o[e] = rs1 * (dn[q][e] - m1 - n1[q][e] * m2);
-          pa[q][e] += gv[q][e] * n1[q][e];
-          pbb[q][e] += gv[q][e];
-        }
-        stv(dr1 + row * D + c, o);
+      for (int e = 0; e < N; ++e) {
+        o[e] = rs1 * (dn[q][e] - m1 - n1[q][e] * m2);
+        pa[q][e] += gv[q][e] * n1[q][e];  // columns past D: accumulated, never stored
+        pbb[q][e] += gv[q][e];
       }
+      bst4<bf16_t>(drs, c < D ? (uint32_t)c * 2 : 0x80000000u, (uint32_t)i * rowb, o);
     }
   }
   wait_vm_all();    // this wave's dr1 stores have completed
@@ -1067,8 +1074,6 @@ __global__ __launch_bounds__(512) void k_tail_bwd_lds(const bf16_t* __restrict__
   Raw<bf16_t, N> px[Q];
 #pragma unroll
   for (int q = 0; q < Q; ++q) ldr(x + base + (long)i0 * D + min((lane + 64 * q) * N, D - N), px[q]);
-  pmu = stats[ST_MU0 * NR + srow + i0];
-  prs = stats[ST_RS0 * NR + srow + i0];
   wait_vm_all();
   __syncthreads();
 
@@ -1079,7 +1084,7 @@ __global__ __launch_bounds__(512) void k_tail_bwd_lds(const bf16_t* __restrict__
     for (int e = 0; e < N; ++e) pa[q][e] = pbb[q][e] = 0.f;
   for (int j = r0; j < r1; ++j) {
     const long row = srow + j;
-    const float mu = pmu, rs = prs;
+    const float mu = lane_f(lmu0, j - r0), rs = lane_f(lrs0, j - r0);
     const int jn = min(j + 1, T - 1);
     Raw<bf16_t, N> cx[Q];
 #pragma unroll
@@ -1087,8 +1092,6 @@ __global__ __launch_bounds__(512) void k_tail_bwd_lds(const bf16_t* __restrict__
       cx[q] = px[q];
       ldr(x + base + (long)jn * D + min((lane + 64 * q) * N, D - N), px[q]);
     }
-    pmu = stats[ST_MU0 * NR + srow + jn];
-    prs = stats[ST_RS0 * NR + srow + jn];
     float n0[Q][N], dn[Q][N], da[Q][N];
     float s1 = 0.f, s2 = 0.f;
 #pragma unroll
@@ -1115,18 +1118,17 @@ __global__ __launch_bounds__(512) void k_tail_bwd_lds(const bf16_t* __restrict__
 #pragma unroll
     for (int q = 0; q < Q; ++q) {
       const int c = (lane + 64 * q) * N;
-      if (c < D) {
-        const uint2 ro = *reinterpret_cast<const uint2*>(sx + ((long)j * D + c) * 2);
-        float own[N], o[N];
-        own[0] = bf_lo(ro.x); own[1] = bf_hi(ro.x); own[2] = bf_lo(ro.y); own[3] = bf_hi(ro.y);
+      const int cc = min(c, D - N);
+      const uint2 ro = *reinterpret_cast<const uint2*>(sx + ((long)j * D + cc) * 2);
+      float own[N], o[N];
+      own[0] = bf_lo(ro.x); own[1] = bf_hi(ro.x); own[2] = bf_lo(ro.y); own[3] = bf_hi(ro.y);
 #pragma unroll
-        for (int e = 0; e < N; ++e) {
-          o[e] = own[e] + rs * (dn[q][e] - m1 - n0[q][e] * m2);
-          pa[q][e] += da[q][e] * n0[q][e];
-          pbb[q][e] += da[q][e];
-        }
-        stv(dx + row * D + c, o);
+      for (int e = 0; e < N; ++e) {
+        o[e] = own[e] + rs * (dn[q][e] - m1 - n0[q][e] * m2);
+        pa[q][e] += da[q][e] * n0[q][e];  // columns past D: accumulated, never stored
+        pbb[q][e] += da[q][e];
       }
+      bst4<bf16_t>(dxs, c < D ? (uint32_t)c * 2 : 0x80000000u, (uint32_t)j * rowb, o);
     }
   }
   __syncthreads();
