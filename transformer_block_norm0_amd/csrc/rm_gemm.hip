@@ -335,7 +335,7 @@ hipError_t launch_gemm(int dtype, bool a_kmajor, bool b_kmajor, const GemmArgs& 
                    (g.a_bs % vw == 0) && (g.b_bs % vw == 0) && aligned16(g.A) && aligned16(g.B);
   prof_begin(kid, s);
   hipError_t e;
-  if (gemm256_supported(dtype, a_kmajor, b_kmajor, g))
+  if (gemm256_supported(dtype, a_kmajor, b_kmajor, g, kid))
     e = launch_gemm256(a_kmajor, b_kmajor, g, kid, s);
   else
     e = dtype == RM_BF16 ? dispatch<bf16_t>(a_kmajor, b_kmajor, g, vec, s)

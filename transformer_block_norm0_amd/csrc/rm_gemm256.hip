@@ -260,29 +260,16 @@ __device__ __forceinline__ void dma_pair(char* sa, char* sb, const Src& s, const
   dma_slab<BKM>(sb, s.B, s.offb, g.b_ld, kslab * BK, wave);
 }
 
-// v = acc (+ bias) (+ residual, already loaded) for the 4 consecutive
-// columns of accumulator block (i, j), v/4 group q held by this lane.
-__device__ __forceinline__ void epi_values(float (&v)[4], const f32x16_t (&acc)[4][4], int i, int j, int q,
-                                           const GemmArgs& g, uint32_t boff, v2u32 res) {
-#pragma unroll
-  for (int e = 0; e < 4; ++e) v[e] = acc[i][j][4 * q + e];
-  if (g.bias) {
-    const v2u32 w = *reinterpret_cast<const __attribute__((address_space(3))) v2u32*>(
-        (uintptr_t)(boff + 2 * (32 * j + 8 * q)));
-    v[0] += __uint_as_float(w.x << 16);
-    v[1] += __uint_as_float(w.x & 0xffff0000u);
-    v[2] += __uint_as_float(w.y << 16);
-    v[3] += __uint_as_float(w.y & 0xffff0000u);
-  }
-  if (g.res) {
-    v[0] += __uint_as_float(res.x << 16);
-    v[1] += __uint_as_float(res.x & 0xffff0000u);
-    v[2] += __uint_as_float(res.y << 16);
-    v[3] += __uint_as_float(res.y & 0xffff0000u);
-  }
+// Four bf16 values (two packed words) added to v.
+__device__ __forceinline__ void add_bf16x4(float (&v)[4], v2u32 w) {
+  v[0] += __uint_as_float(w.x << 16);
+  v[1] += __uint_as_float(w.x & 0xffff0000u);
+  v[2] += __uint_as_float(w.y << 16);
+  v[3] += __uint_as_float(w.y & 0xffff0000u);
 }
 
-// The bf16 residual of m block i: 16 loads of 4 columns (zero where out of range).
+// The bf16 residual of one 32-row block: 16 loads of 4 columns (zero where
+// out of range).
 __device__ __forceinline__ void load_residual(v2u32 (&r)[16], const GemmArgs& g, __amdgpu_buffer_rsrc_t rrs,
                                               uint32_t rld, int m, int nbase, bool mok) {
 #pragma unroll
@@ -295,73 +282,90 @@ __device__ __forceinline__ void load_residual(v2u32 (&r)[16], const GemmArgs& g,
     }
 }
 
-// Tile epilogue straight from the accumulators: v = acc (+ bias) (+ residual).
-// Lane l holds, per (m block i, n block j, v/4 group q), 4 consecutive
-// columns n = 32j + 8q + 4(l/32) of row m = 32i + l%32.
-//   * bf16 output: lanes l and l+32 exchange halves (v_permlane32_swap) so
-//     that each lane holds 8 consecutive columns: lane l < 32 columns
-//     8q..8q+7, lane l+32 columns 8(q+1)..8(q+1)+7 for q = 0, 2; one 16-byte
-//     buffer store each, 32 per wave.
-//   * fp32 output: one 16-byte store per (i, j, q), 64 per wave.
-// Every store is issued (rows past M or columns past N get an out-of-range
-// offset that the buffer unit drops): at least EPI_STORES per wave.  One m
-// block at a time (scheduling barriers between blocks); the residual (bf16)
-// of m block i+1 is loaded while block i is computed and stored.
+// Tile epilogue straight from the accumulators: C = acc (+ bias) (+ residual),
+// bf16.  Lane l holds, per (m block i, n block j, v/4 group q), 4 consecutive
+// columns n = 32j + 8q + 4(l/32) of row m = 32i + l%32.  Lanes l and l+32
+// exchange halves (v_permlane32_swap) so that each lane holds 8 consecutive
+// columns (lane l < 32: 8q..8q+7, lane l+32: 8(q+1)..8(q+1)+7, q = 0, 2) for
+// one 16-byte buffer store: EPI_STORES per wave, every one issued (rows past
+// M or columns past N get an out-of-range offset that the buffer unit drops).
+// BIAS / RES are compile-time, so the epilogue has no branches: the tile's 64
+// bias values per lane are read from LDS once, and the residual of m block
+// i+1 is loaded while block i is computed and stored.
+template <bool BIAS, bool RES>
 __device__ __forceinline__ void epilogue(const f32x16_t (&acc)[4][4], const GemmArgs& g, const Tile& c,
                                          const char* sbias, int wm, int wn, int lane) {
   const int r = lane & 31, h = lane >> 5;
   const int mb = c.m0 + wm * 128 + r;  // + 32 i
   const int nb = wn * 128 + 4 * h;     // + 32 j + 8 q (tile-local)
-  const int esz = g.c_f32 ? 4 : 2;
-  char* cbase = reinterpret_cast<char*>(g.C) + (long)c.t * g.c_bs * esz;
-  const __amdgpu_buffer_rsrc_t crs = make_rsrc(cbase, (long)g.M * g.c_ld * esz);
-  const char* rbase = g.res ? reinterpret_cast<const char*>(g.res) + (long)c.t * g.res_bs * 2 : cbase;
-  const __amdgpu_buffer_rsrc_t rrs = make_rsrc(rbase, g.res ? (long)g.M * g.res_ld * 2 : 0L);
+  char* cbase = reinterpret_cast<char*>(g.C) + (long)c.t * g.c_bs * 2;
+  const __amdgpu_buffer_rsrc_t crs = make_rsrc(cbase, (long)g.M * g.c_ld * 2);
   // byte strides (uniform; every per-token offset is below 2^31)
-  const uint32_t cld = (uint32_t)(g.c_ld * esz), rld = (uint32_t)(g.res_ld * 2);
+  const uint32_t cld = (uint32_t)(g.c_ld * 2);
+  // bias: read once per tile, or once per m block next to a residual (which
+  // needs the registers)
+  v2u32 bias[16];
   uint32_t boff = lds_addr(sbias) + 2 * nb;
+  auto read_bias = [&]() {
+#pragma unroll
+    for (int j = 0; j < 4; ++j)
+#pragma unroll
+      for (int q = 0; q < 4; ++q)
+        bias[4 * j + q] = *reinterpret_cast<const __attribute__((address_space(3))) v2u32*>(
+            (uintptr_t)(boff + 2 * (32 * j + 8 * q)));
+  };
+  if constexpr (BIAS && !RES) read_bias();
   v2u32 res[2][16];
-  if (g.res) load_residual(res[0], g, rrs, rld, mb, c.n0 + nb, mb < g.M);
+  __amdgpu_buffer_rsrc_t rrs;
+  uint32_t rld = 0;
+  if constexpr (RES) {
+    const char* rbase = reinterpret_cast<const char*>(g.res) + (long)c.t * g.res_bs * 2;
+    rrs = make_rsrc(rbase, (long)g.M * g.res_ld * 2);
+    rld = (uint32_t)(g.res_ld * 2);
+    load_residual(res[0], g, rrs, rld, mb, c.n0 + nb, mb < g.M);
+  }
 #pragma unroll
   for (int i = 0; i < 4; ++i) {
     __builtin_amdgcn_sched_barrier(0);
-    asm volatile("" : "+v"(boff));  // re-read the bias per m block instead of keeping 64 values live
     const int m = mb + 32 * i;
     const bool mok = m < g.M;
-    if (g.res && i < 3) load_residual(res[(i + 1) & 1], g, rrs, rld, m + 32, c.n0 + nb, m + 32 < g.M);
-    const v2u32(&rc)[16] = res[i & 1];
+    if constexpr (RES) {
+      if (i < 3) load_residual(res[(i + 1) & 1], g, rrs, rld, m + 32, c.n0 + nb, m + 32 < g.M);
+    }
+    if constexpr (BIAS && RES) {
+      asm volatile("" : "+v"(boff));  // a fresh read per m block, not 64 values kept live
+      read_bias();
+    }
 #pragma unroll
     for (int j = 0; j < 4; ++j) {
-      if (g.c_f32) {
 #pragma unroll
-        for (int q = 0; q < 4; ++q) {
-          const int n = c.n0 + nb + 32 * j + 8 * q;
-          const bool ok = mok && n < g.N;  // N % 8 == 0: the 4 columns are all in or all out
-          float v[4];
-          epi_values(v, acc, i, j, q, g, boff, rc[4 * j + q]);
-          const uint32_t co = ok ? (uint32_t)m * cld + (uint32_t)n * 4 : OUT_OF_RANGE;
-          const v4u32 d = {__float_as_uint(v[0]), __float_as_uint(v[1]), __float_as_uint(v[2]), __float_as_uint(v[3])};
-          __builtin_amdgcn_raw_buffer_store_b128(d, crs, co, 0, 0);
-        }
-      } else {
+      for (int q = 0; q < 4; q += 2) {
+        float v0[4], v1[4];
 #pragma unroll
-        for (int q = 0; q < 4; q += 2) {
-          float v0[4], v1[4];
-          epi_values(v0, acc, i, j, q, g, boff, rc[4 * j + q]);
-          epi_values(v1, acc, i, j, q + 1, g, boff, rc[4 * j + q + 1]);
-          uint32_t a0 = bf16_pair(v0[0], v0[1]), a1 = bf16_pair(v0[2], v0[3]);
-          uint32_t b0 = bf16_pair(v1[0], v1[1]), b1 = bf16_pair(v1[2], v1[3]);
-          const auto s0 = __builtin_amdgcn_permlane32_swap(a0, b0, false, false);
-          const auto s1 = __builtin_amdgcn_permlane32_swap(a1, b1, false, false);
-          a0 = s0[0]; b0 = s0[1];
-          a1 = s1[0]; b1 = s1[1];
-          // now lane < 32 holds (a0 a1 | b0 b1) = columns 8q..8q+7, lane >= 32 (a0 a1 | b0 b1) = 8(q+1)..
-          const int ns = c.n0 + wn * 128 + 32 * j + 8 * (q + h);
-          const bool ok = mok && ns < g.N;
-          const uint32_t co = ok ? (uint32_t)m * cld + (uint32_t)ns * 2 : OUT_OF_RANGE;
-          const v4u32 d = {a0, a1, b0, b1};
-          __builtin_amdgcn_raw_buffer_store_b128(d, crs, co, 0, 0);
+        for (int e = 0; e < 4; ++e) {
+          v0[e] = acc[i][j][4 * q + e];
+          v1[e] = acc[i][j][4 * q + 4 + e];
         }
+        if constexpr (BIAS) {
+          add_bf16x4(v0, bias[4 * j + q]);
+          add_bf16x4(v1, bias[4 * j + q + 1]);
+        }
+        if constexpr (RES) {
+          add_bf16x4(v0, res[i & 1][4 * j + q]);
+          add_bf16x4(v1, res[i & 1][4 * j + q + 1]);
+        }
+        uint32_t a0 = bf16_pair(v0[0], v0[1]), a1 = bf16_pair(v0[2], v0[3]);
+        uint32_t b0 = bf16_pair(v1[0], v1[1]), b1 = bf16_pair(v1[2], v1[3]);
+        const auto s0 = __builtin_amdgcn_permlane32_swap(a0, b0, false, false);
+        const auto s1 = __builtin_amdgcn_permlane32_swap(a1, b1, false, false);
+        a0 = s0[0]; b0 = s0[1];
+        a1 = s1[0]; b1 = s1[1];
+        // now lane < 32 holds (a0 a1 | b0 b1) = columns 8q..8q+7, lane >= 32 (a0 a1 | b0 b1) = 8(q+1)..
+        const int ns = c.n0 + wn * 128 + 32 * j + 8 * (q + h);
+        const bool ok = mok && ns < g.N;
+        const uint32_t co = ok ? (uint32_t)m * cld + (uint32_t)ns * 2 : OUT_OF_RANGE;
+        const v4u32 d = {a0, a1, b0, b1};
+        __builtin_amdgcn_raw_buffer_store_b128(d, crs, co, 0, 0);
       }
     }
   }
@@ -377,7 +381,7 @@ __device__ __forceinline__ void epilogue(const f32x16_t (&acc)[4][4], const Gemm
 // k+2 (this tile's, DMA == 1, or the next tile's, DMA == 2, when there is one;
 // that tile's bias first); the next slab's first fragments are read during
 // the last k step's MFMAs.
-template <bool AK, bool BKM, bool ZERO, int DMA>
+template <bool AK, bool BKM, bool ZERO, int DMA, bool BIAS>
 __device__ __forceinline__ void slab_step(f32x16_t (&acc)[4][4], Frags& f0, Frags& f1, char* sa, char* sb,
                                           const char* na, const char* nb, int kdma, bool tile_start, bool has_next,
                                           const GemmArgs& g, const Src& src, const Tile& nt, char* nbias, int wm,
@@ -400,7 +404,7 @@ __device__ __forceinline__ void slab_step(f32x16_t (&acc)[4][4], Frags& f0, Frag
     dma_pair<AK, BKM>(sa, sb, src, g, kdma, wave);
   } else {
     if (has_next) {
-      if (kdma == 0 && g.bias && wave == 0) dma_bias(nbias, g, nt, lane);
+      if (BIAS && kdma == 0 && wave == 0) dma_bias(nbias, g, nt, lane);
       dma_pair<AK, BKM>(sa, sb, src, g, kdma, wave);
     }
   }
@@ -421,7 +425,7 @@ __device__ __forceinline__ void slab_step(f32x16_t (&acc)[4][4], Frags& f0, Frag
 // tile copy the next tile's slabs 0 and 1; the tile's EPI_STORES stores follow,
 // so at the next tile's first wait at least EPI_STORES operations are newer
 // than the awaited slab: vmcnt(EPI_STORES).
-template <bool AK, bool BKM>
+template <bool AK, bool BKM, bool BIAS, bool RES>
 __device__ __forceinline__ void gemm256_body(const GemmArgs& g) {
   // stage s: A slab at sA + s * TILE_BYTES, B slab at sB + s * TILE_BYTES;
   // bias tiles double buffered
@@ -450,7 +454,7 @@ __device__ __forceinline__ void gemm256_body(const GemmArgs& g) {
   Src cur;
   tile_src<AK, BKM>(cur, g, ct, wave, lane);
   const int nk = g.K / BK;  // even, at least 2
-  if (g.bias && wave == 0) dma_bias(sbias[0], g, ct, lane);
+  if (BIAS && wave == 0) dma_bias(sbias[0], g, ct, lane);
   dma_pair<AK, BKM>(a0, b0, cur, g, 0, wave);
   dma_pair<AK, BKM>(a1, b1, cur, g, 1, wave);
   sync_slab<DMA_PER_SLAB>();
@@ -468,26 +472,26 @@ __device__ __forceinline__ void gemm256_body(const GemmArgs& g) {
     char* nbias = sbias[(it + 1) & 1];
 
     // steps 0 .. nk-3 copy this tile's slabs 2 .. nk-1
-    slab_step<AK, BKM, true, 1>(acc, f0, f1, a0, b0, a1, b1, 2, !first, has_next, g, cur, nt, nbias, wm, wn, wave,
+    slab_step<AK, BKM, true, 1, BIAS>(acc, f0, f1, a0, b0, a1, b1, 2, !first, has_next, g, cur, nt, nbias, wm, wn, wave,
                                 lane);
-    slab_step<AK, BKM, false, 1>(acc, f0, f1, a1, b1, a0, b0, 3, false, has_next, g, cur, nt, nbias, wm, wn, wave,
+    slab_step<AK, BKM, false, 1, BIAS>(acc, f0, f1, a1, b1, a0, b0, 3, false, has_next, g, cur, nt, nbias, wm, wn, wave,
                                  lane);
     for (int k = 2; k < nk - 2; k += 2) {
-      slab_step<AK, BKM, false, 1>(acc, f0, f1, a0, b0, a1, b1, k + 2, false, has_next, g, cur, nt, nbias, wm, wn,
+      slab_step<AK, BKM, false, 1, BIAS>(acc, f0, f1, a0, b0, a1, b1, k + 2, false, has_next, g, cur, nt, nbias, wm, wn,
                                    wave, lane);
-      slab_step<AK, BKM, false, 1>(acc, f0, f1, a1, b1, a0, b0, k + 3, false, has_next, g, cur, nt, nbias, wm, wn,
+      slab_step<AK, BKM, false, 1, BIAS>(acc, f0, f1, a1, b1, a0, b0, k + 3, false, has_next, g, cur, nt, nbias, wm, wn,
                                    wave, lane);
     }
     // steps nk-2, nk-1 copy the next tile's slabs 0, 1 (if any; without a next
     // tile the last step copies nothing and its fragment reads of stage 0 are
     // stale and unused: the same code on both paths keeps the accumulators in
     // AGPRs)
-    slab_step<AK, BKM, false, 2>(acc, f0, f1, a0, b0, a1, b1, 0, false, has_next, g, nxt, nt, nbias, wm, wn, wave,
+    slab_step<AK, BKM, false, 2, BIAS>(acc, f0, f1, a0, b0, a1, b1, 0, false, has_next, g, nxt, nt, nbias, wm, wn, wave,
                                  lane);
-    slab_step<AK, BKM, false, 2>(acc, f0, f1, a1, b1, a0, b0, 1, false, has_next, g, nxt, nt, nbias, wm, wn, wave,
+    slab_step<AK, BKM, false, 2, BIAS>(acc, f0, f1, a1, b1, a0, b0, 1, false, has_next, g, nxt, nt, nbias, wm, wn, wave,
                                  lane);
 
-    epilogue(acc, g, ct, sbias[it & 1], wm, wn, lane);
+    epilogue<BIAS, RES>(acc, g, ct, sbias[it & 1], wm, wn, lane);
     if (!has_next) break;
     tile = next;
     ct = nt;
@@ -508,19 +512,38 @@ int cu_count() {
   return cached[dev];
 }
 
-// One kernel symbol per GEMM of the block, so that profiles name them.
-__global__ __launch_bounds__(256, 1) void gemm_up_bf16(GemmArgs g) { gemm256_body<true, false>(g); }
-__global__ __launch_bounds__(256, 1) void gemm_down_bf16(GemmArgs g) { gemm256_body<true, false>(g); }
-__global__ __launch_bounds__(256, 1) void gemm_dhid_bf16(GemmArgs g) { gemm256_body<true, true>(g); }
-__global__ __launch_bounds__(256, 1) void gemm_dh1_bf16(GemmArgs g) { gemm256_body<true, true>(g); }
-__global__ __launch_bounds__(256, 1) void gemm_dwout_bf16(GemmArgs g) { gemm256_body<false, false>(g); }
-__global__ __launch_bounds__(256, 1) void gemm_dw1_bf16(GemmArgs g) { gemm256_body<false, false>(g); }
-// other callers of the same operand layouts
-__global__ __launch_bounds__(256, 1) void gemm_kn_bf16(GemmArgs g) { gemm256_body<true, false>(g); }
-__global__ __launch_bounds__(256, 1) void gemm_kk_bf16(GemmArgs g) { gemm256_body<true, true>(g); }
-__global__ __launch_bounds__(256, 1) void gemm_mn_bf16(GemmArgs g) { gemm256_body<false, false>(g); }
+// One kernel symbol per GEMM of the block, so that profiles name them; the
+// epilogue (bias, residual) is fixed per kernel.
+__global__ __launch_bounds__(256, 1) void gemm_up_bf16(GemmArgs g) { gemm256_body<true, false, true, false>(g); }
+__global__ __launch_bounds__(256, 1) void gemm_down_bf16(GemmArgs g) { gemm256_body<true, false, true, true>(g); }
+__global__ __launch_bounds__(256, 1) void gemm_dhid_bf16(GemmArgs g) { gemm256_body<true, true, false, false>(g); }
+__global__ __launch_bounds__(256, 1) void gemm_dh1_bf16(GemmArgs g) { gemm256_body<true, true, false, true>(g); }
+__global__ __launch_bounds__(256, 1) void gemm_dwout_bf16(GemmArgs g) { gemm256_body<false, false, false, false>(g); }
+__global__ __launch_bounds__(256, 1) void gemm_dw1_bf16(GemmArgs g) { gemm256_body<false, false, false, false>(g); }
 
 typedef void (*Gemm256Kernel)(GemmArgs);
+
+// The kernel of each GEMM of the block with its operand layouts and epilogue.
+struct Gemm256Entry {
+  int kid;
+  bool a_kmajor, b_kmajor, bias, res;
+  Gemm256Kernel k;
+};
+const Gemm256Entry kGemm256[] = {
+    {KID_GEMM_UP, true, false, true, false, gemm_up_bf16},
+    {KID_GEMM_DOWN, true, false, true, true, gemm_down_bf16},
+    {KID_GEMM_DHID, true, true, false, false, gemm_dhid_bf16},
+    {KID_GEMM_DH1, true, true, false, true, gemm_dh1_bf16},
+    {KID_GEMM_DWOUT, false, false, false, false, gemm_dwout_bf16},
+    {KID_GEMM_DW1, false, false, false, false, gemm_dw1_bf16},
+};
+const Gemm256Entry* gemm256_entry(bool a_kmajor, bool b_kmajor, const GemmArgs& g, int kid) {
+  for (const Gemm256Entry& e : kGemm256)
+    if (e.kid == kid && e.a_kmajor == a_kmajor && e.b_kmajor == b_kmajor && e.bias == (g.bias != nullptr) &&
+        e.res == (g.res != nullptr))
+      return &e;
+  return nullptr;
+}
 
 hipError_t run256(Gemm256Kernel k, const GemmArgs& g, hipStream_t s) {
   const int tiles = ((g.M + BM - 1) / BM) * ((g.N + BN - 1) / BN) * g.batch;
@@ -535,9 +558,9 @@ hipError_t run256(Gemm256Kernel k, const GemmArgs& g, hipStream_t s) {
 
 }  // namespace
 
-bool gemm256_supported(int dtype, bool a_kmajor, bool b_kmajor, const GemmArgs& g) {
-  if (dtype != RM_BF16) return false;
-  if (a_kmajor == false && b_kmajor == true) return false;
+bool gemm256_supported(int dtype, bool a_kmajor, bool b_kmajor, const GemmArgs& g, int kid) {
+  if (dtype != RM_BF16 || g.c_f32) return false;  // bf16 operands and output
+  if (gemm256_entry(a_kmajor, b_kmajor, g, kid) == nullptr) return false;
   if (g.K % (2 * BK) != 0 || g.K < 4 * BK) return false;  // nk even, at least 4
   const long a_cont = a_kmajor ? g.K : g.M, b_cont = b_kmajor ? g.K : g.N;
   if (a_cont % 8 || b_cont % 8 || g.a_ld % 8 || g.b_ld % 8 || g.a_bs % 8 || g.b_bs % 8) return false;
@@ -547,24 +570,21 @@ bool gemm256_supported(int dtype, bool a_kmajor, bool b_kmajor, const GemmArgs& 
   // per-token operand byte offsets fit the 32-bit copy offsets
   const long a_rows = a_kmajor ? g.M : g.K, b_rows = b_kmajor ? g.N : g.K;
   if (a_rows * g.a_ld * 2 > 0xffffffffL || b_rows * g.b_ld * 2 > 0xffffffffL) return false;
-  // the epilogue stores 4 columns per lane; a bias tile is copied in 16-byte pieces
+  // the epilogue stores 8 columns per lane pair; a bias tile is copied in 16-byte pieces
   if (g.N % 8 || g.c_ld % 4 || g.c_bs % 4 || (reinterpret_cast<uintptr_t>(g.C) & 15)) return false;
   if (g.bias && (g.bias_bs % 8 || (reinterpret_cast<uintptr_t>(g.bias) & 15))) return false;
   if (g.res && (g.res_f32 || g.res_ld % 4 || g.res_bs % 4 || (reinterpret_cast<uintptr_t>(g.res) & 15)))
     return false;  // the residual is bf16
   // per-token byte offsets of C and the residual fit the 31-bit buffer range
-  const long csz = g.c_f32 ? 4 : 2, rsz = 2;
-  if ((long)g.M * g.c_ld * csz > 0x7fffffffL) return false;
-  if (g.res && (long)g.M * g.res_ld * rsz > 0x7fffffffL) return false;
+  if ((long)g.M * g.c_ld * 2 > 0x7fffffffL) return false;
+  if (g.res && (long)g.M * g.res_ld * 2 > 0x7fffffffL) return false;
   return true;
 }
 
 hipError_t launch_gemm256(bool a_kmajor, bool b_kmajor, const GemmArgs& g, int kid, hipStream_t s) {
-  if (a_kmajor && !b_kmajor)
-    return run256(kid == KID_GEMM_UP ? gemm_up_bf16 : kid == KID_GEMM_DOWN ? gemm_down_bf16 : gemm_kn_bf16, g, s);
-  if (a_kmajor && b_kmajor)
-    return run256(kid == KID_GEMM_DHID ? gemm_dhid_bf16 : kid == KID_GEMM_DH1 ? gemm_dh1_bf16 : gemm_kk_bf16, g, s);
-  return run256(kid == KID_GEMM_DWOUT ? gemm_dwout_bf16 : kid == KID_GEMM_DW1 ? gemm_dw1_bf16 : gemm_mn_bf16, g, s);
+  const Gemm256Entry* e = gemm256_entry(a_kmajor, b_kmajor, g, kid);
+  if (e == nullptr) return hipErrorInvalidValue;  // callers check gemm256_supported first
+  return run256(e->k, g, s);
 }
 
 }  // namespace rm
