@@ -797,6 +797,7 @@ __global__ __launch_bounds__(MAXT) void k_gate_bwd_ring(const ST* __restrict__ Z
   const uint32_t vu = (uint32_t)(c * SZ), vg = (uint32_t)((H + c) * SZ);
   const uint32_t zrow = (uint32_t)(2 * H * SZ), hrow = (uint32_t)(H * SZ);
 
+  zero_red4(red4);
   // the group's inner-LN statistics (mux, rsx, mug, rsg per row) staged in LDS once
   for (int i = threadIdx.x; i < 4 * ROWS_PER_GROUP; i += blockDim.x) {
     const int r = i >> 2, q = i & 3;
@@ -810,8 +811,18 @@ __global__ __launch_bounds__(MAXT) void k_gate_bwd_ring(const ST* __restrict__ Z
     bld4<ST>(zrs, vg, row * zrow, rg[slot]);
     bld4<ST>(hrs, vu, row * hrow, rd[slot]);
   };
+  // two dropped (out-of-range) stores after each slot's loads, as every row
+  // step issues: the compiler's wait counts at the loop head then match the
+  // steady state instead of forcing the next rows' loads to complete
+  const float zero4[4] = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
-  for (int p = 0; p < RING; ++p) load_row(p, p);
+  for (int p = 0; p < RING; ++p) {
+    __builtin_amdgcn_sched_barrier(0);
+    load_row(p, p);
+    bst4<ST>(drs, 0x80000000u + 64u * p, 0, zero4);  // distinct offsets: not merged as redundant
+    bst4<ST>(drs, 0x80000020u + 64u * p, 0, zero4);
+    __builtin_amdgcn_sched_barrier(0);
+  }
   __syncthreads();
 
   // one row: consume ring slot p, refill it with row r + RING (PREFETCH), reduce, store dZ
@@ -850,7 +861,7 @@ __global__ __launch_bounds__(MAXT) void k_gate_bwd_ring(const ST* __restrict__ Z
       agg[e] += dug[e] * ng[e];
       abg[e] += dug[e];
     }
-    block_sum4(sm, red4, nw, parity);
+    block_sum4(sm, red4, parity);
     parity ^= 1;
     const float m1 = sm[0] * invH, m2 = sm[1] * invH, m3 = sm[2] * invH, m4 = sm[3] * invH;
     float du[4], dg[4];

@@ -192,7 +192,12 @@ __device__ __forceinline__ float wave_sum_dpp(float v) {
 // Sum 4 values over the whole block (nw waves, nw <= 16), fixed order.
 // red: 2 * 16 float4 of LDS, two halves alternating with `parity`, so
 // consecutive calls need one barrier each.  The barrier waits for LDS only.
-__device__ __forceinline__ void block_sum4(float (&v)[4], float4* red, int nw, int parity) {
+// All 16 slots are summed, without branches: the slots of waves >= nw must
+// hold zeros (zero_red4 before the block's first barrier).
+__device__ __forceinline__ void zero_red4(float4* red) {
+  for (int i = threadIdx.x; i < 2 * 16; i += blockDim.x) red[i] = make_float4(0.f, 0.f, 0.f, 0.f);
+}
+__device__ __forceinline__ void block_sum4(float (&v)[4], float4* red, int parity) {
   const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
   float4 s;
   s.x = wave_sum_dpp(v[0]);
@@ -206,17 +211,18 @@ __device__ __forceinline__ void block_sum4(float (&v)[4], float4* red, int nw, i
   __builtin_amdgcn_sched_barrier(0);
   lds_barrier();
   __builtin_amdgcn_sched_barrier(0);
-  float4 a = r[0];
-  // fully unrolled with a uniform guard: a loop here would keep the caller's
-  // whole row of temporaries live through it
+  // lane l reads slot l % 16; each 16-lane row sums its slots with the DPP
+  // butterfly (fixed order), row 0's result broadcast through lane 0
+  const float4 b = r[lane & 15];
+  float a[4] = {b.x, b.y, b.z, b.w};
 #pragma unroll
-  for (int w = 1; w < 16; ++w) {
-    if (w < nw) {
-      const float4 b = r[w];
-      a.x += b.x; a.y += b.y; a.z += b.z; a.w += b.w;
-    }
+  for (int i = 0; i < 4; ++i) {
+    a[i] += dpp_mov<0xB1>(a[i]);   // quad_perm [1,0,3,2]
+    a[i] += dpp_mov<0x4E>(a[i]);   // quad_perm [2,3,0,1]
+    a[i] += dpp_mov<0x141>(a[i]);  // row_half_mirror
+    a[i] += dpp_mov<0x140>(a[i]);  // row_mirror
+    v[i] = lane_f(a[i], 0);
   }
-  v[0] = a.x; v[1] = a.y; v[2] = a.z; v[3] = a.w;
 }
 
 // floor(c / S) for 0 <= c < 2^16, 1 <= S <= 1280 (exact: the quotient's
