@@ -752,12 +752,13 @@ __global__ __launch_bounds__(MAXT) void k_gate_bwd(const ST* __restrict__ Z, con
 // Gate / SiLU / inner LayerNorm backward for H % 4 == 0: one thread per
 // 4-column chunk of U (and the matching chunk of G and d hidden), one
 // workgroup walking the ROWS_PER_GROUP rows (b, t) of one sample group at one
-// token t.  Rows are prefetched P ahead into a register ring (u, g, d hidden,
-// the row's four inner-LN statistics) with unconditional loads from clamped
-// rows, so they stay in flight across the LDS-only barrier of each row's
-// block reduction.  The per-element terms are kept in registers between the
-// reduction and the dZ computation.  Rows past B get zero weight and
-// out-of-range (dropped) buffer stores.
+// token t.  Rows go two at a time: the pair's u, g, d hidden sit in a
+// two-slot register ring, refilled with the next pair (unconditional loads
+// from clamped rows) before the pair's one block reduction of eight sums, so
+// the loads stay in flight across its LDS-only barrier; the row statistics
+// are staged in LDS once.  The per-element terms are kept in registers
+// between the reduction and the dZ computation.  Rows past B get zero weight
+// and out-of-range (dropped) buffer stores.
 //   dux = dh * ug * sigmoid(ug)                  (d of the LN_x output)
 //   dug = dh * ux * sigmoid(ug) * (1 + ug (1 - sigmoid(ug)))
 //   dU  = rsx (dux gx - mean(dux gx) - nx mean(dux gx nx)), same for dG.
@@ -770,7 +771,7 @@ __global__ __launch_bounds__(MAXT) void k_gate_bwd_ring(const ST* __restrict__ Z
                                                         const float* __restrict__ stats, ST* __restrict__ dZ,
                                                         float* __restrict__ pgate, float* __restrict__ pb1, int B,
                                                         int T, int H, int nb) {
-  __shared__ float4 red4[2 * 16];
+  __shared__ float4 red8[2 * 16 * 2];
   __shared__ float4 sst[ROWS_PER_GROUP];
   constexpr int SZ = (int)sizeof(ST);
   const int t = blockIdx.x, grp = blockIdx.y;
@@ -797,7 +798,7 @@ __global__ __launch_bounds__(MAXT) void k_gate_bwd_ring(const ST* __restrict__ Z
   const uint32_t vu = (uint32_t)(c * SZ), vg = (uint32_t)((H + c) * SZ);
   const uint32_t zrow = (uint32_t)(2 * H * SZ), hrow = (uint32_t)(H * SZ);
 
-  zero_red4(red4);
+  zero_red8(red8);
   // the group's inner-LN statistics (mux, rsx, mug, rsg per row) staged in LDS once
   for (int i = threadIdx.x; i < 4 * ROWS_PER_GROUP; i += blockDim.x) {
     const int r = i >> 2, q = i & 3;
@@ -825,67 +826,77 @@ __global__ __launch_bounds__(MAXT) void k_gate_bwd_ring(const ST* __restrict__ Z
   }
   __syncthreads();
 
-  // one row: consume ring slot p, refill it with row r + RING (PREFETCH), reduce, store dZ
+  // two rows (ring slots 0 and 1) per step: consume them, refill the slots
+  // with rows r + RING, r + RING + 1 (PREFETCH), one block reduction of the
+  // two rows' eight sums, store both rows of dZ
   int parity = 0;
-  auto row_step = [&](int p, int r, auto prefetch) {
-    const bool valid = b0 + r <= bl;
-    const float w = valid ? cm : 0.f;
-    const float4 sr = sst[r];
-    const float mux = sr.x, rsx = sr.y, mug = sr.z, rsg = sr.w;
-    float u[4], g[4], dh[4];
-    unpack(ru[p], u);
-    unpack(rg[p], g);
-    unpack(rd[p], dh);
-    const uint32_t row = (uint32_t)(min(b0 + r, bl) * T + t);
-    if constexpr (decltype(prefetch)::value) load_row(p, r + RING);
-    float nx[4], ng[4], dux[4], dug[4];
-    float sm[4] = {0.f, 0.f, 0.f, 0.f};
-    const float ox = -mux * rsx, og = -mug * rsg;
+  auto pair_step = [&](int r, auto prefetch) {
+    float nx[2][4], ng[2][4], dux[2][4], dug[2][4], rsx[2], rsg[2], sm[8];
+    uint32_t rowk[2];
+    bool validk[2];
 #pragma unroll
-    for (int e = 0; e < 4; ++e) {
-      nx[e] = u[e] * rsx + ox;
-      ng[e] = g[e] * rsg + og;
-      const float ux = nx[e] * cgx[e] + cbx[e];
-      const float ug = ng[e] * cgg[e] + cbg[e];
-      const float sgm = sigmoidf_(ug);
-      const float dhw = w * dh[e];  // rows past B and columns past H contribute nothing
-      dux[e] = dhw * ug * sgm;
-      dug[e] = dhw * ux * sgm * (1.f + ug * (1.f - sgm));
-      const float dnx = dux[e] * cgx[e], dng = dug[e] * cgg[e];
-      sm[0] += dnx;
-      sm[1] += dnx * nx[e];
-      sm[2] += dng;
-      sm[3] += dng * ng[e];
-      agx[e] += dux[e] * nx[e];
-      abx[e] += dux[e];
-      agg[e] += dug[e] * ng[e];
-      abg[e] += dug[e];
+    for (int k = 0; k < 2; ++k) {
+      const bool valid = b0 + r + k <= bl;
+      validk[k] = valid;
+      const float w = valid ? cm : 0.f;
+      const float4 sr = sst[r + k];
+      const float mux = sr.x, mug = sr.z;
+      rsx[k] = sr.y;
+      rsg[k] = sr.w;
+      float u[4], g[4], dh[4];
+      unpack(ru[k], u);
+      unpack(rg[k], g);
+      unpack(rd[k], dh);
+      rowk[k] = (uint32_t)(min(b0 + r + k, bl) * T + t);
+      if constexpr (decltype(prefetch)::value) load_row(k, r + k + RING);
+      sm[4 * k] = sm[4 * k + 1] = sm[4 * k + 2] = sm[4 * k + 3] = 0.f;
+      const float ox = -mux * rsx[k], og = -mug * rsg[k];
+#pragma unroll
+      for (int e = 0; e < 4; ++e) {
+        nx[k][e] = u[e] * rsx[k] + ox;
+        ng[k][e] = g[e] * rsg[k] + og;
+        const float ux = nx[k][e] * cgx[e] + cbx[e];
+        const float ug = ng[k][e] * cgg[e] + cbg[e];
+        const float sgm = sigmoidf_(ug);
+        const float dhw = w * dh[e];  // rows past B and columns past H contribute nothing
+        dux[k][e] = dhw * ug * sgm;
+        dug[k][e] = dhw * ux * sgm * (1.f + ug * (1.f - sgm));
+        const float dnx = dux[k][e] * cgx[e], dng = dug[k][e] * cgg[e];
+        sm[4 * k] += dnx;
+        sm[4 * k + 1] += dnx * nx[k][e];
+        sm[4 * k + 2] += dng;
+        sm[4 * k + 3] += dng * ng[k][e];
+        agx[e] += dux[k][e] * nx[k][e];
+        abx[e] += dux[k][e];
+        agg[e] += dug[k][e] * ng[k][e];
+        abg[e] += dug[k][e];
+      }
     }
-    block_sum4(sm, red4, parity);
+    block_sum8(sm, red8, parity);
     parity ^= 1;
-    const float m1 = sm[0] * invH, m2 = sm[1] * invH, m3 = sm[2] * invH, m4 = sm[3] * invH;
-    float du[4], dg[4];
 #pragma unroll
-    for (int e = 0; e < 4; ++e) {
-      du[e] = rsx * (dux[e] * cgx[e] - m1 - nx[e] * m2);
-      dg[e] = rsg * (dug[e] * cgg[e] - m3 - ng[e] * m4);
-      // a row past B has all four sums zero, so du = dg = 0 there; columns
-      // past H are never stored
-      au[e] += du[e];
-      ag[e] += dg[e];
+    for (int k = 0; k < 2; ++k) {
+      const float m1 = sm[4 * k] * invH, m2 = sm[4 * k + 1] * invH, m3 = sm[4 * k + 2] * invH,
+                  m4 = sm[4 * k + 3] * invH;
+      float du[4], dg[4];
+#pragma unroll
+      for (int e = 0; e < 4; ++e) {
+        du[e] = rsx[k] * (dux[k][e] * cgx[e] - m1 - nx[k][e] * m2);
+        dg[e] = rsg[k] * (dug[k][e] * cgg[e] - m3 - ng[k][e] * m4);
+        // a row past B has all four sums zero, so du = dg = 0 there; columns
+        // past H are never stored
+        au[e] += du[e];
+        ag[e] += dg[e];
+      }
+      const bool sok = validk[k] && craw < H;
+      bst4<ST>(drs, sok ? vu : 0x80000000u, rowk[k] * zrow, du);
+      bst4<ST>(drs, sok ? vg : 0x80000000u, rowk[k] * zrow, dg);
     }
-    const bool sok = valid && craw < H;
-    bst4<ST>(drs, sok ? vu : 0x80000000u, row * zrow, du);
-    bst4<ST>(drs, sok ? vg : 0x80000000u, row * zrow, dg);
   };
-  static_assert(ROWS_PER_GROUP % RING == 0, "ring divides the row group");
+  static_assert(RING == 2 && ROWS_PER_GROUP % 2 == 0, "two ring slots, consumed together");
 #pragma unroll 1
-  for (int r0 = 0; r0 < ROWS_PER_GROUP - RING; r0 += RING) {
-#pragma unroll
-    for (int p = 0; p < RING; ++p) row_step(p, r0 + p, std::true_type{});
-  }
-#pragma unroll
-  for (int p = 0; p < RING; ++p) row_step(p, ROWS_PER_GROUP - RING + p, std::false_type{});
+  for (int r0 = 0; r0 < ROWS_PER_GROUP - 2; r0 += 2) pair_step(r0, std::true_type{});
+  pair_step(ROWS_PER_GROUP - 2, std::false_type{});
   if (craw < H) {
     const long blk = (long)nb * T * H;
     const long o = ((long)grp * T + t) * H;
