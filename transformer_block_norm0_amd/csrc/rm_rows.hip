@@ -1335,46 +1335,69 @@ __global__ __launch_bounds__(256) void k_ln0_bwd(const ST* __restrict__ x, const
 }
 
 // ---------------------------------------------------------------------------
-// Fixed-order column sums of partial rows: out[c] = sum_p part[p * pstride + c].
-// 1024 threads = 16 row lanes x 64 columns; lane r sums rows r, r+16, ... in
-// order, then the 16 lane sums are added in order.
+// Fixed-order column sums of partial rows: out[c] = sum_p part[p * pstride + c],
+// twelve jobs in one flat launch (job k owns blocks blk0 .. blk0 + nblk - 1).
+//   * short jobs (P <= 32 rows, many columns): one thread per column sums its
+//     P rows in order, eight loads in flight;
+//   * tall jobs: a block takes 16 columns with 64 row lanes; lane r sums rows
+//     r, r+64, ... (eight loads in flight), then the 64 lane sums are added in
+//     order.
 struct RedJob {
   const float* part;
   long pstride;
   int P;
   int ncols;
   void* out;
+  int blk0;
 };
 struct RedJobs {
   RedJob j[12];
 };
+constexpr int RED_SHORT_ROWS = 32;
+inline int red_blocks(const RedJob& j) { return j.P <= RED_SHORT_ROWS ? (j.ncols + 1023) / 1024 : (j.ncols + 15) / 16; }
+
+__device__ __forceinline__ float sum8(const float* p, long stride) {
+  float v[8];
+#pragma unroll
+  for (int u = 0; u < 8; ++u) v[u] = p[(long)u * stride];
+  return ((v[0] + v[1]) + (v[2] + v[3])) + ((v[4] + v[5]) + (v[6] + v[7]));
+}
 
 template <typename ST>
 __global__ __launch_bounds__(1024) void k_finalize(RedJobs jobs) {
-  __shared__ float red[16][64];
-  const RedJob job = jobs.j[blockIdx.y];
-  const int cx = threadIdx.x & 63, ry = threadIdx.x >> 6;
-  if ((long)blockIdx.x * 64 >= job.ncols) return;  // whole block leaves together
-  const long c = (long)blockIdx.x * 64 + cx;
+  __shared__ float red[64][17];
+  int jid = 0;
+#pragma unroll
+  for (int k = 1; k < 12; ++k)
+    if ((int)blockIdx.x >= jobs.j[k].blk0) jid = k;
+  const RedJob& job = jobs.j[jid];
+  const int b = (int)blockIdx.x - job.blk0;
+  if (job.P <= RED_SHORT_ROWS) {
+    const long c = (long)b * 1024 + threadIdx.x;
+    if (c >= job.ncols) return;
+    const float* p = job.part + c;
+    float s = 0.f;
+    int r = 0;
+    for (; r + 8 <= job.P; r += 8) s += sum8(p + (long)r * job.pstride, job.pstride);
+    for (; r < job.P; ++r) s += p[(long)r * job.pstride];
+    st(reinterpret_cast<ST*>(job.out), c, s);
+    return;
+  }
+  const int cx = threadIdx.x & 15, ry = threadIdx.x >> 4;
+  const long c = (long)b * 16 + cx;
   float s = 0.f;
   if (c < job.ncols) {
     const float* p = job.part + c;
     int r = ry;
-    // eight independent loads in flight per thread (the long reductions are latency-bound)
-    for (; r + 112 < job.P; r += 128) {
-      float v[8];
-#pragma unroll
-      for (int u = 0; u < 8; ++u) v[u] = p[(long)(r + 16 * u) * job.pstride];
-      s += ((v[0] + v[1]) + (v[2] + v[3])) + ((v[4] + v[5]) + (v[6] + v[7]));
-    }
-    for (; r < job.P; r += 16) s += p[(long)r * job.pstride];
+    for (; r + 7 * 64 < job.P; r += 8 * 64) s += sum8(p + (long)r * job.pstride, 64 * job.pstride);
+    for (; r < job.P; r += 64) s += p[(long)r * job.pstride];
   }
   red[ry][cx] = s;
   __syncthreads();
   if (ry == 0 && c < job.ncols) {
     float t = 0.f;
-#pragma unroll
-    for (int k = 0; k < 16; ++k) t += red[k][cx];
+#pragma unroll 16
+    for (int k = 0; k < 64; ++k) t += red[k][cx];
     st(reinterpret_cast<ST*>(job.out), c, t);
   }
 }
@@ -1560,24 +1583,28 @@ hipError_t finalize_t(const rm_dims& d, const rm_grads& g, void* ws, const WsLay
   const float* pt = wsp<float>(ws, L.p_tail);
   const long bl = (long)nb * T * D, bg = (long)nb * T * H;
   RedJobs J;
-  J.j[0] = {pl + 0 * bl, D, nb * T, D, g.ln2_g};
-  J.j[1] = {pl + 1 * bl, D, nb * T, D, g.ln2_b};
-  J.j[2] = {pl + 2 * bl, (long)T * D, nb, T * D, g.bout};
-  J.j[3] = {pg + 0 * bg, H, nb * T, H, g.lnx_g};
-  J.j[4] = {pg + 1 * bg, H, nb * T, H, g.lnx_b};
-  J.j[5] = {pg + 2 * bg, H, nb * T, H, g.lng_g};
-  J.j[6] = {pg + 3 * bg, H, nb * T, H, g.lng_b};
-  J.j[7] = {pg + 4 * bg, (long)T * 2 * H, nb, T * 2 * H, g.b1};
+  J.j[0] = {pl + 0 * bl, D, nb * T, D, g.ln2_g, 0};
+  J.j[1] = {pl + 1 * bl, D, nb * T, D, g.ln2_b, 0};
+  J.j[2] = {pl + 2 * bl, (long)T * D, nb, T * D, g.bout, 0};
+  J.j[3] = {pg + 0 * bg, H, nb * T, H, g.lnx_g, 0};
+  J.j[4] = {pg + 1 * bg, H, nb * T, H, g.lnx_b, 0};
+  J.j[5] = {pg + 2 * bg, H, nb * T, H, g.lng_g, 0};
+  J.j[6] = {pg + 3 * bg, H, nb * T, H, g.lng_b, 0};
+  J.j[7] = {pg + 4 * bg, (long)T * 2 * H, nb, T * 2 * H, g.b1, 0};
   // tail partials: [4][row groups * T][D], or [4][B][D] when the tail ran one sample per workgroup
   const int pt_rows = sample_in_lds(d) ? d.B : nb * T;
   const long bt = (long)pt_rows * D;
-  J.j[8] = {pt + 0 * bt, D, pt_rows, D, g.ln0_g};
-  J.j[9] = {pt + 1 * bt, D, pt_rows, D, g.ln0_b};
-  J.j[10] = {pt + 2 * bt, D, pt_rows, D, g.ln1_g};
-  J.j[11] = {pt + 3 * bt, D, pt_rows, D, g.ln1_b};
-  const int maxc = T * 2 * H;
+  J.j[8] = {pt + 0 * bt, D, pt_rows, D, g.ln0_g, 0};
+  J.j[9] = {pt + 1 * bt, D, pt_rows, D, g.ln0_b, 0};
+  J.j[10] = {pt + 2 * bt, D, pt_rows, D, g.ln1_g, 0};
+  J.j[11] = {pt + 3 * bt, D, pt_rows, D, g.ln1_b, 0};
+  int nblk = 0;
+  for (RedJob& j : J.j) {
+    j.blk0 = nblk;
+    nblk += red_blocks(j);
+  }
   prof_begin(KID_FINALIZE, s);
-  hipLaunchKernelGGL(k_finalize<ST>, dim3((maxc + 63) / 64, 12), dim3(1024), 0, s, J);
+  hipLaunchKernelGGL(k_finalize<ST>, dim3(nblk), dim3(1024), 0, s, J);
   prof_end(KID_FINALIZE, s);
   return hipGetLastError();
 }
