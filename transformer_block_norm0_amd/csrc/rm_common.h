@@ -1,6 +1,8 @@
 // Internal device helpers shared by the RankMixerBlock kernels (gfx950, wave64).
 #pragma once
 
+#include <type_traits>
+
 #include <hip/hip_runtime.h>
 #include <stdint.h>
 
@@ -49,10 +51,20 @@ __device__ __forceinline__ void tm_source(int i, int c, int S, int& src_row, int
 // ---------------------------------------------------------------------------
 // reductions (fixed order: deterministic)
 
+// Sum over the 64 lanes of a wave, result in every lane, without LDS: DPP
+// butterflies inside each 16-lane row (pairs, quads, half-row mirror, row
+// mirror), then the four row sums read from lanes 0, 16, 32, 48.  Fixed order.
 __device__ __forceinline__ float wave_sum(float v) {
-#pragma unroll
-  for (int o = 32; o > 0; o >>= 1) v += __shfl_xor(v, o, 64);
-  return v;
+  auto dpp = [](float a, auto ctrl) {
+    return __builtin_bit_cast(float, __builtin_amdgcn_update_dpp(0, __builtin_bit_cast(int, a), decltype(ctrl)::value,
+                                                                 0xF, 0xF, false));
+  };
+  v += dpp(v, std::integral_constant<int, 0xB1>{});   // quad_perm [1,0,3,2]
+  v += dpp(v, std::integral_constant<int, 0x4E>{});   // quad_perm [2,3,0,1]
+  v += dpp(v, std::integral_constant<int, 0x141>{});  // row_half_mirror
+  v += dpp(v, std::integral_constant<int, 0x140>{});  // row_mirror
+  auto rl = [](float a, int l) { return __builtin_bit_cast(float, __builtin_amdgcn_readlane(__builtin_bit_cast(int, a), l)); };
+  return (rl(v, 0) + rl(v, 16)) + (rl(v, 32) + rl(v, 48));
 }
 
 // Sum NV values over a 256-thread block; every thread gets the totals.
