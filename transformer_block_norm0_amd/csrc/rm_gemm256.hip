@@ -500,17 +500,6 @@ __device__ __forceinline__ void gemm256_body(const GemmArgs& g) {
   }
 }
 
-int cu_count() {
-  static int cached[64] = {0};
-  int dev = 0;
-  if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= 64) return 256;
-  if (cached[dev] == 0) {
-    int n = 0;
-    if (hipDeviceGetAttribute(&n, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess || n <= 0) n = 256;
-    cached[dev] = n;
-  }
-  return cached[dev];
-}
 
 // One kernel symbol per GEMM of the block, so that profiles name them; the
 // epilogue (bias, residual) is fixed per kernel.
@@ -548,7 +537,7 @@ const Gemm256Entry* gemm256_entry(bool a_kmajor, bool b_kmajor, const GemmArgs& 
 hipError_t run256(Gemm256Kernel k, const GemmArgs& g, hipStream_t s) {
   const int tiles = ((g.M + BM - 1) / BM) * ((g.N + BN - 1) / BN) * g.batch;
   // one workgroup per CU (its LDS use allows no more), a multiple of 8 (XCDs)
-  int grid = cu_count() & ~7;
+  int grid = device_cu_count() & ~7;
   if (grid < 8) grid = 8;
   const int need = (tiles + 7) & ~7;
   if (grid > need) grid = need;
@@ -557,6 +546,19 @@ hipError_t run256(Gemm256Kernel k, const GemmArgs& g, hipStream_t s) {
 }
 
 }  // namespace
+
+// Compute units of the current device (cached per device).
+int device_cu_count() {
+  static int cached[64] = {0};
+  int dev = 0;
+  if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= 64) return 256;
+  if (cached[dev] == 0) {
+    int n = 0;
+    if (hipDeviceGetAttribute(&n, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess || n <= 0) n = 256;
+    cached[dev] = n;
+  }
+  return cached[dev];
+}
 
 bool gemm256_supported(int dtype, bool a_kmajor, bool b_kmajor, const GemmArgs& g, int kid) {
   if (dtype != RM_BF16 || g.c_f32) return false;  // bf16 operands and output

@@ -81,6 +81,8 @@ struct GemmArgs {
 hipError_t launch_gemm(int dtype, bool a_kmajor, bool b_kmajor, const GemmArgs& g, int kid,
                        hipStream_t s);
 // 256x256-tile bf16 kernel (direct-to-LDS loads, transposing LDS reads): shapes it takes
+// Compute units of the current device (cached per device).
+int device_cu_count();
 bool gemm256_supported(int dtype, bool a_kmajor, bool b_kmajor, const GemmArgs& g, int kid);
 hipError_t launch_gemm256(bool a_kmajor, bool b_kmajor, const GemmArgs& g, int kid, hipStream_t s);
 

@@ -19,6 +19,7 @@
 #include "rm_internal.h"
 #include "rm_vec.h"
 
+#include <algorithm>
 #include <type_traits>
 
 namespace rm {
@@ -168,6 +169,10 @@ __device__ __forceinline__ void bld4(__amdgpu_buffer_rsrc_t rs, uint32_t voff, u
   }
 }
 
+// N storage elements (N = 1 or 4) from fp32 by one buffer store.
+template <typename ST, int N>
+__device__ __forceinline__ void bstv(__amdgpu_buffer_rsrc_t rs, uint32_t voff, uint32_t soff, const float (&v)[N]);
+
 template <typename ST>
 __device__ __forceinline__ void bst4(__amdgpu_buffer_rsrc_t rs, uint32_t voff, uint32_t soff, const float (&v)[4]) {
   if constexpr (sizeof(ST) == 2) {
@@ -178,6 +183,18 @@ __device__ __forceinline__ void bst4(__amdgpu_buffer_rsrc_t rs, uint32_t voff, u
     typedef uint32_t v4u __attribute__((ext_vector_type(4)));
     const v4u a = {__float_as_uint(v[0]), __float_as_uint(v[1]), __float_as_uint(v[2]), __float_as_uint(v[3])};
     __builtin_amdgcn_raw_buffer_store_b128(a, rs, voff, soff, 0);
+  }
+}
+
+template <typename ST, int N>
+__device__ __forceinline__ void bstv(__amdgpu_buffer_rsrc_t rs, uint32_t voff, uint32_t soff, const float (&v)[N]) {
+  static_assert(N == 1 || N == 4, "element count");
+  if constexpr (N == 4) {
+    bst4<ST>(rs, voff, soff, v);
+  } else if constexpr (sizeof(ST) == 2) {
+    __builtin_amdgcn_raw_buffer_store_b16((unsigned short)f32_to_bf16_bits(v[0]), rs, voff, soff, 0);
+  } else {
+    __builtin_amdgcn_raw_buffer_store_b32(__float_as_uint(v[0]), rs, voff, soff, 0);
   }
 }
 
@@ -405,60 +422,82 @@ __global__ __launch_bounds__(256) void k_gate_fwd(const ST* __restrict__ Z, cons
 }
 
 // ---------------------------------------------------------------------------
-// y = norm2(r2), r2 = out1 + out2 in the storage dtype.  One wave per row.
+// y = norm2(r2), r2 = out1 + out2 in the storage dtype.  One wave per row,
+// persistent: wave w of the grid takes rows w, w + W, w + 2W, ... (W waves in
+// the grid).  The affine of the wave's columns is loaded once; rows are
+// loaded one ahead into two alternating register sets; y and the statistics
+// are written by buffer stores issued on every lane (out-of-range offsets
+// where nothing is written), so the loop has no branches.
 template <typename ST, int N>
 __global__ __launch_bounds__(256) void k_ln2_fwd(const ST* __restrict__ r2, const ST* __restrict__ g2,
                                                  const ST* __restrict__ be2, ST* __restrict__ y,
                                                  float* __restrict__ stats, long NR, int D) {
   constexpr int Q = (MAXD + 64 * N - 1) / (64 * N);
-  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
-  const long row = (long)blockIdx.x * 4 + wave;
-  if (row >= NR) return;
+  constexpr int SZ = (int)sizeof(ST);
+  const int lane = threadIdx.x & 63;
+  const long gw = (long)blockIdx.x * 4 + (threadIdx.x >> 6);
+  const long W = (long)gridDim.x * 4;
+  if (gw >= NR) return;
   const float invD = 1.0f / (float)D;
-  const ST* r = r2 + row * D;
-  float v[Q][N];
-  float s = 0.f;
+  Raw<ST, N> rg[Q], rb[Q], buf[2][Q];
 #pragma unroll
   for (int q = 0; q < Q; ++q) {
-    const int c = (lane + 64 * q) * N;
-    if (c < D) {
-      ldv(r + c, v[q]);
-    } else {
-#pragma unroll
-      for (int e = 0; e < N; ++e) v[q][e] = 0.f;
-    }
-#pragma unroll
-    for (int e = 0; e < N; ++e) s += v[q][e];
+    const int cc = min((lane + 64 * q) * N, D - N);
+    ldr(g2 + cc, rg[q]);
+    ldr(be2 + cc, rb[q]);
   }
-  const float mean = wave_sum(s) * invD;
-  float s2 = 0.f;
+  const __amdgpu_buffer_rsrc_t ys = row_rsrc(y, NR * D * SZ);
+  const __amdgpu_buffer_rsrc_t ms = row_rsrc(stats + ST_MU2 * NR, NR * 4);
+  const __amdgpu_buffer_rsrc_t rss = row_rsrc(stats + ST_RS2 * NR, NR * 4);
+  auto load = [&](int k, long row) {
+    const ST* r = r2 + min(row, NR - 1) * D;
 #pragma unroll
-  for (int q = 0; q < Q; ++q) {
-    const int c = (lane + 64 * q) * N;
-    if (c < D) {
+    for (int q = 0; q < Q; ++q) ldr(r + min((lane + 64 * q) * N, D - N), buf[k][q]);
+  };
+  auto compute = [&](int k, long row) {
+    const bool valid = row < NR;
+    float v[Q][N];
+    float s = 0.f;
+#pragma unroll
+    for (int q = 0; q < Q; ++q) {
+      const float m = (lane + 64 * q) * N < D ? 1.f : 0.f;
+      unpack(buf[k][q], v[q]);
+#pragma unroll
+      for (int e = 0; e < N; ++e) s += m * v[q][e];
+    }
+    const float mean = wave_sum(s) * invD;
+    float s2 = 0.f;
+#pragma unroll
+    for (int q = 0; q < Q; ++q) {
+      const float m = (lane + 64 * q) * N < D ? 1.f : 0.f;
 #pragma unroll
       for (int e = 0; e < N; ++e) {
         const float dd = v[q][e] - mean;
-        s2 += dd * dd;
+        s2 += m * dd * dd;
       }
     }
-  }
-  const float rstd = rsqrtf(wave_sum(s2) * invD + EPS_OUTER);
+    const float rstd = rsqrtf(wave_sum(s2) * invD + EPS_OUTER);
+    const uint32_t soff = (uint32_t)(min(row, NR - 1) * D * SZ);
 #pragma unroll
-  for (int q = 0; q < Q; ++q) {
-    const int c = (lane + 64 * q) * N;
-    if (c < D) {
+    for (int q = 0; q < Q; ++q) {
+      const int c = (lane + 64 * q) * N;
       float gg[N], bb[N], o[N];
-      ldv(g2 + c, gg);
-      ldv(be2 + c, bb);
+      unpack(rg[q], gg);
+      unpack(rb[q], bb);
 #pragma unroll
       for (int e = 0; e < N; ++e) o[e] = (v[q][e] - mean) * rstd * gg[e] + bb[e];
-      stv(y + row * D + c, o);
+      bstv<ST, N>(ys, valid && c < D ? (uint32_t)(c * SZ) : 0x80000000u, soff, o);
     }
-  }
-  if (lane == 0) {
-    stats[ST_MU2 * NR + row] = mean;
-    stats[ST_RS2 * NR + row] = rstd;
+    const uint32_t so = valid && lane == 0 ? (uint32_t)(row * 4) : 0x80000000u;
+    __builtin_amdgcn_raw_buffer_store_b32(__float_as_uint(mean), ms, so, 0, 0);
+    __builtin_amdgcn_raw_buffer_store_b32(__float_as_uint(rstd), rss, so, 0, 0);
+  };
+  load(0, gw);
+  for (long row = gw; row < NR; row += 2 * W) {
+    load(1, row + W);
+    compute(0, row);
+    load(0, row + 2 * W);
+    compute(1, row + W);
   }
 }
 
@@ -1482,7 +1521,8 @@ hipError_t gate_fwd_t(const rm_dims& d, const rm_params& p, void* ws, const WsLa
 template <typename ST>
 hipError_t ln2_fwd_t(const rm_dims& d, const rm_params& p, void* y, void* ws, const WsLayout& L, hipStream_t s) {
   const long NR = (long)d.B * d.T;
-  const dim3 grid((unsigned)((NR + 3) / 4));
+  // persistent waves: four four-wave blocks per CU (the kernel's occupancy)
+  const dim3 grid((unsigned)std::min<long>((NR + 3) / 4, 4L * device_cu_count()));
   prof_begin(KID_LN2_FWD, s);
   if (d.D % 4 == 0)
     hipLaunchKernelGGL((k_ln2_fwd<ST, 4>), grid, dim3(256), 0, s, wsp<ST>(ws, L.r2), cptr<ST>(p.ln2_g),
