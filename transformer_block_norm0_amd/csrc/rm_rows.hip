@@ -169,10 +169,6 @@ __device__ __forceinline__ void bld4(__amdgpu_buffer_rsrc_t rs, uint32_t voff, u
   }
 }
 
-// N storage elements (N = 1 or 4) from fp32 by one buffer store.
-template <typename ST, int N>
-__device__ __forceinline__ void bstv(__amdgpu_buffer_rsrc_t rs, uint32_t voff, uint32_t soff, const float (&v)[N]);
-
 template <typename ST>
 __device__ __forceinline__ void bst4(__amdgpu_buffer_rsrc_t rs, uint32_t voff, uint32_t soff, const float (&v)[4]) {
   if constexpr (sizeof(ST) == 2) {
@@ -186,16 +182,46 @@ __device__ __forceinline__ void bst4(__amdgpu_buffer_rsrc_t rs, uint32_t voff, u
   }
 }
 
+// N storage elements from fp32 by one buffer store (N * sizeof(ST) = 2, 4,
+// 8 or 16 bytes).
 template <typename ST, int N>
 __device__ __forceinline__ void bstv(__amdgpu_buffer_rsrc_t rs, uint32_t voff, uint32_t soff, const float (&v)[N]) {
-  static_assert(N == 1 || N == 4, "element count");
-  if constexpr (N == 4) {
-    bst4<ST>(rs, voff, soff, v);
-  } else if constexpr (sizeof(ST) == 2) {
+  constexpr int BYTES = N * (int)sizeof(ST);
+  static_assert(BYTES == 2 || BYTES == 4 || BYTES == 8 || BYTES == 16, "store width");
+  if constexpr (BYTES == 2) {
     __builtin_amdgcn_raw_buffer_store_b16((unsigned short)f32_to_bf16_bits(v[0]), rs, voff, soff, 0);
   } else {
-    __builtin_amdgcn_raw_buffer_store_b32(__float_as_uint(v[0]), rs, voff, soff, 0);
+    constexpr int W = BYTES / 4;
+    uint32_t w[W];
+#pragma unroll
+    for (int i = 0; i < W; ++i) {
+      if constexpr (sizeof(ST) == 2) w[i] = bf_pack(v[2 * i], v[2 * i + 1]);
+      else w[i] = __float_as_uint(v[i]);
+    }
+    if constexpr (W == 1) {
+      __builtin_amdgcn_raw_buffer_store_b32(w[0], rs, voff, soff, 0);
+    } else if constexpr (W == 2) {
+      typedef uint32_t v2u __attribute__((ext_vector_type(2)));
+      const v2u a = {w[0], w[1]};
+      __builtin_amdgcn_raw_buffer_store_b64(a, rs, voff, soff, 0);
+    } else {
+      typedef uint32_t v4u __attribute__((ext_vector_type(4)));
+      const v4u a = {w[0], w[1], w[2], w[3]};
+      __builtin_amdgcn_raw_buffer_store_b128(a, rs, voff, soff, 0);
+    }
   }
+}
+
+// Resident blocks per compute unit of a kernel at a block size (cached).
+template <typename K>
+int resident_blocks(K kernel, int threads) {
+  static int cached = 0;
+  if (cached == 0) {
+    int n = 0;
+    if (hipOccupancyMaxActiveBlocksPerMultiprocessor(&n, kernel, threads, 0) != hipSuccess || n <= 0) n = 1;
+    cached = n;
+  }
+  return cached;
 }
 
 // ---------------------------------------------------------------------------
@@ -1521,8 +1547,9 @@ hipError_t gate_fwd_t(const rm_dims& d, const rm_params& p, void* ws, const WsLa
 template <typename ST>
 hipError_t ln2_fwd_t(const rm_dims& d, const rm_params& p, void* y, void* ws, const WsLayout& L, hipStream_t s) {
   const long NR = (long)d.B * d.T;
-  // persistent waves: four four-wave blocks per CU (the kernel's occupancy)
-  const dim3 grid((unsigned)std::min<long>((NR + 3) / 4, 4L * device_cu_count()));
+  // persistent: as many four-wave blocks as stay resident
+  const int rb = d.D % 4 == 0 ? resident_blocks(k_ln2_fwd<ST, 4>, 256) : resident_blocks(k_ln2_fwd<ST, 1>, 256);
+  const dim3 grid((unsigned)std::min<long>((NR + 3) / 4, (long)rb * device_cu_count()));
   prof_begin(KID_LN2_FWD, s);
   if (d.D % 4 == 0)
     hipLaunchKernelGGL((k_ln2_fwd<ST, 4>), grid, dim3(256), 0, s, wsp<ST>(ws, L.r2), cptr<ST>(p.ln2_g),
