@@ -36,7 +36,7 @@ sys.path.insert(0, ROOT)
 from rankmixer_inputs import PRODUCTION, WORKLOADS, make_case  # noqa: E402
 
 # MI355X published peaks
-PEAK_TFLOPS = {"bf16": 2516.6, "f32": 157.3}   # dense MFMA: 256 CU x 2.4 GHz x (4096 | 256) flop/clk
+PEAK_TFLOPS = {"bf16": 2516.6, "f16": 2516.6, "f32": 157.3}   # dense MFMA: 256 CU x 2.4 GHz x (4096 | 256) flop/clk
 PEAK_HBM_GBS = 8000.0
 
 
@@ -192,7 +192,7 @@ def main():
         rb.prof_enable(False)
         prof = rb.prof_collect()
         flops = gemm_flops(d)
-        sz = 2 if w.dtype == "bf16" else 4
+        sz = 4 if w.dtype == "f32" else 2
         rbytes = row_bytes(d, sz)
         step_ms_sum = 0.0
         for name, (ms, n) in prof.items():
@@ -257,7 +257,8 @@ def main():
         log(f"  {cpu['value']:.4g} tokens/s on {cpu['cores']} threads")
 
     out = {
-        "metric": "fwd+bwd tokens/s and % MFMA peak, B1024 T64 D1280 k2 bf16, 1 GPU",
+        "metric": ("fwd+bwd tokens/s and % MFMA peak, B1024 T64 D1280 k2 bf16, 1 GPU" if w.name == PRODUCTION
+                   else f"fwd+bwd tokens/s and % MFMA peak, {w.name}, 1 GPU"),
         "value": round(value, 1),
         "unit": "tokens/s",
         "n_gpus": 1,

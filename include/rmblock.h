@@ -20,7 +20,7 @@
  *
  * Conventions shared by every entry point
  *   - All tensors are dense, row-major, contiguous, in the storage dtype of
- *     rm_dims.dtype (fp32 or bf16).  Device pointers only; the caller owns
+ *     rm_dims.dtype (fp32, bf16 or fp16).  Device pointers only; the caller owns
  *     every buffer.  The library never allocates, frees or synchronises
  *     (except the instrumentation calls rm_prof_*, which say so).
  *   - `stream` is a hipStream_t (0 = the null stream) of the current device.
@@ -28,7 +28,7 @@
  *   - Validation (dims, dtype, null pointers, alignment, workspace size) runs
  *     on the host before anything is enqueued; on failure nothing is launched
  *     and the status says why.  RM_E_HIP means a launch failed.
- *   - Arithmetic: storage dtype (bf16 or fp32) for inputs, parameters,
+ *   - Arithmetic: storage dtype (fp32, bf16 or fp16) for inputs, parameters,
  *     outputs, gradients and every saved or intermediate tensor; fp32
  *     accumulation and statistics; round to nearest even on every store.  Results are bitwise repeatable for
  *     identical inputs (fixed-order reductions, no floating-point atomics).
@@ -45,7 +45,10 @@ extern "C" {
 
 #define RM_ABI_VERSION 1
 
-typedef enum { RM_F32 = 0, RM_BF16 = 1 } rm_dtype;
+/* Storage dtypes.  Besides the bf16 production workload, the page's section
+ * "Run the benchmark" runs the block with fp32 and fp16 storage; every
+ * storage dtype computes in fp32 inside the kernels. */
+typedef enum { RM_F32 = 0, RM_BF16 = 1, RM_F16 = 2 } rm_dtype;
 
 typedef enum {
   RM_OK = 0,
@@ -53,7 +56,7 @@ typedef enum {
   RM_E_NULL = 2,       /* a required pointer is NULL                           */
   RM_E_ALIGN = 3,      /* a pointer is not aligned to its element size         */
   RM_E_WORKSPACE = 4,  /* ws_bytes < rm_workspace_bytes(dims)                  */
-  RM_E_DTYPE = 5,      /* dtype is neither RM_F32 nor RM_BF16                  */
+  RM_E_DTYPE = 5,      /* dtype is not RM_F32, RM_BF16 or RM_F16               */
   RM_E_HIP = 6,        /* a HIP launch or runtime call failed                  */
   RM_E_ARG = 7         /* any other invalid argument                            */
 } rm_status;

@@ -21,7 +21,8 @@ reproduced without their runner, so NumPy's PCG64 stands in with a fixed draw
 order: w1, b1, wout, bout, then (only when random LayerNorm affines are asked
 for) gamma/beta of norm0, norm1, norm2, norm_x, norm_gate, then x; dy comes
 from PCG64(seed + 1000).  Values are drawn in float64 and rounded once to the
-storage dtype (round-to-nearest-even); bf16 is carried as uint16 bit patterns.
+storage dtype (round-to-nearest-even); bf16 and fp16 are carried as uint16 bit
+patterns.
 """
 from __future__ import annotations
 
@@ -36,7 +37,7 @@ PARAM_NAMES = (
     "ln0_g", "ln0_b", "ln1_g", "ln1_b", "ln2_g", "ln2_b",
 )
 
-DTYPES = ("f32", "bf16")
+DTYPES = ("f32", "bf16", "f16")
 
 
 @dataclasses.dataclass(frozen=True)
@@ -60,7 +61,7 @@ class Workload:
     """One synthetic workload: shape, storage dtype, seed, LayerNorm affine mode."""
     name: str
     dims: Dims
-    dtype: str            # "f32" or "bf16"
+    dtype: str            # "f32", "bf16" or "f16"
     seed: int
     ln_affine: str        # "unit" (gamma=1, beta=0) or "random" (U[0.5,1.5] / U[-0.1,0.1])
 
@@ -79,6 +80,10 @@ WORKLOADS = {w.name: w for w in (
     # the pages' public check shape and seed (page 1, "Public checks and instructor coverage")
     _w("B4_T16_D128_k2_f32_public", 4, 16, 128, 2, "f32", 7101, "unit"),
     _w("B4_T16_D128_k2_bf16_public", 4, 16, 128, 2, "bf16", 7101, "unit"),
+    # fp16 storage (page 1, "Run the benchmark": the --dtype float16 run)
+    _w("B4_T16_D128_k2_f16_public", 4, 16, 128, 2, "f16", 7101, "unit"),
+    _w("B256_T16_D256_k3_f16_lnrand", 256, 16, 256, 3, "f16", 8, "random"),
+    _w("B1024_T64_D1280_k2_f16", 1024, 64, 1280, 2, "f16", 6, "unit"),
 )}
 
 PRODUCTION = "B1024_T64_D1280_k2_bf16"
@@ -91,7 +96,7 @@ def in_envelope(d: Dims) -> bool:
 
 
 # ---------------------------------------------------------------------------
-# storage rounding (bf16 as uint16 bit patterns)
+# storage rounding (bf16 and fp16 as uint16 bit patterns)
 
 def f64_to_bf16_bits(a: np.ndarray) -> np.ndarray:
     """Round float64 values to bfloat16 (through float32, both round-to-nearest-even)."""
@@ -111,6 +116,11 @@ def to_storage(a64: np.ndarray, dtype: str) -> np.ndarray:
         return np.ascontiguousarray(a64, dtype=np.float32)
     if dtype == "bf16":
         return f64_to_bf16_bits(a64)
+    if dtype == "f16":
+        # float64 -> float16 directly, round-to-nearest-even (beyond the range: inf)
+        with np.errstate(over="ignore"):
+            h = np.asarray(a64, dtype=np.float64).astype(np.float16)
+        return np.ascontiguousarray(h.view(np.uint16))
     raise ValueError(f"unknown dtype {dtype!r}")
 
 
@@ -119,6 +129,8 @@ def storage_to_f64(a: np.ndarray, dtype: str) -> np.ndarray:
         return np.asarray(a, dtype=np.float64)
     if dtype == "bf16":
         return bf16_bits_to_f32(a).astype(np.float64)
+    if dtype == "f16":
+        return np.ascontiguousarray(a, dtype=np.uint16).view(np.float16).astype(np.float64)
     raise ValueError(f"unknown dtype {dtype!r}")
 
 

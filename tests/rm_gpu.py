@@ -9,8 +9,9 @@ import numpy as np
 
 from rankmixer_inputs import PARAM_NAMES, storage_to_f64
 
-# max |gpu - oracle| / max |oracle| per tensor (fp32 storage / bf16 storage)
-TOL = {"f32": 1e-4, "bf16": 3e-2}
+# max |gpu - oracle| / max |oracle| per tensor (fp32 storage / 16-bit storage)
+TOL = {"f32": 1e-4, "bf16": 3e-2, "f16": 3e-2}
+TORCH16 = {"bf16": "bfloat16", "f16": "float16"}
 
 GRAD_KEYS = ("dx",) + tuple("d" + n for n in PARAM_NAMES)
 
@@ -22,15 +23,15 @@ def say(msg: str):
 
 def to_torch(a: np.ndarray, dtype: str, device="cuda"):
     import torch
-    if dtype == "bf16":
-        return torch.from_numpy(np.ascontiguousarray(a).view(np.int16)).to(device).view(torch.bfloat16)
+    if dtype in TORCH16:
+        return torch.from_numpy(np.ascontiguousarray(a).view(np.int16)).to(device).view(getattr(torch, TORCH16[dtype]))
     return torch.from_numpy(np.ascontiguousarray(a, dtype=np.float32)).to(device)
 
 
 def from_torch(t, dtype: str) -> np.ndarray:
     import torch
-    if dtype == "bf16":
-        return storage_to_f64(t.view(torch.int16).cpu().numpy().view(np.uint16), "bf16")
+    if dtype in TORCH16:
+        return storage_to_f64(t.view(torch.int16).cpu().numpy().view(np.uint16), dtype)
     return t.cpu().numpy().astype(np.float64)
 
 
@@ -87,7 +88,7 @@ class DeviceCase:
     def raw_bits(self) -> dict:
         """Exact bit patterns of every output (for determinism checks)."""
         import torch
-        view = torch.int16 if self.dtype == "bf16" else torch.int32
+        view = torch.int16 if self.dtype in TORCH16 else torch.int32
         out = {"y": self.y.view(view).cpu().numpy(), "dx": self.dx.view(view).cpu().numpy()}
         for n, t in self.grads.items():
             out["d" + n] = t.view(view).cpu().numpy()
@@ -100,8 +101,8 @@ class DeviceCase:
         raw = self.ws[off:off + nbytes]
         if f32:
             return raw.view(torch.float32).cpu().numpy().astype(np.float64).reshape(shape)
-        if self.dtype == "bf16":
-            return storage_to_f64(raw.view(torch.int16).cpu().numpy().view(np.uint16), "bf16").reshape(shape)
+        if self.dtype in TORCH16:
+            return storage_to_f64(raw.view(torch.int16).cpu().numpy().view(np.uint16), self.dtype).reshape(shape)
         return raw.view(torch.float32).cpu().numpy().astype(np.float64).reshape(shape)
 
 

@@ -40,15 +40,15 @@ def test_library_exports_every_declared_symbol(rb):
 
 
 def tail_per_sample(B, T, D, dtype):
-    """bf16 samples of at most 160 KB, 16-byte rows, 4-element token-mix chunks: backward tail one sample per workgroup."""
-    return dtype == "bf16" and D % 8 == 0 and (D // T) % 4 == 0 and T * D * 2 <= 64 * 1280 * 2
+    """16-bit samples of at most 160 KB, 16-byte rows, 4-element token-mix chunks: backward tail one sample per workgroup."""
+    return dtype in ("bf16", "f16") and D % 8 == 0 and (D // T) % 4 == 0 and T * D * 2 <= 64 * 1280 * 2
 
 
 def expected_workspace_bytes(B, T, D, k, dtype):
     """The workspace layout restated from rmblock.h / the library's documented regions."""
     al = lambda v: (v + 255) // 256 * 256
     N, H = B * T, k * D
-    sz = 2 if dtype == "bf16" else 4
+    sz = 4 if dtype == "f32" else 2
     nb = (B + 63) // 64
     sizes = [N * D * sz, N * 2 * H * sz, N * H * sz, N * D * sz, 10 * N * 4,     # saved by the forward
              N * D * sz, N * H * sz, N * 2 * H * sz, N * D * sz, N * D * sz,     # backward scratch
@@ -62,7 +62,7 @@ def expected_workspace_bytes(B, T, D, k, dtype):
 
 @pytest.mark.parametrize("shape", [(1, 8, 64, 2), (4, 16, 128, 2), (999, 40, 1000, 3), (1024, 64, 1280, 2),
                                    (3, 13, 65, 3)])
-@pytest.mark.parametrize("dtype", ["f32", "bf16"])
+@pytest.mark.parametrize("dtype", ["f32", "bf16", "f16"])
 def test_workspace_bytes_formula(rb, shape, dtype):
     d = rb.dims(*shape, dtype)
     assert rb.workspace_bytes(d) == expected_workspace_bytes(*shape, dtype)
@@ -109,9 +109,11 @@ def test_bad_arguments_rejected_before_launch(rb):
     assert lib.rm_block_fwd(by(d), by(params), 1026, 1024, 4096, wsb, None) == 3
     p_mis = rb.rmblock.CParams(*([256] * 5 + [258] + [256] * 8))
     assert lib.rm_block_fwd(by(d), by(p_mis), 1024, 1024, 4096, wsb, None) == 3
-    # bf16 elements need only 2-byte alignment, but odd addresses fail
-    d16, p16, g16, wsb16 = _valid_call_args(rb, "bf16")
-    assert lib.rm_block_fwd(by(d16), by(p16), 1025, 1024, 4096, wsb16, None) == 3
+    # bf16 and fp16 elements need only 2-byte alignment, but odd addresses fail
+    for dt in ("bf16", "f16"):
+        d16, p16, g16, wsb16 = _valid_call_args(rb, dt)
+        assert lib.rm_block_fwd(by(d16), by(p16), 1025, 1024, 4096, wsb16, None) == 3
+        assert lib.rm_block_bwd(by(d16), by(p16), 1024, 1024, 4096, wsb16, 2049, by(g16), None) == 3
     # unknown dtype
     dbad = rb.rmblock.CDims(4, 16, 128, 2, 7)
     assert lib.rm_block_fwd(by(dbad), by(params), 1024, 1024, 4096, wsb, None) == 5

@@ -35,7 +35,7 @@ def oracle_results(case):
 
 @pytest.mark.parametrize("shape", [(1, 8, 64), (2, 64, 64), (3, 13, 65), (5, 8, 1280), (4, 16, 128),
                                    (7, 40, 1000)])
-@pytest.mark.parametrize("dtype", ["f32", "bf16"])
+@pytest.mark.parametrize("dtype", ["f32", "bf16", "f16"])
 def test_token_mix_bit_exact(shape, dtype):
     import torch
     import transformer_block_norm0_amd as rb
@@ -46,6 +46,10 @@ def test_token_mix_bit_exact(shape, dtype):
         bits = rng.integers(0, 1 << 16, size=(B, T, D), dtype=np.uint16)
         bits.flat[:4] = [0x8000, 0x7FC1, 0xFF81, 0x7F80]   # -0.0, NaN payloads, +inf
         inp = torch.from_numpy(bits.view(np.int16)).cuda().view(torch.bfloat16)
+    elif dtype == "f16":
+        bits = rng.integers(0, 1 << 16, size=(B, T, D), dtype=np.uint16)
+        bits.flat[:4] = [0x8000, 0x7E01, 0xFE01, 0x7C00]   # -0.0, NaN payloads, +inf
+        inp = torch.from_numpy(bits.view(np.int16)).cuda().view(torch.float16)
     else:
         bits = rng.integers(0, 1 << 32, size=(B, T, D), dtype=np.uint32)
         bits.flat[:4] = [0x80000000, 0x7FC00001, 0xFF800123, 0x7F800000]
@@ -53,7 +57,7 @@ def test_token_mix_bit_exact(shape, dtype):
     out = torch.empty_like(inp)
     rb.token_mix(rb.dims(B, T, D, 2, dtype), inp, out)
     torch.cuda.synchronize()
-    iview = torch.int16 if dtype == "bf16" else torch.int32
+    iview = torch.int32 if dtype == "f32" else torch.int16
     got = out.view(iview).cpu().numpy().view(bits.dtype)
     S = D // T
     want = bits.reshape(B, T, T, S).swapaxes(1, 2).reshape(B, T, D)
@@ -68,6 +72,8 @@ SMALL = [
     ("B4_T16_D128_k2_f32_public", None),
     ("B4_T16_D128_k2_bf16_public", None),
     ("B256_T16_D256_k3_f32", None),
+    ("B4_T16_D128_k2_f16_public", None),
+    ("B256_T16_D256_k3_f16_lnrand", None),
 ]
 EDGE = [  # (B, T, D, k): B=1 minimum dims; S=1; odd D (unaligned bf16 rows); S=160 and H=3840;
     (1, 8, 64, 2), (2, 64, 64, 3), (3, 13, 65, 3), (5, 8, 1280, 3), (67, 16, 256, 2), (130, 8, 96, 3)]
@@ -119,7 +125,7 @@ def test_parity_small_workloads(name):
 
 
 @pytest.mark.parametrize("shape", EDGE)
-@pytest.mark.parametrize("dtype", ["f32", "bf16"])
+@pytest.mark.parametrize("dtype", ["f32", "bf16", "f16"])
 def test_parity_edge_shapes(shape, dtype):
     B, T, D, k = shape
     check_case(make_custom(B, T, D, k, dtype, seed=B * 31 + T * 7 + D + k, ln_affine="random"))
@@ -223,3 +229,8 @@ def test_full_size_B1024_T64_D1280_k2_bf16_sampled():
 
 def test_full_size_B999_T40_D1000_k3_f32_sampled():
     sampled_check("B999_T40_D1000_k3_f32_lnrand", samples=(0, 500, -1), tokens=(0, 17, -1))
+
+
+def test_full_size_B1024_T64_D1280_k2_f16_sampled():
+    """fp16 storage (page 1, "Run the benchmark": the --dtype float16 run) at the production shape."""
+    sampled_check("B1024_T64_D1280_k2_f16", samples=(0, 300, -1), tokens=(0, 41, -1))

@@ -361,11 +361,28 @@ def test_backward_zero_gamma2_special_case():
             assert np.all(g[name] == 0.0), name
 
 
-def test_generated_case_runs_and_is_finite():
-    case = make_custom(2, 8, 64, 2, "bf16", seed=11)
+@pytest.mark.parametrize("dtype", ["f32", "bf16", "f16"])
+def test_generated_case_runs_and_is_finite(dtype):
+    case = make_custom(2, 8, 64, 2, dtype, seed=11)
     x, p, dy = as_f64(case)
     y, g = oracle.forward_backward(x, p, dy)
     assert y.shape == x.shape
     assert np.all(np.isfinite(y))
     for name in oracle.GRAD_NAMES:
         assert np.all(np.isfinite(g[name])), name
+
+
+def test_f16_storage_rounding():
+    """fp16 storage: exactly representable values round-trip; a value halfway
+    between two fp16 neighbours goes to the even one; overflow gives inf."""
+    from rankmixer_inputs import storage_to_f64, to_storage
+    exact = np.array([0.0, -0.0, 1.0, -2.5, 65504.0, 2.0 ** -24, 1.0 + 2.0 ** -10])
+    bits = to_storage(exact, "f16")
+    assert bits.dtype == np.uint16
+    np.testing.assert_array_equal(storage_to_f64(bits, "f16"), exact)
+    assert bits[1] == 0x8000 and bits[2] == 0x3C00 and bits[4] == 0x7BFF and bits[5] == 0x0001
+    # 1 + 2^-11 lies halfway between 1 (even mantissa) and 1 + 2^-10: rounds to 1
+    # 1 + 3*2^-11 lies halfway between 1 + 2^-10 (odd) and 1 + 2^-9 (even): rounds up
+    half = to_storage(np.array([1.0 + 2.0 ** -11, 1.0 + 3 * 2.0 ** -11]), "f16")
+    np.testing.assert_array_equal(storage_to_f64(half, "f16"), [1.0, 1.0 + 2.0 ** -9])
+    assert storage_to_f64(to_storage(np.array([70000.0]), "f16"), "f16")[0] == np.inf

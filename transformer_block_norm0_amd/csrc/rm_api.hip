@@ -31,7 +31,7 @@ const char* const kKernelNames[KID_COUNT] = {
     "tail_bwd"};
 
 bool dims_valid(const rm_dims& d) {
-  if (d.dtype != RM_F32 && d.dtype != RM_BF16) return false;
+  if (d.dtype != RM_F32 && d.dtype != RM_BF16 && d.dtype != RM_F16) return false;
   if (d.B < 1 || d.B > 1024) return false;
   if (d.T < 8 || d.T > 64) return false;
   if (d.D < 64 || d.D > 1280) return false;
@@ -45,7 +45,7 @@ static size_t align256(size_t x) { return (x + 255) & ~(size_t)255; }
 WsLayout ws_layout(const rm_dims& d) {
   WsLayout L{};
   const size_t N = (size_t)d.B * d.T, D = d.D, H = (size_t)d.k * d.D, T = d.T;
-  const size_t sz = d.dtype == RM_BF16 ? 2 : 4;
+  const size_t sz = d.dtype == RM_F32 ? 4 : 2;
   size_t off = 0;
   auto take = [&](size_t bytes) {
     off = align256(off);
@@ -128,11 +128,11 @@ bool aligned(const void* p, size_t a) { return (reinterpret_cast<uintptr_t>(p) %
 
 rm_status check_common(const rm_dims* dims, const rm_params* p, const void* ws, size_t ws_bytes) {
   if (!dims || !p) return RM_E_NULL;
-  if (dims->dtype != RM_F32 && dims->dtype != RM_BF16) return RM_E_DTYPE;
+  if (dims->dtype != RM_F32 && dims->dtype != RM_BF16 && dims->dtype != RM_F16) return RM_E_DTYPE;
   if (!dims_valid(*dims)) return RM_E_DIMS;
   const void* ptrs[] = {p->w1, p->b1, p->wout, p->bout, p->lnx_g, p->lnx_b, p->lng_g,
                         p->lng_b, p->ln0_g, p->ln0_b, p->ln1_g, p->ln1_b, p->ln2_g, p->ln2_b};
-  const size_t es = dims->dtype == RM_BF16 ? 2 : 4;
+  const size_t es = dims->dtype == RM_F32 ? 4 : 2;
   for (const void* q : ptrs) {
     if (!q) return RM_E_NULL;
     if (!aligned(q, es)) return RM_E_ALIGN;
@@ -158,7 +158,7 @@ const char* rm_status_string(int s) {
     case RM_E_NULL: return "a required pointer is NULL";
     case RM_E_ALIGN: return "a pointer is misaligned (elements: element size; workspace: 256 bytes)";
     case RM_E_WORKSPACE: return "workspace smaller than rm_workspace_bytes()";
-    case RM_E_DTYPE: return "dtype must be RM_F32 or RM_BF16";
+    case RM_E_DTYPE: return "dtype must be RM_F32, RM_BF16 or RM_F16";
     case RM_E_HIP: return "HIP launch or runtime error";
     case RM_E_ARG: return "invalid argument";
     default: return "unknown status";
@@ -172,11 +172,11 @@ size_t rm_workspace_bytes(const rm_dims* dims) {
 
 rm_status rm_ws_region(const rm_dims* dims, int region, size_t* offset, size_t* bytes) {
   if (!dims || !offset || !bytes) return RM_E_NULL;
-  if (dims->dtype != RM_F32 && dims->dtype != RM_BF16) return RM_E_DTYPE;
+  if (dims->dtype != RM_F32 && dims->dtype != RM_BF16 && dims->dtype != RM_F16) return RM_E_DTYPE;
   if (!dims_valid(*dims)) return RM_E_DIMS;
   const WsLayout L = ws_layout(*dims);
   const size_t N = (size_t)dims->B * dims->T, D = dims->D, H = (size_t)dims->k * dims->D;
-  const size_t sz = dims->dtype == RM_BF16 ? 2 : 4;
+  const size_t sz = dims->dtype == RM_F32 ? 4 : 2;
   switch (region) {
     case RM_WS_H1: *offset = L.h1; *bytes = N * D * sz; return RM_OK;
     case RM_WS_Z: *offset = L.z; *bytes = N * 2 * H * sz; return RM_OK;
@@ -192,7 +192,7 @@ rm_status rm_block_fwd(const rm_dims* dims, const rm_params* p, const void* x, v
   rm_status st = check_common(dims, p, ws, ws_bytes);
   if (st != RM_OK) return st;
   if (!x || !y) return RM_E_NULL;
-  const size_t es = dims->dtype == RM_BF16 ? 2 : 4;
+  const size_t es = dims->dtype == RM_F32 ? 4 : 2;
   if (!aligned(x, es) || !aligned(y, es)) return RM_E_ALIGN;
   const rm_dims d = *dims;
   const WsLayout L = ws_layout(d);
@@ -231,7 +231,7 @@ rm_status rm_block_bwd(const rm_dims* dims, const rm_params* p, const void* x, c
   rm_status st = check_common(dims, p, ws, ws_bytes);
   if (st != RM_OK) return st;
   if (!x || !dy || !dx || !g) return RM_E_NULL;
-  const size_t es = dims->dtype == RM_BF16 ? 2 : 4;
+  const size_t es = dims->dtype == RM_F32 ? 4 : 2;
   if (!aligned(x, es) || !aligned(dy, es) || !aligned(dx, es)) return RM_E_ALIGN;
   const void* gptrs[] = {g->w1, g->b1, g->wout, g->bout, g->lnx_g, g->lnx_b, g->lng_g,
                          g->lng_b, g->ln0_g, g->ln0_b, g->ln1_g, g->ln1_b, g->ln2_g, g->ln2_b};
@@ -286,10 +286,10 @@ rm_status rm_block_bwd(const rm_dims* dims, const rm_params* p, const void* x, c
 
 rm_status rm_token_mix(const rm_dims* dims, const void* in, void* out, void* stream) {
   if (!dims) return RM_E_NULL;
-  if (dims->dtype != RM_F32 && dims->dtype != RM_BF16) return RM_E_DTYPE;
+  if (dims->dtype != RM_F32 && dims->dtype != RM_BF16 && dims->dtype != RM_F16) return RM_E_DTYPE;
   if (!dims_valid(*dims)) return RM_E_DIMS;
   if (!in || !out) return RM_E_NULL;
-  const size_t es = dims->dtype == RM_BF16 ? 2 : 4;
+  const size_t es = dims->dtype == RM_F32 ? 4 : 2;
   if (!aligned(in, es) || !aligned(out, es)) return RM_E_ALIGN;
   if (in == out) return RM_E_ARG;
   return hip_status(launch_token_mix(*dims, in, out, reinterpret_cast<hipStream_t>(stream)));

@@ -9,22 +9,28 @@
 namespace rm {
 
 // ---------------------------------------------------------------------------
-// storage types.  bf16 is carried as its 16-bit pattern.
+// storage types.  bf16 and fp16 are carried as their 16-bit patterns.
 
 struct bf16_t {
+  uint16_t u;
+};
+struct f16_t {
   uint16_t u;
 };
 
 __device__ __forceinline__ float to_f32(float v) { return v; }
 __device__ __forceinline__ float to_f32(bf16_t v) { return __uint_as_float(((uint32_t)v.u) << 16); }
-
-// float -> bf16, round to nearest even; NaN stays a (quiet) NaN.
-__device__ __forceinline__ uint16_t f32_to_bf16_bits(float f) {
-  uint32_t u = __float_as_uint(f);
-  if ((u & 0x7fffffffu) > 0x7f800000u) return (uint16_t)((u >> 16) | 0x0040u);
-  u += 0x7fffu + ((u >> 16) & 1u);
-  return (uint16_t)(u >> 16);
+__device__ __forceinline__ float to_f32(f16_t v) { return (float)__builtin_bit_cast(_Float16, v.u); }
+// fp16 bit pattern -> fp32 (exact)
+__device__ __forceinline__ float h_to_f32(uint32_t bits16) {
+  return (float)__builtin_bit_cast(_Float16, (uint16_t)bits16);
 }
+// float -> fp16, round to nearest even (the hardware conversion's default mode).
+__device__ __forceinline__ uint16_t f32_to_f16_bits(float f) { return __builtin_bit_cast(uint16_t, (_Float16)f); }
+
+// float -> bf16, round to nearest even (the gfx950 conversion instruction);
+// NaN stays a (quiet) NaN.
+__device__ __forceinline__ uint16_t f32_to_bf16_bits(float f) { return __builtin_bit_cast(uint16_t, (__bf16)f); }
 
 template <typename ST> __device__ __forceinline__ ST from_f32(float f);
 template <> __device__ __forceinline__ float from_f32<float>(float f) { return f; }
@@ -32,6 +38,35 @@ template <> __device__ __forceinline__ bf16_t from_f32<bf16_t>(float f) {
   bf16_t r;
   r.u = f32_to_bf16_bits(f);
   return r;
+}
+template <> __device__ __forceinline__ f16_t from_f32<f16_t>(float f) {
+  f16_t r;
+  r.u = f32_to_f16_bits(f);
+  return r;
+}
+// 16-bit storage bits of a float, per storage type
+template <typename ST> __device__ __forceinline__ uint32_t to_bits16(float f);
+template <> __device__ __forceinline__ uint32_t to_bits16<bf16_t>(float f) { return f32_to_bf16_bits(f); }
+template <> __device__ __forceinline__ uint32_t to_bits16<f16_t>(float f) { return f32_to_f16_bits(f); }
+// the low / high element of a word of two 16-bit storage values, as fp32
+template <typename ST> __device__ __forceinline__ float lo16(uint32_t w);
+template <typename ST> __device__ __forceinline__ float hi16(uint32_t w);
+template <> __device__ __forceinline__ float lo16<bf16_t>(uint32_t w) { return __uint_as_float(w << 16); }
+template <> __device__ __forceinline__ float hi16<bf16_t>(uint32_t w) { return __uint_as_float(w & 0xffff0000u); }
+template <> __device__ __forceinline__ float lo16<f16_t>(uint32_t w) { return h_to_f32(w & 0xffffu); }
+template <> __device__ __forceinline__ float hi16<f16_t>(uint32_t w) { return h_to_f32(w >> 16); }
+// two floats packed as two 16-bit storage values (a in the low half), round
+// to nearest even: one v_cvt_pk_bf16_f32 / v_cvt_pk_f16_f32
+template <typename ST> __device__ __forceinline__ uint32_t pack16x2(float a, float b) {
+  typedef float f32x2 __attribute__((ext_vector_type(2)));
+  const f32x2 v = {a, b};
+  if constexpr (std::is_same<ST, f16_t>::value) {
+    typedef _Float16 h2 __attribute__((ext_vector_type(2)));
+    return __builtin_bit_cast(uint32_t, __builtin_convertvector(v, h2));
+  } else {
+    typedef __bf16 b2 __attribute__((ext_vector_type(2)));
+    return __builtin_bit_cast(uint32_t, __builtin_convertvector(v, b2));
+  }
 }
 
 template <typename ST> __device__ __forceinline__ float ld(const ST* p, long i) { return to_f32(p[i]); }

@@ -10,8 +10,9 @@
 //   * one workgroup = 256 threads = 4 waves (2 x 2), block tile BM x BN,
 //     wave tile (BM/2) x (BN/2) built from 32x32 MFMA tiles:
 //       bf16: v_mfma_f32_32x32x16_bf16 (8 K-contiguous bf16 per lane per operand)
+//       fp16: v_mfma_f32_32x32x16_f16  (the same layout, fp16 operands)
 //       fp32: v_mfma_f32_32x32x2f32    (fp32 operands, never a lower precision)
-//   * K is staged 128 bytes at a time (64 bf16 / 32 fp32) into LDS rows that
+//   * K is staged 128 bytes at a time (64 16-bit / 32 fp32) into LDS rows that
 //     are K-contiguous for both operands ([mn][k]); the 16-byte chunks of a
 //     row are XOR-swizzled by (row/2)%8 so the MFMA fragment reads (32 rows,
 //     same chunk) hit distinct banks;
@@ -27,6 +28,8 @@
 //     that XCD's L2;
 //   * the epilogue adds bias[t] and a residual and stores fp32 or the storage
 //     dtype (round to nearest even).
+#include <type_traits>
+
 #include "rm_common.h"
 #include "rm_internal.h"
 
@@ -34,6 +37,7 @@ namespace rm {
 namespace {
 
 typedef __attribute__((__vector_size__(8 * sizeof(__bf16)))) __bf16 bf16x8_t;
+typedef __attribute__((__vector_size__(8 * sizeof(_Float16)))) _Float16 f16x8_t;
 typedef __attribute__((__vector_size__(16 * sizeof(float)))) float f32x16_t;
 
 template <typename ST>
@@ -43,6 +47,8 @@ struct Cfg<bf16_t> {
   static constexpr int VW = 8;   // elements per 16-byte vector
   static constexpr int BK = 64;  // K per LDS slab (128 bytes)
 };
+template <>
+struct Cfg<f16_t> : Cfg<bf16_t> {};
 template <>
 struct Cfg<float> {
   static constexpr int VW = 4;
@@ -231,18 +237,24 @@ __global__ __launch_bounds__(256, 2) void k_gemm(GemmArgs g) {
     for (int ks = 0; ks < 4; ++ks) {
       const int chunk = 2 * ks + hl;
       if constexpr (sizeof(ST) == 2) {
-        bf16x8_t a[TM], b[TN];
+        // bf16: v_mfma_f32_32x32x16_bf16; fp16: v_mfma_f32_32x32x16_f16 (same fragment layout)
+        typedef std::conditional_t<std::is_same<ST, f16_t>::value, f16x8_t, bf16x8_t> frag_t;
+        frag_t a[TM], b[TN];
 #pragma unroll
         for (int i = 0; i < TM; ++i)
-          a[i] = *reinterpret_cast<const bf16x8_t*>(As + swz(wm * WTM + 32 * i + r32, chunk));
+          a[i] = *reinterpret_cast<const frag_t*>(As + swz(wm * WTM + 32 * i + r32, chunk));
 #pragma unroll
         for (int j = 0; j < TN; ++j)
-          b[j] = *reinterpret_cast<const bf16x8_t*>(Bs + swz(wn * WTN + 32 * j + r32, chunk));
+          b[j] = *reinterpret_cast<const frag_t*>(Bs + swz(wn * WTN + 32 * j + r32, chunk));
 #pragma unroll
         for (int i = 0; i < TM; ++i)
 #pragma unroll
-          for (int j = 0; j < TN; ++j)
-            acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a[i], b[j], acc[i][j], 0, 0, 0);
+          for (int j = 0; j < TN; ++j) {
+            if constexpr (std::is_same<ST, f16_t>::value)
+              acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_f16(a[i], b[j], acc[i][j], 0, 0, 0);
+            else
+              acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a[i], b[j], acc[i][j], 0, 0, 0);
+          }
       } else {
         float4 a[TM], b[TN];
 #pragma unroll
@@ -327,7 +339,7 @@ inline bool aligned16(const void* p) { return (reinterpret_cast<uintptr_t>(p) & 
 
 hipError_t launch_gemm(int dtype, bool a_kmajor, bool b_kmajor, const GemmArgs& g, int kid, hipStream_t s) {
   if (g.M <= 0 || g.N <= 0 || g.K <= 0 || g.batch <= 0) return hipSuccess;
-  const int vw = dtype == RM_BF16 ? 8 : 4;
+  const int vw = dtype == RM_F32 ? 4 : 8;
   // 16-byte vector loads need every contiguous extent, stride and batch
   // offset to be a multiple of the vector width and 16-byte aligned bases.
   const long a_cont = a_kmajor ? g.K : g.M, b_cont = b_kmajor ? g.K : g.N;
@@ -336,10 +348,11 @@ hipError_t launch_gemm(int dtype, bool a_kmajor, bool b_kmajor, const GemmArgs& 
   prof_begin(kid, s);
   hipError_t e;
   if (gemm256_supported(dtype, a_kmajor, b_kmajor, g, kid))
-    e = launch_gemm256(a_kmajor, b_kmajor, g, kid, s);
+    e = launch_gemm256(dtype, a_kmajor, b_kmajor, g, kid, s);
   else
-    e = dtype == RM_BF16 ? dispatch<bf16_t>(a_kmajor, b_kmajor, g, vec, s)
-                         : dispatch<float>(a_kmajor, b_kmajor, g, vec, s);
+    e = dtype == RM_BF16  ? dispatch<bf16_t>(a_kmajor, b_kmajor, g, vec, s)
+        : dtype == RM_F16 ? dispatch<f16_t>(a_kmajor, b_kmajor, g, vec, s)
+                          : dispatch<float>(a_kmajor, b_kmajor, g, vec, s);
   prof_end(kid, s);
   return e;
 }

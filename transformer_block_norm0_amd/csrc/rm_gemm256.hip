@@ -1,4 +1,4 @@
-// bf16 T-batched GEMM with 256x256 workgroup tiles for gfx950 (CDNA4).
+// bf16 / fp16 T-batched GEMM with 256x256 workgroup tiles for gfx950 (CDNA4).
 //
 // Same contract as the general kernel (GemmArgs; page 1 of "Subgraph-fusion-
 // based Mega-kernel Generation", section "Exact computation": one independent
@@ -6,7 +6,7 @@
 // aligned, 8-element-multiple rows.
 //
 //   * 4 waves (2 x 2), each owning a 128 x 128 output tile: 4 x 4 MFMA
-//     v_mfma_f32_32x32x16_bf16 tiles, 256 fp32 accumulators per lane (AGPRs,
+//     v_mfma_f32_32x32x16_bf16 (or _f16) tiles, 256 fp32 accumulators per lane (AGPRs,
 //     one wave per SIMD).  Per 16-deep k step a wave reads 8 KB of operand
 //     fragments from LDS for 16 MFMAs (64 bytes of LDS per clock per CU at
 //     full MFMA rate).
@@ -37,6 +37,8 @@
 //     ever made.
 //   * Rows past M or N are loaded from a clamped valid address and their
 //     results dropped at the store.
+#include <type_traits>
+
 #include "rm_common.h"
 #include "rm_internal.h"
 
@@ -44,6 +46,7 @@ namespace rm {
 namespace {
 
 typedef __attribute__((__vector_size__(8 * sizeof(__bf16)))) __bf16 bf16x8_t;
+typedef __attribute__((__vector_size__(8 * sizeof(_Float16)))) _Float16 f16x8_t;
 typedef __attribute__((__vector_size__(16 * sizeof(float)))) float f32x16_t;
 typedef short short4_t __attribute__((ext_vector_type(4)));
 typedef short short8_t __attribute__((ext_vector_type(8)));
@@ -60,10 +63,11 @@ constexpr int KSTEPS = BK / 16;           // MFMA k steps per slab
 // offset, which the buffer unit drops).
 constexpr int EPI_STORES = 32;
 
-// Two fp32 values as packed bf16 (round to nearest even: v_cvt_pk_bf16_f32).
-__device__ __forceinline__ uint32_t bf16_pair(float a, float b) {
-  return (uint32_t)__builtin_bit_cast(unsigned short, (__bf16)a) |
-         ((uint32_t)__builtin_bit_cast(unsigned short, (__bf16)b) << 16);
+// Two fp32 values as a packed pair of the 16-bit storage type ST, round to
+// nearest even (one v_cvt_pk_bf16_f32 / v_cvt_pk_f16_f32).
+template <typename ST>
+__device__ __forceinline__ uint32_t pair16(float a, float b) {
+  return pack16x2<ST>(a, b);
 }
 
 // K-major slab: 256 rows x 128 bytes (8 chunks of 16 B, one cache line per
@@ -131,11 +135,11 @@ __device__ __forceinline__ void dma_slab(char* lds, const bf16_t* __restrict__ b
 
 // MFMA fragment (32 rows of m or n, 16 of k at k-step ks) for this lane.
 template <bool KMAJ>
-__device__ __forceinline__ bf16x8_t read_frag(const char* lds, int row0, int ks, int lane) {
+__device__ __forceinline__ short8_t read_frag(const char* lds, int row0, int ks, int lane) {
   if constexpr (KMAJ) {
     const int row = row0 + (lane & 31);
     const int chunk = 2 * ks + (lane >> 5);
-    return *reinterpret_cast<const bf16x8_t*>(lds + kswz(row, chunk));
+    return *reinterpret_cast<const short8_t*>(lds + kswz(row, chunk));
   } else {
     const int g = lane >> 4, li = lane & 15;
     const int krow = 16 * ks + 8 * (g >> 1) + (li >> 2);
@@ -144,14 +148,14 @@ __device__ __forceinline__ bf16x8_t read_frag(const char* lds, int row0, int ks,
     const int off1 = mswz(krow + 4, col >> 3) + (col & 7) * 2;
     const short4_t lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_short4*)(lds + off0));
     const short4_t hi = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_short4*)(lds + off1));
-    const short8_t v = __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7);
-    return __builtin_bit_cast(bf16x8_t, v);
+    return __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7);
   }
 }
 
 // Operand fragments of one 16-deep k step: 4 of A (m blocks), 4 of B (n blocks).
+// Eight 16-bit elements per lane per fragment, bf16 or fp16 by the kernel.
 struct Frags {
-  bf16x8_t a[4], b[4];
+  short8_t a[4], b[4];
 };
 
 template <bool AK, bool BKM>
@@ -166,15 +170,24 @@ __device__ __forceinline__ void read_frags(Frags& f, const char* a_s, const char
 // 16 MFMAs of one k step.  The B fragment is the MFMA's first operand, so
 // each 32 x 32 accumulator block holds C transposed: element v of lane l is
 // C[m = l%32][n = 8*(v/4) + 4*(l/32) + v%4], four consecutive n per lane.
-// ZERO: the tile's first k step starts from zero accumulators.
-template <bool ZERO>
+// ZERO: the tile's first k step starts from zero accumulators.  ST selects
+// v_mfma_f32_32x32x16_bf16 or v_mfma_f32_32x32x16_f16 (same operand layout).
+template <typename ST, bool ZERO>
 __device__ __forceinline__ void mfma16(f32x16_t (&acc)[4][4], const Frags& f) {
   const f32x16_t zero = {};
 #pragma unroll
   for (int i = 0; i < 4; ++i)
 #pragma unroll
-    for (int j = 0; j < 4; ++j)
-      acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(f.b[j], f.a[i], ZERO ? zero : acc[i][j], 0, 0, 0);
+    for (int j = 0; j < 4; ++j) {
+      if constexpr (std::is_same<ST, f16_t>::value)
+        acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_f16(__builtin_bit_cast(f16x8_t, f.b[j]),
+                                                           __builtin_bit_cast(f16x8_t, f.a[i]),
+                                                           ZERO ? zero : acc[i][j], 0, 0, 0);
+      else
+        acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(__builtin_bit_cast(bf16x8_t, f.b[j]),
+                                                            __builtin_bit_cast(bf16x8_t, f.a[i]),
+                                                            ZERO ? zero : acc[i][j], 0, 0, 0);
+    }
 }
 
 // Scheduling pattern for 16 MFMAs whose fragments are already in registers,
@@ -260,16 +273,17 @@ __device__ __forceinline__ void dma_pair(char* sa, char* sb, const Src& s, const
   dma_slab<BKM>(sb, s.B, s.offb, g.b_ld, kslab * BK, wave);
 }
 
-// Four bf16 values (two packed words) added to v.
-__device__ __forceinline__ void add_bf16x4(float (&v)[4], v2u32 w) {
-  v[0] += __uint_as_float(w.x << 16);
-  v[1] += __uint_as_float(w.x & 0xffff0000u);
-  v[2] += __uint_as_float(w.y << 16);
-  v[3] += __uint_as_float(w.y & 0xffff0000u);
+// Four 16-bit storage values (two packed words) added to v.
+template <typename ST>
+__device__ __forceinline__ void add16x4(float (&v)[4], v2u32 w) {
+  v[0] += lo16<ST>(w.x);
+  v[1] += hi16<ST>(w.x);
+  v[2] += lo16<ST>(w.y);
+  v[3] += hi16<ST>(w.y);
 }
 
-// The bf16 residual of one 32-row block: 16 loads of 4 columns (zero where
-// out of range).
+// The residual (storage dtype) of one 32-row block: 16 loads of 4 columns
+// (zero where out of range).
 __device__ __forceinline__ void load_residual(v2u32 (&r)[16], const GemmArgs& g, __amdgpu_buffer_rsrc_t rrs,
                                               uint32_t rld, int m, int nbase, bool mok) {
 #pragma unroll
@@ -292,7 +306,7 @@ __device__ __forceinline__ void load_residual(v2u32 (&r)[16], const GemmArgs& g,
 // BIAS / RES are compile-time, so the epilogue has no branches: the tile's 64
 // bias values per lane are read from LDS once, and the residual of m block
 // i+1 is loaded while block i is computed and stored.
-template <bool BIAS, bool RES>
+template <typename ST, bool BIAS, bool RES>
 __device__ __forceinline__ void epilogue(const f32x16_t (&acc)[4][4], const GemmArgs& g, const Tile& c,
                                          const char* sbias, int wm, int wn, int lane) {
   const int r = lane & 31, h = lane >> 5;
@@ -347,15 +361,15 @@ __device__ __forceinline__ void epilogue(const f32x16_t (&acc)[4][4], const Gemm
           v1[e] = acc[i][j][4 * q + 4 + e];
         }
         if constexpr (BIAS) {
-          add_bf16x4(v0, bias[4 * j + q]);
-          add_bf16x4(v1, bias[4 * j + q + 1]);
+          add16x4<ST>(v0, bias[4 * j + q]);
+          add16x4<ST>(v1, bias[4 * j + q + 1]);
         }
         if constexpr (RES) {
-          add_bf16x4(v0, res[i & 1][4 * j + q]);
-          add_bf16x4(v1, res[i & 1][4 * j + q + 1]);
+          add16x4<ST>(v0, res[i & 1][4 * j + q]);
+          add16x4<ST>(v1, res[i & 1][4 * j + q + 1]);
         }
-        uint32_t a0 = bf16_pair(v0[0], v0[1]), a1 = bf16_pair(v0[2], v0[3]);
-        uint32_t b0 = bf16_pair(v1[0], v1[1]), b1 = bf16_pair(v1[2], v1[3]);
+        uint32_t a0 = pair16<ST>(v0[0], v0[1]), a1 = pair16<ST>(v0[2], v0[3]);
+        uint32_t b0 = pair16<ST>(v1[0], v1[1]), b1 = pair16<ST>(v1[2], v1[3]);
         const auto s0 = __builtin_amdgcn_permlane32_swap(a0, b0, false, false);
         const auto s1 = __builtin_amdgcn_permlane32_swap(a1, b1, false, false);
         a0 = s0[0]; b0 = s0[1];
@@ -381,22 +395,22 @@ __device__ __forceinline__ void epilogue(const f32x16_t (&acc)[4][4], const Gemm
 // k+2 (this tile's, DMA == 1, or the next tile's, DMA == 2, when there is one;
 // that tile's bias first); the next slab's first fragments are read during
 // the last k step's MFMAs.
-template <bool AK, bool BKM, bool ZERO, int DMA, bool BIAS>
+template <typename ST, bool AK, bool BKM, bool ZERO, int DMA, bool BIAS>
 __device__ __forceinline__ void slab_step(f32x16_t (&acc)[4][4], Frags& f0, Frags& f1, char* sa, char* sb,
                                           const char* na, const char* nb, int kdma, bool tile_start, bool has_next,
                                           const GemmArgs& g, const Src& src, const Tile& nt, char* nbias, int wm,
                                           int wn, int wave, int lane) {
   constexpr int NR = (AK ? 4 : 8) + (BKM ? 4 : 8);
   read_frags<AK, BKM>(f1, sa, sb, wm, wn, 1, lane);
-  mfma16<ZERO>(acc, f0);
+  mfma16<ST, ZERO>(acc, f0);
   interleave<NR>();
   __builtin_amdgcn_sched_barrier(0);
   read_frags<AK, BKM>(f0, sa, sb, wm, wn, 2, lane);
-  mfma16<false>(acc, f1);
+  mfma16<ST, false>(acc, f1);
   interleave<NR>();
   __builtin_amdgcn_sched_barrier(0);
   read_frags<AK, BKM>(f1, sa, sb, wm, wn, 3, lane);
-  mfma16<false>(acc, f0);
+  mfma16<ST, false>(acc, f0);
   interleave<NR>();
   if (tile_start) sync_slab<EPI_STORES>();  // >= EPI_STORES stores are newer than slab k+1's copies
   else sync_slab<0>();
@@ -410,7 +424,7 @@ __device__ __forceinline__ void slab_step(f32x16_t (&acc)[4][4], Frags& f0, Frag
   }
   __builtin_amdgcn_sched_barrier(0);
   read_frags<AK, BKM>(f0, na, nb, wm, wn, 0, lane);
-  mfma16<false>(acc, f1);
+  mfma16<ST, false>(acc, f1);
   interleave<NR>();
 }
 
@@ -425,7 +439,7 @@ __device__ __forceinline__ void slab_step(f32x16_t (&acc)[4][4], Frags& f0, Frag
 // tile copy the next tile's slabs 0 and 1; the tile's EPI_STORES stores follow,
 // so at the next tile's first wait at least EPI_STORES operations are newer
 // than the awaited slab: vmcnt(EPI_STORES).
-template <bool AK, bool BKM, bool BIAS, bool RES>
+template <typename ST, bool AK, bool BKM, bool BIAS, bool RES>
 __device__ __forceinline__ void gemm256_body(const GemmArgs& g) {
   // stage s: A slab at sA + s * TILE_BYTES, B slab at sB + s * TILE_BYTES;
   // bias tiles double buffered
@@ -472,26 +486,26 @@ __device__ __forceinline__ void gemm256_body(const GemmArgs& g) {
     char* nbias = sbias[(it + 1) & 1];
 
     // steps 0 .. nk-3 copy this tile's slabs 2 .. nk-1
-    slab_step<AK, BKM, true, 1, BIAS>(acc, f0, f1, a0, b0, a1, b1, 2, !first, has_next, g, cur, nt, nbias, wm, wn, wave,
+    slab_step<ST, AK, BKM, true, 1, BIAS>(acc, f0, f1, a0, b0, a1, b1, 2, !first, has_next, g, cur, nt, nbias, wm, wn, wave,
                                 lane);
-    slab_step<AK, BKM, false, 1, BIAS>(acc, f0, f1, a1, b1, a0, b0, 3, false, has_next, g, cur, nt, nbias, wm, wn, wave,
+    slab_step<ST, AK, BKM, false, 1, BIAS>(acc, f0, f1, a1, b1, a0, b0, 3, false, has_next, g, cur, nt, nbias, wm, wn, wave,
                                  lane);
     for (int k = 2; k < nk - 2; k += 2) {
-      slab_step<AK, BKM, false, 1, BIAS>(acc, f0, f1, a0, b0, a1, b1, k + 2, false, has_next, g, cur, nt, nbias, wm, wn,
+      slab_step<ST, AK, BKM, false, 1, BIAS>(acc, f0, f1, a0, b0, a1, b1, k + 2, false, has_next, g, cur, nt, nbias, wm, wn,
                                    wave, lane);
-      slab_step<AK, BKM, false, 1, BIAS>(acc, f0, f1, a1, b1, a0, b0, k + 3, false, has_next, g, cur, nt, nbias, wm, wn,
+      slab_step<ST, AK, BKM, false, 1, BIAS>(acc, f0, f1, a1, b1, a0, b0, k + 3, false, has_next, g, cur, nt, nbias, wm, wn,
                                    wave, lane);
     }
     // steps nk-2, nk-1 copy the next tile's slabs 0, 1 (if any; without a next
     // tile the last step copies nothing and its fragment reads of stage 0 are
     // stale and unused: the same code on both paths keeps the accumulators in
     // AGPRs)
-    slab_step<AK, BKM, false, 2, BIAS>(acc, f0, f1, a0, b0, a1, b1, 0, false, has_next, g, nxt, nt, nbias, wm, wn, wave,
+    slab_step<ST, AK, BKM, false, 2, BIAS>(acc, f0, f1, a0, b0, a1, b1, 0, false, has_next, g, nxt, nt, nbias, wm, wn, wave,
                                  lane);
-    slab_step<AK, BKM, false, 2, BIAS>(acc, f0, f1, a1, b1, a0, b0, 1, false, has_next, g, nxt, nt, nbias, wm, wn, wave,
+    slab_step<ST, AK, BKM, false, 2, BIAS>(acc, f0, f1, a1, b1, a0, b0, 1, false, has_next, g, nxt, nt, nbias, wm, wn, wave,
                                  lane);
 
-    epilogue<BIAS, RES>(acc, g, ct, sbias[it & 1], wm, wn, lane);
+    epilogue<ST, BIAS, RES>(acc, g, ct, sbias[it & 1], wm, wn, lane);
     if (!has_next) break;
     tile = next;
     ct = nt;
@@ -501,14 +515,22 @@ __device__ __forceinline__ void gemm256_body(const GemmArgs& g) {
 }
 
 
-// One kernel symbol per GEMM of the block, so that profiles name them; the
-// epilogue (bias, residual) is fixed per kernel.
-__global__ __launch_bounds__(256, 1) void gemm_up_bf16(GemmArgs g) { gemm256_body<true, false, true, false>(g); }
-__global__ __launch_bounds__(256, 1) void gemm_down_bf16(GemmArgs g) { gemm256_body<true, false, true, true>(g); }
-__global__ __launch_bounds__(256, 1) void gemm_dhid_bf16(GemmArgs g) { gemm256_body<true, true, false, false>(g); }
-__global__ __launch_bounds__(256, 1) void gemm_dh1_bf16(GemmArgs g) { gemm256_body<true, true, false, true>(g); }
-__global__ __launch_bounds__(256, 1) void gemm_dwout_bf16(GemmArgs g) { gemm256_body<false, false, false, false>(g); }
-__global__ __launch_bounds__(256, 1) void gemm_dw1_bf16(GemmArgs g) { gemm256_body<false, false, false, false>(g); }
+// One kernel symbol per GEMM of the block and storage type, so that profiles
+// name them; the epilogue (bias, residual) is fixed per kernel.
+#define RM_GEMM256_KERNELS(SFX, ST)                                                                            \
+  __global__ __launch_bounds__(256, 1) void gemm_up_##SFX(GemmArgs g) { gemm256_body<ST, true, false, true, false>(g); } \
+  __global__ __launch_bounds__(256, 1) void gemm_down_##SFX(GemmArgs g) { gemm256_body<ST, true, false, true, true>(g); } \
+  __global__ __launch_bounds__(256, 1) void gemm_dhid_##SFX(GemmArgs g) {                                       \
+    gemm256_body<ST, true, true, false, false>(g);                                                                   \
+  }                                                                                                                  \
+  __global__ __launch_bounds__(256, 1) void gemm_dh1_##SFX(GemmArgs g) { gemm256_body<ST, true, true, false, true>(g); } \
+  __global__ __launch_bounds__(256, 1) void gemm_dwout_##SFX(GemmArgs g) {                                      \
+    gemm256_body<ST, false, false, false, false>(g);                                                                 \
+  }                                                                                                                  \
+  __global__ __launch_bounds__(256, 1) void gemm_dw1_##SFX(GemmArgs g) { gemm256_body<ST, false, false, false, false>(g); }
+RM_GEMM256_KERNELS(bf16, bf16_t)
+RM_GEMM256_KERNELS(f16, f16_t)
+#undef RM_GEMM256_KERNELS
 
 typedef void (*Gemm256Kernel)(GemmArgs);
 
@@ -516,15 +538,15 @@ typedef void (*Gemm256Kernel)(GemmArgs);
 struct Gemm256Entry {
   int kid;
   bool a_kmajor, b_kmajor, bias, res;
-  Gemm256Kernel k;
+  Gemm256Kernel bf16, f16;
 };
 const Gemm256Entry kGemm256[] = {
-    {KID_GEMM_UP, true, false, true, false, gemm_up_bf16},
-    {KID_GEMM_DOWN, true, false, true, true, gemm_down_bf16},
-    {KID_GEMM_DHID, true, true, false, false, gemm_dhid_bf16},
-    {KID_GEMM_DH1, true, true, false, true, gemm_dh1_bf16},
-    {KID_GEMM_DWOUT, false, false, false, false, gemm_dwout_bf16},
-    {KID_GEMM_DW1, false, false, false, false, gemm_dw1_bf16},
+    {KID_GEMM_UP, true, false, true, false, gemm_up_bf16, gemm_up_f16},
+    {KID_GEMM_DOWN, true, false, true, true, gemm_down_bf16, gemm_down_f16},
+    {KID_GEMM_DHID, true, true, false, false, gemm_dhid_bf16, gemm_dhid_f16},
+    {KID_GEMM_DH1, true, true, false, true, gemm_dh1_bf16, gemm_dh1_f16},
+    {KID_GEMM_DWOUT, false, false, false, false, gemm_dwout_bf16, gemm_dwout_f16},
+    {KID_GEMM_DW1, false, false, false, false, gemm_dw1_bf16, gemm_dw1_f16},
 };
 const Gemm256Entry* gemm256_entry(bool a_kmajor, bool b_kmajor, const GemmArgs& g, int kid) {
   for (const Gemm256Entry& e : kGemm256)
@@ -561,7 +583,7 @@ int device_cu_count() {
 }
 
 bool gemm256_supported(int dtype, bool a_kmajor, bool b_kmajor, const GemmArgs& g, int kid) {
-  if (dtype != RM_BF16 || g.c_f32) return false;  // bf16 operands and output
+  if ((dtype != RM_BF16 && dtype != RM_F16) || g.c_f32) return false;  // 16-bit operands and output
   if (gemm256_entry(a_kmajor, b_kmajor, g, kid) == nullptr) return false;
   if (g.K % (2 * BK) != 0 || g.K < 4 * BK) return false;  // nk even, at least 4
   const long a_cont = a_kmajor ? g.K : g.M, b_cont = b_kmajor ? g.K : g.N;
@@ -583,10 +605,10 @@ bool gemm256_supported(int dtype, bool a_kmajor, bool b_kmajor, const GemmArgs& 
   return true;
 }
 
-hipError_t launch_gemm256(bool a_kmajor, bool b_kmajor, const GemmArgs& g, int kid, hipStream_t s) {
+hipError_t launch_gemm256(int dtype, bool a_kmajor, bool b_kmajor, const GemmArgs& g, int kid, hipStream_t s) {
   const Gemm256Entry* e = gemm256_entry(a_kmajor, b_kmajor, g, kid);
   if (e == nullptr) return hipErrorInvalidValue;  // callers check gemm256_supported first
-  return run256(e->k, g, s);
+  return run256(dtype == RM_F16 ? e->f16 : e->bf16, g, s);
 }
 
 }  // namespace rm

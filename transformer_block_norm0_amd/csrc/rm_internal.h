@@ -45,14 +45,15 @@ struct WsLayout {
 
 bool dims_valid(const rm_dims& d);
 
-// One bf16 sample (T x D) fits the 160 KB LDS of a workgroup, rows are whole
+// One 16-bit (bf16 or fp16) sample (T x D) fits the 160 KB LDS of a workgroup, rows are whole
 // 16-byte pieces (D % 8 == 0) and 4-element chunks have contiguous token-mix
 // sources: the prologue and the backward tail then run one sample per
 // workgroup, staged in LDS by direct copies (which also need a 16-byte
 // aligned x).
 constexpr long SAMPLE_LDS_BYTES = 64L * 1280 * 2;
 inline bool sample_in_lds(const rm_dims& d) {
-  return d.dtype == RM_BF16 && d.D % 8 == 0 && (d.D / d.T) % 4 == 0 && (long)d.T * d.D * 2 <= SAMPLE_LDS_BYTES;
+  return (d.dtype == RM_BF16 || d.dtype == RM_F16) && d.D % 8 == 0 && (d.D / d.T) % 4 == 0 &&
+         (long)d.T * d.D * 2 <= SAMPLE_LDS_BYTES;
 }
 WsLayout ws_layout(const rm_dims& d);
 
@@ -80,11 +81,11 @@ struct GemmArgs {
 
 hipError_t launch_gemm(int dtype, bool a_kmajor, bool b_kmajor, const GemmArgs& g, int kid,
                        hipStream_t s);
-// 256x256-tile bf16 kernel (direct-to-LDS loads, transposing LDS reads): shapes it takes
+// 256x256-tile bf16 / fp16 kernel (direct-to-LDS loads, transposing LDS reads): shapes it takes
 // Compute units of the current device (cached per device).
 int device_cu_count();
 bool gemm256_supported(int dtype, bool a_kmajor, bool b_kmajor, const GemmArgs& g, int kid);
-hipError_t launch_gemm256(bool a_kmajor, bool b_kmajor, const GemmArgs& g, int kid, hipStream_t s);
+hipError_t launch_gemm256(int dtype, bool a_kmajor, bool b_kmajor, const GemmArgs& g, int kid, hipStream_t s);
 
 // ---------------------------------------------------------------------------
 // row kernels

@@ -173,7 +173,7 @@ template <typename ST>
 __device__ __forceinline__ void bst4(__amdgpu_buffer_rsrc_t rs, uint32_t voff, uint32_t soff, const float (&v)[4]) {
   if constexpr (sizeof(ST) == 2) {
     typedef uint32_t v2u __attribute__((ext_vector_type(2)));
-    const v2u a = {bf_pack(v[0], v[1]), bf_pack(v[2], v[3])};
+    const v2u a = {pack16x2<ST>(v[0], v[1]), pack16x2<ST>(v[2], v[3])};
     __builtin_amdgcn_raw_buffer_store_b64(a, rs, voff, soff, 0);
   } else {
     typedef uint32_t v4u __attribute__((ext_vector_type(4)));
@@ -189,13 +189,13 @@ __device__ __forceinline__ void bstv(__amdgpu_buffer_rsrc_t rs, uint32_t voff, u
   constexpr int BYTES = N * (int)sizeof(ST);
   static_assert(BYTES == 2 || BYTES == 4 || BYTES == 8 || BYTES == 16, "store width");
   if constexpr (BYTES == 2) {
-    __builtin_amdgcn_raw_buffer_store_b16((unsigned short)f32_to_bf16_bits(v[0]), rs, voff, soff, 0);
+    __builtin_amdgcn_raw_buffer_store_b16((unsigned short)to_bits16<ST>(v[0]), rs, voff, soff, 0);
   } else {
     constexpr int W = BYTES / 4;
     uint32_t w[W];
 #pragma unroll
     for (int i = 0; i < W; ++i) {
-      if constexpr (sizeof(ST) == 2) w[i] = bf_pack(v[2 * i], v[2 * i + 1]);
+      if constexpr (sizeof(ST) == 2) w[i] = pack16x2<ST>(v[2 * i], v[2 * i + 1]);
       else w[i] = __float_as_uint(v[i]);
     }
     if constexpr (W == 1) {
@@ -225,7 +225,7 @@ int resident_blocks(K kernel, int threads) {
 }
 
 // ---------------------------------------------------------------------------
-// Forward prologue for bf16 with the whole sample staged in LDS (T*D*2 bytes,
+// Forward prologue for 16-bit storage with the whole sample staged in LDS (T*D*2 bytes,
 // at most 160 KB), so x is read from HBM once.  One workgroup (16 waves) per
 // sample b, one wave per row, 4-element chunks (D % 4 == 0, S % 4 == 0):
 //   1. each wave loads its rows of x[b] once, computes norm0's statistics in
@@ -241,9 +241,10 @@ __device__ __forceinline__ float load_bypass_l1(const float* p) {
   return __hip_atomic_load(p, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
 }
 
-__global__ __launch_bounds__(1024) void k_prologue_lds(const bf16_t* __restrict__ x, const bf16_t* __restrict__ g0,
-                                                       const bf16_t* __restrict__ be0, const bf16_t* __restrict__ g1,
-                                                       const bf16_t* __restrict__ be1, bf16_t* __restrict__ h1,
+template <typename ST>
+__global__ __launch_bounds__(1024) void k_prologue_lds(const ST* __restrict__ x, const ST* __restrict__ g0,
+                                                       const ST* __restrict__ be0, const ST* __restrict__ g1,
+                                                       const ST* __restrict__ be1, ST* __restrict__ h1,
                                                        float* __restrict__ stats, int B, int T, int D) {
   constexpr int N = 4;
   constexpr int Q = MAXD / (64 * N);
@@ -259,7 +260,7 @@ __global__ __launch_bounds__(1024) void k_prologue_lds(const bf16_t* __restrict_
 
   // 1. statistics of norm0, raw rows into LDS
   for (int j = wave; j < T; j += nw) {
-    Raw<bf16_t, N> rr[Q];
+    Raw<ST, N> rr[Q];
     float v[Q][N];
     float s = 0.f;
 #pragma unroll
@@ -295,7 +296,7 @@ __global__ __launch_bounds__(1024) void k_prologue_lds(const bf16_t* __restrict_
   // 2. per-lane source rows and their statistics; out1's affine for this lane's columns
   float mu[Q], rs[Q];
   int jq[Q];
-  Raw<bf16_t, N> rg1[Q], rb1[Q];
+  Raw<ST, N> rg1[Q], rb1[Q];
 #pragma unroll
   for (int q = 0; q < Q; ++q) {
     const int c = (lane + 64 * q) * N;
@@ -321,8 +322,8 @@ __global__ __launch_bounds__(1024) void k_prologue_lds(const bf16_t* __restrict_
       float a[N], gg[N], bb[N], xi[N];
       const uint2 ra = *reinterpret_cast<const uint2*>(sx + ((long)j * D + sc) * 2);
       const uint2 rx = *reinterpret_cast<const uint2*>(sx + ((long)i * D + cc) * 2);
-      a[0] = bf_lo(ra.x); a[1] = bf_hi(ra.x); a[2] = bf_lo(ra.y); a[3] = bf_hi(ra.y);
-      xi[0] = bf_lo(rx.x); xi[1] = bf_hi(rx.x); xi[2] = bf_lo(rx.y); xi[3] = bf_hi(rx.y);
+      a[0] = lo16<ST>(ra.x); a[1] = hi16<ST>(ra.x); a[2] = lo16<ST>(ra.y); a[3] = hi16<ST>(ra.y);
+      xi[0] = lo16<ST>(rx.x); xi[1] = hi16<ST>(rx.x); xi[2] = lo16<ST>(rx.y); xi[3] = hi16<ST>(rx.y);
       ldv(g0 + sc, gg);
       ldv(be0 + sc, bb);
       const float m = c < D ? 1.f : 0.f;
@@ -975,7 +976,7 @@ __global__ __launch_bounds__(MAXT) void k_gate_bwd_ring(const ST* __restrict__ Z
   }
 }
 
-// Backward tail for bf16, one workgroup (8 waves) per sample b with the
+// Backward tail for 16-bit storage, one workgroup (8 waves) per sample b with the
 // sample staged in LDS (at most 160 KB), so the two token-mix gathers read
 // LDS instead of re-fetching 40-byte pieces of HBM lines.  Wave w owns the
 // contiguous rows R*w .. R*w+R-1 (R = ceil(T / 8)) in both row phases.
@@ -1013,10 +1014,11 @@ __device__ __forceinline__ void sum_wave_rows(const float* lds, float* __restric
   }
 }
 
-__global__ __launch_bounds__(512) void k_tail_bwd_lds(const bf16_t* __restrict__ x, const bf16_t* __restrict__ dh1,
-                                                       const bf16_t* __restrict__ g0, const bf16_t* __restrict__ be0,
-                                                       const bf16_t* __restrict__ g1, const float* __restrict__ stats,
-                                                       bf16_t* __restrict__ dr1, bf16_t* __restrict__ dx,
+template <typename ST>
+__global__ __launch_bounds__(512) void k_tail_bwd_lds(const ST* __restrict__ x, const ST* __restrict__ dh1,
+                                                       const ST* __restrict__ g0, const ST* __restrict__ be0,
+                                                       const ST* __restrict__ g1, const float* __restrict__ stats,
+                                                       ST* __restrict__ dr1, ST* __restrict__ dx,
                                                        float* __restrict__ part, int B, int T, int D) {
   constexpr int N = 4;
   constexpr int Q = MAXD / (64 * N);
@@ -1059,7 +1061,7 @@ __global__ __launch_bounds__(512) void k_tail_bwd_lds(const bf16_t* __restrict__
   // the first row's d(out1), gathered gamma0 / beta0 and statistics
   int jq[Q];
   float mu0[Q], rs0[Q];
-  Raw<bf16_t, N> rg1[Q], rgg0[Q], pdh[Q], pg0[Q], pb0[Q];
+  Raw<ST, N> rg1[Q], rgg0[Q], pdh[Q], pg0[Q], pb0[Q];
 #pragma unroll
   for (int q = 0; q < Q; ++q) {
     const int cc = min((lane + 64 * q) * N, D - N);
@@ -1092,7 +1094,7 @@ __global__ __launch_bounds__(512) void k_tail_bwd_lds(const bf16_t* __restrict__
     const long row = srow + i;
     const float mu1 = lane_f(lmu1, i - r0), rs1 = lane_f(lrs1, i - r0);
     const int in = min(i + 1, T - 1);
-    Raw<bf16_t, N> cdh[Q], cg0[Q], cb0[Q];
+    Raw<ST, N> cdh[Q], cg0[Q], cb0[Q];
 #pragma unroll
     for (int q = 0; q < Q; ++q) {
       const int cc = min((lane + 64 * q) * N, D - N);
@@ -1115,8 +1117,8 @@ __global__ __launch_bounds__(512) void k_tail_bwd_lds(const bf16_t* __restrict__
       const uint2 ra = *reinterpret_cast<const uint2*>(sx + ((long)jq[q] * D + sc) * 2);
       const uint2 rx = *reinterpret_cast<const uint2*>(sx + ((long)i * D + cc) * 2);
       float a[N], xi[N], gg0[N], bb0[N], gg1[N];
-      a[0] = bf_lo(ra.x); a[1] = bf_hi(ra.x); a[2] = bf_lo(ra.y); a[3] = bf_hi(ra.y);
-      xi[0] = bf_lo(rx.x); xi[1] = bf_hi(rx.x); xi[2] = bf_lo(rx.y); xi[3] = bf_hi(rx.y);
+      a[0] = lo16<ST>(ra.x); a[1] = hi16<ST>(ra.x); a[2] = lo16<ST>(ra.y); a[3] = hi16<ST>(ra.y);
+      xi[0] = lo16<ST>(rx.x); xi[1] = hi16<ST>(rx.x); xi[2] = lo16<ST>(rx.y); xi[3] = hi16<ST>(rx.y);
       unpack(cdh[q], gv[q]);
       unpack(cg0[q], gg0);
       unpack(cb0[q], bb0);
@@ -1141,7 +1143,7 @@ __global__ __launch_bounds__(512) void k_tail_bwd_lds(const bf16_t* __restrict__
         pa[q][e] += gv[q][e] * n1[q][e];  // columns past D: accumulated, never stored
         pbb[q][e] += gv[q][e];
       }
-      bst4<bf16_t>(drs, c < D ? (uint32_t)c * 2 : 0x80000000u, (uint32_t)i * rowb, o);
+      bst4<ST>(drs, c < D ? (uint32_t)c * 2 : 0x80000000u, (uint32_t)i * rowb, o);
     }
   }
   wait_vm_all();    // this wave's dr1 stores have completed
@@ -1158,7 +1160,7 @@ __global__ __launch_bounds__(512) void k_tail_bwd_lds(const bf16_t* __restrict__
   __syncthreads();
   if (r1 > r0) copy_to_lds(dr1 + (srow + r0) * D, sx + (long)r0 * D * 2, (r1 - r0) * D * 2, 0, 64, lane);
   // the first row's x and statistics
-  Raw<bf16_t, N> px[Q];
+  Raw<ST, N> px[Q];
 #pragma unroll
   for (int q = 0; q < Q; ++q) ldr(x + base + (long)i0 * D + min((lane + 64 * q) * N, D - N), px[q]);
   wait_vm_all();
@@ -1173,7 +1175,7 @@ __global__ __launch_bounds__(512) void k_tail_bwd_lds(const bf16_t* __restrict__
     const long row = srow + j;
     const float mu = lane_f(lmu0, j - r0), rs = lane_f(lrs0, j - r0);
     const int jn = min(j + 1, T - 1);
-    Raw<bf16_t, N> cx[Q];
+    Raw<ST, N> cx[Q];
 #pragma unroll
     for (int q = 0; q < Q; ++q) {
       cx[q] = px[q];
@@ -1189,7 +1191,7 @@ __global__ __launch_bounds__(512) void k_tail_bwd_lds(const bf16_t* __restrict__
       // da0[j, c] = dr1[c/S, j*S + c%S]
       const int sc = j * S + (cc - jq[q] * S);
       const uint2 rd = *reinterpret_cast<const uint2*>(sx + ((long)jq[q] * D + sc) * 2);
-      da[q][0] = bf_lo(rd.x); da[q][1] = bf_hi(rd.x); da[q][2] = bf_lo(rd.y); da[q][3] = bf_hi(rd.y);
+      da[q][0] = lo16<ST>(rd.x); da[q][1] = hi16<ST>(rd.x); da[q][2] = lo16<ST>(rd.y); da[q][3] = hi16<ST>(rd.y);
       float xv[N], cg0[N];
       unpack(cx[q], xv);
       unpack(rgg0[q], cg0);
@@ -1208,14 +1210,14 @@ __global__ __launch_bounds__(512) void k_tail_bwd_lds(const bf16_t* __restrict__
       const int cc = min(c, D - N);
       const uint2 ro = *reinterpret_cast<const uint2*>(sx + ((long)j * D + cc) * 2);
       float own[N], o[N];
-      own[0] = bf_lo(ro.x); own[1] = bf_hi(ro.x); own[2] = bf_lo(ro.y); own[3] = bf_hi(ro.y);
+      own[0] = lo16<ST>(ro.x); own[1] = hi16<ST>(ro.x); own[2] = lo16<ST>(ro.y); own[3] = hi16<ST>(ro.y);
 #pragma unroll
       for (int e = 0; e < N; ++e) {
         o[e] = own[e] + rs * (dn[q][e] - m1 - n0[q][e] * m2);
         pa[q][e] += da[q][e] * n0[q][e];  // columns past D: accumulated, never stored
         pbb[q][e] += da[q][e];
       }
-      bst4<bf16_t>(dxs, c < D ? (uint32_t)c * 2 : 0x80000000u, (uint32_t)j * rowb, o);
+      bst4<ST>(dxs, c < D ? (uint32_t)c * 2 : 0x80000000u, (uint32_t)j * rowb, o);
     }
   }
   __syncthreads();
@@ -1496,11 +1498,16 @@ template <typename ST>
 hipError_t prologue_t(const rm_dims& d, const rm_params& p, const void* x, void* ws, const WsLayout& L,
                       hipStream_t s) {
   prof_begin(KID_PROLOGUE, s);
-  if (sample_in_lds(d))
-    hipLaunchKernelGGL(k_prologue_lds, dim3(d.B), dim3(1024), 0, s, cptr<bf16_t>(x), cptr<bf16_t>(p.ln0_g),
-                       cptr<bf16_t>(p.ln0_b), cptr<bf16_t>(p.ln1_g), cptr<bf16_t>(p.ln1_b), wsp<bf16_t>(ws, L.h1),
-                       wsp<float>(ws, L.stats), d.B, d.T, d.D);
-  else if (vec4_rows(d))
+  if constexpr (sizeof(ST) == 2) {
+    if (sample_in_lds(d)) {
+      hipLaunchKernelGGL(k_prologue_lds<ST>, dim3(d.B), dim3(1024), 0, s, cptr<ST>(x), cptr<ST>(p.ln0_g),
+                         cptr<ST>(p.ln0_b), cptr<ST>(p.ln1_g), cptr<ST>(p.ln1_b), wsp<ST>(ws, L.h1),
+                         wsp<float>(ws, L.stats), d.B, d.T, d.D);
+      prof_end(KID_PROLOGUE, s);
+      return hipGetLastError();
+    }
+  }
+  if (vec4_rows(d))
     hipLaunchKernelGGL((k_prologue<ST, 4>), dim3(d.B), dim3(512), 0, s, cptr<ST>(x), cptr<ST>(p.ln0_g),
                        cptr<ST>(p.ln0_b), cptr<ST>(p.ln1_g), cptr<ST>(p.ln1_b), wsp<ST>(ws, L.h1),
                        wsp<float>(ws, L.stats), d.B, d.T, d.D);
@@ -1609,14 +1616,16 @@ hipError_t tail_bwd_t(const rm_dims& d, const rm_params& p, const void* x, void*
                       hipStream_t s) {
   const dim3 grid(d.T, L.nb);
   hipError_t e;
-  if (sample_in_lds(d)) {
-    prof_begin(KID_TAIL_BWD, s);
-    hipLaunchKernelGGL(k_tail_bwd_lds, dim3(d.B), dim3(512), 0, s, cptr<bf16_t>(x), wsp<bf16_t>(ws, L.dh1),
-                       cptr<bf16_t>(p.ln0_g), cptr<bf16_t>(p.ln0_b), cptr<bf16_t>(p.ln1_g), wsp<float>(ws, L.stats),
-                       wsp<bf16_t>(ws, L.dr1), reinterpret_cast<bf16_t*>(dx), wsp<float>(ws, L.p_tail), d.B, d.T,
-                       d.D);
-    prof_end(KID_TAIL_BWD, s);
-    return hipGetLastError();
+  if constexpr (sizeof(ST) == 2) {
+    if (sample_in_lds(d)) {
+      prof_begin(KID_TAIL_BWD, s);
+      hipLaunchKernelGGL(k_tail_bwd_lds<ST>, dim3(d.B), dim3(512), 0, s, cptr<ST>(x), wsp<ST>(ws, L.dh1),
+                         cptr<ST>(p.ln0_g), cptr<ST>(p.ln0_b), cptr<ST>(p.ln1_g), wsp<float>(ws, L.stats),
+                         wsp<ST>(ws, L.dr1), reinterpret_cast<ST*>(dx), wsp<float>(ws, L.p_tail), d.B, d.T,
+                         d.D);
+      prof_end(KID_TAIL_BWD, s);
+      return hipGetLastError();
+    }
   }
   prof_begin(KID_LN1_BWD, s);
   if (vec4_rows(d))
@@ -1679,7 +1688,7 @@ hipError_t finalize_t(const rm_dims& d, const rm_grads& g, void* ws, const WsLay
 }  // namespace
 
 #define RM_DISPATCH(fn, ...) \
-  ((d.dtype == RM_BF16) ? fn<bf16_t>(__VA_ARGS__) : fn<float>(__VA_ARGS__))
+  ((d.dtype == RM_BF16) ? fn<bf16_t>(__VA_ARGS__) : (d.dtype == RM_F16) ? fn<f16_t>(__VA_ARGS__) : fn<float>(__VA_ARGS__))
 
 hipError_t launch_prologue(const rm_dims& d, const rm_params& p, const void* x, void* ws, const WsLayout& L,
                            hipStream_t s) {
@@ -1709,7 +1718,7 @@ hipError_t launch_finalize(const rm_dims& d, const rm_grads& g, void* ws, const 
 hipError_t launch_token_mix(const rm_dims& d, const void* in, void* out, hipStream_t s) {
   const long rows = (long)d.B * d.T;
   prof_begin(KID_TOKEN_MIX, s);
-  if (d.dtype == RM_BF16)
+  if (d.dtype != RM_F32)
     hipLaunchKernelGGL(k_token_mix<uint16_t>, dim3((unsigned)rows), dim3(256), 0, s,
                        reinterpret_cast<const uint16_t*>(in), reinterpret_cast<uint16_t*>(out), d.T, d.D);
   else

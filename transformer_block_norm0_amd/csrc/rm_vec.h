@@ -2,15 +2,14 @@
 // 4-byte accesses), plus block reductions for row kernels.
 #pragma once
 
+#include <type_traits>
+
 #include "rm_common.h"
 
 namespace rm {
 
 __device__ __forceinline__ float bf_lo(uint32_t w) { return __uint_as_float(w << 16); }
 __device__ __forceinline__ float bf_hi(uint32_t w) { return __uint_as_float(w & 0xffff0000u); }
-__device__ __forceinline__ uint32_t bf_pack(float a, float b) {
-  return (uint32_t)f32_to_bf16_bits(a) | ((uint32_t)f32_to_bf16_bits(b) << 16);
-}
 
 // p must be aligned to N elements.
 template <int N>
@@ -29,23 +28,27 @@ __device__ __forceinline__ void ldv(const float* __restrict__ p, float (&v)[N]) 
   }
 }
 
-template <int N>
-__device__ __forceinline__ void ldv(const bf16_t* __restrict__ p, float (&v)[N]) {
+// 16-bit storage (bf16 or fp16)
+template <typename ST>
+constexpr bool is_half16 = std::is_same<ST, bf16_t>::value || std::is_same<ST, f16_t>::value;
+
+template <typename ST, int N, std::enable_if_t<is_half16<ST>, int> = 0>
+__device__ __forceinline__ void ldv(const ST* __restrict__ p, float (&v)[N]) {
   if constexpr (N == 1) {
     v[0] = to_f32(p[0]);
   } else if constexpr (N == 2) {
     const uint32_t a = *reinterpret_cast<const uint32_t*>(p);
-    v[0] = bf_lo(a); v[1] = bf_hi(a);
+    v[0] = lo16<ST>(a); v[1] = hi16<ST>(a);
   } else if constexpr (N == 4) {
     const uint2 a = *reinterpret_cast<const uint2*>(p);
-    v[0] = bf_lo(a.x); v[1] = bf_hi(a.x); v[2] = bf_lo(a.y); v[3] = bf_hi(a.y);
+    v[0] = lo16<ST>(a.x); v[1] = hi16<ST>(a.x); v[2] = lo16<ST>(a.y); v[3] = hi16<ST>(a.y);
   } else {
-    static_assert(N % 8 == 0, "bf16 vector width");
+    static_assert(N % 8 == 0, "16-bit vector width");
 #pragma unroll
     for (int i = 0; i < N; i += 8) {
       const uint4 a = *reinterpret_cast<const uint4*>(p + i);
-      v[i] = bf_lo(a.x); v[i + 1] = bf_hi(a.x); v[i + 2] = bf_lo(a.y); v[i + 3] = bf_hi(a.y);
-      v[i + 4] = bf_lo(a.z); v[i + 5] = bf_hi(a.z); v[i + 6] = bf_lo(a.w); v[i + 7] = bf_hi(a.w);
+      v[i] = lo16<ST>(a.x); v[i + 1] = hi16<ST>(a.x); v[i + 2] = lo16<ST>(a.y); v[i + 3] = hi16<ST>(a.y);
+      v[i + 4] = lo16<ST>(a.z); v[i + 5] = hi16<ST>(a.z); v[i + 6] = lo16<ST>(a.w); v[i + 7] = hi16<ST>(a.w);
     }
   }
 }
@@ -62,19 +65,20 @@ __device__ __forceinline__ void stv(float* __restrict__ p, const float (&v)[N]) 
   }
 }
 
-template <int N>
-__device__ __forceinline__ void stv(bf16_t* __restrict__ p, const float (&v)[N]) {
+template <typename ST, int N, std::enable_if_t<is_half16<ST>, int> = 0>
+__device__ __forceinline__ void stv(ST* __restrict__ p, const float (&v)[N]) {
   if constexpr (N == 1) {
-    p[0].u = f32_to_bf16_bits(v[0]);
+    p[0].u = (uint16_t)to_bits16<ST>(v[0]);
   } else if constexpr (N == 2) {
-    *reinterpret_cast<uint32_t*>(p) = bf_pack(v[0], v[1]);
+    *reinterpret_cast<uint32_t*>(p) = pack16x2<ST>(v[0], v[1]);
   } else if constexpr (N == 4) {
-    *reinterpret_cast<uint2*>(p) = make_uint2(bf_pack(v[0], v[1]), bf_pack(v[2], v[3]));
+    *reinterpret_cast<uint2*>(p) = make_uint2(pack16x2<ST>(v[0], v[1]), pack16x2<ST>(v[2], v[3]));
   } else {
 #pragma unroll
     for (int i = 0; i < N; i += 8)
-      *reinterpret_cast<uint4*>(p + i) = make_uint4(bf_pack(v[i], v[i + 1]), bf_pack(v[i + 2], v[i + 3]),
-                                                    bf_pack(v[i + 4], v[i + 5]), bf_pack(v[i + 6], v[i + 7]));
+      *reinterpret_cast<uint4*>(p + i) =
+          make_uint4(pack16x2<ST>(v[i], v[i + 1]), pack16x2<ST>(v[i + 2], v[i + 3]), pack16x2<ST>(v[i + 4], v[i + 5]),
+                     pack16x2<ST>(v[i + 6], v[i + 7]));
   }
 }
 
@@ -126,15 +130,15 @@ __device__ __forceinline__ void unpack(const Raw<float, N>& r, float (&v)[N]) {
   for (int e = 0; e < N; ++e) v[e] = __uint_as_float(r.w[e]);
 }
 
-template <int N>
-__device__ __forceinline__ void unpack(const Raw<bf16_t, N>& r, float (&v)[N]) {
+template <typename ST, int N, std::enable_if_t<is_half16<ST>, int> = 0>
+__device__ __forceinline__ void unpack(const Raw<ST, N>& r, float (&v)[N]) {
   if constexpr (N == 1) {
-    v[0] = bf_lo(r.w[0]);
+    v[0] = lo16<ST>(r.w[0]);
   } else {
 #pragma unroll
     for (int e = 0; e < N; e += 2) {
-      v[e] = bf_lo(r.w[e / 2]);
-      v[e + 1] = bf_hi(r.w[e / 2]);
+      v[e] = lo16<ST>(r.w[e / 2]);
+      v[e + 1] = hi16<ST>(r.w[e / 2]);
     }
   }
 }

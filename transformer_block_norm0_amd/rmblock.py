@@ -16,7 +16,7 @@ import os
 PKG = os.path.dirname(os.path.abspath(__file__))
 LIB_PATH = os.path.join(PKG, "librmblock.so")
 
-RM_F32, RM_BF16 = 0, 1
+RM_F32, RM_BF16, RM_F16 = 0, 1, 2
 RM_WS_H1, RM_WS_Z, RM_WS_HID, RM_WS_R2, RM_WS_STATS = range(5)
 STAT_NAMES = ("mu0", "rs0", "mu1", "rs1", "mux", "rsx", "mug", "rsg", "mu2", "rs2")
 
@@ -89,7 +89,7 @@ def library():
 
 
 def dims(B: int, T: int, D: int, k: int, dtype: str) -> CDims:
-    return CDims(B, T, D, k, {"f32": RM_F32, "bf16": RM_BF16}[dtype])
+    return CDims(B, T, D, k, {"f32": RM_F32, "bf16": RM_BF16, "f16": RM_F16}[dtype])
 
 
 def workspace_bytes(d: CDims) -> int:
@@ -123,7 +123,7 @@ def _stream(stream) -> int | None:
 
 def _torch_dtype(d: CDims):
     import torch
-    return torch.bfloat16 if d.dtype == RM_BF16 else torch.float32
+    return {RM_BF16: torch.bfloat16, RM_F16: torch.float16}.get(d.dtype, torch.float32)
 
 
 def _check(t, d: CDims, shape, name):
