@@ -112,6 +112,8 @@ def main():
     ap.add_argument("--cpu-seconds", type=float, default=10.0)
     ap.add_argument("--no-protocol", action="store_true", help="skip the per-iteration flush protocol pass")
     ap.add_argument("--no-kernel-times", action="store_true", help="skip the event-instrumented pass")
+    ap.add_argument("--graph", action="store_true",
+                    help="also time the step replayed from one captured HIP graph (launch-bound small shapes)")
     ap.add_argument("--copy-calibration-mib", type=int, default=0,
                     help="run one plain device-to-device copy of this many MiB first (reference for HBM counters)")
     args = ap.parse_args()
@@ -179,6 +181,35 @@ def main():
     log(f"B={d.B} T={d.T} D={d.D} k={d.k} H={d.H} T_local={d.T} a2a_bytes=0 mode=fwd+bwd")
     log(f"{args.steps} steps: {ms_step:.3f} ms/step (host {1e3 * host_s / args.steps:.3f}), "
         f"{value:.4g} tokens/s, {tflops:.1f} TFLOP/s = {pct_peak:.1f}% of {w.dtype} MFMA peak")
+
+    # the same step captured once into a HIP graph and replayed (no per-launch host work)
+    graph = None
+    if args.graph:
+        side = torch.cuda.Stream()
+        side.wait_stream(stream)
+        with torch.cuda.stream(side):
+            step_on = lambda: (dc.fwd(side), dc.bwd(side))  # noqa: E731
+            step_on()
+        side.synchronize()
+        g = torch.cuda.CUDAGraph()
+        with torch.cuda.graph(g, stream=side):
+            dc.fwd(side)
+            dc.bwd(side)
+        for _ in range(args.warmup):
+            g.replay()
+        torch.cuda.synchronize()
+        gs = torch.cuda.current_stream()
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        e0.record(gs)
+        for _ in range(args.steps):
+            g.replay()
+        e1.record(gs)
+        torch.cuda.synchronize()
+        g_ms = e0.elapsed_time(e1) / args.steps
+        graph = {"ms_per_step": round(g_ms, 4), "tokens_per_s": round(tokens / (g_ms / 1e3), 1),
+                 "eager_ms_per_step": round(ms_step, 4)}
+        log(f"graph replay: {g_ms:.4f} ms/step ({tokens / (g_ms / 1e3):.4g} tokens/s) vs eager {ms_step:.4f}")
+        del g
 
     # per-kernel HIP events (library instrumentation) over a second timed pass
     kernels = {}
@@ -278,6 +309,7 @@ def main():
         "roofline": roofline,
         "cpu_baseline": cpu,
         "pages_protocol": protocol,
+        "graph_replay": graph,
         "kernels": kernels,
     }
     print(json.dumps(out), flush=True)

@@ -234,3 +234,36 @@ def test_full_size_B999_T40_D1000_k3_f32_sampled():
 def test_full_size_B1024_T64_D1280_k2_f16_sampled():
     """fp16 storage (page 1, "Run the benchmark": the --dtype float16 run) at the production shape."""
     sampled_check("B1024_T64_D1280_k2_f16", samples=(0, 300, -1), tokens=(0, 41, -1))
+
+
+@pytest.mark.parametrize("name", ["B4_T16_D128_k2_bf16_public", "B8_T8_D64_k2_f32", "B4_T16_D128_k2_f16_public"])
+def test_graph_replay_matches_eager(name):
+    """fwd+bwd captured once into a HIP graph: every replay, with eager work and
+    cleared outputs and workspace in between, gives the eager run's bits."""
+    import torch
+    say(f"graph replay {name}")
+    dc = DeviceCase(make_case(WORKLOADS[name]))
+    dc.run()
+    ref = dc.raw_bits()
+    side = torch.cuda.Stream()
+    side.wait_stream(torch.cuda.current_stream())
+    with torch.cuda.stream(side):
+        dc.fwd(side)
+        dc.bwd(side)
+    side.synchronize()
+    g = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(g, stream=side):
+        dc.fwd(side)
+        dc.bwd(side)
+    torch.cuda.synchronize()
+    for rep in range(3):
+        for t in [dc.y, dc.dx, dc.ws] + list(dc.grads.values()):
+            t.zero_()
+        torch.cuda.synchronize()
+        g.replay()
+        torch.cuda.synchronize()
+        got = dc.raw_bits()
+        for k in ref:
+            assert np.array_equal(ref[k], got[k]), (rep, k)
+        dc.run()  # eager work between replays
+    del g
