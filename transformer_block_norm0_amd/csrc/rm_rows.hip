@@ -837,7 +837,7 @@ __global__ __launch_bounds__(MAXT) void k_gate_bwd_ring(const ST* __restrict__ Z
                                                         const float* __restrict__ stats, ST* __restrict__ dZ,
                                                         float* __restrict__ pgate, float* __restrict__ pb1, int B,
                                                         int T, int H, int nb) {
-  __shared__ float4 red8[2 * 16 * 2];
+  __shared__ float4 red8[2 * 16 * RING];
   __shared__ float4 sst[ROWS_PER_GROUP];
   constexpr int SZ = (int)sizeof(ST);
   const int t = blockIdx.x, grp = blockIdx.y;
@@ -864,7 +864,7 @@ __global__ __launch_bounds__(MAXT) void k_gate_bwd_ring(const ST* __restrict__ Z
   const uint32_t vu = (uint32_t)(c * SZ), vg = (uint32_t)((H + c) * SZ);
   const uint32_t zrow = (uint32_t)(2 * H * SZ), hrow = (uint32_t)(H * SZ);
 
-  zero_red8(red8);
+  zero_red<RING>(red8);
   // the group's inner-LN statistics (mux, rsx, mug, rsg per row) staged in LDS once
   for (int i = threadIdx.x; i < 4 * ROWS_PER_GROUP; i += blockDim.x) {
     const int r = i >> 2, q = i & 3;
@@ -892,16 +892,16 @@ __global__ __launch_bounds__(MAXT) void k_gate_bwd_ring(const ST* __restrict__ Z
   }
   __syncthreads();
 
-  // two rows (ring slots 0 and 1) per step: consume them, refill the slots
-  // with rows r + RING, r + RING + 1 (PREFETCH), one block reduction of the
-  // two rows' eight sums, store both rows of dZ
+  // RING rows (all ring slots) per step: consume them, refill the slots with
+  // rows r + RING .. r + 2 RING - 1 (PREFETCH), one block reduction of the
+  // rows' 4 RING sums, store the rows of dZ
   int parity = 0;
   auto pair_step = [&](int r, auto prefetch) {
-    float nx[2][4], ng[2][4], dux[2][4], dug[2][4], rsx[2], rsg[2], sm[8];
-    uint32_t rowk[2];
-    bool validk[2];
+    float nx[RING][4], ng[RING][4], dux[RING][4], dug[RING][4], rsx[RING], rsg[RING], sm[4 * RING];
+    uint32_t rowk[RING];
+    bool validk[RING];
 #pragma unroll
-    for (int k = 0; k < 2; ++k) {
+    for (int k = 0; k < RING; ++k) {
       const bool valid = b0 + r + k <= bl;
       validk[k] = valid;
       const float w = valid ? cm : 0.f;
@@ -938,10 +938,10 @@ __global__ __launch_bounds__(MAXT) void k_gate_bwd_ring(const ST* __restrict__ Z
         abg[e] += dug[k][e];
       }
     }
-    block_sum8(sm, red8, parity);
+    block_sum_x4<RING>(sm, red8, parity);
     parity ^= 1;
 #pragma unroll
-    for (int k = 0; k < 2; ++k) {
+    for (int k = 0; k < RING; ++k) {
       const float m1 = sm[4 * k] * invH, m2 = sm[4 * k + 1] * invH, m3 = sm[4 * k + 2] * invH,
                   m4 = sm[4 * k + 3] * invH;
       float du[4], dg[4];
@@ -959,10 +959,10 @@ __global__ __launch_bounds__(MAXT) void k_gate_bwd_ring(const ST* __restrict__ Z
       bst4<ST>(drs, sok ? vg : 0x80000000u, rowk[k] * zrow, dg);
     }
   };
-  static_assert(RING == 2 && ROWS_PER_GROUP % 2 == 0, "two ring slots, consumed together");
+  static_assert(ROWS_PER_GROUP % RING == 0, "the ring slots are consumed together");
 #pragma unroll 1
-  for (int r0 = 0; r0 < ROWS_PER_GROUP - 2; r0 += 2) pair_step(r0, std::true_type{});
-  pair_step(ROWS_PER_GROUP - 2, std::false_type{});
+  for (int r0 = 0; r0 < ROWS_PER_GROUP - RING; r0 += RING) pair_step(r0, std::true_type{});
+  pair_step(ROWS_PER_GROUP - RING, std::false_type{});
   if (craw < H) {
     const long blk = (long)nb * T * H;
     const long o = ((long)grp * T + t) * H;
@@ -976,25 +976,27 @@ __global__ __launch_bounds__(MAXT) void k_gate_bwd_ring(const ST* __restrict__ Z
   }
 }
 
-// Backward tail for 16-bit storage, one workgroup (8 waves) per sample b with the
-// sample staged in LDS (at most 160 KB), so the two token-mix gathers read
-// LDS instead of re-fetching 40-byte pieces of HBM lines.  Wave w owns the
-// contiguous rows R*w .. R*w+R-1 (R = ceil(T / 8)) in both row phases.
+// Backward tail for 16-bit storage, one workgroup (8 waves) per sample b with
+// the sample staged in LDS (at most 160 KB), so the token-mix gathers read LDS
+// instead of 40-byte pieces of HBM lines.  Wave w owns the contiguous rows
+// R*w .. R*w+R-1 (R = ceil(T / 8)) in both row phases.
 //   1. x[b] -> LDS by direct 16-byte copies, all in flight together (plain
 //      loads when x is not 16-byte aligned);
-//   2. norm1 backward per row i: r1 = token_mix(norm0(x)) + x is rebuilt
-//      from LDS (norm0 statistics saved by the forward),
-//      dr1 = rstd1 (dn - mean(dn) - n1 mean(dn n1)), dn = d(out1) gamma1,
-//      written to `dr1`; partial sums d(out1) n1 and d(out1) per column.
-//      The next row's d(out1) and gathered gamma0/beta0 are loaded while the
-//      current row is computed; row statistics are read once per wave, one
-//      row per lane;
-//   3. the 8 waves' column partials added through LDS (fixed order) and
-//      stored; each wave's own dr1 rows copied back into LDS (over x);
-//   4. norm0 backward per row j: da0 = token_mix(dr1) gathered from LDS,
-//      dx = dr1 + rstd0 (dn - mean(dn) - n0 mean(dn n0)), dn = da0 gamma0,
-//      n0 from x (global, next row prefetched) and the saved statistics;
-//      column partials da0 n0 and da0 added through LDS at the end.
+//   2. norm1 backward per row i: r1 = token_mix(norm0(x)) + x, the mixed term
+//      gathered from LDS (column run i of every row) and the residual x[i]
+//      read from global memory; dr1 = rstd1 (dn - mean(dn) - n1 mean(dn n1)),
+//      dn = d(out1) gamma1.  Each lane writes its dr1 values into the LDS
+//      slots its own gather just read: that run of x is needed by row i only,
+//      and the slot of dr1[i, c] is the slot of da0 = token_mix(dr1) at
+//      [c / S, i S + c % S], so after the phase LDS holds da0 row by row;
+//   3. norm0 backward per row j: da0[j] is LDS row j, dr1[j] is gathered from
+//      LDS, n0 from x[j] (global, next row prefetched) and the saved
+//      statistics; dx = dr1 + rstd0 (dn - mean(dn) - n0 mean(dn n0)),
+//      dn = da0 gamma0;
+//   4. the 8 waves' column partials of both phases added through LDS in a
+//      fixed order and stored.
+// The next row's global operands are loaded while the current row is
+// computed; row statistics are read once per wave, one row per lane.
 // Partials: part[k][b][col], k = 0..3: dgamma0, dbeta0, dgamma1, dbeta1.
 // Needs D % 8 == 0 (16-byte rows), S % 4 == 0, T * D * 2 <= 160 KB.
 __device__ __forceinline__ void wave_partials_to_lds(const float (&acc)[MAXD / 256][4], float* lds, int wave,
@@ -1018,8 +1020,8 @@ template <typename ST>
 __global__ __launch_bounds__(512) void k_tail_bwd_lds(const ST* __restrict__ x, const ST* __restrict__ dh1,
                                                        const ST* __restrict__ g0, const ST* __restrict__ be0,
                                                        const ST* __restrict__ g1, const float* __restrict__ stats,
-                                                       ST* __restrict__ dr1, ST* __restrict__ dx,
-                                                       float* __restrict__ part, int B, int T, int D) {
+                                                       ST* __restrict__ dx, float* __restrict__ part, int B, int T,
+                                                       int D) {
   constexpr int N = 4;
   constexpr int Q = MAXD / (64 * N);
   __shared__ __attribute__((aligned(16))) char sx[PRO_LDS_BYTES];
@@ -1037,12 +1039,8 @@ __global__ __launch_bounds__(512) void k_tail_bwd_lds(const ST* __restrict__ x, 
   const int R = (T + nw - 1) / nw;
   const int r0 = min(wave * R, T), r1 = min(r0 + R, T);  // this wave's rows (none if r0 == T)
   const int i0 = min(r0, T - 1);
-  // the sample's dr1 and dx rows as buffers: every store is issued (columns
-  // past D get an out-of-range offset and are dropped), so the compiler's
-  // wait counts stay exact across the row loops
-  const uint32_t rowb = (uint32_t)D * 2;
-  const __amdgpu_buffer_rsrc_t drs = row_rsrc(dr1 + srow * D, (long)T * D * 2);
-  const __amdgpu_buffer_rsrc_t dxs = row_rsrc(dx + srow * D, (long)T * D * 2);
+  const __amdgpu_buffer_rsrc_t dxs = row_rsrc(dx + srow * D, (long)T * D * (long)sizeof(ST));
+  const uint32_t rowb = (uint32_t)D * (uint32_t)sizeof(ST);
 
   // 1. x[b] -> LDS
   if ((reinterpret_cast<uintptr_t>(x) & 15) == 0) {
@@ -1058,10 +1056,10 @@ __global__ __launch_bounds__(512) void k_tail_bwd_lds(const ST* __restrict__ x, 
     }
   }
   // gather sources of this lane's columns: row c/S (same for every row of the sample);
-  // the first row's d(out1), gathered gamma0 / beta0 and statistics
+  // the first row's d(out1), x, gathered gamma0 / beta0
   int jq[Q];
   float mu0[Q], rs0[Q];
-  Raw<ST, N> rg1[Q], rgg0[Q], pdh[Q], pg0[Q], pb0[Q];
+  Raw<ST, N> rg1[Q], rgg0[Q], pdh[Q], px[Q], pg0[Q], pb0[Q];
 #pragma unroll
   for (int q = 0; q < Q; ++q) {
     const int cc = min((lane + 64 * q) * N, D - N);
@@ -1072,6 +1070,7 @@ __global__ __launch_bounds__(512) void k_tail_bwd_lds(const ST* __restrict__ x, 
     ldr(g1 + cc, rg1[q]);
     ldr(g0 + cc, rgg0[q]);
     ldr(dh1 + (srow + i0) * D + cc, pdh[q]);
+    ldr(x + base + (long)i0 * D + cc, px[q]);
     const int sc = i0 * S + (cc - j * S);
     ldr(g0 + sc, pg0[q]);
     ldr(be0 + sc, pb0[q]);
@@ -1084,24 +1083,25 @@ __global__ __launch_bounds__(512) void k_tail_bwd_lds(const ST* __restrict__ x, 
   wait_vm_all();
   __syncthreads();
 
-  // 2. norm1 backward
-  float pa[Q][N], pbb[Q][N];
+  // 2. norm1 backward; dr1 into the LDS slots just gathered from
+  float pa1[Q][N], pb1[Q][N];
 #pragma unroll
   for (int q = 0; q < Q; ++q)
 #pragma unroll
-    for (int e = 0; e < N; ++e) pa[q][e] = pbb[q][e] = 0.f;
+    for (int e = 0; e < N; ++e) pa1[q][e] = pb1[q][e] = 0.f;
   for (int i = r0; i < r1; ++i) {
-    const long row = srow + i;
     const float mu1 = lane_f(lmu1, i - r0), rs1 = lane_f(lrs1, i - r0);
     const int in = min(i + 1, T - 1);
-    Raw<ST, N> cdh[Q], cg0[Q], cb0[Q];
+    Raw<ST, N> cdh[Q], cx[Q], cg0[Q], cb0[Q];
 #pragma unroll
     for (int q = 0; q < Q; ++q) {
       const int cc = min((lane + 64 * q) * N, D - N);
       cdh[q] = pdh[q];
+      cx[q] = px[q];
       cg0[q] = pg0[q];
       cb0[q] = pb0[q];
       ldr(dh1 + (srow + in) * D + cc, pdh[q]);
+      ldr(x + base + (long)in * D + cc, px[q]);
       const int scn = in * S + (cc - jq[q] * S);
       ldr(g0 + scn, pg0[q]);
       ldr(be0 + scn, pb0[q]);
@@ -1115,10 +1115,9 @@ __global__ __launch_bounds__(512) void k_tail_bwd_lds(const ST* __restrict__ x, 
       const float m = c < D ? 1.f : 0.f;
       const int sc = i * S + (cc - jq[q] * S);
       const uint2 ra = *reinterpret_cast<const uint2*>(sx + ((long)jq[q] * D + sc) * 2);
-      const uint2 rx = *reinterpret_cast<const uint2*>(sx + ((long)i * D + cc) * 2);
       float a[N], xi[N], gg0[N], bb0[N], gg1[N];
       a[0] = lo16<ST>(ra.x); a[1] = hi16<ST>(ra.x); a[2] = lo16<ST>(ra.y); a[3] = hi16<ST>(ra.y);
-      xi[0] = lo16<ST>(rx.x); xi[1] = hi16<ST>(rx.x); xi[2] = lo16<ST>(rx.y); xi[3] = hi16<ST>(rx.y);
+      unpack(cx[q], xi);
       unpack(cdh[q], gv[q]);
       unpack(cg0[q], gg0);
       unpack(cb0[q], bb0);
@@ -1136,43 +1135,32 @@ __global__ __launch_bounds__(512) void k_tail_bwd_lds(const ST* __restrict__ x, 
 #pragma unroll
     for (int q = 0; q < Q; ++q) {
       const int c = (lane + 64 * q) * N;
+      const int cc = min(c, D - N);
       float o[N];
 #pragma unroll
       for (int e = 0; e < N; ++e) {
         o[e] = rs1 * (dn[q][e] - m1 - n1[q][e] * m2);
-        pa[q][e] += gv[q][e] * n1[q][e];  // columns past D: accumulated, never stored
-        pbb[q][e] += gv[q][e];
+        pa1[q][e] += gv[q][e] * n1[q][e];  // columns past D: accumulated, never stored
+        pb1[q][e] += gv[q][e];
       }
-      bst4<ST>(drs, c < D ? (uint32_t)c * 2 : 0x80000000u, (uint32_t)i * rowb, o);
+      // dr1[i, c] -> the slot of da0[c / S, i S + c % S] (the gather source read above)
+      const int sc = i * S + (cc - jq[q] * S);
+      if (c < D)
+        *reinterpret_cast<uint2*>(sx + ((long)jq[q] * D + sc) * 2) =
+            make_uint2(pack16x2<ST>(o[0], o[1]), pack16x2<ST>(o[2], o[3]));
     }
   }
-  wait_vm_all();    // this wave's dr1 stores have completed
-  __syncthreads();  // every wave is done with x in LDS
+  __syncthreads();  // LDS holds da0 = token_mix(dr1)
 
-  // 3. norm1 partials; each wave's own dr1 rows -> LDS
-  wave_partials_to_lds(pa, lf, wave, lane, D);
-  __syncthreads();
-  sum_wave_rows(lf, part + 2 * pblk + (long)b * D, nw, D);
-  __syncthreads();
-  wave_partials_to_lds(pbb, lf, wave, lane, D);
-  __syncthreads();
-  sum_wave_rows(lf, part + 3 * pblk + (long)b * D, nw, D);
-  __syncthreads();
-  if (r1 > r0) copy_to_lds(dr1 + (srow + r0) * D, sx + (long)r0 * D * 2, (r1 - r0) * D * 2, 0, 64, lane);
-  // the first row's x and statistics
-  Raw<ST, N> px[Q];
-#pragma unroll
-  for (int q = 0; q < Q; ++q) ldr(x + base + (long)i0 * D + min((lane + 64 * q) * N, D - N), px[q]);
-  wait_vm_all();
-  __syncthreads();
-
-  // 4. norm0 backward
+  // 3. norm0 backward
+  float pa0[Q][N], pb0s[Q][N];
 #pragma unroll
   for (int q = 0; q < Q; ++q)
 #pragma unroll
-    for (int e = 0; e < N; ++e) pa[q][e] = pbb[q][e] = 0.f;
+    for (int e = 0; e < N; ++e) pa0[q][e] = pb0s[q][e] = 0.f;
+#pragma unroll
+  for (int q = 0; q < Q; ++q) ldr(x + base + (long)i0 * D + min((lane + 64 * q) * N, D - N), px[q]);
   for (int j = r0; j < r1; ++j) {
-    const long row = srow + j;
     const float mu = lane_f(lmu0, j - r0), rs = lane_f(lrs0, j - r0);
     const int jn = min(j + 1, T - 1);
     Raw<ST, N> cx[Q];
@@ -1188,9 +1176,7 @@ __global__ __launch_bounds__(512) void k_tail_bwd_lds(const ST* __restrict__ x, 
       const int c = (lane + 64 * q) * N;
       const int cc = min(c, D - N);
       const float m = c < D ? 1.f : 0.f;
-      // da0[j, c] = dr1[c/S, j*S + c%S]
-      const int sc = j * S + (cc - jq[q] * S);
-      const uint2 rd = *reinterpret_cast<const uint2*>(sx + ((long)jq[q] * D + sc) * 2);
+      const uint2 rd = *reinterpret_cast<const uint2*>(sx + ((long)j * D + cc) * 2);  // da0[j, c]
       da[q][0] = lo16<ST>(rd.x); da[q][1] = hi16<ST>(rd.x); da[q][2] = lo16<ST>(rd.y); da[q][3] = hi16<ST>(rd.y);
       float xv[N], cg0[N];
       unpack(cx[q], xv);
@@ -1208,26 +1194,38 @@ __global__ __launch_bounds__(512) void k_tail_bwd_lds(const ST* __restrict__ x, 
     for (int q = 0; q < Q; ++q) {
       const int c = (lane + 64 * q) * N;
       const int cc = min(c, D - N);
-      const uint2 ro = *reinterpret_cast<const uint2*>(sx + ((long)j * D + cc) * 2);
+      // dr1[j, c], stored at the slot of da0[c / S, j S + c % S]
+      const int sc = j * S + (cc - jq[q] * S);
+      const uint2 ro = *reinterpret_cast<const uint2*>(sx + ((long)jq[q] * D + sc) * 2);
       float own[N], o[N];
       own[0] = lo16<ST>(ro.x); own[1] = hi16<ST>(ro.x); own[2] = lo16<ST>(ro.y); own[3] = hi16<ST>(ro.y);
 #pragma unroll
       for (int e = 0; e < N; ++e) {
         o[e] = own[e] + rs * (dn[q][e] - m1 - n0[q][e] * m2);
-        pa[q][e] += da[q][e] * n0[q][e];  // columns past D: accumulated, never stored
-        pbb[q][e] += da[q][e];
+        pa0[q][e] += da[q][e] * n0[q][e];  // columns past D: accumulated, never stored
+        pb0s[q][e] += da[q][e];
       }
-      bst4<ST>(dxs, c < D ? (uint32_t)c * 2 : 0x80000000u, (uint32_t)j * rowb, o);
+      bst4<ST>(dxs, c < D ? (uint32_t)(c * (int)sizeof(ST)) : 0x80000000u, (uint32_t)j * rowb, o);
     }
   }
   __syncthreads();
-  wave_partials_to_lds(pa, lf, wave, lane, D);
+
+  // 4. column partials of both phases (the LDS is free again)
+  wave_partials_to_lds(pa0, lf, wave, lane, D);
   __syncthreads();
   sum_wave_rows(lf, part + (long)b * D, nw, D);
   __syncthreads();
-  wave_partials_to_lds(pbb, lf, wave, lane, D);
+  wave_partials_to_lds(pb0s, lf, wave, lane, D);
   __syncthreads();
   sum_wave_rows(lf, part + pblk + (long)b * D, nw, D);
+  __syncthreads();
+  wave_partials_to_lds(pa1, lf, wave, lane, D);
+  __syncthreads();
+  sum_wave_rows(lf, part + 2 * pblk + (long)b * D, nw, D);
+  __syncthreads();
+  wave_partials_to_lds(pb1, lf, wave, lane, D);
+  __syncthreads();
+  sum_wave_rows(lf, part + 3 * pblk + (long)b * D, nw, D);
 }
 
 // norm1 backward:  dr1 = rstd1 * (dn - mean(dn) - n1 * mean(dn * n1)),  dn = d(out1) * gamma1,
@@ -1621,8 +1619,7 @@ hipError_t tail_bwd_t(const rm_dims& d, const rm_params& p, const void* x, void*
       prof_begin(KID_TAIL_BWD, s);
       hipLaunchKernelGGL(k_tail_bwd_lds<ST>, dim3(d.B), dim3(512), 0, s, cptr<ST>(x), wsp<ST>(ws, L.dh1),
                          cptr<ST>(p.ln0_g), cptr<ST>(p.ln0_b), cptr<ST>(p.ln1_g), wsp<float>(ws, L.stats),
-                         wsp<ST>(ws, L.dr1), reinterpret_cast<ST*>(dx), wsp<float>(ws, L.p_tail), d.B, d.T,
-                         d.D);
+                         reinterpret_cast<ST*>(dx), wsp<float>(ws, L.p_tail), d.B, d.T, d.D);
       prof_end(KID_TAIL_BWD, s);
       return hipGetLastError();
     }

@@ -154,14 +154,16 @@ __device__ __forceinline__ void lds_barrier() {
   asm volatile("" ::: "memory");
 }
 
-// Sum 8 values over the whole block (nw waves, nw <= 16), fixed order, like
-// block_sum4: red is 2 * 16 * 2 float4 of LDS (halves alternating with
-// `parity`), the slots of waves >= nw zeroed by zero_red8 before the block's
+// Sum 4*NQ values over the whole block (nw waves, nw <= 16), fixed order,
+// like block_sum4: red is 2 * 16 * NQ float4 of LDS (halves alternating with
+// `parity`), the slots of waves >= nw zeroed by zero_red before the block's
 // first barrier.
-__device__ __forceinline__ void zero_red8(float4* red) {
-  for (int i = threadIdx.x; i < 2 * 16 * 2; i += blockDim.x) red[i] = make_float4(0.f, 0.f, 0.f, 0.f);
+template <int NQ>
+__device__ __forceinline__ void zero_red(float4* red) {
+  for (int i = threadIdx.x; i < 2 * 16 * NQ; i += blockDim.x) red[i] = make_float4(0.f, 0.f, 0.f, 0.f);
 }
-__device__ __forceinline__ void block_sum8(float (&v)[8], float4* red, int parity);
+template <int NQ>
+__device__ __forceinline__ void block_sum_x4(float (&v)[4 * NQ], float4* red, int parity);
 
 // Sum NV values over the whole block (nw waves, nw <= 16), fixed order.
 // red: 2 * NV * 16 floats of LDS, used as two alternating halves selected by
@@ -238,34 +240,37 @@ __device__ __forceinline__ void block_sum4(float (&v)[4], float4* red, int parit
   }
 }
 
-__device__ __forceinline__ void block_sum8(float (&v)[8], float4* red, int parity) {
+template <int NQ>
+__device__ __forceinline__ void block_sum_x4(float (&v)[4 * NQ], float4* red, int parity) {
   const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
-  float4 s0, s1;
-  s0.x = wave_sum_dpp(v[0]);
-  s0.y = wave_sum_dpp(v[1]);
-  s0.z = wave_sum_dpp(v[2]);
-  s0.w = wave_sum_dpp(v[3]);
-  s1.x = wave_sum_dpp(v[4]);
-  s1.y = wave_sum_dpp(v[5]);
-  s1.z = wave_sum_dpp(v[6]);
-  s1.w = wave_sum_dpp(v[7]);
-  float4* r = red + parity * 32;
+  float4 sw[NQ];
+#pragma unroll
+  for (int k = 0; k < NQ; ++k) {
+    sw[k].x = wave_sum_dpp(v[4 * k]);
+    sw[k].y = wave_sum_dpp(v[4 * k + 1]);
+    sw[k].z = wave_sum_dpp(v[4 * k + 2]);
+    sw[k].w = wave_sum_dpp(v[4 * k + 3]);
+  }
+  float4* r = red + parity * 16 * NQ;
   if (lane == 0) {
-    r[2 * wave] = s0;
-    r[2 * wave + 1] = s1;
+#pragma unroll
+    for (int k = 0; k < NQ; ++k) r[NQ * wave + k] = sw[k];
   }
   __builtin_amdgcn_sched_barrier(0);
   lds_barrier();
   __builtin_amdgcn_sched_barrier(0);
-  const float4 b0 = r[2 * (lane & 15)], b1 = r[2 * (lane & 15) + 1];
-  float a[8] = {b0.x, b0.y, b0.z, b0.w, b1.x, b1.y, b1.z, b1.w};
 #pragma unroll
-  for (int i = 0; i < 8; ++i) {
-    a[i] += dpp_mov<0xB1>(a[i]);
-    a[i] += dpp_mov<0x4E>(a[i]);
-    a[i] += dpp_mov<0x141>(a[i]);
-    a[i] += dpp_mov<0x140>(a[i]);
-    v[i] = lane_f(a[i], 0);
+  for (int k = 0; k < NQ; ++k) {
+    const float4 b = r[NQ * (lane & 15) + k];
+    float a[4] = {b.x, b.y, b.z, b.w};
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      a[i] += dpp_mov<0xB1>(a[i]);
+      a[i] += dpp_mov<0x4E>(a[i]);
+      a[i] += dpp_mov<0x141>(a[i]);
+      a[i] += dpp_mov<0x140>(a[i]);
+      v[4 * k + i] = lane_f(a[i], 0);
+    }
   }
 }
 
