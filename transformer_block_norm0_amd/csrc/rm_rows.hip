@@ -258,7 +258,9 @@ __global__ __launch_bounds__(1024) void k_prologue_lds(const ST* __restrict__ x,
   const int S = D / T;
   const float invS = 1.0f / (float)S, invD = 1.0f / (float)D;
 
-  // 1. statistics of norm0, raw rows into LDS
+  // 1. statistics of norm0 (collected one row per lane, stored after the
+  // loop), raw rows into LDS
+  float lmu0 = 0.f, lrs0 = 0.f;
   for (int j = wave; j < T; j += nw) {
     Raw<ST, N> rr[Q];
     float v[Q][N];
@@ -286,9 +288,15 @@ __global__ __launch_bounds__(1024) void k_prologue_lds(const ST* __restrict__ x,
       if (c < D) *reinterpret_cast<uint2*>(sx + ((long)j * D + c) * 2) = make_uint2(rr[q].w[0], rr[q].w[1]);
     }
     const float rstd = rsqrtf(wave_sum_dpp(s2) * invD + EPS_OUTER);
-    if (lane == 0) {
-      stats[ST_MU0 * NR + (long)b * T + j] = mean;
-      stats[ST_RS0 * NR + (long)b * T + j] = rstd;
+    const int k = (j - wave) / nw;  // this wave's k-th row
+    lmu0 = lane == k ? mean : lmu0;
+    lrs0 = lane == k ? rstd : lrs0;
+  }
+  {
+    const int nr = wave < T ? (T - wave + nw - 1) / nw : 0;
+    if (lane < nr) {
+      stats[ST_MU0 * NR + (long)b * T + wave + lane * nw] = lmu0;
+      stats[ST_RS0 * NR + (long)b * T + wave + lane * nw] = lrs0;
     }
   }
   __syncthreads();
@@ -309,7 +317,11 @@ __global__ __launch_bounds__(1024) void k_prologue_lds(const ST* __restrict__ x,
     ldr(be1 + cc, rb1[q]);
   }
 
-  // 3. out1 rows
+  // 3. out1 rows; h1 by buffer stores issued on every lane (columns past D
+  // get an out-of-range offset), the row statistics collected one row per
+  // lane and stored after the loop, so the loop has no branches
+  const __amdgpu_buffer_rsrc_t hrs = row_rsrc(h1 + base, (long)T * D * (long)sizeof(ST));
+  float lmu = 0.f, lrs = 0.f;
   for (int i = wave; i < T; i += nw) {
     float r[Q][N];
     float s = 0.f;
@@ -349,19 +361,21 @@ __global__ __launch_bounds__(1024) void k_prologue_lds(const ST* __restrict__ x,
 #pragma unroll
     for (int q = 0; q < Q; ++q) {
       const int c = (lane + 64 * q) * N;
-      if (c < D) {
-        float gg[N], bb[N], o[N];
-        unpack(rg1[q], gg);
-        unpack(rb1[q], bb);
+      float gg[N], bb[N], o[N];
+      unpack(rg1[q], gg);
+      unpack(rb1[q], bb);
 #pragma unroll
-        for (int e = 0; e < N; ++e) o[e] = (r[q][e] - mean) * rstd * gg[e] + bb[e];
-        stv(h1 + base + (long)i * D + c, o);
-      }
+      for (int e = 0; e < N; ++e) o[e] = (r[q][e] - mean) * rstd * gg[e] + bb[e];
+      bst4<ST>(hrs, c < D ? (uint32_t)(c * (int)sizeof(ST)) : 0x80000000u, (uint32_t)(i * D * (int)sizeof(ST)), o);
     }
-    if (lane == 0) {
-      stats[ST_MU1 * NR + (long)b * T + i] = mean;
-      stats[ST_RS1 * NR + (long)b * T + i] = rstd;
-    }
+    const int k = (i - wave) / nw;  // this wave's k-th row
+    lmu = lane == k ? mean : lmu;
+    lrs = lane == k ? rstd : lrs;
+  }
+  const int nr = wave < T ? (T - wave + nw - 1) / nw : 0;
+  if (lane < nr) {
+    stats[ST_MU1 * NR + (long)b * T + wave + lane * nw] = lmu;
+    stats[ST_RS1 * NR + (long)b * T + wave + lane * nw] = lrs;
   }
 }
 
