@@ -102,22 +102,6 @@ __device__ __forceinline__ float wave_sum(float v) {
   return (rl(v, 0) + rl(v, 16)) + (rl(v, 32) + rl(v, 48));
 }
 
-// Sum NV values over a 256-thread block; every thread gets the totals.
-// scratch: at least 4*NV floats of LDS.  Contains two barriers.
-template <int NV>
-__device__ __forceinline__ void block_sum256(float (&v)[NV], float* scratch) {
-  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
-#pragma unroll
-  for (int i = 0; i < NV; ++i) {
-    float s = wave_sum(v[i]);
-    if (lane == 0) scratch[i * 4 + wave] = s;
-  }
-  __syncthreads();
-#pragma unroll
-  for (int i = 0; i < NV; ++i)
-    v[i] = (scratch[i * 4 + 0] + scratch[i * 4 + 1]) + (scratch[i * 4 + 2] + scratch[i * 4 + 3]);
-  __syncthreads();
-}
 
 // sigmoid(v) = 1 / (1 + exp(-v)) with the hardware exp2 and reciprocal (about
 // 2 ulp); saturates cleanly to 0 and 1 for large |v|.

@@ -110,11 +110,6 @@ __device__ __forceinline__ void ldr(const ST* __restrict__ p, Raw<ST, N>& r) {
   }
 }
 
-template <typename ST, int N>
-__device__ __forceinline__ void zero_raw(Raw<ST, N>& r) {
-#pragma unroll
-  for (int i = 0; i < Raw<ST, N>::W; ++i) r.w[i] = 0u;
-}
 
 // Hide a value from the optimiser (no code emitted): forces a recomputation
 // after a barrier instead of keeping earlier results alive across it.
@@ -154,10 +149,13 @@ __device__ __forceinline__ void lds_barrier() {
   asm volatile("" ::: "memory");
 }
 
-// Sum 4*NQ values over the whole block (nw waves, nw <= 16), fixed order,
-// like block_sum4: red is 2 * 16 * NQ float4 of LDS (halves alternating with
-// `parity`), the slots of waves >= nw zeroed by zero_red before the block's
-// first barrier.
+// Sum 4*NQ values over the whole block (nw waves, nw <= 16), fixed order.
+// Each wave reduces its values with DPP and writes NQ float4 to its slots of
+// red (2 * 16 * NQ float4 of LDS, two halves alternating with `parity`, so
+// consecutive calls need one barrier each; the barrier waits for LDS only).
+// After it lane l reads wave l%16's slots and each 16-lane row adds the 16
+// waves' values with a DPP butterfly, without branches: the slots of waves
+// >= nw must hold zeros (zero_red before the block's first barrier).
 template <int NQ>
 __device__ __forceinline__ void zero_red(float4* red) {
   for (int i = threadIdx.x; i < 2 * 16 * NQ; i += blockDim.x) red[i] = make_float4(0.f, 0.f, 0.f, 0.f);
@@ -204,41 +202,6 @@ __device__ __forceinline__ float wave_sum_dpp(float v) {
   return (lane_f(v, 0) + lane_f(v, 16)) + (lane_f(v, 32) + lane_f(v, 48));
 }
 
-// Sum 4 values over the whole block (nw waves, nw <= 16), fixed order.
-// red: 2 * 16 float4 of LDS, two halves alternating with `parity`, so
-// consecutive calls need one barrier each.  The barrier waits for LDS only.
-// All 16 slots are summed, without branches: the slots of waves >= nw must
-// hold zeros (zero_red4 before the block's first barrier).
-__device__ __forceinline__ void zero_red4(float4* red) {
-  for (int i = threadIdx.x; i < 2 * 16; i += blockDim.x) red[i] = make_float4(0.f, 0.f, 0.f, 0.f);
-}
-__device__ __forceinline__ void block_sum4(float (&v)[4], float4* red, int parity) {
-  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
-  float4 s;
-  s.x = wave_sum_dpp(v[0]);
-  s.y = wave_sum_dpp(v[1]);
-  s.z = wave_sum_dpp(v[2]);
-  s.w = wave_sum_dpp(v[3]);
-  float4* r = red + parity * 16;
-  if (lane == 0) r[wave] = s;
-  // scheduling barriers: no arithmetic of the next row moves above the
-  // barrier (it would keep two rows' temporaries live at once)
-  __builtin_amdgcn_sched_barrier(0);
-  lds_barrier();
-  __builtin_amdgcn_sched_barrier(0);
-  // lane l reads slot l % 16; each 16-lane row sums its slots with the DPP
-  // butterfly (fixed order), row 0's result broadcast through lane 0
-  const float4 b = r[lane & 15];
-  float a[4] = {b.x, b.y, b.z, b.w};
-#pragma unroll
-  for (int i = 0; i < 4; ++i) {
-    a[i] += dpp_mov<0xB1>(a[i]);   // quad_perm [1,0,3,2]
-    a[i] += dpp_mov<0x4E>(a[i]);   // quad_perm [2,3,0,1]
-    a[i] += dpp_mov<0x141>(a[i]);  // row_half_mirror
-    a[i] += dpp_mov<0x140>(a[i]);  // row_mirror
-    v[i] = lane_f(a[i], 0);
-  }
-}
 
 template <int NQ>
 __device__ __forceinline__ void block_sum_x4(float (&v)[4 * NQ], float4* red, int parity) {
