@@ -261,14 +261,22 @@ __global__ __launch_bounds__(1024) void k_prologue_lds(const ST* __restrict__ x,
   // 1. statistics of norm0 (collected one row per lane, stored after the
   // loop), raw rows into LDS
   float lmu0 = 0.f, lrs0 = 0.f;
+  // the wave's next row is loaded while the current one is reduced
+  Raw<ST, N> pr[Q];
+#pragma unroll
+  for (int q = 0; q < Q; ++q) ldr(x + base + (long)min(wave, T - 1) * D + min((lane + 64 * q) * N, D - N), pr[q]);
   for (int j = wave; j < T; j += nw) {
     Raw<ST, N> rr[Q];
     float v[Q][N];
     float s = 0.f;
 #pragma unroll
     for (int q = 0; q < Q; ++q) {
+      rr[q] = pr[q];
+      ldr(x + base + (long)min(j + nw, T - 1) * D + min((lane + 64 * q) * N, D - N), pr[q]);
+    }
+#pragma unroll
+    for (int q = 0; q < Q; ++q) {
       const int c = (lane + 64 * q) * N;
-      ldr(x + base + (long)j * D + min(c, D - N), rr[q]);
       unpack(rr[q], v[q]);
       const float m = c < D ? 1.f : 0.f;
 #pragma unroll
