@@ -868,7 +868,6 @@ __global__ __launch_bounds__(MAXT) void k_gate_bwd_ring(const ST* __restrict__ Z
   const float invH = 1.0f / (float)H;
   const int craw = threadIdx.x * 4;
   const int c = min(craw, H - 4);
-  const float cm = craw < H ? 1.f : 0.f;
   float cgx[4], cbx[4], cgg[4], cbg[4];
   ldv(gx + c, cgx);
   ldv(bx + c, cbx);
@@ -894,11 +893,13 @@ __global__ __launch_bounds__(MAXT) void k_gate_bwd_ring(const ST* __restrict__ Z
     reinterpret_cast<float*>(sst)[i] = stats[(ST_MUX + q) * NR + row];
   }
   Raw<ST, 4> ru[RING], rg[RING], rd[RING];
+  // d hidden of rows past B and of columns past H reads as zero (out-of-range
+  // offset), which zeroes every term of theirs
   auto load_row = [&](int slot, int r) {
     const uint32_t row = (uint32_t)(min(b0 + r, bl) * T + t);
     bld4<ST>(zrs, vu, row * zrow, ru[slot]);
     bld4<ST>(zrs, vg, row * zrow, rg[slot]);
-    bld4<ST>(hrs, vu, row * hrow, rd[slot]);
+    bld4<ST>(hrs, (b0 + r <= bl && craw < H) ? vu : 0x80000000u, row * hrow, rd[slot]);
   };
   // two dropped (out-of-range) stores after each slot's loads, as every row
   // step issues: the compiler's wait counts at the loop head then match the
@@ -919,14 +920,12 @@ __global__ __launch_bounds__(MAXT) void k_gate_bwd_ring(const ST* __restrict__ Z
   // rows' 4 RING sums, store the rows of dZ
   int parity = 0;
   auto pair_step = [&](int r, auto prefetch) {
-    float nx[RING][4], ng[RING][4], dux[RING][4], dug[RING][4], rsx[RING], rsg[RING], sm[4 * RING];
+    float nx[RING][4], ng[RING][4], dnx[RING][4], dng[RING][4], rsx[RING], rsg[RING], sm[4 * RING];
     uint32_t rowk[RING];
     bool validk[RING];
 #pragma unroll
     for (int k = 0; k < RING; ++k) {
-      const bool valid = b0 + r + k <= bl;
-      validk[k] = valid;
-      const float w = valid ? cm : 0.f;
+      validk[k] = b0 + r + k <= bl;
       const float4 sr = sst[r + k];
       const float mux = sr.x, mug = sr.z;
       rsx[k] = sr.y;
@@ -946,18 +945,20 @@ __global__ __launch_bounds__(MAXT) void k_gate_bwd_ring(const ST* __restrict__ Z
         const float ux = nx[k][e] * cgx[e] + cbx[e];
         const float ug = ng[k][e] * cgg[e] + cbg[e];
         const float sgm = sigmoidf_(ug);
-        const float dhw = w * dh[e];  // rows past B and columns past H contribute nothing
-        dux[k][e] = dhw * ug * sgm;
-        dug[k][e] = dhw * ux * sgm * (1.f + ug * (1.f - sgm));
-        const float dnx = dux[k][e] * cgx[e], dng = dug[k][e] * cgg[e];
-        sm[4 * k] += dnx;
-        sm[4 * k + 1] += dnx * nx[k][e];
-        sm[4 * k + 2] += dng;
-        sm[4 * k + 3] += dng * ng[k][e];
-        agx[e] += dux[k][e] * nx[k][e];
-        abx[e] += dux[k][e];
-        agg[e] += dug[k][e] * ng[k][e];
-        abg[e] += dug[k][e];
+        // dux = dh ug s;  dug = dh ux s (1 + ug (1 - s)) = dh ux (s + ug s (1 - s))
+        const float us = ug * sgm;
+        const float dux = dh[e] * us;
+        const float dug = (dh[e] * ux) * fmaf(us, 1.f - sgm, sgm);
+        dnx[k][e] = dux * cgx[e];
+        dng[k][e] = dug * cgg[e];
+        sm[4 * k] += dnx[k][e];
+        sm[4 * k + 1] += dnx[k][e] * nx[k][e];
+        sm[4 * k + 2] += dng[k][e];
+        sm[4 * k + 3] += dng[k][e] * ng[k][e];
+        agx[e] += dux * nx[k][e];
+        abx[e] += dux;
+        agg[e] += dug * ng[k][e];
+        abg[e] += dug;
       }
     }
     block_sum_x4<RING>(sm, red8, parity);
@@ -969,8 +970,8 @@ __global__ __launch_bounds__(MAXT) void k_gate_bwd_ring(const ST* __restrict__ Z
       float du[4], dg[4];
 #pragma unroll
       for (int e = 0; e < 4; ++e) {
-        du[e] = rsx[k] * (dux[k][e] * cgx[e] - m1 - nx[k][e] * m2);
-        dg[e] = rsg[k] * (dug[k][e] * cgg[e] - m3 - ng[k][e] * m4);
+        du[e] = rsx[k] * (dnx[k][e] - m1 - nx[k][e] * m2);
+        dg[e] = rsg[k] * (dng[k][e] - m3 - ng[k][e] * m4);
         // a row past B has all four sums zero, so du = dg = 0 there; columns
         // past H are never stored
         au[e] += du[e];
