@@ -859,7 +859,7 @@ __global__ __launch_bounds__(MAXT) void k_gate_bwd_ring(const ST* __restrict__ Z
                                                         const float* __restrict__ stats, ST* __restrict__ dZ,
                                                         float* __restrict__ pgate, float* __restrict__ pb1, int B,
                                                         int T, int H, int nb) {
-  __shared__ float4 red8[2 * 16 * RING];
+  __shared__ float red8[2 * 16 * 8];
   __shared__ float4 sst[ROWS_PER_GROUP];
   constexpr int SZ = (int)sizeof(ST);
   const int t = blockIdx.x, grp = blockIdx.y;
@@ -885,7 +885,7 @@ __global__ __launch_bounds__(MAXT) void k_gate_bwd_ring(const ST* __restrict__ Z
   const uint32_t vu = (uint32_t)(c * SZ), vg = (uint32_t)((H + c) * SZ);
   const uint32_t zrow = (uint32_t)(2 * H * SZ), hrow = (uint32_t)(H * SZ);
 
-  zero_red<RING>(red8);
+  zero_red(red8);
   // the group's inner-LN statistics (mux, rsx, mug, rsg per row) staged in LDS once
   for (int i = threadIdx.x; i < 4 * ROWS_PER_GROUP; i += blockDim.x) {
     const int r = i >> 2, q = i & 3;
@@ -961,17 +961,19 @@ __global__ __launch_bounds__(MAXT) void k_gate_bwd_ring(const ST* __restrict__ Z
         abg[e] += dug;
       }
     }
-    block_sum_x4<RING>(sm, red8, parity);
+    static_assert(4 * RING == 8, "one block reduction of the pair's eight sums");
+    block_sum8(sm, red8, parity);
     parity ^= 1;
 #pragma unroll
     for (int k = 0; k < RING; ++k) {
-      const float m1 = sm[4 * k] * invH, m2 = sm[4 * k + 1] * invH, m3 = sm[4 * k + 2] * invH,
-                  m4 = sm[4 * k + 3] * invH;
+      // rs (dn - m1 - n m2) = dn rs + (n (-rs m2) - rs m1): two FMAs per element
+      const float c1x = -rsx[k] * (sm[4 * k] * invH), c2x = -rsx[k] * (sm[4 * k + 1] * invH);
+      const float c1g = -rsg[k] * (sm[4 * k + 2] * invH), c2g = -rsg[k] * (sm[4 * k + 3] * invH);
       float du[4], dg[4];
 #pragma unroll
       for (int e = 0; e < 4; ++e) {
-        du[e] = rsx[k] * (dnx[k][e] - m1 - nx[k][e] * m2);
-        dg[e] = rsg[k] * (dng[k][e] - m3 - ng[k][e] * m4);
+        du[e] = fmaf(dnx[k][e], rsx[k], fmaf(nx[k][e], c2x, c1x));
+        dg[e] = fmaf(dng[k][e], rsg[k], fmaf(ng[k][e], c2g, c1g));
         // a row past B has all four sums zero, so du = dg = 0 there; columns
         // past H are never stored
         au[e] += du[e];

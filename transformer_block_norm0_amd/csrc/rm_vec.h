@@ -149,19 +149,21 @@ __device__ __forceinline__ void lds_barrier() {
   asm volatile("" ::: "memory");
 }
 
-// Sum 4*NQ values over the whole block (nw waves, nw <= 16), fixed order.
-// Each wave reduces its values with DPP and writes NQ float4 to its slots of
-// red (2 * 16 * NQ float4 of LDS, two halves alternating with `parity`, so
-// consecutive calls need one barrier each; the barrier waits for LDS only).
-// After it lane l reads wave l%16's slots and each 16-lane row adds the 16
-// waves' values with a DPP butterfly, without branches: the slots of waves
-// >= nw must hold zeros (zero_red before the block's first barrier).
-template <int NQ>
-__device__ __forceinline__ void zero_red(float4* red) {
-  for (int i = threadIdx.x; i < 2 * 16 * NQ; i += blockDim.x) red[i] = make_float4(0.f, 0.f, 0.f, 0.f);
+// Sum 8 values over the whole block (nw waves, nw <= 16), fixed order, the
+// totals in every lane.  red: 2 * 16 * 8 floats of LDS, two halves
+// alternating with `parity`, so consecutive calls need one barrier each (the
+// barrier waits for LDS only).  Inside the wave a transposing reduce-scatter
+// halves the number of values per lane at each lane distance (32, 16, 8), so
+// the wave's eight sums cost 18 VALU operations instead of eight full
+// butterflies; lane l then holds the wave's sum l/8 and lanes l%8 == 0 write
+// it to the wave's slots.  After the barrier lane l reads wave l%16's sums
+// 2(l/16) and 2(l/16)+1 and each 16-lane row adds the 16 waves with a DPP
+// butterfly, without branches: the slots of waves >= nw must hold zeros
+// (zero_red before the block's first barrier).
+__device__ __forceinline__ void zero_red(float* red) {
+  for (int i = threadIdx.x; i < 2 * 16 * 8; i += blockDim.x) red[i] = 0.f;
 }
-template <int NQ>
-__device__ __forceinline__ void block_sum_x4(float (&v)[4 * NQ], float4* red, int parity);
+__device__ __forceinline__ void block_sum8(float (&v)[8], float* red, int parity);
 
 // Sum NV values over the whole block (nw waves, nw <= 16), fixed order.
 // red: 2 * NV * 16 floats of LDS, used as two alternating halves selected by
@@ -203,37 +205,56 @@ __device__ __forceinline__ float wave_sum_dpp(float v) {
 }
 
 
-template <int NQ>
-__device__ __forceinline__ void block_sum_x4(float (&v)[4 * NQ], float4* red, int parity) {
+// Lane-half and row swaps (gfx950): x holds value i, y value i' of every
+// lane.  v_permlane32_swap exchanges x's lanes 32..63 with y's lanes 0..31, so
+// afterwards lanes 0..31 hold (own x, partner's x) and lanes 32..63
+// (partner's y, own y), partner = lane ^ 32; the sum of the pair is x summed
+// over the two lanes in the lower half and y in the upper.  v_permlane16_swap
+// does the same for the odd and even 16-lane rows (partner = lane ^ 16).
+__device__ __forceinline__ float swap32_sum(float x, float y) {
+  const auto s = __builtin_amdgcn_permlane32_swap(__float_as_uint(x), __float_as_uint(y), false, false);
+  return __uint_as_float(s[0]) + __uint_as_float(s[1]);
+}
+__device__ __forceinline__ float swap16_sum(float x, float y) {
+  const auto s = __builtin_amdgcn_permlane16_swap(__float_as_uint(x), __float_as_uint(y), false, false);
+  return __uint_as_float(s[0]) + __uint_as_float(s[1]);
+}
+
+__device__ __forceinline__ void block_sum8(float (&v)[8], float* red, int parity) {
   const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
-  float4 sw[NQ];
+  // lanes 0..31: sums 0..3 over {l, l^32}; lanes 32..63: sums 4..7
+  float s[4];
 #pragma unroll
-  for (int k = 0; k < NQ; ++k) {
-    sw[k].x = wave_sum_dpp(v[4 * k]);
-    sw[k].y = wave_sum_dpp(v[4 * k + 1]);
-    sw[k].z = wave_sum_dpp(v[4 * k + 2]);
-    sw[k].w = wave_sum_dpp(v[4 * k + 3]);
-  }
-  float4* r = red + parity * 16 * NQ;
-  if (lane == 0) {
+  for (int i = 0; i < 4; ++i) s[i] = swap32_sum(v[i], v[i + 4]);
+  // 16-lane row q (= lane/16) holds sums 2q, 2q+1 over 4 lanes
+  float t[2];
 #pragma unroll
-    for (int k = 0; k < NQ; ++k) r[NQ * wave + k] = sw[k];
-  }
+  for (int j = 0; j < 2; ++j) t[j] = swap16_sum(s[j], s[j + 2]);
+  // lanes with bit 3 clear keep sum 2q, the others 2q+1, each adding its
+  // partner's (lane ^ 8, row_ror:8) copy; then the 8-lane half-row butterfly
+  const bool odd = (lane & 8) != 0;
+  float u = (odd ? t[1] : t[0]) + dpp_mov<0x128>(odd ? t[0] : t[1]);
+  u += dpp_mov<0xB1>(u);   // quad_perm [1,0,3,2]
+  u += dpp_mov<0x4E>(u);   // quad_perm [2,3,0,1]
+  u += dpp_mov<0x141>(u);  // row_half_mirror
+  float* r = red + parity * 16 * 8;
+  if ((lane & 7) == 0) r[8 * wave + (lane >> 3)] = u;  // the wave's sum lane/8
   __builtin_amdgcn_sched_barrier(0);
   lds_barrier();
   __builtin_amdgcn_sched_barrier(0);
+  const float2 b = *reinterpret_cast<const float2*>(r + 8 * (lane & 15) + 2 * (lane >> 4));
+  float a[2] = {b.x, b.y};
 #pragma unroll
-  for (int k = 0; k < NQ; ++k) {
-    const float4 b = r[NQ * (lane & 15) + k];
-    float a[4] = {b.x, b.y, b.z, b.w};
+  for (int i = 0; i < 2; ++i) {
+    a[i] += dpp_mov<0xB1>(a[i]);
+    a[i] += dpp_mov<0x4E>(a[i]);
+    a[i] += dpp_mov<0x141>(a[i]);
+    a[i] += dpp_mov<0x140>(a[i]);  // row_mirror: the 16 waves' total in every lane of the row
+  }
 #pragma unroll
-    for (int i = 0; i < 4; ++i) {
-      a[i] += dpp_mov<0xB1>(a[i]);
-      a[i] += dpp_mov<0x4E>(a[i]);
-      a[i] += dpp_mov<0x141>(a[i]);
-      a[i] += dpp_mov<0x140>(a[i]);
-      v[4 * k + i] = lane_f(a[i], 0);
-    }
+  for (int q = 0; q < 4; ++q) {
+    v[2 * q] = lane_f(a[0], 16 * q);
+    v[2 * q + 1] = lane_f(a[1], 16 * q);
   }
 }
 
