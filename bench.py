@@ -71,6 +71,29 @@ def row_bytes(d, sz):
     }
 
 
+def unfused_elementwise_bytes(d, sz):
+    """HBM bytes of the block's norm / elementwise work done one eager operator at a time: every
+    operator reads its inputs once and writes its output once (GEMM operand and result traffic
+    excluded).  U_D, U_H = one [B,T,D] / [B,T,H] tensor in the storage dtype.
+      forward:  norm0 2 U_D, token-mix copy 2, residual add 3, norm1 2, +bout 2, residual add 3,
+                norm2 2 (16 U_D); +b1 on Z 4 U_H, LN_x 2, LN_gate 2, silu 2, gating product 3 (13 U_H)
+      backward: norm2 bwd with its affine sums 5 U_D, dbout 1, residual add of dh1 3, norm1 bwd 5,
+                inverse token mix 2, norm0 bwd 5, dx = dr1 + dx0 3 (24 U_D); gating product bwd
+                5 U_H, silu bwd 3, LN_x bwd 5, LN_gate bwd 5, concatenating dZ 4, db1 2 (24 U_H)"""
+    N = d.B * d.T
+    u_d, u_h = N * d.D * sz, N * d.k * d.D * sz
+    return 40 * u_d + 37 * u_h
+
+
+def fused_elementwise_bytes(d, sz, row_kernels):
+    """The same work in this library: the row kernels' algorithmic bytes (row_bytes) plus what the
+    GEMM epilogues read for it (the two residuals and the two biases)."""
+    rb = row_bytes(d, sz)
+    N = d.B * d.T
+    epi = 2 * N * d.D * sz + d.T * (2 * d.k * d.D + d.D) * sz
+    return sum(rb[k] for k in row_kernels) + epi
+
+
 def step_flops(d):
     return 18.0 * d.B * d.T * d.D * d.k * d.D
 
@@ -258,6 +281,19 @@ def main():
         if traffic is not None:
             roofline["traffic"] = traffic
 
+    # bytes of the norm / elementwise work: unfused count vs this library (algorithmic and measured)
+    sz = 4 if w.dtype == "f32" else 2
+    rk = [k for k in kernels if k in row_bytes(d, sz)] or (
+        ["prologue", "gate_fwd", "ln2_fwd", "ln2_bwd", "gate_bwd", "tail_bwd", "finalize"])
+    unf = unfused_elementwise_bytes(d, sz)
+    fus = fused_elementwise_bytes(d, sz, rk)
+    meas = [load_traffic(k, w.name) for k in rk]
+    elementwise = {"unfused_bytes_per_step": int(unf), "fused_bytes_per_step": int(fus),
+                   "fused_row_kernels_measured_bytes": (int(sum(meas)) if meas and None not in meas else None),
+                   "unfused_over_fused": round(unf / fus, 2), "row_kernels": rk}
+    log(f"elementwise bytes per step: unfused {unf / 1e9:.2f} GB, fused {fus / 1e9:.2f} GB "
+        f"({unf / fus:.2f}x less)")
+
     # the pages' protocol: flush caches, sync, event span per iteration, drop the first sample
     protocol = None
     if not args.no_protocol:
@@ -306,6 +342,7 @@ def main():
         "tflops": round(tflops, 2),
         "pct_mfma_peak": round(pct_peak, 2),
         "peak_device_bytes": int(peak_mem),
+        "elementwise_bytes": elementwise,
         "roofline": roofline,
         "cpu_baseline": cpu,
         "pages_protocol": protocol,

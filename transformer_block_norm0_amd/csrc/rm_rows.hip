@@ -40,6 +40,14 @@ __host__ __device__ __forceinline__ const ST* cptr(const void* p) { return reint
 // i*S + c%S of a0, recomputed from x and norm0's statistics (kept in LDS).
 // N = elements per lane chunk; N > 1 needs D % N == 0 and S % N == 0 so a
 // chunk's gather source is N contiguous, aligned elements.
+// r1 = token_mix(norm0(x)) + x for one gathered element a of row j (nmr =
+// -mu0[j] rstd0[j], rs = rstd0[j]), the gathered affine gg/bb and the
+// residual xi.  Both forward prologues and both norm1 backwards use it, so
+// the backward recomputes the forward's r1 bit for bit.
+__device__ __forceinline__ float mixed_residual(float a, float rs, float nmr, float gg, float bb, float xi) {
+  return fmaf(fmaf(a, rs, nmr), gg, bb) + xi;
+}
+
 template <typename ST, int N>
 __global__ __launch_bounds__(512) void k_prologue(const ST* __restrict__ x, const ST* __restrict__ g0,
                                                   const ST* __restrict__ be0, const ST* __restrict__ g1,
@@ -106,9 +114,9 @@ __global__ __launch_bounds__(512) void k_prologue(const ST* __restrict__ x, cons
         ldv(g0 + sc, gg);
         ldv(be0 + sc, bb);
         ldv(x + base + (long)i * D + c, xi);
-        const float mu = s_mu0[j], rs = s_rs0[j];
+        const float rs = s_rs0[j], nmr = -s_mu0[j] * rs;
 #pragma unroll
-        for (int e = 0; e < N; ++e) r[q][e] = (a[e] - mu) * rs * gg[e] + bb[e] + xi[e];
+        for (int e = 0; e < N; ++e) r[q][e] = mixed_residual(a[e], rs, nmr, gg[e], bb[e], xi[e]);
       } else {
 #pragma unroll
         for (int e = 0; e < N; ++e) r[q][e] = 0.f;
@@ -310,7 +318,7 @@ __global__ __launch_bounds__(1024) void k_prologue_lds(const ST* __restrict__ x,
   __syncthreads();
 
   // 2. per-lane source rows and their statistics; out1's affine for this lane's columns
-  float mu[Q], rs[Q];
+  float nmr[Q], rs[Q];
   int jq[Q];
   Raw<ST, N> rg1[Q], rb1[Q];
 #pragma unroll
@@ -319,8 +327,8 @@ __global__ __launch_bounds__(1024) void k_prologue_lds(const ST* __restrict__ x,
     const int cc = min(c, D - N);
     const int j = div_small(cc, invS);
     jq[q] = j;
-    mu[q] = load_bypass_l1(stats + ST_MU0 * NR + (long)b * T + j);
     rs[q] = load_bypass_l1(stats + ST_RS0 * NR + (long)b * T + j);
+    nmr[q] = -load_bypass_l1(stats + ST_MU0 * NR + (long)b * T + j) * rs[q];
     ldr(g1 + cc, rg1[q]);
     ldr(be1 + cc, rb1[q]);
   }
@@ -349,7 +357,7 @@ __global__ __launch_bounds__(1024) void k_prologue_lds(const ST* __restrict__ x,
       const float m = c < D ? 1.f : 0.f;
 #pragma unroll
       for (int e = 0; e < N; ++e) {
-        r[q][e] = (a[e] - mu[q]) * rs[q] * gg[e] + bb[e] + xi[e];
+        r[q][e] = mixed_residual(a[e], rs[q], nmr[q], gg[e], bb[e], xi[e]);
         s += m * r[q][e];
       }
     }
@@ -366,6 +374,7 @@ __global__ __launch_bounds__(1024) void k_prologue_lds(const ST* __restrict__ x,
       }
     }
     const float rstd = rsqrtf(wave_sum_dpp(s2) * invD + EPS_OUTER);
+    const float nmrs = -mean * rstd;
 #pragma unroll
     for (int q = 0; q < Q; ++q) {
       const int c = (lane + 64 * q) * N;
@@ -373,7 +382,7 @@ __global__ __launch_bounds__(1024) void k_prologue_lds(const ST* __restrict__ x,
       unpack(rg1[q], gg);
       unpack(rb1[q], bb);
 #pragma unroll
-      for (int e = 0; e < N; ++e) o[e] = (r[q][e] - mean) * rstd * gg[e] + bb[e];
+      for (int e = 0; e < N; ++e) o[e] = fmaf(fmaf(r[q][e], rstd, nmrs), gg[e], bb[e]);
       bst4<ST>(hrs, c < D ? (uint32_t)(c * (int)sizeof(ST)) : 0x80000000u, (uint32_t)(i * D * (int)sizeof(ST)), o);
     }
     const int k = (i - wave) / nw;  // this wave's k-th row
@@ -1083,15 +1092,15 @@ __global__ __launch_bounds__(512) void k_tail_bwd_lds(const ST* __restrict__ x, 
   // gather sources of this lane's columns: row c/S (same for every row of the sample);
   // the first row's d(out1), x, gathered gamma0 / beta0
   int jq[Q];
-  float mu0[Q], rs0[Q];
+  float nmr0[Q], rs0[Q];
   Raw<ST, N> rg1[Q], rgg0[Q], pdh[Q], px[Q], pg0[Q], pb0[Q];
 #pragma unroll
   for (int q = 0; q < Q; ++q) {
     const int cc = min((lane + 64 * q) * N, D - N);
     const int j = div_small(cc, invS);
     jq[q] = j;
-    mu0[q] = stats[ST_MU0 * NR + srow + j];
     rs0[q] = stats[ST_RS0 * NR + srow + j];
+    nmr0[q] = -stats[ST_MU0 * NR + srow + j] * rs0[q];
     ldr(g1 + cc, rg1[q]);
     ldr(g0 + cc, rgg0[q]);
     ldr(dh1 + (srow + i0) * D + cc, pdh[q]);
@@ -1149,7 +1158,7 @@ __global__ __launch_bounds__(512) void k_tail_bwd_lds(const ST* __restrict__ x, 
       unpack(rg1[q], gg1);
 #pragma unroll
       for (int e = 0; e < N; ++e) {
-        const float r1v = (a[e] - mu0[q]) * rs0[q] * gg0[e] + bb0[e] + xi[e];
+        const float r1v = mixed_residual(a[e], rs0[q], nmr0[q], gg0[e], bb0[e], xi[e]);
         n1[q][e] = (r1v - mu1) * rs1;
         dn[q][e] = m * gv[q][e] * gg1[e];
         s1 += dn[q][e];
@@ -1312,7 +1321,7 @@ __global__ __launch_bounds__(256) void k_ln1_bwd(const ST* __restrict__ x, const
       ldv(g1 + c, cg1);
 #pragma unroll
       for (int e = 0; e < N; ++e) {
-        const float r1 = (a[e] - mu0[q]) * rs0[q] * cg0[e] + cb0[e] + xi[e];
+        const float r1 = mixed_residual(a[e], rs0[q], -mu0[q] * rs0[q], cg0[e], cb0[e], xi[e]);
         n1[q][e] = (r1 - mu1) * rs1;
         dn[q][e] = m * gv[e] * cg1[e];
         s1 += dn[q][e];
