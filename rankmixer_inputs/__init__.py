@@ -84,6 +84,8 @@ WORKLOADS = {w.name: w for w in (
     _w("B4_T16_D128_k2_f16_public", 4, 16, 128, 2, "f16", 7101, "unit"),
     _w("B256_T16_D256_k3_f16_lnrand", 256, 16, 256, 3, "f16", 8, "random"),
     _w("B1024_T64_D1280_k2_f16", 1024, 64, 1280, 2, "f16", 6, "unit"),
+    # every dimension at the envelope's maximum (H = 3840)
+    _w("B1024_T64_D1280_k3_bf16_lnrand", 1024, 64, 1280, 3, "bf16", 9, "random"),
 )}
 
 PRODUCTION = "B1024_T64_D1280_k2_bf16"

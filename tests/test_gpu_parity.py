@@ -236,6 +236,12 @@ def test_full_size_B1024_T64_D1280_k2_f16_sampled():
     sampled_check("B1024_T64_D1280_k2_f16", samples=(0, 300, -1), tokens=(0, 41, -1))
 
 
+def test_full_size_envelope_maximum_sampled():
+    """B, T, D and k all at the maximum of page 1's envelope ("Public checks and instructor
+    coverage"): H = 3840 takes the general gate backward, random LayerNorm affines."""
+    sampled_check("B1024_T64_D1280_k3_bf16_lnrand", samples=(0, 777, -1), tokens=(0, 29, -1))
+
+
 @pytest.mark.parametrize("name", ["B4_T16_D128_k2_bf16_public", "B8_T8_D64_k2_f32", "B4_T16_D128_k2_f16_public"])
 def test_graph_replay_matches_eager(name):
     """fwd+bwd captured once into a HIP graph: every replay, with eager work and
