@@ -438,19 +438,22 @@ __global__ __launch_bounds__(256) void k_gate_fwd(const ST* __restrict__ Z, cons
   float vu = 0.f, vg = 0.f;
 #pragma unroll
   for (int q = 0; q < Q; ++q) {
+    // masked deviation m (z - mu) as one FMA: m z + (-m mu)
     const float m = ((lane + 64 * q) * N < H) ? 1.f : 0.f;
+    const float omu = -m * mu_u, omg = -m * mu_g;
     float u[N], g[N];
     unpack(ru[q], u);
     unpack(rg[q], g);
 #pragma unroll
     for (int e = 0; e < N; ++e) {
-      const float du = u[e] - mu_u, dg = g[e] - mu_g;
-      vu += m * du * du;
-      vg += m * dg * dg;
+      const float du = fmaf(u[e], m, omu), dg = fmaf(g[e], m, omg);
+      vu = fmaf(du, du, vu);
+      vg = fmaf(dg, dg, vg);
     }
   }
   const float rs_u = rsqrtf(wave_sum(vu) * invH + EPS_INNER);
   const float rs_g = rsqrtf(wave_sum(vg) * invH + EPS_INNER);
+  const float nmr_u = -mu_u * rs_u, nmr_g = -mu_g * rs_g;
 #pragma unroll
   for (int q = 0; q < Q; ++q) {
     const int c = (lane + 64 * q) * N;
@@ -464,8 +467,8 @@ __global__ __launch_bounds__(256) void k_gate_fwd(const ST* __restrict__ Z, cons
       ldv(bg + c, cbg);
 #pragma unroll
       for (int e = 0; e < N; ++e) {
-        const float ux = (u[e] - mu_u) * rs_u * cgx[e] + cbx[e];
-        const float ug = (g[e] - mu_g) * rs_g * cgg[e] + cbg[e];
+        const float ux = fmaf(fmaf(u[e], rs_u, nmr_u), cgx[e], cbx[e]);
+        const float ug = fmaf(fmaf(g[e], rs_g, nmr_g), cgg[e], cbg[e]);
         o[e] = ux * (ug * sigmoidf_(ug));
       }
       stv(hid + row * H + c, o);
@@ -688,8 +691,8 @@ __device__ __forceinline__ void gate_terms(const Raw<ST, N>& ru, const Raw<ST, N
   unpack(rbg, cbg);
 #pragma unroll
   for (int e = 0; e < N; ++e) {
-    o.nx[e] = (u[e] - mux) * rsx;
-    o.ng[e] = (g[e] - mug) * rsg;
+    o.nx[e] = fmaf(u[e], rsx, -mux * rsx);  // the forward's form of the normalised value
+    o.ng[e] = fmaf(g[e], rsg, -mug * rsg);
     const float ux = o.nx[e] * cgx[e] + cbx[e];
     const float ug = o.ng[e] * cgg[e] + cbg[e];
     const float sgm = sigmoidf_(ug);
