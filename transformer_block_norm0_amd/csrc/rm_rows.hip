@@ -1441,9 +1441,10 @@ __global__ __launch_bounds__(256) void k_ln0_bwd(const ST* __restrict__ x, const
 // twelve jobs in one flat launch (job k owns blocks blk0 .. blk0 + nblk - 1).
 //   * short jobs (P <= 32 rows, many columns): one thread per column sums its
 //     P rows in order, eight loads in flight;
-//   * tall jobs: a block takes 16 columns with 64 row lanes; lane r sums rows
-//     r, r+64, ... (eight loads in flight), then the 64 lane sums are added in
-//     order.
+//   * tall jobs: a block takes 64 columns with 16 row lanes (one wave per row
+//     lane, so each load instruction reads 256 contiguous bytes of a row);
+//     row lane r sums rows r, r+16, ... (eight loads in flight), then the 16
+//     lane sums are added in order.
 struct RedJob {
   const float* part;
   long pstride;
@@ -1456,7 +1457,10 @@ struct RedJobs {
   RedJob j[12];
 };
 constexpr int RED_SHORT_ROWS = 32;
-inline int red_blocks(const RedJob& j) { return j.P <= RED_SHORT_ROWS ? (j.ncols + 1023) / 1024 : (j.ncols + 15) / 16; }
+constexpr int RED_TALL_COLS = 64, RED_TALL_LANES = 16;  // 1024 threads
+inline int red_blocks(const RedJob& j) {
+  return j.P <= RED_SHORT_ROWS ? (j.ncols + 1023) / 1024 : (j.ncols + RED_TALL_COLS - 1) / RED_TALL_COLS;
+}
 
 __device__ __forceinline__ float sum8(const float* p, long stride) {
   float v[8];
@@ -1467,7 +1471,7 @@ __device__ __forceinline__ float sum8(const float* p, long stride) {
 
 template <typename ST>
 __global__ __launch_bounds__(1024) void k_finalize(RedJobs jobs) {
-  __shared__ float red[64][17];
+  __shared__ float red[RED_TALL_LANES][RED_TALL_COLS + 1];
   int jid = 0;
 #pragma unroll
   for (int k = 1; k < 12; ++k)
@@ -1485,21 +1489,22 @@ __global__ __launch_bounds__(1024) void k_finalize(RedJobs jobs) {
     st(reinterpret_cast<ST*>(job.out), c, s);
     return;
   }
-  const int cx = threadIdx.x & 15, ry = threadIdx.x >> 4;
-  const long c = (long)b * 16 + cx;
+  const int cx = threadIdx.x & (RED_TALL_COLS - 1), ry = threadIdx.x / RED_TALL_COLS;
+  const long c = (long)b * RED_TALL_COLS + cx;
   float s = 0.f;
   if (c < job.ncols) {
     const float* p = job.part + c;
+    constexpr int L = RED_TALL_LANES;
     int r = ry;
-    for (; r + 7 * 64 < job.P; r += 8 * 64) s += sum8(p + (long)r * job.pstride, 64 * job.pstride);
-    for (; r < job.P; r += 64) s += p[(long)r * job.pstride];
+    for (; r + 7 * L < job.P; r += 8 * L) s += sum8(p + (long)r * job.pstride, L * job.pstride);
+    for (; r < job.P; r += L) s += p[(long)r * job.pstride];
   }
   red[ry][cx] = s;
   __syncthreads();
   if (ry == 0 && c < job.ncols) {
     float t = 0.f;
-#pragma unroll 16
-    for (int k = 0; k < 64; ++k) t += red[k][cx];
+#pragma unroll
+    for (int k = 0; k < RED_TALL_LANES; ++k) t += red[k][cx];
     st(reinterpret_cast<ST*>(job.out), c, t);
   }
 }
