@@ -38,6 +38,7 @@ from rankmixer_inputs import PRODUCTION, WORKLOADS, make_case  # noqa: E402
 # MI355X published peaks
 PEAK_TFLOPS = {"bf16": 2516.6, "f16": 2516.6, "f32": 157.3}   # dense MFMA: 256 CU x 2.4 GHz x (4096 | 256) flop/clk
 PEAK_HBM_GBS = 8000.0
+PEAK_VALU_F32 = 157.3   # TFLOP/s, fp32 vector FMA: the small-batch kernels' contractions run on the VALU
 
 
 def log(msg):
@@ -50,6 +51,14 @@ def gemm_flops(d):
     return {"gemm_up": 2.0 * B * T * D * 2 * H, "gemm_down": 2.0 * B * T * H * D,
             "gemm_dhid": 2.0 * B * T * D * H, "gemm_dwout": 2.0 * T * H * D * B,
             "gemm_dw1": 2.0 * T * D * 2 * H * B, "gemm_dh1": 2.0 * B * T * 2 * H * D}
+
+
+def small_flops(d):
+    """Algorithmic flops of the small-batch kernels (B <= 8), whose per-token contractions are fp32
+    VALU FMA loops: the forward's two products, the backward's four; the last kernel has none."""
+    B, T, D, H = d.B, d.T, d.D, d.k * d.D
+    f = 2.0 * B * T * D * 2 * H + 2.0 * B * T * H * D
+    return {"small_fwd": f, "small_bwd": 2.0 * f}
 
 
 def row_bytes(d, sz):
@@ -137,6 +146,9 @@ def main():
     ap.add_argument("--no-kernel-times", action="store_true", help="skip the event-instrumented pass")
     ap.add_argument("--graph", action="store_true",
                     help="also time the step replayed from one captured HIP graph (launch-bound small shapes)")
+    ap.add_argument("--kernels", choices=["auto", "main"], default="auto",
+                    help="auto: B<=8, D<=128, H<=256 shapes take the small-batch kernels (3 launches per step); "
+                         "main: every shape takes the main kernel set")
     ap.add_argument("--copy-calibration-mib", type=int, default=0,
                     help="run one plain device-to-device copy of this many MiB first (reference for HBM counters)")
     args = ap.parse_args()
@@ -152,6 +164,7 @@ def main():
         print("bench.py: no GPU visible", file=sys.stderr)
         sys.exit(1)
     rb.library()
+    rb.small_path(args.kernels == "auto")
 
     w = WORKLOADS[args.workload]
     d = w.dims
@@ -246,6 +259,7 @@ def main():
         rb.prof_enable(False)
         prof = rb.prof_collect()
         flops = gemm_flops(d)
+        sflops = small_flops(d)
         sz = 4 if w.dtype == "f32" else 2
         rbytes = row_bytes(d, sz)
         step_ms_sum = 0.0
@@ -258,6 +272,9 @@ def main():
             if name in flops:
                 ent["tflops"] = round(flops[name] / (avg / 1e3) / 1e12, 2)
                 ent["frac_peak"] = round(ent["tflops"] / PEAK_TFLOPS[w.dtype], 4)
+            elif name in sflops:
+                ent["tflops"] = round(sflops[name] / (avg / 1e3) / 1e12, 4)
+                ent["frac_peak"] = round(ent["tflops"] / PEAK_VALU_F32, 6)
             elif name in rbytes:
                 ent["gbs"] = round(rbytes[name] / (avg / 1e3) / 1e9, 1)
                 ent["frac_peak"] = round(ent["gbs"] / PEAK_HBM_GBS, 4)
@@ -268,7 +285,11 @@ def main():
         log(f"  sum of kernel means {step_ms_sum:.3f} ms/step (instrumented)")
         dom = max(kernels.items(), key=lambda kv: kv[1]["avg_ms"])
         name, ent = dom
-        if "tflops" in ent:
+        if name in sflops:
+            roofline = {"kernel": name, "bound": "alu", "achieved": ent["tflops"], "peak": PEAK_VALU_F32,
+                        "unit": "TFLOP/s", "frac": ent["frac_peak"], "traffic": None, "avg_ms": ent["avg_ms"],
+                        "per_launch": f"{sflops[name]:.4g} flop"}
+        elif "tflops" in ent:
             roofline = {"kernel": name, "bound": "mfma", "achieved": ent["tflops"], "peak": PEAK_TFLOPS[w.dtype],
                         "unit": "TFLOP/s", "frac": round(ent["tflops"] / PEAK_TFLOPS[w.dtype], 4),
                         "traffic": None, "avg_ms": ent["avg_ms"],
@@ -281,8 +302,10 @@ def main():
         if traffic is not None:
             roofline["traffic"] = traffic
 
-    # bytes of the norm / elementwise work: unfused count vs this library (algorithmic and measured)
+    # bytes of the norm / elementwise work: unfused count vs this library (algorithmic and measured);
+    # not reported for the small-batch kernels, which hold a token's rows on chip
     sz = 4 if w.dtype == "f32" else 2
+    small_run = any(k.startswith("small_") for k in kernels)
     rk = [k for k in kernels if k in row_bytes(d, sz)] or (
         ["prologue", "gate_fwd", "ln2_fwd", "ln2_bwd", "gate_bwd", "tail_bwd", "finalize"])
     unf = unfused_elementwise_bytes(d, sz)
@@ -293,6 +316,8 @@ def main():
                    "unfused_over_fused": round(unf / fus, 2), "row_kernels": rk}
     log(f"elementwise bytes per step: unfused {unf / 1e9:.2f} GB, fused {fus / 1e9:.2f} GB "
         f"({unf / fus:.2f}x less)")
+    if small_run:
+        elementwise = None
 
     # the pages' protocol: flush caches, sync, event span per iteration, drop the first sample
     protocol = None
@@ -338,7 +363,7 @@ def main():
         "dtype": w.dtype,
         "data": "synthetic (seeded N(0,1) inputs and upstream grad, he-uniform weights)",
         "config": {"workload": w.name, "B": d.B, "T": d.T, "D": d.D, "k": d.k, "H": d.H,
-                   "tokens_per_step": tokens, "parallelism": "single GPU"},
+                   "tokens_per_step": tokens, "parallelism": "single GPU", "kernels": args.kernels},
         "tflops": round(tflops, 2),
         "pct_mfma_peak": round(pct_peak, 2),
         "peak_device_bytes": int(peak_mem),

@@ -103,6 +103,16 @@ rm_status rm_block_fwd(const rm_dims* dims, const rm_params* p, const void* x, v
 rm_status rm_block_bwd(const rm_dims* dims, const rm_params* p, const void* x, const void* dy,
                        void* ws, size_t ws_bytes, void* dx, const rm_grads* g, void* stream);
 
+/* Small-batch path (on by default).  For B <= 8, D <= 128 and H <= 256 the
+ * same computation (page 1, "Exact computation") runs as one launch for the
+ * forward (one workgroup per token, its rows in LDS) and two for the
+ * backward, instead of one launch per fused step; the saved state in ws is
+ * the same, so either backward may follow either forward.  on = 0 sends
+ * every shape through the main path, 1 (the default) lets the shapes above
+ * take the small path.  Process-wide setting, read at each rm_block_fwd /
+ * rm_block_bwd call; RM_E_ARG for any other value. */
+rm_status rm_small_path(int on);
+
 /* Token mixing alone (page 1, "Exact computation", token mixing paragraph):
  * out[b,i,j*S+s] = in[b,j,i*S+s], S = D/T.  A pure permutation of element bits
  * (no arithmetic), through the same device index function the block uses.

@@ -4,6 +4,8 @@ Metric per tensor: max |gpu - oracle| / max |oracle|; bound 1e-4 for fp32
 storage and 3e-2 for bf16 storage (fp32 accumulation in both).  Every output
 must be finite.  Token mixing is compared bit for bit.
 """
+import contextlib
+
 import numpy as np
 import pytest
 
@@ -119,16 +121,71 @@ def dbeta0_summand_scale(case, cache):
     return float(np.max(np.abs(oracle.token_mix(dr1)).sum(axis=(0, 1))))
 
 
-@pytest.mark.parametrize("name", [n for n, _ in SMALL])
-def test_parity_small_workloads(name):
-    check_case(make_case(WORKLOADS[name]))
+# ---------------------------------------------------------------------------
+# the two kernel sets: shapes inside B <= 8, D <= 128, H <= 256 take the
+# small-batch kernels by default (rm_small_path); "main" forces the main path
+
+def small_shape(B, D, k):
+    return B <= 8 and D <= 128 and k * D <= 256
 
 
-@pytest.mark.parametrize("shape", EDGE)
+@contextlib.contextmanager
+def kernel_set(which):
+    import transformer_block_norm0_amd as rb
+    rb.small_path(which == "small")
+    try:
+        yield
+    finally:
+        rb.small_path(True)
+
+
+SMALL_RUNS = [(n, ks) for n, _ in SMALL for ks in ("main", "small")
+              if ks == "main" or small_shape(WORKLOADS[n].dims.B, WORKLOADS[n].dims.D, WORKLOADS[n].dims.k)]
+EDGE_RUNS = [(sh, ks) for sh in EDGE for ks in ("main", "small") if ks == "main" or small_shape(sh[0], sh[2], sh[3])]
+
+
+@pytest.mark.parametrize("name,kernels", SMALL_RUNS)
+def test_parity_small_workloads(name, kernels):
+    with kernel_set(kernels):
+        check_case(make_case(WORKLOADS[name]))
+
+
+@pytest.mark.parametrize("shape,kernels", EDGE_RUNS)
 @pytest.mark.parametrize("dtype", ["f32", "bf16", "f16"])
-def test_parity_edge_shapes(shape, dtype):
+def test_parity_edge_shapes(shape, kernels, dtype):
     B, T, D, k = shape
-    check_case(make_custom(B, T, D, k, dtype, seed=B * 31 + T * 7 + D + k, ln_affine="random"))
+    with kernel_set(kernels):
+        check_case(make_custom(B, T, D, k, dtype, seed=B * 31 + T * 7 + D + k, ln_affine="random"))
+
+
+@pytest.mark.parametrize("fwd_set,bwd_set", [("small", "main"), ("main", "small")])
+@pytest.mark.parametrize("name", ["B4_T16_D128_k2_bf16_public", "B8_T8_D64_k2_f32", "B4_T16_D128_k2_f16_public"])
+def test_small_and_main_paths_interchange(name, fwd_set, bwd_set):
+    """Both kernel sets save the same state in the workspace: either backward follows either forward."""
+    import torch
+    case = make_case(WORKLOADS[name])
+    dc = DeviceCase(case)
+    with kernel_set(fwd_set):
+        dc.fwd()
+    with kernel_set(bwd_set):
+        dc.bwd()
+    torch.cuda.synchronize()
+    got = dc.results()
+    ref, _ = oracle_results(case)
+    compare(got, ref, ["y"] + list(GRAD_KEYS), TOL[case["dtype"]], f"{name} fwd {fwd_set} bwd {bwd_set}")
+
+
+def test_small_path_bitwise_repeatable():
+    """Two fwd+bwd runs of the small-batch kernels on identical inputs give identical bits."""
+    case = make_case(WORKLOADS["B4_T16_D128_k2_bf16_public"])
+    with kernel_set("small"):
+        a = DeviceCase(case)
+        a.run()
+        b = DeviceCase(case)
+        b.run()
+        ra, rb_ = a.raw_bits(), b.raw_bits()
+    for k in ra:
+        assert np.array_equal(ra[k], rb_[k]), k
 
 
 def test_bitwise_repeatable():

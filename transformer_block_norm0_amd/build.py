@@ -16,7 +16,7 @@ CSRC = os.path.join(PKG, "csrc")
 INCLUDE = os.path.join(ROOT, "include")
 BUILD = os.path.join(ROOT, "_build")
 LIB = os.path.join(PKG, "librmblock.so")
-SOURCES = ("rm_api.hip", "rm_rows.hip", "rm_gemm.hip", "rm_gemm256.hip")
+SOURCES = ("rm_api.hip", "rm_rows.hip", "rm_gemm.hip", "rm_gemm256.hip", "rm_small.hip")
 ARCH = os.environ.get("RM_OFFLOAD_ARCH", "gfx950")
 
 HIPCC = os.environ.get("HIPCC", "/opt/rocm/bin/hipcc")

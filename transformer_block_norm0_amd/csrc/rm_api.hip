@@ -28,7 +28,7 @@ namespace rm {
 const char* const kKernelNames[KID_COUNT] = {
     "prologue", "gemm_up", "gate_fwd", "gemm_down", "ln2_fwd", "ln2_bwd", "gemm_dhid",
     "gate_bwd", "gemm_dwout", "gemm_dw1", "gemm_dh1", "ln1_bwd", "ln0_bwd", "finalize", "token_mix",
-    "tail_bwd"};
+    "tail_bwd", "small_fwd", "small_bwd", "small_fin"};
 
 bool dims_valid(const rm_dims& d) {
   if (d.dtype != RM_F32 && d.dtype != RM_BF16 && d.dtype != RM_F16) return false;
@@ -145,6 +145,9 @@ rm_status check_common(const rm_dims* dims, const rm_params* p, const void* ws, 
 
 rm_status hip_status(hipError_t e) { return e == hipSuccess ? RM_OK : RM_E_HIP; }
 
+// rm_small_path: whether shapes the small-batch kernels take use them
+int g_small_path = 1;
+
 }  // namespace
 
 extern "C" {
@@ -200,6 +203,7 @@ rm_status rm_block_fwd(const rm_dims* dims, const rm_params* p, const void* x, v
   char* w = reinterpret_cast<char*>(ws);
   const long T = d.T, D = d.D, H = (long)d.k * d.D;
   hipError_t e;
+  if (g_small_path && small_supported(d)) return hip_status(launch_small_fwd(d, *p, x, y, ws, L, s));
 
   if ((e = launch_prologue(d, *p, x, ws, L, s)) != hipSuccess) return hip_status(e);
 
@@ -245,6 +249,7 @@ rm_status rm_block_bwd(const rm_dims* dims, const rm_params* p, const void* x, c
   char* w = reinterpret_cast<char*>(ws);
   const long T = d.T, D = d.D, H = (long)d.k * d.D;
   hipError_t e;
+  if (g_small_path && small_supported(d)) return hip_status(launch_small_bwd(d, *p, x, dy, ws, L, dx, *g, s));
 
   if ((e = launch_ln2_bwd(d, *p, dy, ws, L, s)) != hipSuccess) return hip_status(e);
 
@@ -281,6 +286,12 @@ rm_status rm_block_bwd(const rm_dims* dims, const rm_params* p, const void* x, c
 
   if ((e = launch_tail_bwd(d, *p, x, dx, ws, L, s)) != hipSuccess) return hip_status(e);
   if ((e = launch_finalize(d, *g, ws, L, s)) != hipSuccess) return hip_status(e);
+  return RM_OK;
+}
+
+rm_status rm_small_path(int on) {
+  if (on != 0 && on != 1) return RM_E_ARG;
+  g_small_path = on;
   return RM_OK;
 }
 

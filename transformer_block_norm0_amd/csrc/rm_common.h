@@ -83,6 +83,14 @@ __device__ __forceinline__ void tm_source(int i, int c, int S, int& src_row, int
   src_col = i * S + (c - j * S);
 }
 
+// r1 = token_mix(norm0(x)) + x for one gathered element a of row j (nmr =
+// -mu0[j] rstd0[j], rs = rstd0[j]), the gathered affine gg/bb and the
+// residual xi.  Every forward prologue and norm1 backward uses it, so
+// the backward recomputes the forward's r1 bit for bit.
+__device__ __forceinline__ float mixed_residual(float a, float rs, float nmr, float gg, float bb, float xi) {
+  return fmaf(fmaf(a, rs, nmr), gg, bb) + xi;
+}
+
 // ---------------------------------------------------------------------------
 // reductions (fixed order: deterministic)
 

@@ -40,14 +40,6 @@ __host__ __device__ __forceinline__ const ST* cptr(const void* p) { return reint
 // i*S + c%S of a0, recomputed from x and norm0's statistics (kept in LDS).
 // N = elements per lane chunk; N > 1 needs D % N == 0 and S % N == 0 so a
 // chunk's gather source is N contiguous, aligned elements.
-// r1 = token_mix(norm0(x)) + x for one gathered element a of row j (nmr =
-// -mu0[j] rstd0[j], rs = rstd0[j]), the gathered affine gg/bb and the
-// residual xi.  Both forward prologues and both norm1 backwards use it, so
-// the backward recomputes the forward's r1 bit for bit.
-__device__ __forceinline__ float mixed_residual(float a, float rs, float nmr, float gg, float bb, float xi) {
-  return fmaf(fmaf(a, rs, nmr), gg, bb) + xi;
-}
-
 template <typename ST, int N>
 __global__ __launch_bounds__(512) void k_prologue(const ST* __restrict__ x, const ST* __restrict__ g0,
                                                   const ST* __restrict__ be0, const ST* __restrict__ g1,

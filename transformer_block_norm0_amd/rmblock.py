@@ -79,6 +79,8 @@ def _lib():
         lib.rm_prof_name.restype = ctypes.c_char_p
         lib.rm_prof_collect.argtypes = [P(ctypes.c_double), P(ctypes.c_int64), ctypes.c_int]
         lib.rm_prof_collect.restype = ctypes.c_int
+        lib.rm_small_path.argtypes = [ctypes.c_int]
+        lib.rm_small_path.restype = ctypes.c_int
         _LIB = lib
     return _LIB
 
@@ -86,6 +88,14 @@ def _lib():
 def library():
     """The loaded ctypes library (raises if it has not been built)."""
     return _lib()
+
+
+def small_path(on: bool) -> None:
+    """rm_small_path: let B <= 8, D <= 128, H <= 256 shapes take the small-batch kernels (the default),
+    or send every shape through the main path."""
+    st = _lib().rm_small_path(1 if on else 0)
+    if st:
+        raise RmError(st, "rm_small_path")
 
 
 def dims(B: int, T: int, D: int, k: int, dtype: str) -> CDims:
