@@ -128,6 +128,22 @@ def test_bad_arguments_rejected_before_launch(rb):
         assert lib.rm_status_string(code)
 
 
+def test_small_path_switch(rb):
+    """rm_small_path takes 0 or 1 only; argument checks run before either kernel set is chosen."""
+    lib = rb.library()
+    lib.rm_small_path.argtypes = [ctypes.c_int]
+    assert lib.rm_small_path(2) == 7 and lib.rm_small_path(-1) == 7
+    d, params, grads, wsb = _valid_call_args(rb)  # inside the small-batch envelope
+    by = ctypes.byref
+    try:
+        for on in (0, 1):
+            assert lib.rm_small_path(on) == 0
+            assert lib.rm_block_fwd(by(d), by(params), None, 1024, 4096, wsb, None) == 2
+            assert lib.rm_block_bwd(by(d), by(params), 1024, 1024, 4096, wsb - 256, 2048, by(grads), None) == 4
+    finally:
+        assert lib.rm_small_path(1) == 0
+
+
 def test_no_oracle_or_fallback_in_product_path():
     """The product package never imports the oracle and has no CPU compute path."""
     pkg = os.path.join(ROOT, "transformer_block_norm0_amd")
