@@ -78,7 +78,9 @@ SMALL = [
     ("B256_T16_D256_k3_f16_lnrand", None),
 ]
 EDGE = [  # (B, T, D, k): B=1 minimum dims; S=1; odd D (unaligned bf16 rows); S=160 and H=3840;
-    (1, 8, 64, 2), (2, 64, 64, 3), (3, 13, 65, 3), (5, 8, 1280, 3), (67, 16, 256, 2), (130, 8, 96, 3)]
+    # ragged tiles; the small-batch envelope's maximum (B*T = 512 rows, D = 128, H = 256)
+    (1, 8, 64, 2), (2, 64, 64, 3), (3, 13, 65, 3), (5, 8, 1280, 3), (67, 16, 256, 2), (130, 8, 96, 3),
+    (8, 64, 128, 2)]
 
 
 def check_case(case, intermediates=True):
