@@ -55,6 +55,23 @@ __device__ __forceinline__ float rnd(float v) {
   return to_f32(from_f32<ST>(v));
 }
 
+// 8 consecutive storage elements at a 16-byte aligned address, as fp32
+__device__ __forceinline__ void ld8(const float* p, float (&v)[8]) {
+  const float4 a = reinterpret_cast<const float4*>(p)[0], b = reinterpret_cast<const float4*>(p)[1];
+  v[0] = a.x; v[1] = a.y; v[2] = a.z; v[3] = a.w;
+  v[4] = b.x; v[5] = b.y; v[6] = b.z; v[7] = b.w;
+}
+template <typename ST>
+__device__ __forceinline__ void ld8(const ST* p, float (&v)[8]) {
+  const uint4 q = *reinterpret_cast<const uint4*>(p);
+  const uint32_t w[4] = {q.x, q.y, q.z, q.w};
+#pragma unroll
+  for (int i = 0; i < 4; ++i) {
+    v[2 * i] = lo16<ST>(w[i]);
+    v[2 * i + 1] = hi16<ST>(w[i]);
+  }
+}
+
 // mean and rstd of a row held as v[q] at columns lane + 64 q (< n), two passes
 template <int Q>
 __device__ __forceinline__ void row_stats(const float (&v)[Q], int n, float eps, float& mean, float& rstd) {
@@ -351,15 +368,17 @@ __global__ __launch_bounds__(FWD_THREADS) void k_small_bwd_tok(SmallArgs a) {
   column_sum<ST, QD>(po, D, B, s_tmp, nullptr, reinterpret_cast<ST*>(a.g.bout) + (long)t * D);
   __syncthreads();
 
-  // 2. dwout[t][h][n] = sum_b hidden[b,h] d out2[b,n]
+  // 2. dwout[t][h][n] = sum_b hidden[b,h] d out2[b,n]: thread column n = tid % D,
+  // rows h = tid / D, + FWD_THREADS / D, ... (coalesced stores)
   {
     ST* dwo = reinterpret_cast<ST*>(a.g.wout) + (long)t * H * D;
-    for (long i = tid; i < (long)H * D; i += FWD_THREADS) {
-      const int h = (int)(i / D), n = (int)(i - (long)h * D);
-      float s = 0.f;
-      for (int k = 0; k < B; ++k) s = fmaf(s_hid[k][h], s_do2[k][n], s);
-      st(dwo, i, s);
-    }
+    const int per = FWD_THREADS / D, n = tid % D;
+    if (tid < per * D)
+      for (int h = tid / D; h < H; h += per) {
+        float s = 0.f;
+        for (int k = 0; k < B; ++k) s = fmaf(s_hid[k][h], s_do2[k][n], s);
+        st(dwo, (long)h * D + n, s);
+      }
   }
   // 3. d hidden[b,h] = d out2[b] . wout[t][h], one thread per h, into s_tmp
   // until every thread has read hidden
@@ -437,15 +456,18 @@ __global__ __launch_bounds__(FWD_THREADS) void k_small_bwd_tok(SmallArgs a) {
   }
   __syncthreads();
 
-  // 5. dw1[t][c][n] = sum_b out1[b,c] dZ[b,n]
+  // 5. dw1[t][c][n] = sum_b out1[b,c] dZ[b,n]: thread column n = tid % 2H,
+  // rows c = tid / 2H, + FWD_THREADS / 2H, ... (coalesced stores)
   {
+    static_assert(2 * SH <= FWD_THREADS, "one pass covers every column of dw1");
     ST* dw1 = reinterpret_cast<ST*>(a.g.w1) + (long)t * D * 2 * H;
-    for (long i = tid; i < (long)D * 2 * H; i += FWD_THREADS) {
-      const int c = (int)(i / (2 * H)), n = (int)(i - (long)c * 2 * H);
-      float s = 0.f;
-      for (int k = 0; k < B; ++k) s = fmaf(s_h1[k][c], s_z[k][n], s);
-      st(dw1, i, s);
-    }
+    const int per = FWD_THREADS / (2 * H), n = tid % (2 * H);
+    if (tid < per * 2 * H)
+      for (int c = tid / (2 * H); c < D; c += per) {
+        float s = 0.f;
+        for (int k = 0; k < B; ++k) s = fmaf(s_h1[k][c], s_z[k][n], s);
+        st(dw1, (long)c * 2 * H + n, s);
+      }
   }
   // 6. d out1[b,c] = dZ[b] . w1[t][c] + d out2[b,c].  The threads form
   // FWD_THREADS / D groups of D (one column c each); group g sums its slice
@@ -456,15 +478,32 @@ __global__ __launch_bounds__(FWD_THREADS) void k_small_bwd_tok(SmallArgs a) {
     const ST* w1 = P(a.p.w1) + (long)t * D * 2 * H;
     float* part = s_tmp_buf;  // [NG][SB][D], NG * D <= FWD_THREADS
     const int c = tid % D, grp = tid / D, ns = (2 * H + NG - 1) / NG;
+    // loads of 8 consecutive elements when every slice boundary and the row
+    // length are multiples of 8 (each load then stays inside its slice) and
+    // the rows start 16-byte aligned
+    const bool vec8 = (ns % 8) == 0 && ((2 * H) % 8) == 0 && ((2 * H * (int)sizeof(ST)) % 16) == 0 &&
+                      (reinterpret_cast<uintptr_t>(w1) & 15) == 0;
     if (grp < NG) {
       const int n0 = grp * ns, n1 = min(2 * H, n0 + ns);
       float acc[SB];
 #pragma unroll
       for (int k = 0; k < SB; ++k) acc[k] = 0.f;
-      for (int n = n0; n < n1; ++n) {
-        const float w = ld(w1, (long)c * 2 * H + n);
+      const ST* wr = w1 + (long)c * 2 * H;
+      if (vec8) {
+        for (int n = n0; n < n1; n += 8) {
+          float w[8];
+          ld8(wr + n, w);
 #pragma unroll
-        for (int k = 0; k < SB; ++k) acc[k] = fmaf(s_z[k][n], w, acc[k]);
+          for (int e = 0; e < 8; ++e)
+#pragma unroll
+            for (int k = 0; k < SB; ++k) acc[k] = fmaf(s_z[k][n + e], w[e], acc[k]);
+        }
+      } else {
+        for (int n = n0; n < n1; ++n) {
+          const float w = ld(wr, n);
+#pragma unroll
+          for (int k = 0; k < SB; ++k) acc[k] = fmaf(s_z[k][n], w, acc[k]);
+        }
       }
 #pragma unroll
       for (int k = 0; k < SB; ++k) part[(grp * SB + k) * D + c] = acc[k];
