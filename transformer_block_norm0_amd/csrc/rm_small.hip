@@ -316,7 +316,9 @@ __global__ __launch_bounds__(FWD_THREADS) void k_small_bwd_tok(SmallArgs a) {
   const float* stats = reinterpret_cast<const float*>(a.ws + a.L.stats);
   float* p_ln2 = reinterpret_cast<float*>(a.ws + a.L.p_ln2);    // [2][T][D]: dgamma2, dbeta2
   float* p_gate = reinterpret_cast<float*>(a.ws + a.L.p_gate);  // [4][T][H]: dgamma_x, dbeta_x, dgamma_g, dbeta_g
-  float* p_ln1 = reinterpret_cast<float*>(a.ws + a.L.dz);       // [2][T][D]: dgamma1, dbeta1
+  // [2][T][D]: dgamma1, dbeta1, in the dZ region (dZ stays in LDS here; its
+  // B*T*2H storage elements hold 2*T*D floats for every B >= 1, k >= 2)
+  float* p_ln1 = reinterpret_cast<float*>(a.ws + a.L.dz);
   const int b = wave;
   const long row = (long)b * T + t;
 
