@@ -177,6 +177,38 @@ def test_small_and_main_paths_interchange(name, fwd_set, bwd_set):
     compare(got, ref, ["y"] + list(GRAD_KEYS), TOL[case["dtype"]], f"{name} fwd {fwd_set} bwd {bwd_set}")
 
 
+@pytest.mark.parametrize("shape,kernels", [((8, 64, 128, 2), "small"), ((8, 64, 128, 2), "main"),
+                                            ((1, 8, 64, 2), "small"), ((3, 13, 65, 3), "small"),
+                                            ((3, 13, 65, 3), "main"), ((67, 16, 256, 2), "main")])
+@pytest.mark.parametrize("dtype", ["f32", "bf16"])
+def test_writes_stay_inside_buffers(shape, kernels, dtype):
+    """The workspace and every output live inside larger buffers with guard bytes on both sides:
+    after fwd+bwd the guards are unchanged and the results still match the oracle."""
+    import torch
+    B, T, D, k = shape
+    case = make_custom(B, T, D, k, dtype, seed=B * 17 + T + D + k, ln_affine="random")
+    dc = DeviceCase(case)
+    G = 4096  # guard bytes on each side (a multiple of 256: the workspace stays 256-byte aligned)
+    guards = []
+
+    def guarded(t):
+        nbytes = t.numel() * t.element_size()
+        buf = torch.full((nbytes + 2 * G,), 0xA5, dtype=torch.uint8, device=t.device)
+        guards.append(buf)
+        return buf[G:G + nbytes].view(t.dtype).view(t.shape)
+
+    dc.ws = guarded(dc.ws)
+    dc.y, dc.dx = guarded(dc.y), guarded(dc.dx)
+    dc.grads = {n: guarded(g) for n, g in dc.grads.items()}
+    with kernel_set(kernels):
+        dc.run()
+    for buf in guards:
+        head, tail = buf[:G].cpu().numpy(), buf[-G:].cpu().numpy()
+        assert np.all(head == 0xA5) and np.all(tail == 0xA5)
+    ref, _ = oracle_results(case)
+    compare(dc.results(), ref, ["y"] + list(GRAD_KEYS), TOL[case["dtype"]], f"{case['name']} guarded {kernels}")
+
+
 def test_small_path_bitwise_repeatable():
     """Two fwd+bwd runs of the small-batch kernels on identical inputs give identical bits."""
     case = make_case(WORKLOADS["B4_T16_D128_k2_bf16_public"])
