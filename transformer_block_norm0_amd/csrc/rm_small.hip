@@ -23,6 +23,8 @@
 // the norm0 backward -> dx, and every affine gradient summed over the tokens
 // in a fixed order.  Every sum runs in a fixed order: results are bitwise
 // repeatable.
+#include <type_traits>
+
 #include "rm_common.h"
 #include "rm_internal.h"
 
@@ -69,6 +71,40 @@ __device__ __forceinline__ void ld8(const ST* p, float (&v)[8]) {
   for (int i = 0; i < 4; ++i) {
     v[2 * i] = lo16<ST>(w[i]);
     v[2 * i + 1] = hi16<ST>(w[i]);
+  }
+}
+
+// p[i], p[i+1] = v0, v1 (storage type, round to nearest even) with one store;
+// the caller guarantees p + i is aligned to two elements
+template <typename ST>
+__device__ __forceinline__ void st2(ST* p, long i, float v0, float v1) {
+  if constexpr (std::is_same<ST, float>::value) *reinterpret_cast<float2*>(p + i) = make_float2(v0, v1);
+  else *reinterpret_cast<uint32_t*>(p + i) = pack16x2<ST>(v0, v1);
+}
+
+// rows r = 0 .. nrows-1 of a weight gradient g (row length len, g + r len + n):
+// g[r][n] = sum_k a(k, r) b(k, n) over the token's rows k < B.  One or, for
+// 16-bit storage with len even and g aligned to two elements, two consecutive
+// columns per thread (one 4-byte store for both instead of two 2-byte ones),
+// rows strided over the threads; fixed order k = 0 .. B-1, so either form
+// gives the same bits.
+template <typename ST, typename FA, typename FB>
+__device__ __forceinline__ void weight_grad(ST* g, int nrows, int len, int B, FA a, FB b) {
+  const int tid = threadIdx.x;
+  const bool pairs = sizeof(ST) == 2 && (len % 2) == 0 && (reinterpret_cast<uintptr_t>(g) % (2 * sizeof(ST))) == 0;
+  const int w = pairs ? 2 : 1, ncol = len / w;  // column groups per row
+  const int per = FWD_THREADS / ncol;           // rows per pass (ncol <= FWD_THREADS)
+  if (tid >= per * ncol) return;
+  const int n = (tid % ncol) * w;
+  for (int r = tid / ncol; r < nrows; r += per) {
+    float s0 = 0.f, s1 = 0.f;
+    for (int k = 0; k < B; ++k) {
+      const float ak = a(k, r);
+      s0 = fmaf(ak, b(k, n), s0);
+      if (pairs) s1 = fmaf(ak, b(k, n + 1), s1);
+    }
+    if (pairs) st2(g, (long)r * len + n, s0, s1);
+    else st(g, (long)r * len + n, s0);
   }
 }
 
@@ -370,18 +406,9 @@ __global__ __launch_bounds__(FWD_THREADS) void k_small_bwd_tok(SmallArgs a) {
   column_sum<ST, QD>(po, D, B, s_tmp, nullptr, reinterpret_cast<ST*>(a.g.bout) + (long)t * D);
   __syncthreads();
 
-  // 2. dwout[t][h][n] = sum_b hidden[b,h] d out2[b,n]: thread column n = tid % D,
-  // rows h = tid / D, + FWD_THREADS / D, ... (coalesced stores)
-  {
-    ST* dwo = reinterpret_cast<ST*>(a.g.wout) + (long)t * H * D;
-    const int per = FWD_THREADS / D, n = tid % D;
-    if (tid < per * D)
-      for (int h = tid / D; h < H; h += per) {
-        float s = 0.f;
-        for (int k = 0; k < B; ++k) s = fmaf(s_hid[k][h], s_do2[k][n], s);
-        st(dwo, (long)h * D + n, s);
-      }
-  }
+  // 2. dwout[t][h][n] = sum_b hidden[b,h] d out2[b,n]
+  weight_grad(reinterpret_cast<ST*>(a.g.wout) + (long)t * H * D, H, D, B,
+              [&](int k, int h) { return s_hid[k][h]; }, [&](int k, int n) { return s_do2[k][n]; });
   // 3. d hidden[b,h] = d out2[b] . wout[t][h], one thread per h, into s_tmp
   // until every thread has read hidden
   {
@@ -458,19 +485,10 @@ __global__ __launch_bounds__(FWD_THREADS) void k_small_bwd_tok(SmallArgs a) {
   }
   __syncthreads();
 
-  // 5. dw1[t][c][n] = sum_b out1[b,c] dZ[b,n]: thread column n = tid % 2H,
-  // rows c = tid / 2H, + FWD_THREADS / 2H, ... (coalesced stores)
-  {
-    static_assert(2 * SH <= FWD_THREADS, "one pass covers every column of dw1");
-    ST* dw1 = reinterpret_cast<ST*>(a.g.w1) + (long)t * D * 2 * H;
-    const int per = FWD_THREADS / (2 * H), n = tid % (2 * H);
-    if (tid < per * 2 * H)
-      for (int c = tid / (2 * H); c < D; c += per) {
-        float s = 0.f;
-        for (int k = 0; k < B; ++k) s = fmaf(s_h1[k][c], s_z[k][n], s);
-        st(dw1, (long)c * 2 * H + n, s);
-      }
-  }
+  // 5. dw1[t][c][n] = sum_b out1[b,c] dZ[b,n]
+  static_assert(2 * SH <= FWD_THREADS && SD <= FWD_THREADS, "one pass covers every column of a weight gradient");
+  weight_grad(reinterpret_cast<ST*>(a.g.w1) + (long)t * D * 2 * H, D, 2 * H, B,
+              [&](int k, int c) { return s_h1[k][c]; }, [&](int k, int n) { return s_z[k][n]; });
   // 6. d out1[b,c] = dZ[b] . w1[t][c] + d out2[b,c].  The threads form
   // FWD_THREADS / D groups of D (one column c each); group g sums its slice
   // of the n range into s_tmp (free here) and the slices are added in group
