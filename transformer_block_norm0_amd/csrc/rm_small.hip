@@ -127,7 +127,8 @@ __device__ __forceinline__ void row_stats(const float (&v)[Q], int n, float eps,
   rstd = rsqrtf(wave_sum(s2) / (float)n + eps);
 }
 
-template <typename ST>
+// NB: rows accumulated per output in the contraction loops, a power of two >= B
+template <typename ST, int NB>
 __global__ __launch_bounds__(FWD_THREADS) void k_small_fwd(SmallArgs a) {
   __shared__ float s_mu0[SB * 64], s_rs0[SB * 64];
   __shared__ float s_h1[SB][SD];      // out1, later r2
@@ -202,13 +203,13 @@ __global__ __launch_bounds__(FWD_THREADS) void k_small_fwd(SmallArgs a) {
     const ST* w1 = P(a.p.w1) + (long)t * D * 2 * H;
     ST* z = reinterpret_cast<ST*>(a.ws + a.L.z);
     for (int n = tid; n < 2 * H; n += FWD_THREADS) {
-      float acc[SB];
+      float acc[NB];
 #pragma unroll
-      for (int k = 0; k < SB; ++k) acc[k] = 0.f;
+      for (int k = 0; k < NB; ++k) acc[k] = 0.f;
       for (int c = 0; c < D; ++c) {
         const float w = ld(w1, (long)c * 2 * H + n);
 #pragma unroll
-        for (int k = 0; k < SB; ++k) acc[k] = fmaf(s_h1[k][c], w, acc[k]);  // rows past B: unused
+        for (int k = 0; k < NB; ++k) acc[k] = fmaf(s_h1[k][c], w, acc[k]);  // rows past B: unused
       }
       const float bias = ld(P(a.p.b1), (long)t * 2 * H + n);
       for (int k = 0; k < B; ++k) {
@@ -265,16 +266,16 @@ __global__ __launch_bounds__(FWD_THREADS) void k_small_fwd(SmallArgs a) {
     const int n = tid % D, grp = tid / D, hs = (H + NG - 1) / NG;
     if (grp < NG) {
       const int h0 = grp * hs, h1 = min(H, h0 + hs);
-      float acc[SB];
+      float acc[NB];
 #pragma unroll
-      for (int k = 0; k < SB; ++k) acc[k] = 0.f;
+      for (int k = 0; k < NB; ++k) acc[k] = 0.f;
       for (int h = h0; h < h1; ++h) {
         const float w = ld(wo, (long)h * D + n);
 #pragma unroll
-        for (int k = 0; k < SB; ++k) acc[k] = fmaf(s_hid[k][h], w, acc[k]);
+        for (int k = 0; k < NB; ++k) acc[k] = fmaf(s_hid[k][h], w, acc[k]);
       }
 #pragma unroll
-      for (int k = 0; k < SB; ++k) part[(grp * SB + k) * D + n] = acc[k];
+      for (int k = 0; k < NB; ++k) part[(grp * SB + k) * D + n] = acc[k];
     }
     __syncthreads();
     ST* r2 = reinterpret_cast<ST*>(a.ws + a.L.r2);
@@ -334,7 +335,7 @@ __device__ __forceinline__ void column_sum(const float (&v)[Q], int n, int B, fl
   }
 }
 
-template <typename ST>
+template <typename ST, int NB>
 __global__ __launch_bounds__(FWD_THREADS) void k_small_bwd_tok(SmallArgs a) {
   __shared__ float s_do2[SB][SD];
   __shared__ float s_hid[SB][SH];   // hidden, later d hidden
@@ -414,13 +415,13 @@ __global__ __launch_bounds__(FWD_THREADS) void k_small_bwd_tok(SmallArgs a) {
   {
     const ST* wo = P(a.p.wout) + (long)t * H * D;
     for (int h = tid; h < H; h += FWD_THREADS) {
-      float acc[SB];
+      float acc[NB];
 #pragma unroll
-      for (int k = 0; k < SB; ++k) acc[k] = 0.f;
+      for (int k = 0; k < NB; ++k) acc[k] = 0.f;
       for (int n = 0; n < D; ++n) {
         const float w = ld(wo, (long)h * D + n);
 #pragma unroll
-        for (int k = 0; k < SB; ++k) acc[k] = fmaf(s_do2[k][n], w, acc[k]);
+        for (int k = 0; k < NB; ++k) acc[k] = fmaf(s_do2[k][n], w, acc[k]);
       }
       for (int k = 0; k < B; ++k) s_tmp[k][h] = rnd<ST>(acc[k]);
     }
@@ -505,9 +506,9 @@ __global__ __launch_bounds__(FWD_THREADS) void k_small_bwd_tok(SmallArgs a) {
                       (reinterpret_cast<uintptr_t>(w1) & 15) == 0;
     if (grp < NG) {
       const int n0 = grp * ns, n1 = min(2 * H, n0 + ns);
-      float acc[SB];
+      float acc[NB];
 #pragma unroll
-      for (int k = 0; k < SB; ++k) acc[k] = 0.f;
+      for (int k = 0; k < NB; ++k) acc[k] = 0.f;
       const ST* wr = w1 + (long)c * 2 * H;
       if (vec8) {
         for (int n = n0; n < n1; n += 8) {
@@ -516,17 +517,17 @@ __global__ __launch_bounds__(FWD_THREADS) void k_small_bwd_tok(SmallArgs a) {
 #pragma unroll
           for (int e = 0; e < 8; ++e)
 #pragma unroll
-            for (int k = 0; k < SB; ++k) acc[k] = fmaf(s_z[k][n + e], w[e], acc[k]);
+            for (int k = 0; k < NB; ++k) acc[k] = fmaf(s_z[k][n + e], w[e], acc[k]);
         }
       } else {
         for (int n = n0; n < n1; ++n) {
           const float w = ld(wr, n);
 #pragma unroll
-          for (int k = 0; k < SB; ++k) acc[k] = fmaf(s_z[k][n], w, acc[k]);
+          for (int k = 0; k < NB; ++k) acc[k] = fmaf(s_z[k][n], w, acc[k]);
         }
       }
 #pragma unroll
-      for (int k = 0; k < SB; ++k) part[(grp * SB + k) * D + c] = acc[k];
+      for (int k = 0; k < NB; ++k) part[(grp * SB + k) * D + c] = acc[k];
     }
     __syncthreads();
     for (int i = tid; i < B * D; i += FWD_THREADS) {
@@ -671,10 +672,26 @@ __global__ __launch_bounds__(FIN_THREADS) void k_small_bwd_fin(SmallArgs a) {
   }
 }
 
+// the kernel instance for the batch: rows accumulated = B rounded up to 1, 2, 4 or 8
+template <typename ST>
+void launch_fwd_rows(const SmallArgs& a, hipStream_t s) {
+  if (a.B <= 1) hipLaunchKernelGGL((k_small_fwd<ST, 1>), dim3(a.T), dim3(FWD_THREADS), 0, s, a);
+  else if (a.B <= 2) hipLaunchKernelGGL((k_small_fwd<ST, 2>), dim3(a.T), dim3(FWD_THREADS), 0, s, a);
+  else if (a.B <= 4) hipLaunchKernelGGL((k_small_fwd<ST, 4>), dim3(a.T), dim3(FWD_THREADS), 0, s, a);
+  else hipLaunchKernelGGL((k_small_fwd<ST, SB>), dim3(a.T), dim3(FWD_THREADS), 0, s, a);
+}
+template <typename ST>
+void launch_bwd_rows(const SmallArgs& a, hipStream_t s) {
+  if (a.B <= 1) hipLaunchKernelGGL((k_small_bwd_tok<ST, 1>), dim3(a.T), dim3(FWD_THREADS), 0, s, a);
+  else if (a.B <= 2) hipLaunchKernelGGL((k_small_bwd_tok<ST, 2>), dim3(a.T), dim3(FWD_THREADS), 0, s, a);
+  else if (a.B <= 4) hipLaunchKernelGGL((k_small_bwd_tok<ST, 4>), dim3(a.T), dim3(FWD_THREADS), 0, s, a);
+  else hipLaunchKernelGGL((k_small_bwd_tok<ST, SB>), dim3(a.T), dim3(FWD_THREADS), 0, s, a);
+}
+
 template <typename ST>
 hipError_t small_fwd_t(const SmallArgs& a, hipStream_t s) {
   prof_begin(KID_SMALL_FWD, s);
-  hipLaunchKernelGGL(k_small_fwd<ST>, dim3(a.T), dim3(FWD_THREADS), 0, s, a);
+  launch_fwd_rows<ST>(a, s);
   prof_end(KID_SMALL_FWD, s);
   return hipGetLastError();
 }
@@ -682,7 +699,7 @@ hipError_t small_fwd_t(const SmallArgs& a, hipStream_t s) {
 template <typename ST>
 hipError_t small_bwd_t(const SmallArgs& a, hipStream_t s) {
   prof_begin(KID_SMALL_BWD, s);
-  hipLaunchKernelGGL(k_small_bwd_tok<ST>, dim3(a.T), dim3(FWD_THREADS), 0, s, a);
+  launch_bwd_rows<ST>(a, s);
   prof_end(KID_SMALL_BWD, s);
   hipError_t e = hipGetLastError();
   if (e != hipSuccess) return e;
