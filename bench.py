@@ -164,7 +164,6 @@ def main():
         print("bench.py: no GPU visible", file=sys.stderr)
         sys.exit(1)
     rb.library()
-    rb.small_path(args.kernels == "auto")
 
     w = WORKLOADS[args.workload]
     d = w.dims
@@ -172,7 +171,7 @@ def main():
     case = make_case(w)
     sys.path.insert(0, os.path.join(ROOT, "tests"))
     from rm_gpu import DeviceCase  # noqa: E402  (moves the case to the device, calls the C ABI)
-    dc = DeviceCase(case)
+    dc = DeviceCase(case, kernels=args.kernels)
     del case
     torch.cuda.synchronize()
     stream = torch.cuda.current_stream()

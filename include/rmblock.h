@@ -25,6 +25,10 @@
  *     (except the instrumentation calls rm_prof_*, which say so).
  *   - `stream` is a hipStream_t (0 = the null stream) of the current device.
  *     Work is enqueued on it; results are valid once the caller syncs it.
+ *   - Apart from the instrumentation records (rm_prof_*), the library keeps
+ *     no state between calls: everything a call does is fixed by its
+ *     arguments, so calls on distinct streams with distinct workspaces may run
+ *     from several threads at once.
  *   - Validation (dims, dtype, null pointers, alignment, workspace size) runs
  *     on the host before anything is enqueued; on failure nothing is launched
  *     and the status says why.  RM_E_HIP means a launch failed.
@@ -43,7 +47,7 @@
 extern "C" {
 #endif
 
-#define RM_ABI_VERSION 1
+#define RM_ABI_VERSION 2
 
 /* Storage dtypes.  Besides the bf16 production workload, the page's section
  * "Run the benchmark" runs the block with fp32 and fp16 storage; every
@@ -61,10 +65,21 @@ typedef enum {
   RM_E_ARG = 7         /* any other invalid argument                            */
 } rm_status;
 
-/* Block dimensions.  H = k*D.  dtype is an rm_dtype value. */
+/* Kernel-set choice, per call (rm_dims.flags).  By default (0) shapes with
+ * B <= 8, D <= 128 and H <= 256 run the same computation (page 1, "Exact
+ * computation") as one launch for the forward (one workgroup per token, its
+ * rows in LDS) and two for the backward, instead of one launch per fused
+ * step; every other shape takes the main kernels.  RM_FLAG_MAIN_KERNELS sends
+ * the call through the main kernels whatever the shape.  Both kernel sets save
+ * the same state in ws, so either backward may follow either forward.  Any
+ * other bit set: RM_E_ARG. */
+#define RM_FLAG_MAIN_KERNELS 1
+
+/* Block dimensions.  H = k*D.  dtype is an rm_dtype value; flags holds RM_FLAG_* bits. */
 typedef struct {
   int32_t B, T, D, k;
   int32_t dtype;
+  int32_t flags;
 } rm_dims;
 
 /* Parameters (device pointers, storage dtype):
@@ -103,16 +118,6 @@ rm_status rm_block_fwd(const rm_dims* dims, const rm_params* p, const void* x, v
 rm_status rm_block_bwd(const rm_dims* dims, const rm_params* p, const void* x, const void* dy,
                        void* ws, size_t ws_bytes, void* dx, const rm_grads* g, void* stream);
 
-/* Small-batch path (on by default).  For B <= 8, D <= 128 and H <= 256 the
- * same computation (page 1, "Exact computation") runs as one launch for the
- * forward (one workgroup per token, its rows in LDS) and two for the
- * backward, instead of one launch per fused step; the saved state in ws is
- * the same, so either backward may follow either forward.  on = 0 sends
- * every shape through the main path, 1 (the default) lets the shapes above
- * take the small path.  Process-wide setting, read at each rm_block_fwd /
- * rm_block_bwd call; RM_E_ARG for any other value. */
-rm_status rm_small_path(int on);
-
 /* Token mixing alone (page 1, "Exact computation", token mixing paragraph):
  * out[b,i,j*S+s] = in[b,j,i*S+s], S = D/T.  A pure permutation of element bits
  * (no arithmetic), through the same device index function the block uses.
@@ -136,10 +141,11 @@ int rm_abi_version(void);
 
 /* Instrumentation.  While enabled, every kernel launched by rm_block_fwd /
  * rm_block_bwd is bracketed by two hipEvents recorded on the caller's stream
- * (creating events as needed: this mode allocates).  rm_prof_collect
- * synchronises those events, adds their elapsed times per kernel id into
- * ms[id] and launches[id] (arrays of rm_prof_kernels() entries) and releases
- * the pending records. */
+ * (creating events as needed: this mode allocates).  Open brackets are kept
+ * per stream, so calls on several streams from several threads pair their
+ * events correctly.  rm_prof_collect synchronises those events, adds their
+ * elapsed times per kernel id into ms[id] and launches[id] (arrays of
+ * rm_prof_kernels() entries) and releases the pending records. */
 rm_status rm_prof_enable(int on);
 int rm_prof_kernels(void);
 const char* rm_prof_name(int id);

@@ -38,13 +38,13 @@ def from_torch(t, dtype: str) -> np.ndarray:
 class DeviceCase:
     """A case's tensors on the device plus output buffers and the workspace."""
 
-    def __init__(self, case: dict, device="cuda"):
+    def __init__(self, case: dict, device="cuda", kernels="auto"):
         import torch
         import transformer_block_norm0_amd as rb
         self.case = case
         self.dtype = case["dtype"]
         d = case["dims"]
-        self.cd = rb.dims(d.B, d.T, d.D, d.k, self.dtype)
+        self.cd = rb.dims(d.B, d.T, d.D, d.k, self.dtype, kernels)
         self.params = {n: to_torch(v, self.dtype, device) for n, v in case["params"].items()}
         self.x = to_torch(case["x"], self.dtype, device)
         self.dy = to_torch(case["dy"], self.dtype, device)
@@ -65,13 +65,21 @@ class DeviceCase:
             assert v.data_ptr() % 16 != 0
             setattr(self, name, v)
 
-    def fwd(self, stream=None):
+    def _dims(self, kernels):
         import transformer_block_norm0_amd as rb
-        rb.block_fwd(self.cd, self.params, self.x, self.y, self.ws, stream=stream)
+        if kernels is None:
+            return self.cd
+        c = self.cd
+        return rb.dims(c.B, c.T, c.D, c.k, self.dtype, kernels)
 
-    def bwd(self, stream=None):
+    def fwd(self, stream=None, kernels=None):
+        """rm_block_fwd; kernels ("auto" / "main") overrides the case's kernel set for this call."""
         import transformer_block_norm0_amd as rb
-        rb.block_bwd(self.cd, self.params, self.x, self.dy, self.ws, self.dx, self.grads, stream=stream)
+        rb.block_fwd(self._dims(kernels), self.params, self.x, self.y, self.ws, stream=stream)
+
+    def bwd(self, stream=None, kernels=None):
+        import transformer_block_norm0_amd as rb
+        rb.block_bwd(self._dims(kernels), self.params, self.x, self.dy, self.ws, self.dx, self.grads, stream=stream)
 
     def run(self):
         import torch
@@ -110,6 +118,10 @@ def rel_err(got: np.ndarray, ref: np.ndarray) -> float:
     assert got.shape == ref.shape, (got.shape, ref.shape)
     den = max(float(np.max(np.abs(ref))), 1e-30)
     return float(np.max(np.abs(got - ref))) / den
+
+
+# (label, {tensor: error}) of every full-size comparison, printed in pytest's terminal summary
+FULL_SIZE_REPORT: list = []
 
 
 def compare(got: dict, ref: dict, keys, tol: float, label: str) -> dict:

@@ -36,7 +36,7 @@ def test_library_exports_every_declared_symbol(rb):
     lib = rb.library()
     for name in header_functions():
         assert hasattr(lib, name), f"{name} declared in rmblock.h but not exported"
-    assert lib.rm_abi_version() == 1
+    assert lib.rm_abi_version() == 2
 
 
 def tail_per_sample(B, T, D, dtype):
@@ -128,20 +128,33 @@ def test_bad_arguments_rejected_before_launch(rb):
         assert lib.rm_status_string(code)
 
 
-def test_small_path_switch(rb):
-    """rm_small_path takes 0 or 1 only; argument checks run before either kernel set is chosen."""
+def test_kernel_set_flag_is_per_call(rb):
+    """The kernel set is a field of each call's rm_dims (no process-wide switch): unknown flag
+    bits are rejected, and argument checks run before either kernel set is chosen."""
     lib = rb.library()
-    lib.rm_small_path.argtypes = [ctypes.c_int]
-    assert lib.rm_small_path(2) == 7 and lib.rm_small_path(-1) == 7
+    assert not hasattr(lib, "rm_small_path")
     d, params, grads, wsb = _valid_call_args(rb)  # inside the small-batch envelope
     by = ctypes.byref
-    try:
-        for on in (0, 1):
-            assert lib.rm_small_path(on) == 0
-            assert lib.rm_block_fwd(by(d), by(params), None, 1024, 4096, wsb, None) == 2
-            assert lib.rm_block_bwd(by(d), by(params), 1024, 1024, 4096, wsb - 256, 2048, by(grads), None) == 4
-    finally:
-        assert lib.rm_small_path(1) == 0
+    for flags in (2, 4, -1, 1 << 30):
+        d.flags = flags
+        assert lib.rm_block_fwd(by(d), by(params), 1024, 1024, 4096, wsb, None) == 7
+        assert lib.rm_block_bwd(by(d), by(params), 1024, 1024, 4096, wsb, 2048, by(grads), None) == 7
+        assert lib.rm_token_mix(by(d), 1024, 2048, None) == 7
+    for flags in (0, rb.rmblock.RM_FLAG_MAIN_KERNELS):
+        d.flags = flags
+        assert lib.rm_block_fwd(by(d), by(params), None, 1024, 4096, wsb, None) == 2
+        assert lib.rm_block_bwd(by(d), by(params), 1024, 1024, 4096, wsb - 256, 2048, by(grads), None) == 4
+    assert rb.dims(4, 16, 128, 2, "bf16").flags == 0
+    assert rb.dims(4, 16, 128, 2, "bf16", "main").flags == 1
+
+
+def test_profiler_pairs_events_per_stream():
+    """The instrumentation keeps its open event brackets per stream (a list searched by stream
+    and kernel id), not one process-wide open slot."""
+    src = open(os.path.join(ROOT, "transformer_block_norm0_amd", "csrc", "rm_api.hip")).read()
+    assert "g_open_evt" not in src and "g_open_kid" not in src
+    assert "std::vector<OpenRec> g_open" in src
+    assert "g_open[i].s != s || g_open[i].kid != kid" in src
 
 
 def test_no_oracle_or_fallback_in_product_path():

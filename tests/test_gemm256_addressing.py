@@ -1,0 +1,262 @@
+"""Host replica of the 256x256-tile GEMM's address generation (CPU only).
+
+The index formulas of transformer_block_norm0_amd/csrc/rm_gemm256.hip are
+restated here in NumPy: the persistent, XCD-aware tile schedule (which tiles
+each workgroup takes), tile_of, the per-lane slab offsets of both operand
+layouts (K-major rows with the (row/2)%8 chunk swizzle, M/N-major k-rows with
+the 4*(k%4) swizzle), the per-slab offset, the bias copy, the residual loads
+and the epilogue stores.  For every 16-bit GEMM of the block that the kernel
+takes, over a grid of shapes inside the envelope of page 1 ("Public checks and
+instructor coverage"), the test checks that
+
+  * every tile of every token is visited exactly once by the schedule;
+  * every 16-byte copy reads 8 valid elements of the token's operand (clamped
+    rows or columns are valid ones), and lies inside the buffer resource the
+    kernel builds for that operand, so the range check never zeroes data;
+  * each slab's copies fill each LDS stage exactly once, and the fragment
+    reads find there the element the swizzle says;
+  * the bias copy, the residual loads and the epilogue stores stay inside
+    their tensors, and the stores write every element of C exactly once.
+
+The forward and backward GEMM arguments are those the library passes
+(page 1, "Exact computation": one GEMM per token t, activations [B,T,.]
+row-major with the token stride between rows)."""
+from __future__ import annotations
+
+import itertools
+
+import numpy as np
+import pytest
+
+BM = BN = 256
+BK = 64
+CUS = 256   # MI355X compute units
+
+
+def gemms_of_block(B, T, D, k):
+    """The six GEMMs of one forward+backward with the library's operand layouts.
+
+    Returns name -> dict(M, N, K, batch, a_kmajor, b_kmajor, A, a_bs, a_ld, B, b_bs, b_ld,
+    C, c_bs, c_ld, bias, bias_bs, res, res_bs, res_ld) with tensors named by what they
+    hold; tensor sizes in elements are in the second return value."""
+    H = k * D
+    N = B * T
+    sizes = {"h1": N * D, "Z": N * 2 * H, "hid": N * H, "r2": N * D, "do2": N * D, "dhid": N * H,
+             "dZ": N * 2 * H, "dh1": N * D, "w1": T * D * 2 * H, "b1": T * 2 * H, "wout": T * H * D,
+             "bout": T * D, "dw1": T * D * 2 * H, "dwout": T * H * D}
+    g = {}
+    g["up"] = dict(M=B, N=2 * H, K=D, a_kmajor=True, b_kmajor=False, A="h1", a_bs=D, a_ld=T * D,
+                   B="w1", b_bs=D * 2 * H, b_ld=2 * H, C="Z", c_bs=2 * H, c_ld=T * 2 * H,
+                   bias="b1", bias_bs=2 * H, res=None)
+    g["down"] = dict(M=B, N=D, K=H, a_kmajor=True, b_kmajor=False, A="hid", a_bs=H, a_ld=T * H,
+                     B="wout", b_bs=H * D, b_ld=D, C="r2", c_bs=D, c_ld=T * D,
+                     bias="bout", bias_bs=D, res="h1", res_bs=D, res_ld=T * D)
+    g["dhid"] = dict(M=B, N=H, K=D, a_kmajor=True, b_kmajor=True, A="do2", a_bs=D, a_ld=T * D,
+                     B="wout", b_bs=H * D, b_ld=D, C="dhid", c_bs=H, c_ld=T * H, bias=None, res=None)
+    g["dwout"] = dict(M=H, N=D, K=B, a_kmajor=False, b_kmajor=False, A="hid", a_bs=H, a_ld=T * H,
+                      B="do2", b_bs=D, b_ld=T * D, C="dwout", c_bs=H * D, c_ld=D, bias=None, res=None)
+    g["dw1"] = dict(M=D, N=2 * H, K=B, a_kmajor=False, b_kmajor=False, A="h1", a_bs=D, a_ld=T * D,
+                    B="dZ", b_bs=2 * H, b_ld=T * 2 * H, C="dw1", c_bs=D * 2 * H, c_ld=2 * H,
+                    bias=None, res=None)
+    g["dh1"] = dict(M=B, N=D, K=2 * H, a_kmajor=True, b_kmajor=True, A="dZ", a_bs=2 * H, a_ld=T * 2 * H,
+                    B="w1", b_bs=D * 2 * H, b_ld=2 * H, C="dh1", c_bs=D, c_ld=T * D,
+                    bias=None, res="do2", res_bs=D, res_ld=T * D)
+    for v in g.values():
+        v["batch"] = T
+    return g, sizes
+
+
+def supported(g):
+    """The kernel's eligibility test for 16-bit operands and output (all base pointers 256-byte
+    aligned, as the workspace regions and tensor allocations are)."""
+    M, N, K = g["M"], g["N"], g["K"]
+    if K % (2 * BK) or K < 4 * BK:
+        return False
+    a_cont = K if g["a_kmajor"] else M
+    b_cont = K if g["b_kmajor"] else N
+    if a_cont % 8 or b_cont % 8 or g["a_ld"] % 8 or g["b_ld"] % 8 or g["a_bs"] % 8 or g["b_bs"] % 8:
+        return False
+    if (not g["a_kmajor"] and M < 8) or (not g["b_kmajor"] and N < 8):
+        return False
+    a_rows = M if g["a_kmajor"] else K
+    b_rows = N if g["b_kmajor"] else K
+    if a_rows * g["a_ld"] * 2 > 0xFFFFFFFF or b_rows * g["b_ld"] * 2 > 0xFFFFFFFF:
+        return False
+    if N % 8 or g["c_ld"] % 4 or g["c_bs"] % 4:
+        return False
+    if g["bias"] and g["bias_bs"] % 8:
+        return False
+    if g["res"] and (g["res_ld"] % 4 or g["res_bs"] % 4):
+        return False
+    if M * g["c_ld"] * 2 > 0x7FFFFFFF:
+        return False
+    if g["res"] and M * g["res_ld"] * 2 > 0x7FFFFFFF:
+        return False
+    return True
+
+
+def schedule(M, N, batch):
+    """Logical tiles each workgroup takes, in order: list of arrays."""
+    tiles_m, tiles_n = -(-M // BM), -(-N // BN)
+    total = tiles_m * tiles_n * batch
+    grid = max(8, CUS & ~7)
+    grid = min(grid, (total + 7) & ~7)
+    nslots = grid >> 3
+    q, rem = total >> 3, total & 7
+    out = []
+    for blk in range(grid):
+        xcd, slot = blk & 7, blk >> 3
+        lo = xcd * q + min(xcd, rem)
+        hi = lo + q + (1 if xcd < rem else 0)
+        out.append(np.arange(lo + slot, hi, nslots))
+    return out, tiles_m, tiles_n
+
+
+def tile_of(logical, tiles_m, per_t):
+    t = logical // per_t
+    in_t = logical - t * per_t
+    tn = in_t // tiles_m
+    return t, (in_t - tn * tiles_m) * BM, tn * BN
+
+
+def operand_extent(kmajor, ld, K, MN):
+    return ((MN - 1) * ld + K) * 2 if kmajor else ((K - 1) * ld + MN) * 2
+
+
+def slab_offsets(kmajor, ld, mn0, MN):
+    """Per (wave, i, lane): byte offset, element row/col of the piece, and its LDS byte address
+    within the stage, for the slab at k0 = 0.  Arrays of shape [4, 8, 64]."""
+    wave, i, lane = np.meshgrid(np.arange(4), np.arange(8), np.arange(64), indexing="ij")
+    if kmajor:
+        row = 64 * wave + 8 * i + (lane >> 3)
+        chunk = (lane & 7) ^ ((row >> 1) & 7)
+        mn = np.minimum(mn0 + row, MN - 1)
+        off = (mn * ld + chunk * 8) * 2
+        lds = (64 * wave + 8 * i) * 128 + 16 * lane
+        return off, mn, chunk * 8, lds, row      # row: tile row of the piece (k within slab = chunk*8..)
+    krow = 16 * wave + 2 * i + (lane >> 5)
+    chunk = (lane & 31) ^ ((krow & 3) << 2)
+    mn = np.minimum(mn0 + chunk * 8, MN - 8)
+    off = (krow * ld + mn) * 2
+    lds = (16 * wave + 2 * i) * 512 + 16 * lane
+    return off, mn, krow, lds, chunk
+
+
+def kswz(row, chunk):
+    return row * 128 + ((chunk ^ ((row >> 1) & 7)) << 4)
+
+
+def mswz(krow, chunk):
+    return krow * 512 + ((chunk ^ ((krow & 3) << 2)) << 4)
+
+
+def check_operand(kmajor, ld, bs, K, MN, mn0, batch, total_elems):
+    ext = operand_extent(kmajor, ld, K, MN)
+    # the resource of the last token stays inside the tensor
+    assert (batch - 1) * bs * 2 + ext <= total_elems * 2
+    off, mn, sub, lds, slot = slab_offsets(kmajor, ld, mn0, MN)
+    nk = K // BK
+    # every LDS byte of the 32 KB stage is written exactly once per slab
+    assert np.array_equal(np.sort(lds.ravel()), np.arange(0, 256 * BK * 2, 16))
+    if kmajor:
+        # LDS slot holds row `slot` (tile-local), logical chunk sub/8; the fragment read of
+        # that (row, chunk) addresses the same slot
+        assert np.array_equal(kswz(slot, sub // 8), lds)
+        assert np.all(mn < MN) and np.all(mn >= 0)
+    else:
+        assert np.array_equal(mswz(sub, slot), lds)
+        assert np.all(mn >= 0) and np.all(mn + 7 < MN)
+    for ks in (0, nk - 1):
+        k0 = ks * BK
+        koff = k0 * 2 if kmajor else k0 * ld * 2
+        byte = off + koff
+        assert np.all(byte >= 0) and np.all(byte + 16 <= ext), "copy outside the operand resource"
+        assert np.all(byte + 16 <= 0xFFFFFFFF)
+        if kmajor:
+            assert np.all(k0 + sub + 7 < K)
+        else:
+            assert np.all(k0 + sub < K)
+
+
+def check_epilogue(g, m0, n0, written, sizes):
+    M, N = g["M"], g["N"]
+    lane = np.arange(64)
+    r, h = lane & 31, lane >> 5
+    c_ext = min(M * g["c_ld"] * 2, 0x7FFFFFFF)
+    for wave in range(4):
+        wm, wn = wave >> 1, wave & 1
+        mb = m0 + wm * 128 + r
+        for i, j, q in itertools.product(range(4), range(4), (0, 2)):
+            m = mb + 32 * i
+            ns = n0 + wn * 128 + 32 * j + 8 * (q + h)
+            ok = (m < M) & (ns < N)
+            co = m * g["c_ld"] * 2 + ns * 2
+            assert np.all(co[ok] + 16 <= c_ext)
+            np.add.at(written, (m[ok][:, None], ns[ok][:, None] + np.arange(8)), 1)
+        if g["res"]:
+            r_ext = M * g["res_ld"] * 2
+            for i, j, q in itertools.product(range(4), range(4), range(4)):
+                m = mb + 32 * i
+                n = n0 + wn * 128 + 4 * h + 32 * j + 8 * q
+                ok = (m < M) & (n < N)
+                ro = m * g["res_ld"] * 2 + n * 2
+                assert np.all(n[ok] + 3 < N) and np.all(ro[ok] + 8 <= r_ext)
+    if g["bias"]:
+        n = np.minimum(n0 + 8 * (lane & 31), N - 8)
+        assert np.all(n >= 0) and np.all(n * 2 + 16 <= N * 2)
+
+
+def check_gemm(name, g, sizes):
+    M, N, K, batch = g["M"], g["N"], g["K"], g["batch"]
+    sched, tiles_m, tiles_n = schedule(M, N, batch)
+    per_t = tiles_m * tiles_n
+    visited = np.concatenate(sched)
+    assert np.array_equal(np.sort(visited), np.arange(per_t * batch)), f"{name}: schedule"
+    # the kernel's own copies of the next tile use the next logical tile of the same slot
+    assert (batch - 1) * g["c_bs"] * 2 + M * g["c_ld"] * 2 >= 0
+    # last token's C region inside the tensor
+    assert (batch - 1) * g["c_bs"] + (M - 1) * g["c_ld"] + N <= sizes[g["C"]]
+    if g["res"]:
+        assert (batch - 1) * g["res_bs"] + (M - 1) * g["res_ld"] + N <= sizes[g["res"]]
+    if g["bias"]:
+        assert (batch - 1) * g["bias_bs"] + N <= sizes[g["bias"]]
+    written = np.zeros((M, N), dtype=np.int32)
+    for logical in range(per_t):      # one token's tiles; other tokens differ by the base only
+        t, m0, n0 = tile_of(logical, tiles_m, per_t)
+        assert t == 0
+        check_operand(g["a_kmajor"], g["a_ld"], g["a_bs"], K, M, m0, batch, sizes[g["A"]])
+        check_operand(g["b_kmajor"], g["b_ld"], g["b_bs"], K, N, n0, batch, sizes[g["B"]])
+        check_epilogue(g, m0, n0, written, sizes)
+    assert np.all(written == 1), f"{name}: epilogue coverage"
+
+
+SHAPES = [  # (B, T, D, k): the production shape, the envelope's corners, tile tails of every size
+    (1024, 64, 1280, 2), (1024, 64, 1280, 3), (1024, 32, 512, 2), (256, 16, 256, 3), (1024, 40, 1000, 3),
+    (512, 16, 640, 3), (384, 8, 384, 3), (300, 8, 384, 3), (256, 8, 64, 2), (128, 8, 72, 3),
+    (640, 8, 136, 2), (896, 64, 1216, 3), (1000, 40, 1120, 2), (768, 16, 1280, 2), (257, 32, 1024, 3),
+    (128, 64, 128, 2), (1024, 8, 1272, 3), (512, 32, 992, 2)]
+
+
+@pytest.mark.parametrize("shape", SHAPES)
+def test_gemm256_addresses_stay_in_bounds(shape):
+    B, T, D, k = shape
+    gemms, sizes = gemms_of_block(B, T, D, k)
+    taken = 0
+    for name, g in gemms.items():
+        if supported(g):
+            check_gemm(name, g, sizes)
+            taken += 1
+    if shape in ((1024, 64, 1280, 2), (1024, 32, 512, 2)):
+        assert taken == 6
+
+
+def test_replica_catches_a_planted_slip():
+    """The checks are not vacuous: a copy offset one row too far fails them."""
+    B, T, D, k = 384, 8, 384, 3
+    gemms, sizes = gemms_of_block(B, T, D, k)
+    g = gemms["dwout"]
+    ext = operand_extent(False, g["a_ld"], g["K"], g["M"])
+    off, *_ = slab_offsets(False, g["a_ld"], 2 * BM, g["M"])
+    koff = (g["K"] // BK - 1) * BK * g["a_ld"] * 2
+    assert np.all(off + koff + 16 <= ext)
+    assert not np.all(off + koff + g["a_ld"] * 2 * BK + 16 <= ext)

@@ -4,14 +4,13 @@ Metric per tensor: max |gpu - oracle| / max |oracle|; bound 1e-4 for fp32
 storage and 3e-2 for bf16 storage (fp32 accumulation in both).  Every output
 must be finite.  Token mixing is compared bit for bit.
 """
-import contextlib
-
 import numpy as np
 import pytest
 
 import oracle
 from rankmixer_inputs import WORKLOADS, as_f64, make_case, make_custom
-from rm_gpu import GRAD_KEYS, TOL, DeviceCase, compare, say
+from oracle_chunked import oracle_by_chunks
+from rm_gpu import FULL_SIZE_REPORT, GRAD_KEYS, TOL, DeviceCase, compare, say
 
 pytestmark = pytest.mark.gpu
 
@@ -83,10 +82,10 @@ EDGE = [  # (B, T, D, k): B=1 minimum dims; S=1; odd D (unaligned bf16 rows); S=
     (8, 64, 128, 2)]
 
 
-def check_case(case, intermediates=True):
-    label = case["name"]
+def check_case(case, intermediates=True, kernels="auto"):
+    label = f"{case['name']} ({kernels} kernels)"
     say(f"case {label}: gpu fwd+bwd")
-    dc = DeviceCase(case)
+    dc = DeviceCase(case, kernels=kernels)
     dc.run()
     got = dc.results()
     say(f"case {label}: oracle")
@@ -125,20 +124,16 @@ def dbeta0_summand_scale(case, cache):
 
 # ---------------------------------------------------------------------------
 # the two kernel sets: shapes inside B <= 8, D <= 128, H <= 256 take the
-# small-batch kernels by default (rm_small_path); "main" forces the main path
+# small-batch kernels by default; rm_dims.flags = RM_FLAG_MAIN_KERNELS ("main")
+# sends a call through the main kernels.  "small" below names the default on
+# such a shape.
 
 def small_shape(B, D, k):
     return B <= 8 and D <= 128 and k * D <= 256
 
 
-@contextlib.contextmanager
-def kernel_set(which):
-    import transformer_block_norm0_amd as rb
-    rb.small_path(which == "small")
-    try:
-        yield
-    finally:
-        rb.small_path(True)
+def kernel_flag(which):
+    return "main" if which == "main" else "auto"
 
 
 SMALL_RUNS = [(n, ks) for n, _ in SMALL for ks in ("main", "small")
@@ -148,16 +143,15 @@ EDGE_RUNS = [(sh, ks) for sh in EDGE for ks in ("main", "small") if ks == "main"
 
 @pytest.mark.parametrize("name,kernels", SMALL_RUNS)
 def test_parity_small_workloads(name, kernels):
-    with kernel_set(kernels):
-        check_case(make_case(WORKLOADS[name]))
+    check_case(make_case(WORKLOADS[name]), kernels=kernel_flag(kernels))
 
 
 @pytest.mark.parametrize("shape,kernels", EDGE_RUNS)
 @pytest.mark.parametrize("dtype", ["f32", "bf16", "f16"])
 def test_parity_edge_shapes(shape, kernels, dtype):
     B, T, D, k = shape
-    with kernel_set(kernels):
-        check_case(make_custom(B, T, D, k, dtype, seed=B * 31 + T * 7 + D + k, ln_affine="random"))
+    check_case(make_custom(B, T, D, k, dtype, seed=B * 31 + T * 7 + D + k, ln_affine="random"),
+               kernels=kernel_flag(kernels))
 
 
 @pytest.mark.parametrize("fwd_set,bwd_set", [("small", "main"), ("main", "small")])
@@ -167,10 +161,8 @@ def test_small_and_main_paths_interchange(name, fwd_set, bwd_set):
     import torch
     case = make_case(WORKLOADS[name])
     dc = DeviceCase(case)
-    with kernel_set(fwd_set):
-        dc.fwd()
-    with kernel_set(bwd_set):
-        dc.bwd()
+    dc.fwd(kernels=kernel_flag(fwd_set))
+    dc.bwd(kernels=kernel_flag(bwd_set))
     torch.cuda.synchronize()
     got = dc.results()
     ref, _ = oracle_results(case)
@@ -187,7 +179,7 @@ def test_writes_stay_inside_buffers(shape, kernels, dtype):
     import torch
     B, T, D, k = shape
     case = make_custom(B, T, D, k, dtype, seed=B * 17 + T + D + k, ln_affine="random")
-    dc = DeviceCase(case)
+    dc = DeviceCase(case, kernels=kernel_flag(kernels))
     G = 4096  # guard bytes on each side (a multiple of 256: the workspace stays 256-byte aligned)
     guards = []
 
@@ -200,8 +192,7 @@ def test_writes_stay_inside_buffers(shape, kernels, dtype):
     dc.ws = guarded(dc.ws)
     dc.y, dc.dx = guarded(dc.y), guarded(dc.dx)
     dc.grads = {n: guarded(g) for n, g in dc.grads.items()}
-    with kernel_set(kernels):
-        dc.run()
+    dc.run()
     for buf in guards:
         head, tail = buf[:G].cpu().numpy(), buf[-G:].cpu().numpy()
         assert np.all(head == 0xA5) and np.all(tail == 0xA5)
@@ -212,12 +203,11 @@ def test_writes_stay_inside_buffers(shape, kernels, dtype):
 def test_small_path_bitwise_repeatable():
     """Two fwd+bwd runs of the small-batch kernels on identical inputs give identical bits."""
     case = make_case(WORKLOADS["B4_T16_D128_k2_bf16_public"])
-    with kernel_set("small"):
-        a = DeviceCase(case)
-        a.run()
-        b = DeviceCase(case)
-        b.run()
-        ra, rb_ = a.raw_bits(), b.raw_bits()
+    a = DeviceCase(case)
+    a.run()
+    b = DeviceCase(case)
+    b.run()
+    ra, rb_ = a.raw_bits(), b.raw_bits()
     for k in ra:
         assert np.array_equal(ra[k], rb_[k]), k
 
@@ -309,17 +299,69 @@ def sampled_check(name, samples=(0, -1), tokens=(0, -1)):
         assert np.all(np.isfinite(v)), k
 
 
+def full_check(case, chunk=64):
+    """y and all 15 gradients against the unchanged oracle over every sample
+    (run on chunks of samples, parameter gradients added in float64)."""
+    d = case["dims"]
+    name = case["name"]
+    tol = TOL[case["dtype"]]
+    assert d.S != 1   # dbeta0 would vanish exactly (check_case handles that case)
+    say(f"case {name}: gpu fwd+bwd (full size)")
+    dc = DeviceCase(case)
+    dc.run()
+    got = dc.results()
+    del dc
+    x, p, dy = as_f64(case)
+    num = {"y": 0.0, "dx": 0.0}
+    den = {"y": 0.0, "dx": 0.0}
+
+    def visit(b0, b1, y_c, dx_c):
+        say(f"case {name}: oracle on samples {b0}..{b1 - 1}")
+        for key, ref in (("y", y_c), ("dx", dx_c)):
+            g = got[key][b0:b1]
+            assert np.all(np.isfinite(g)), key
+            num[key] = max(num[key], float(np.max(np.abs(g - ref))))
+            den[key] = max(den[key], float(np.max(np.abs(ref))))
+
+    sums = oracle_by_chunks(x, p, dy, chunk, visit)
+    errs = {k: num[k] / max(den[k], 1e-30) for k in num}
+    errs.update(compare(got, sums, [k for k in GRAD_KEYS if k != "dx"], tol, f"{name} parameter gradients"))
+    say(f"{name} all outputs: " + " ".join(f"{k}={v:.2e}" for k, v in errs.items()))
+    FULL_SIZE_REPORT.append((f"{name} [{case['dtype']}, tol {tol:g}]", errs))
+    bad = {k: v for k, v in errs.items() if not v <= tol}
+    assert not bad, f"{name}: over tolerance {tol}: {bad}"
+    return errs
+
+
 def test_full_size_B1024_T32_D512_k2_bf16():
     """Small enough for the complete oracle: every output and gradient compared."""
     check_case(make_case(WORKLOADS["B1024_T32_D512_k2_bf16_lnrand"]), intermediates=False)
 
 
-def test_full_size_B1024_T64_D1280_k2_bf16_sampled():
-    sampled_check("B1024_T64_D1280_k2_bf16", samples=(0, 511, -1), tokens=(0, 37, -1))
+@pytest.mark.timeout(900)
+def test_full_size_B1024_T64_D1280_k2_bf16():
+    """The production workload: y and all 15 gradients over every sample."""
+    full_check(make_case(WORKLOADS["B1024_T64_D1280_k2_bf16"]))
 
 
-def test_full_size_B999_T40_D1000_k3_f32_sampled():
-    sampled_check("B999_T40_D1000_k3_f32_lnrand", samples=(0, 500, -1), tokens=(0, 17, -1))
+@pytest.mark.timeout(900)
+def test_full_size_B999_T40_D1000_k3_f32():
+    """Ragged fp32 workload (D/T = 25, no dimension a multiple of the tiles): every output."""
+    full_check(make_case(WORKLOADS["B999_T40_D1000_k3_f32_lnrand"]))
+
+
+@pytest.mark.timeout(900)
+@pytest.mark.parametrize("shape,dtype", [((1024, 40, 1000, 3), "bf16"), ((512, 16, 640, 3), "bf16"),
+                                         ((384, 8, 384, 3), "bf16"), ((384, 8, 384, 3), "f16"),
+                                         ((300, 8, 384, 3), "bf16")])
+def test_tile_tails_16bit(shape, dtype):
+    """16-bit shapes whose GEMMs take the 256x256-tile kernels with partial tiles:
+    (1024,40,1000,3): both weight-gradient GEMMs with M and N tails (232/112, 184/232);
+    (512,16,640,3) and (384,8,384,3): N tails of 128 on the down, d-hidden, dwout and d-out1
+    GEMMs, M tails of 128 on the weight-gradient GEMMs, and (384,...) M tails of 128 on the
+    row-major GEMMs; (300,8,384,3): M tails of 44 rows (not a multiple of 32) on those."""
+    B, T, D, k = shape
+    full_check(make_custom(B, T, D, k, dtype, seed=B + T + D + k + 11, ln_affine="random"))
 
 
 def test_full_size_B1024_T64_D1280_k2_f16_sampled():

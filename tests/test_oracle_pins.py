@@ -386,3 +386,27 @@ def test_f16_storage_rounding():
     half = to_storage(np.array([1.0 + 2.0 ** -11, 1.0 + 3 * 2.0 ** -11]), "f16")
     np.testing.assert_array_equal(storage_to_f64(half, "f16"), [1.0, 1.0 + 2.0 ** -9])
     assert storage_to_f64(to_storage(np.array([70000.0]), "f16"), "f16")[0] == np.inf
+
+
+def test_chunked_oracle_equals_whole_batch():
+    """The chunked run the large-workload parity tests use gives the whole-batch
+    oracle's outputs: y and dx chunk by chunk, parameter gradients as sums."""
+    import sys
+    sys.path.insert(0, os.path.dirname(os.path.abspath(__file__)))
+    from oracle_chunked import oracle_by_chunks
+    case = make_custom(11, 8, 64, 3, "f32", seed=21, ln_affine="random")
+    x, p, dy = as_f64(case)
+    y, g = oracle.forward_backward(x, p, dy)
+    seen = []
+
+    def visit(b0, b1, y_c, dx_c):
+        seen.append((b0, b1))
+        np.testing.assert_allclose(y_c, y[b0:b1], rtol=0, atol=1e-12)
+        np.testing.assert_allclose(dx_c, g["dx"][b0:b1], rtol=0, atol=1e-12)
+
+    sums = oracle_by_chunks(x, p, dy, 4, visit)
+    assert seen == [(0, 4), (4, 8), (8, 11)]
+    assert set(sums) == set(g) - {"dx"}
+    for k, v in sums.items():
+        scale = max(1.0, float(np.max(np.abs(g[k]))))
+        np.testing.assert_allclose(v, g[k], rtol=0, atol=1e-12 * scale, err_msg=k)

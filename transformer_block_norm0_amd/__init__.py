@@ -5,9 +5,9 @@ and a ctypes binding (rmblock.py).  Importing it does not load the library;
 the first call does, and raises if it has not been built.
 """
 from .rmblock import (PARAM_NAMES, RM_BF16, RM_F32, RmError, alloc_workspace, block_bwd, block_fwd, dims,
-                      kernel_names, library, param_shapes, prof_collect, prof_enable, small_path, token_mix,
+                      kernel_names, library, param_shapes, prof_collect, prof_enable, token_mix,
                       workspace_bytes, ws_region)
 
 __all__ = ["PARAM_NAMES", "RM_BF16", "RM_F32", "RmError", "alloc_workspace", "block_bwd", "block_fwd", "dims",
-           "kernel_names", "library", "param_shapes", "prof_collect", "prof_enable", "small_path", "token_mix",
+           "kernel_names", "library", "param_shapes", "prof_collect", "prof_enable", "token_mix",
            "workspace_bytes", "ws_region"]

@@ -80,12 +80,16 @@ struct ProfRec {
   int kid;
   hipEvent_t a, b;
 };
+struct OpenRec {
+  hipStream_t s;
+  int kid;
+  hipEvent_t a;
+};
 std::mutex g_mu;
 bool g_prof = false;
 std::vector<ProfRec> g_recs;
 std::vector<hipEvent_t> g_pool;
-hipEvent_t g_open_evt = nullptr;
-int g_open_kid = -1;
+std::vector<OpenRec> g_open;  // brackets begun and not yet ended, per stream
 
 hipEvent_t get_event() {
   if (!g_pool.empty()) {
@@ -102,20 +106,32 @@ hipEvent_t get_event() {
 void prof_begin(int kid, hipStream_t s) {
   std::lock_guard<std::mutex> lk(g_mu);
   if (!g_prof) return;
-  g_open_evt = get_event();
-  g_open_kid = kid;
-  if (g_open_evt && hipEventRecord(g_open_evt, s) != hipSuccess) g_open_evt = nullptr;
+  hipEvent_t a = get_event();
+  if (!a) return;
+  if (hipEventRecord(a, s) != hipSuccess) {
+    g_pool.push_back(a);
+    return;
+  }
+  g_open.push_back({s, kid, a});
 }
 
 void prof_end(int kid, hipStream_t s) {
   std::lock_guard<std::mutex> lk(g_mu);
-  if (!g_prof || !g_open_evt || g_open_kid != kid) return;
-  hipEvent_t b = get_event();
-  if (!b) return;
-  if (hipEventRecord(b, s) != hipSuccess) return;
-  g_recs.push_back({kid, g_open_evt, b});
-  g_open_evt = nullptr;
-  g_open_kid = -1;
+  if (!g_prof) return;
+  // the latest bracket this stream opened for this kernel
+  for (size_t i = g_open.size(); i-- > 0;) {
+    if (g_open[i].s != s || g_open[i].kid != kid) continue;
+    const hipEvent_t a = g_open[i].a;
+    g_open.erase(g_open.begin() + (long)i);
+    hipEvent_t b = get_event();
+    if (b && hipEventRecord(b, s) == hipSuccess) {
+      g_recs.push_back({kid, a, b});
+    } else {
+      g_pool.push_back(a);
+      if (b) g_pool.push_back(b);
+    }
+    return;
+  }
 }
 
 }  // namespace rm
@@ -130,6 +146,7 @@ rm_status check_common(const rm_dims* dims, const rm_params* p, const void* ws, 
   if (!dims || !p) return RM_E_NULL;
   if (dims->dtype != RM_F32 && dims->dtype != RM_BF16 && dims->dtype != RM_F16) return RM_E_DTYPE;
   if (!dims_valid(*dims)) return RM_E_DIMS;
+  if (dims->flags & ~RM_FLAG_MAIN_KERNELS) return RM_E_ARG;
   const void* ptrs[] = {p->w1, p->b1, p->wout, p->bout, p->lnx_g, p->lnx_b, p->lng_g,
                         p->lng_b, p->ln0_g, p->ln0_b, p->ln1_g, p->ln1_b, p->ln2_g, p->ln2_b};
   const size_t es = dims->dtype == RM_F32 ? 4 : 2;
@@ -145,8 +162,8 @@ rm_status check_common(const rm_dims* dims, const rm_params* p, const void* ws, 
 
 rm_status hip_status(hipError_t e) { return e == hipSuccess ? RM_OK : RM_E_HIP; }
 
-// rm_small_path: whether shapes the small-batch kernels take use them
-int g_small_path = 1;
+// The small-batch kernels run this call: its shape fits them and the caller did not ask for the main kernels.
+bool use_small(const rm_dims& d) { return !(d.flags & RM_FLAG_MAIN_KERNELS) && small_supported(d); }
 
 }  // namespace
 
@@ -203,7 +220,7 @@ rm_status rm_block_fwd(const rm_dims* dims, const rm_params* p, const void* x, v
   char* w = reinterpret_cast<char*>(ws);
   const long T = d.T, D = d.D, H = (long)d.k * d.D;
   hipError_t e;
-  if (g_small_path && small_supported(d)) return hip_status(launch_small_fwd(d, *p, x, y, ws, L, s));
+  if (use_small(d)) return hip_status(launch_small_fwd(d, *p, x, y, ws, L, s));
 
   if ((e = launch_prologue(d, *p, x, ws, L, s)) != hipSuccess) return hip_status(e);
 
@@ -249,7 +266,7 @@ rm_status rm_block_bwd(const rm_dims* dims, const rm_params* p, const void* x, c
   char* w = reinterpret_cast<char*>(ws);
   const long T = d.T, D = d.D, H = (long)d.k * d.D;
   hipError_t e;
-  if (g_small_path && small_supported(d)) return hip_status(launch_small_bwd(d, *p, x, dy, ws, L, dx, *g, s));
+  if (use_small(d)) return hip_status(launch_small_bwd(d, *p, x, dy, ws, L, dx, *g, s));
 
   if ((e = launch_ln2_bwd(d, *p, dy, ws, L, s)) != hipSuccess) return hip_status(e);
 
@@ -289,12 +306,6 @@ rm_status rm_block_bwd(const rm_dims* dims, const rm_params* p, const void* x, c
   return RM_OK;
 }
 
-rm_status rm_small_path(int on) {
-  if (on != 0 && on != 1) return RM_E_ARG;
-  g_small_path = on;
-  return RM_OK;
-}
-
 rm_status rm_token_mix(const rm_dims* dims, const void* in, void* out, void* stream) {
   if (!dims) return RM_E_NULL;
   if (dims->dtype != RM_F32 && dims->dtype != RM_BF16 && dims->dtype != RM_F16) return RM_E_DTYPE;
@@ -302,7 +313,7 @@ rm_status rm_token_mix(const rm_dims* dims, const void* in, void* out, void* str
   if (!in || !out) return RM_E_NULL;
   const size_t es = dims->dtype == RM_F32 ? 4 : 2;
   if (!aligned(in, es) || !aligned(out, es)) return RM_E_ALIGN;
-  if (in == out) return RM_E_ARG;
+  if (in == out || (dims->flags & ~RM_FLAG_MAIN_KERNELS)) return RM_E_ARG;
   return hip_status(launch_token_mix(*dims, in, out, reinterpret_cast<hipStream_t>(stream)));
 }
 

@@ -11,10 +11,12 @@
 //     fragments from LDS for 16 MFMAs (64 bytes of LDS per clock per CU at
 //     full MFMA rate).
 //   * Operand slabs (64 deep in K, 32 KB per operand) are copied global ->
-//     LDS with the gfx950 16-byte direct loads (no register staging) through
-//     two stages.  The copies are inline assembly with explicit wait counts,
-//     so the compiler neither waits for them at every LDS read nor reorders
-//     them.
+//     LDS with the gfx950 16-byte buffer loads that write LDS directly (no
+//     register staging) through two stages.  Each copy goes through a buffer
+//     resource that spans exactly the token's operand from the slab's first
+//     element on, so an address outside it reads zero instead of faulting.
+//     The copies are inline assembly with explicit wait counts, so the
+//     compiler neither waits for them at every LDS read nor reorders them.
 //   * One barrier per slab, before its last k step: the fragments of k steps
 //     2..4 are read during the MFMAs of the step before, then the barrier
 //     (next slab landed, this slab fully read), the copy of slab k+2 into the
@@ -37,6 +39,7 @@
 //     ever made.
 //   * Rows past M or N are loaded from a clamped valid address and their
 //     results dropped at the store.
+#include <atomic>
 #include <type_traits>
 
 #include "rm_common.h"
@@ -106,13 +109,22 @@ __device__ __forceinline__ void slab_offsets(uint32_t (&off)[DMA_PER_OPERAND], l
   }
 }
 
-// One 16-byte direct global -> LDS load per lane from the uniform base plus
-// this lane's byte offset: lane l's bytes land at LDS address lds + 16*l.
-// Issued through inline assembly so that the compiler's own wait-count
-// bookkeeping ignores it; the pipeline waits for these loads explicitly
-// (sync_slab) before any LDS read of their data.
-__device__ __forceinline__ void dma16(uint32_t voff, const void* sbase, uint32_t lds) {
-  asm volatile("global_load_lds_dwordx4 %0, %1" ::"v"(voff), "s"(sbase), "{m0}"(lds) : "memory");
+// Buffer resource over `bytes` bytes from `base` (gfx9 word 3 with a 32-bit
+// data format; a zero format would disable the access).  Offsets at or beyond
+// the extent read zero / write nothing.  The extent is a 32-bit byte count.
+constexpr int RSRC_WORD3 = 0x00020000;
+__device__ __forceinline__ __amdgpu_buffer_rsrc_t rsrc32(const void* base, uint32_t bytes) {
+  return __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(base), (short)0, (int)bytes, RSRC_WORD3);
+}
+
+// One 16-byte buffer load per lane that writes LDS directly: bytes
+// [voff, voff + 16) of the resource land at LDS address lds + 16*l for lane l
+// (zeros where they lie outside the resource).  Issued through inline
+// assembly so that the compiler's own wait-count bookkeeping ignores it; the
+// pipeline waits for these loads explicitly (sync_slab) before any LDS read
+// of their data.
+__device__ __forceinline__ void dma16(uint32_t voff, __amdgpu_buffer_rsrc_t rs, uint32_t lds) {
+  asm volatile("buffer_load_dwordx4 %0, %1, 0 offen lds" ::"v"(voff), "s"(rs), "{m0}"(lds) : "memory");
 }
 
 // LDS byte address of a pointer into a __shared__ object.
@@ -121,15 +133,17 @@ __device__ __forceinline__ uint32_t lds_addr(const char* p) {
 }
 
 // Copy the slab starting at k0 into LDS with 16-byte direct loads (wave is
-// uniform, so the LDS addresses are scalar).
+// uniform, so the LDS addresses are scalar).  The resource spans the token's
+// operand; the slab's offset (k0 elements along a row, or k0 rows) is added
+// to each lane's offset, so every piece is range-checked against the operand.
 template <bool KMAJ>
-__device__ __forceinline__ void dma_slab(char* lds, const bf16_t* __restrict__ base,
-                                         const uint32_t (&off)[DMA_PER_OPERAND], long ld, int k0, int wave) {
-  const bf16_t* b = base + (KMAJ ? (long)k0 : (long)k0 * ld);
+__device__ __forceinline__ void dma_slab(char* lds, __amdgpu_buffer_rsrc_t rs, const uint32_t (&off)[DMA_PER_OPERAND],
+                                         long ld, int k0, int wave) {
+  const uint32_t koff = (uint32_t)(KMAJ ? (long)k0 * 2 : (long)k0 * ld * 2);
 #pragma unroll
   for (int i = 0; i < DMA_PER_OPERAND; ++i) {
     const int dst = KMAJ ? (64 * wave + 8 * i) * 128 : (16 * wave + 2 * i) * 512;
-    dma16(off[i], b, lds_addr(lds + dst));
+    dma16(off[i] + koff, rs, lds_addr(lds + dst));
   }
 }
 
@@ -219,10 +233,8 @@ __device__ __forceinline__ void sync_slab() {
   __builtin_amdgcn_sched_barrier(0);
 }
 
-// Raw buffer resource: base, byte extent, gfx9 word 3 with a 32-bit data
-// format (a zero format would disable the access).  Offsets at or beyond the
-// extent read zero / write nothing.
-constexpr int RSRC_WORD3 = 0x00020000;
+// Raw buffer resource for the epilogue: base and a byte extent of at most
+// 2^31 - 1, so that OUT_OF_RANGE lies beyond every extent.
 constexpr uint32_t OUT_OF_RANGE = 0x80000000u;
 __device__ __forceinline__ __amdgpu_buffer_rsrc_t make_rsrc(const void* base, long bytes) {
   const int n = (int)min(bytes, 0x7fffffffL);
@@ -243,28 +255,35 @@ __device__ __forceinline__ Tile tile_of(int logical, int tiles_m, int per_t) {
   return c;
 }
 
-// Operand source of one tile: per-token base pointers and this thread's
-// four slab offsets for A and B.
+// Byte extent of one token's operand: from its first element to one past its
+// last.  K-major: rows (m or n) of K contiguous elements; M/N-major: K rows of
+// MN contiguous elements.
+__device__ __forceinline__ uint32_t operand_extent(bool kmajor, long ld, int K, int MN) {
+  return (uint32_t)(kmajor ? ((long)(MN - 1) * ld + K) * 2 : ((long)(K - 1) * ld + MN) * 2);
+}
+
+// Operand source of one tile: buffer resources over the token's A and B
+// operands and this thread's eight slab offsets for each.
 struct Src {
-  const bf16_t* A;
-  const bf16_t* B;
+  __amdgpu_buffer_rsrc_t A, B;
   uint32_t offa[DMA_PER_OPERAND], offb[DMA_PER_OPERAND];
 };
 template <bool AK, bool BKM>
 __device__ __forceinline__ void tile_src(Src& s, const GemmArgs& g, const Tile& c, int wave, int lane) {
-  s.A = reinterpret_cast<const bf16_t*>(g.A) + (long)c.t * g.a_bs;
-  s.B = reinterpret_cast<const bf16_t*>(g.B) + (long)c.t * g.b_bs;
+  s.A = rsrc32(reinterpret_cast<const char*>(g.A) + (long)c.t * g.a_bs * 2, operand_extent(AK, g.a_ld, g.K, g.M));
+  s.B = rsrc32(reinterpret_cast<const char*>(g.B) + (long)c.t * g.b_bs * 2, operand_extent(BKM, g.b_ld, g.K, g.N));
   slab_offsets<AK>(s.offa, g.a_ld, c.m0, g.M, wave, lane);
   slab_offsets<BKM>(s.offb, g.b_ld, c.n0, g.N, wave, lane);
 }
 
 // The tile's 256 bias values (bf16, 512 bytes) copied by wave 0 into a 1 KB
 // LDS area (lanes 32..63 write a second copy); issued just before the tile's
-// first slab, so the wait for that slab covers it.
+// first slab, so the wait for that slab covers it.  The resource spans the
+// token's N bias values.
 __device__ __forceinline__ void dma_bias(char* dst, const GemmArgs& g, const Tile& c, int lane) {
-  const bf16_t* b = reinterpret_cast<const bf16_t*>(g.bias) + (long)c.t * g.bias_bs;
+  const char* b = reinterpret_cast<const char*>(g.bias) + (long)c.t * g.bias_bs * 2;
   const int n = min(c.n0 + 8 * (lane & 31), g.N - 8);
-  dma16((uint32_t)n * 2, b, lds_addr(dst));
+  dma16((uint32_t)n * 2, rsrc32(b, (uint32_t)g.N * 2), lds_addr(dst));
 }
 
 template <bool AK, bool BKM>
@@ -569,17 +588,18 @@ hipError_t run256(Gemm256Kernel k, const GemmArgs& g, hipStream_t s) {
 
 }  // namespace
 
-// Compute units of the current device (cached per device).
+// Compute units of the current device (cached per device; concurrent first
+// calls store the same value).
 int device_cu_count() {
-  static int cached[64] = {0};
+  static std::atomic<int> cached[64];
   int dev = 0;
   if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= 64) return 256;
-  if (cached[dev] == 0) {
-    int n = 0;
+  int n = cached[dev].load(std::memory_order_relaxed);
+  if (n == 0) {
     if (hipDeviceGetAttribute(&n, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess || n <= 0) n = 256;
-    cached[dev] = n;
+    cached[dev].store(n, std::memory_order_relaxed);
   }
-  return cached[dev];
+  return n;
 }
 
 bool gemm256_supported(int dtype, bool a_kmajor, bool b_kmajor, const GemmArgs& g, int kid) {

@@ -33,9 +33,13 @@ class RmError(RuntimeError):
         super().__init__(f"{where}: {STATUS.get(status, status)} ({_lib().rm_status_string(status).decode()})")
 
 
+RM_FLAG_MAIN_KERNELS = 1
+KERNEL_SETS = {"auto": 0, "main": RM_FLAG_MAIN_KERNELS}
+
+
 class CDims(ctypes.Structure):
     _fields_ = [("B", ctypes.c_int32), ("T", ctypes.c_int32), ("D", ctypes.c_int32),
-                ("k", ctypes.c_int32), ("dtype", ctypes.c_int32)]
+                ("k", ctypes.c_int32), ("dtype", ctypes.c_int32), ("flags", ctypes.c_int32)]
 
 
 class CParams(ctypes.Structure):
@@ -79,8 +83,6 @@ def _lib():
         lib.rm_prof_name.restype = ctypes.c_char_p
         lib.rm_prof_collect.argtypes = [P(ctypes.c_double), P(ctypes.c_int64), ctypes.c_int]
         lib.rm_prof_collect.restype = ctypes.c_int
-        lib.rm_small_path.argtypes = [ctypes.c_int]
-        lib.rm_small_path.restype = ctypes.c_int
         _LIB = lib
     return _LIB
 
@@ -90,16 +92,10 @@ def library():
     return _lib()
 
 
-def small_path(on: bool) -> None:
-    """rm_small_path: let B <= 8, D <= 128, H <= 256 shapes take the small-batch kernels (the default),
-    or send every shape through the main path."""
-    st = _lib().rm_small_path(1 if on else 0)
-    if st:
-        raise RmError(st, "rm_small_path")
-
-
-def dims(B: int, T: int, D: int, k: int, dtype: str) -> CDims:
-    return CDims(B, T, D, k, {"f32": RM_F32, "bf16": RM_BF16, "f16": RM_F16}[dtype])
+def dims(B: int, T: int, D: int, k: int, dtype: str, kernels: str = "auto") -> CDims:
+    """rm_dims of a call.  kernels="auto" lets B <= 8, D <= 128, H <= 256 shapes take the
+    small-batch kernels; "main" sends the call through the main kernel set."""
+    return CDims(B, T, D, k, {"f32": RM_F32, "bf16": RM_BF16, "f16": RM_F16}[dtype], KERNEL_SETS[kernels])
 
 
 def workspace_bytes(d: CDims) -> int:
