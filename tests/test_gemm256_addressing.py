@@ -156,7 +156,8 @@ def check_operand(kmajor, ld, bs, K, MN, mn0, batch, total_elems):
     assert (batch - 1) * bs * 2 + ext <= total_elems * 2
     off, mn, sub, lds, slot = slab_offsets(kmajor, ld, mn0, MN)
     nk = K // BK
-    # every LDS byte of the 32 KB stage is written exactly once per slab
+    # every LDS byte of the 32 KB stage is written exactly once per slab (A: 2 stages, B: 3 stages,
+    # 160 KB in all)
     assert np.array_equal(np.sort(lds.ravel()), np.arange(0, 256 * BK * 2, 16))
     if kmajor:
         # LDS slot holds row `slot` (tile-local), logical chunk sub/8; the fragment read of
@@ -202,8 +203,12 @@ def check_epilogue(g, m0, n0, written, sizes):
                 ro = m * g["res_ld"] * 2 + n * 2
                 assert np.all(n[ok] + 3 < N) and np.all(ro[ok] + 8 <= r_ext)
     if g["bias"]:
-        n = np.minimum(n0 + 8 * (lane & 31), N - 8)
-        assert np.all(n >= 0) and np.all(n * 2 + 16 <= N * 2)
+        # the epilogue's bias loads: 4 consecutive values at columns n0 + wn*128 + 4h + 32j + 8q
+        for wn in range(2):
+            for j, q in itertools.product(range(4), range(4)):
+                n = n0 + wn * 128 + 4 * h + 32 * j + 8 * q
+                ok = n < N
+                assert np.all(n[ok] + 3 < N) and np.all(n[ok] * 2 + 8 <= N * 2)
 
 
 def check_gemm(name, g, sizes):
@@ -260,3 +265,90 @@ def test_replica_catches_a_planted_slip():
     koff = (g["K"] // BK - 1) * BK * g["a_ld"] * 2
     assert np.all(off + koff + 16 <= ext)
     assert not np.all(off + koff + g["a_ld"] * 2 * BK + 16 <= ext)
+
+
+# ---------------------------------------------------------------------------
+# the copy pipeline: stages, issue order and wait counts of one wave
+
+DMA_PER_OPERAND = 8
+EPI_STORES = 32
+WAIT_STEADY = DMA_PER_OPERAND
+WAIT_AFTER_EPILOGUE = DMA_PER_OPERAND + EPI_STORES
+
+
+def simulate_pipeline(nk, ntiles, epilogue_extra=0):
+    """Replays the kernel's per-wave event sequence for `ntiles` tiles of `nk` slabs: copy issues
+    (A ring of 2 stages, B ring of 3; the last tile's next-tile copies are issued too, through a
+    resource of extent 0), the epilogue's vector-memory operations, waits (vmcnt N + barrier)
+    and the fragment reads of each slab.  Vector-memory operations complete in issue order, so
+    after a wait with count N every operation but the newest N is complete.  Checks that every
+    slab's copies are complete before its first read, that no copy targets a stage whose
+    previous slab may still be read, and that no copy is in flight at the end."""
+    ops = []               # ("A"|"B"|"E", slab)
+    done = 0               # ops[:done] complete
+    stage_of = {}          # (operand, global slab) -> stage
+    reading = {}           # (operand, stage) -> global slab whose reads are not yet fenced
+
+    def issue(op, slab):
+        ring = 2 if op == "A" else 3
+        st = slab % ring
+        assert (op, st) not in reading or reading[(op, st)] is None, f"{op} stage {st} overwritten while read"
+        stage_of[(op, slab)] = st
+        ops.extend([(op, slab)] * DMA_PER_OPERAND)   # one 16-byte copy per lane and instruction
+
+    def wait(n):
+        nonlocal done
+        done = max(done, len(ops) - n)
+        for key in reading:        # the barrier: every wave's reads before it are finished
+            reading[key] = None
+
+    def read(slab):
+        for op in ("A", "B"):
+            assert (op, slab) in stage_of, f"slab {slab} {op} never copied"
+            last = len(ops) - 1 - ops[::-1].index((op, slab))
+            assert last < done, f"slab {slab} {op} read before its copy completed"
+            reading[(op, stage_of[(op, slab)])] = slab
+
+    S = lambda t, k: t * nk + k          # global slab index
+    # prologue
+    for op, k in (("A", 0), ("B", 0), ("A", 1), ("B", 1), ("B", 2)):
+        issue(op, S(0, k))
+    wait(3 * DMA_PER_OPERAND)
+    read(S(0, 0))                          # first k step's fragments
+    for t in range(ntiles):
+        has_next = t + 1 < ntiles
+        for k in range(nk):
+            read(S(t, k))                  # k steps 1..3 of slab k
+            wait(WAIT_AFTER_EPILOGUE if (k == 0 and t > 0) else WAIT_STEADY)
+            ka, kb = k + 2, k + 3
+            # copies of the next tile are issued even without one (slab indices past the last
+            # tile: empty copies into freed stages)
+            issue("A", S(t, ka))
+            issue("B", S(t, kb))
+            if k + 1 < nk:
+                read(S(t, k + 1))          # next slab's first fragments
+            elif has_next:
+                read(S(t + 1, 0))
+        for e in range(EPI_STORES + epilogue_extra):
+            ops.append(("E", (t, e)))
+    wait(0)                                # the kernel's final wait
+    assert done == len(ops)
+
+
+@pytest.mark.parametrize("nk", [4, 6, 16, 20, 40, 80, 120])
+@pytest.mark.parametrize("ntiles", [1, 2, 3, 7])
+def test_gemm256_pipeline_waits(nk, ntiles):
+    simulate_pipeline(nk, ntiles)
+    simulate_pipeline(nk, ntiles, epilogue_extra=64 + 64)   # residual and bias loads in the epilogue
+
+
+def test_pipeline_replica_catches_a_short_wait():
+    """A steady-state wait one slab too loose (two B slabs left in flight) is caught."""
+    global WAIT_STEADY
+    saved = WAIT_STEADY
+    WAIT_STEADY = 2 * DMA_PER_OPERAND
+    try:
+        with pytest.raises(AssertionError):
+            simulate_pipeline(20, 2)
+    finally:
+        WAIT_STEADY = saved

@@ -12,16 +12,19 @@
 //     full MFMA rate).
 //   * Operand slabs (64 deep in K, 32 KB per operand) are copied global ->
 //     LDS with the gfx950 16-byte buffer loads that write LDS directly (no
-//     register staging) through two stages.  Each copy goes through a buffer
+//     register staging): A through a ring of two stages, B through a ring of
+//     three, so two B slabs and one A slab are in flight while a slab is
+//     multiplied (the whole 160 KB of LDS).  Each copy goes through a buffer
 //     resource that spans exactly the token's operand from the slab's first
 //     element on, so an address outside it reads zero instead of faulting.
 //     The copies are inline assembly with explicit wait counts, so the
 //     compiler neither waits for them at every LDS read nor reorders them.
 //   * One barrier per slab, before its last k step: the fragments of k steps
 //     2..4 are read during the MFMAs of the step before, then the barrier
-//     (next slab landed, this slab fully read), the copy of slab k+2 into the
-//     stage just freed, and the next slab's first fragments are read during
-//     the last k step's MFMAs.  No LDS latency is exposed inside a tile.
+//     (next slab landed, this slab fully read), the copies of A slab k+2 and
+//     B slab k+3 into the stages just freed, and the next slab's first
+//     fragments are read during the last k step's MFMAs.  No LDS latency is
+//     exposed inside a tile.
 //   * Persistent: one workgroup per CU walks a range of tiles; the copy
 //     stream continues into the next tile and a tile's results are stored
 //     straight from the accumulators while the next tile's copies land.
@@ -58,7 +61,6 @@ typedef uint32_t v4u32 __attribute__((ext_vector_type(4)));
 typedef __attribute__((address_space(3))) short4_t lds_short4;
 
 constexpr int BM = 256, BN = 256, BK = 64;
-constexpr int STAGES = 2;
 constexpr int TILE_BYTES = 256 * BK * 2;  // one operand slab: 256 x 64 bf16 = 32 KB
 constexpr int KSTEPS = BK / 16;           // MFMA k steps per slab
 // Buffer stores the epilogue issues per tile per wave at least (32 for bf16
@@ -268,28 +270,70 @@ struct Src {
   __amdgpu_buffer_rsrc_t A, B;
   uint32_t offa[DMA_PER_OPERAND], offb[DMA_PER_OPERAND];
 };
+// active = false gives resources of extent 0: every copy through them reads
+// nothing and writes zeros (the next tile's copies when there is none).
 template <bool AK, bool BKM>
-__device__ __forceinline__ void tile_src(Src& s, const GemmArgs& g, const Tile& c, int wave, int lane) {
-  s.A = rsrc32(reinterpret_cast<const char*>(g.A) + (long)c.t * g.a_bs * 2, operand_extent(AK, g.a_ld, g.K, g.M));
-  s.B = rsrc32(reinterpret_cast<const char*>(g.B) + (long)c.t * g.b_bs * 2, operand_extent(BKM, g.b_ld, g.K, g.N));
+__device__ __forceinline__ void tile_src(Src& s, const GemmArgs& g, const Tile& c, int wave, int lane,
+                                         bool active = true) {
+  s.A = rsrc32(reinterpret_cast<const char*>(g.A) + (long)c.t * g.a_bs * 2,
+               active ? operand_extent(AK, g.a_ld, g.K, g.M) : 0u);
+  s.B = rsrc32(reinterpret_cast<const char*>(g.B) + (long)c.t * g.b_bs * 2,
+               active ? operand_extent(BKM, g.b_ld, g.K, g.N) : 0u);
   slab_offsets<AK>(s.offa, g.a_ld, c.m0, g.M, wave, lane);
   slab_offsets<BKM>(s.offb, g.b_ld, c.n0, g.N, wave, lane);
 }
 
-// The tile's 256 bias values (bf16, 512 bytes) copied by wave 0 into a 1 KB
-// LDS area (lanes 32..63 write a second copy); issued just before the tile's
-// first slab, so the wait for that slab covers it.  The resource spans the
-// token's N bias values.
-__device__ __forceinline__ void dma_bias(char* dst, const GemmArgs& g, const Tile& c, int lane) {
-  const char* b = reinterpret_cast<const char*>(g.bias) + (long)c.t * g.bias_bs * 2;
-  const int n = min(c.n0 + 8 * (lane & 31), g.N - 8);
-  dma16((uint32_t)n * 2, rsrc32(b, (uint32_t)g.N * 2), lds_addr(dst));
+template <bool KMAJ>
+__device__ __forceinline__ void dma_operand(char* stage, __amdgpu_buffer_rsrc_t rs, const uint32_t (&off)[DMA_PER_OPERAND],
+                                            long ld, int kslab, int wave) {
+  dma_slab<KMAJ>(stage, rs, off, ld, kslab * BK, wave);
 }
 
-template <bool AK, bool BKM>
-__device__ __forceinline__ void dma_pair(char* sa, char* sb, const Src& s, const GemmArgs& g, int kslab, int wave) {
-  dma_slab<AK>(sa, s.A, s.offa, g.a_ld, kslab * BK, wave);
-  dma_slab<BKM>(sb, s.B, s.offb, g.b_ld, kslab * BK, wave);
+// Piece i of dma_slab alone (the same source offset and LDS destination).
+template <bool KMAJ>
+__device__ __forceinline__ void dma_piece(char* stage, __amdgpu_buffer_rsrc_t rs, uint32_t off, uint32_t koff, int i,
+                                          int wave) {
+  const int dst = KMAJ ? (64 * wave + 8 * i) * 128 : (16 * wave + 2 * i) * 512;
+  dma16(off + koff, rs, lds_addr(stage + dst));
+}
+
+// Byte offset of a slab along an operand: k0 elements along each row (K-major) or k0 rows.
+template <bool KMAJ>
+__device__ __forceinline__ uint32_t slab_koff(long ld, int kslab) {
+  return (uint32_t)(KMAJ ? (long)kslab * BK * 2 : (long)kslab * BK * ld * 2);
+}
+
+// The last k step of a slab: its 16 MFMAs, with the copies of the freed
+// stages (8 A pieces, then 8 B pieces) issued one after each MFMA and the
+// next slab's first-k-step fragments read after MFMAs 8..15.  Each group is
+// fenced (sched_barrier), so the copies issue in the shadow of the MFMAs
+// instead of as a burst while the matrix pipe waits.  There are no branches:
+// copies that have no source go through a resource of extent 0.
+template <typename ST, bool AK, bool BKM>
+__device__ __forceinline__ void last_kstep(f32x16_t (&acc)[4][4], const Frags& f1, Frags& f0, const char* na,
+                                           const char* nb, char* sa, char* sb, __amdgpu_buffer_rsrc_t rsa,
+                                           const uint32_t (&offa)[DMA_PER_OPERAND], uint32_t koffa,
+                                           __amdgpu_buffer_rsrc_t rsb, const uint32_t (&offb)[DMA_PER_OPERAND],
+                                           uint32_t koffb, int wm, int wn, int wave, int lane) {
+#pragma unroll
+  for (int x = 0; x < 16; ++x) {
+    const int i = x >> 2, j = x & 3;
+    if constexpr (std::is_same<ST, f16_t>::value)
+      acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_f16(__builtin_bit_cast(f16x8_t, f1.b[j]),
+                                                         __builtin_bit_cast(f16x8_t, f1.a[i]), acc[i][j], 0, 0, 0);
+    else
+      acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(__builtin_bit_cast(bf16x8_t, f1.b[j]),
+                                                          __builtin_bit_cast(bf16x8_t, f1.a[i]), acc[i][j], 0, 0, 0);
+    if (x < 8) {
+      dma_piece<AK>(sa, rsa, offa[x], koffa, x, wave);
+    } else {
+      dma_piece<BKM>(sb, rsb, offb[x - 8], koffb, x - 8, wave);
+      const int r = x - 8;
+      if (r < 4) f0.a[r] = read_frag<AK>(na, wm * 128 + 32 * r, 0, lane);
+      else f0.b[r - 4] = read_frag<BKM>(nb, wn * 128 + 32 * (r - 4), 0, lane);
+    }
+    __builtin_amdgcn_sched_barrier(0);
+  }
 }
 
 // Four 16-bit storage values (two packed words) added to v.
@@ -301,17 +345,17 @@ __device__ __forceinline__ void add16x4(float (&v)[4], v2u32 w) {
   v[3] += hi16<ST>(w.y);
 }
 
-// The residual (storage dtype) of one 32-row block: 16 loads of 4 columns
-// (zero where out of range).
-__device__ __forceinline__ void load_residual(v2u32 (&r)[16], const GemmArgs& g, __amdgpu_buffer_rsrc_t rrs,
-                                              uint32_t rld, int m, int nbase, bool mok) {
+// 16 loads of 4 consecutive storage values of one row of a [., ld] tensor:
+// columns nbase + 32j + 8q (zero where the row or the column is out of range).
+__device__ __forceinline__ void load_row4x16(v2u32 (&r)[16], const GemmArgs& g, __amdgpu_buffer_rsrc_t rs, uint32_t row_off,
+                                             int nbase, bool mok) {
 #pragma unroll
   for (int j = 0; j < 4; ++j)
 #pragma unroll
     for (int q = 0; q < 4; ++q) {
       const int n = nbase + 32 * j + 8 * q;
-      const uint32_t ro = (mok && n < g.N) ? (uint32_t)m * rld + (uint32_t)n * 2 : OUT_OF_RANGE;
-      r[4 * j + q] = __builtin_bit_cast(v2u32, __builtin_amdgcn_raw_buffer_load_b64(rrs, ro, 0, 0));
+      const uint32_t ro = (mok && n < g.N) ? row_off + (uint32_t)n * 2 : OUT_OF_RANGE;
+      r[4 * j + q] = __builtin_bit_cast(v2u32, __builtin_amdgcn_raw_buffer_load_b64(rs, ro, 0, 0));
     }
 }
 
@@ -322,12 +366,13 @@ __device__ __forceinline__ void load_residual(v2u32 (&r)[16], const GemmArgs& g,
 // columns (lane l < 32: 8q..8q+7, lane l+32: 8(q+1)..8(q+1)+7, q = 0, 2) for
 // one 16-byte buffer store: EPI_STORES per wave, every one issued (rows past
 // M or columns past N get an out-of-range offset that the buffer unit drops).
-// BIAS / RES are compile-time, so the epilogue has no branches: the tile's 64
-// bias values per lane are read from LDS once, and the residual of m block
-// i+1 is loaded while block i is computed and stored.
+// BIAS / RES are compile-time, so the epilogue has no branches.  The bias
+// (64 values per lane) is loaded from the token's bias row once per tile, or
+// once per m block next to a residual (which needs the registers); the
+// residual of m block i+1 is loaded while block i is computed and stored.
 template <typename ST, bool BIAS, bool RES>
-__device__ __forceinline__ void epilogue(const f32x16_t (&acc)[4][4], const GemmArgs& g, const Tile& c,
-                                         const char* sbias, int wm, int wn, int lane) {
+__device__ __forceinline__ void epilogue(const f32x16_t (&acc)[4][4], const GemmArgs& g, const Tile& c, int wm, int wn,
+                                         int lane) {
   const int r = lane & 31, h = lane >> 5;
   const int mb = c.m0 + wm * 128 + r;  // + 32 i
   const int nb = wn * 128 + 4 * h;     // + 32 j + 8 q (tile-local)
@@ -335,19 +380,12 @@ __device__ __forceinline__ void epilogue(const f32x16_t (&acc)[4][4], const Gemm
   const __amdgpu_buffer_rsrc_t crs = make_rsrc(cbase, (long)g.M * g.c_ld * 2);
   // byte strides (uniform; every per-token offset is below 2^31)
   const uint32_t cld = (uint32_t)(g.c_ld * 2);
-  // bias: read once per tile, or once per m block next to a residual (which
-  // needs the registers)
   v2u32 bias[16];
-  uint32_t boff = lds_addr(sbias) + 2 * nb;
-  auto read_bias = [&]() {
-#pragma unroll
-    for (int j = 0; j < 4; ++j)
-#pragma unroll
-      for (int q = 0; q < 4; ++q)
-        bias[4 * j + q] = *reinterpret_cast<const __attribute__((address_space(3))) v2u32*>(
-            (uintptr_t)(boff + 2 * (32 * j + 8 * q)));
-  };
-  if constexpr (BIAS && !RES) read_bias();
+  __amdgpu_buffer_rsrc_t brs;
+  if constexpr (BIAS) {
+    brs = make_rsrc(reinterpret_cast<const char*>(g.bias) + (long)c.t * g.bias_bs * 2, (long)g.N * 2);
+    if constexpr (!RES) load_row4x16(bias, g, brs, 0u, c.n0 + nb, true);
+  }
   v2u32 res[2][16];
   __amdgpu_buffer_rsrc_t rrs;
   uint32_t rld = 0;
@@ -355,19 +393,16 @@ __device__ __forceinline__ void epilogue(const f32x16_t (&acc)[4][4], const Gemm
     const char* rbase = reinterpret_cast<const char*>(g.res) + (long)c.t * g.res_bs * 2;
     rrs = make_rsrc(rbase, (long)g.M * g.res_ld * 2);
     rld = (uint32_t)(g.res_ld * 2);
-    load_residual(res[0], g, rrs, rld, mb, c.n0 + nb, mb < g.M);
+    load_row4x16(res[0], g, rrs, (uint32_t)mb * rld, c.n0 + nb, mb < g.M);
   }
 #pragma unroll
   for (int i = 0; i < 4; ++i) {
     __builtin_amdgcn_sched_barrier(0);
     const int m = mb + 32 * i;
     const bool mok = m < g.M;
+    if constexpr (BIAS && RES) load_row4x16(bias, g, brs, 0u, c.n0 + nb, true);
     if constexpr (RES) {
-      if (i < 3) load_residual(res[(i + 1) & 1], g, rrs, rld, m + 32, c.n0 + nb, m + 32 < g.M);
-    }
-    if constexpr (BIAS && RES) {
-      asm volatile("" : "+v"(boff));  // a fresh read per m block, not 64 values kept live
-      read_bias();
+      if (i < 3) load_row4x16(res[(i + 1) & 1], g, rrs, (uint32_t)(m + 32) * rld, c.n0 + nb, m + 32 < g.M);
     }
 #pragma unroll
     for (int j = 0; j < 4; ++j) {
@@ -405,20 +440,29 @@ __device__ __forceinline__ void epilogue(const f32x16_t (&acc)[4][4], const Gemm
   __builtin_amdgcn_sched_barrier(0);
 }
 
-// One slab step.  On entry f0 holds slab k's first-k-step fragments (stage
-// sa/sb).  The second, third and fourth k steps' fragments are read while
-// the previous k step's MFMAs issue; then this wave waits for its LDS reads
-// and for slab k+1 (stage na/nb): at most WAIT newer vector-memory
-// operations (the previous tile's stores at a tile's first step, none
-// otherwise), and the workgroup barrier; the stage just freed receives slab
-// k+2 (this tile's, DMA == 1, or the next tile's, DMA == 2, when there is one;
-// that tile's bias first); the next slab's first fragments are read during
-// the last k step's MFMAs.
-template <typename ST, bool AK, bool BKM, bool ZERO, int DMA, bool BIAS>
+// Wait counts of the slab steps (see gemm256_body).
+constexpr int WAIT_STEADY = DMA_PER_OPERAND;
+constexpr int WAIT_AFTER_EPILOGUE = DMA_PER_OPERAND + EPI_STORES;
+static_assert(WAIT_AFTER_EPILOGUE <= 63, "vmcnt range");
+
+// Where a slab step's copies come from: this tile's slab (CUR), the next
+// tile's (NXT, only when there is a next tile), or nothing.
+enum { FROM_CUR = 0, FROM_NXT = 1 };
+
+// One slab step k of a tile with nk slabs.  On entry f0 holds slab k's
+// first-k-step fragments (A stage sa, B stage sb).  The second, third and
+// fourth k steps' fragments are read while the previous k step's MFMAs
+// issue; then this wave waits for its LDS reads and for slab k+1 (stages na,
+// nb), leaving at most `wait` newer vector-memory operations in flight (the
+// caller's count, see gemm256_body), and the workgroup barrier.  The stages
+// just freed receive A slab k+2 (sa) and B slab k+3 (sb): from this tile
+// (k+2 < nk, k+3 < nk) or the next one (when there is one).  The next slab's
+// first fragments are read during the last k step's MFMAs.
+template <typename ST, bool AK, bool BKM, bool ZERO, int SRC_A, int SRC_B>
 __device__ __forceinline__ void slab_step(f32x16_t (&acc)[4][4], Frags& f0, Frags& f1, char* sa, char* sb,
-                                          const char* na, const char* nb, int kdma, bool tile_start, bool has_next,
-                                          const GemmArgs& g, const Src& src, const Tile& nt, char* nbias, int wm,
-                                          int wn, int wave, int lane) {
+                                          const char* na, const char* nb, int k, int nk, int wait,
+                                          const GemmArgs& g, const Src& cur, const Src& nxt, int wm, int wn, int wave,
+                                          int lane) {
   constexpr int NR = (AK ? 4 : 8) + (BKM ? 4 : 8);
   read_frags<AK, BKM>(f1, sa, sb, wm, wn, 1, lane);
   mfma16<ST, ZERO>(acc, f0);
@@ -431,20 +475,15 @@ __device__ __forceinline__ void slab_step(f32x16_t (&acc)[4][4], Frags& f0, Frag
   read_frags<AK, BKM>(f1, sa, sb, wm, wn, 3, lane);
   mfma16<ST, false>(acc, f0);
   interleave<NR>();
-  if (tile_start) sync_slab<EPI_STORES>();  // >= EPI_STORES stores are newer than slab k+1's copies
-  else sync_slab<0>();
-  if constexpr (DMA == 1) {
-    dma_pair<AK, BKM>(sa, sb, src, g, kdma, wave);
-  } else {
-    if (has_next) {
-      if (BIAS && kdma == 0 && wave == 0) dma_bias(nbias, g, nt, lane);
-      dma_pair<AK, BKM>(sa, sb, src, g, kdma, wave);
-    }
-  }
-  __builtin_amdgcn_sched_barrier(0);
-  read_frags<AK, BKM>(f0, na, nb, wm, wn, 0, lane);
-  mfma16<ST, false>(acc, f1);
-  interleave<NR>();
+  if (wait == WAIT_AFTER_EPILOGUE) sync_slab<WAIT_AFTER_EPILOGUE>();
+  else sync_slab<WAIT_STEADY>();
+  // copies into the freed stages: A slab k+2 and B slab k+3, from this tile or the next one
+  const Src& srca = SRC_A == FROM_CUR ? cur : nxt;
+  const Src& srcb = SRC_B == FROM_CUR ? cur : nxt;
+  const uint32_t koffa = slab_koff<AK>(g.a_ld, SRC_A == FROM_CUR ? k + 2 : k + 2 - nk);
+  const uint32_t koffb = slab_koff<BKM>(g.b_ld, SRC_B == FROM_CUR ? k + 3 : k + 3 - nk);
+  last_kstep<ST, AK, BKM>(acc, f1, f0, na, nb, sa, sb, srca.A, srca.offa, koffa, srcb.B, srcb.offb, koffb, wm, wn,
+                          wave, lane);
 }
 
 // Persistent kernel: one workgroup per CU.  Workgroup w runs on XCD w % 8;
@@ -452,23 +491,35 @@ __device__ __forceinline__ void slab_step(f32x16_t (&acc)[4][4], Frags& f0, Frag
 // tile, then M tile) and its workgroups take every (grid/8)-th tile of it, so
 // the tiles in flight on one XCD share operands in that XCD's L2.
 //
-// Pipeline (slab index s runs on across tiles, stage s % 2; nk is even): step
-// k copies slab k+2 into the stage freed by slab k, after the barrier that
-// waits for slab k+1, the only copy then in flight.  The last two steps of a
-// tile copy the next tile's slabs 0 and 1; the tile's EPI_STORES stores follow,
-// so at the next tile's first wait at least EPI_STORES operations are newer
-// than the awaited slab: vmcnt(EPI_STORES).
+// Pipeline.  Slab index s runs on across tiles (nk, the slabs per tile, is
+// even).  A slabs use a ring of 2 LDS stages (s % 2), B slabs a ring of 3
+// (rotating at run time): the whole 160 KB of LDS.  Step k, once slab k is
+// fully read, copies A slab k+2 and then B slab k+3 into the stages it frees,
+// so one A slab and two B slabs are in flight while a slab is multiplied
+// (B, the operand with more misses in L2, runs one slab further ahead: a
+// copy-only run of these operand streams delivers 15-20 % more bytes per
+// clock with B two slabs ahead than with both one ahead).  The copies of the
+// last three steps of a tile come from the next tile (if any).
+//
+// Wait counts (vector-memory operations complete in issue order; every wave
+// issues DMA_PER_OPERAND copies per operand and slab, on every step, also
+// when they have no source).  Step k waits for slab k+1, whose last copy is
+// A(k+1), issued at step k-1 just before B(k+2):
+//   * steady state: B(k+2) may stay in flight: WAIT_STEADY = DMA_PER_OPERAND;
+//   * a tile's first step (not the first tile): the previous tile's epilogue
+//     (EPI_STORES stores, every one issued) follows B(k+2):
+//     WAIT_AFTER_EPILOGUE = DMA_PER_OPERAND + EPI_STORES.
+// The first tile's prologue issues A(0) B(0) A(1) B(1) B(2), waits for slab
+// 0 with the last three in flight, and its first step keeps B(2) in flight.
+// The kernel ends with a wait for every copy.
+
 template <typename ST, bool AK, bool BKM, bool BIAS, bool RES>
 __device__ __forceinline__ void gemm256_body(const GemmArgs& g) {
-  // stage s: A slab at sA + s * TILE_BYTES, B slab at sB + s * TILE_BYTES;
-  // bias tiles double buffered
-  __shared__ __attribute__((aligned(1024))) char sA[STAGES * TILE_BYTES];
-  __shared__ __attribute__((aligned(1024))) char sB[STAGES * TILE_BYTES];
-  __shared__ __attribute__((aligned(1024))) char sbias[2][1024];
+  // A ring: sA + s * TILE_BYTES, s = 0, 1; B ring: sB + r * TILE_BYTES, r = 0, 1, 2
+  __shared__ __attribute__((aligned(1024))) char sA[2 * TILE_BYTES];
+  __shared__ __attribute__((aligned(1024))) char sB[3 * TILE_BYTES];
   char* const a0 = sA;
-  char* const b0 = sB;
   char* const a1 = sA + TILE_BYTES;
-  char* const b1 = sB + TILE_BYTES;
 
   const int tid = threadIdx.x, lane = tid & 63;
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);  // uniform per wave: scalar address arithmetic
@@ -486,51 +537,91 @@ __device__ __forceinline__ void gemm256_body(const GemmArgs& g) {
   Tile ct = tile_of(tile, tiles_m, per_t);
   Src cur;
   tile_src<AK, BKM>(cur, g, ct, wave, lane);
-  const int nk = g.K / BK;  // even, at least 2
-  if (BIAS && wave == 0) dma_bias(sbias[0], g, ct, lane);
-  dma_pair<AK, BKM>(a0, b0, cur, g, 0, wave);
-  dma_pair<AK, BKM>(a1, b1, cur, g, 1, wave);
-  sync_slab<DMA_PER_SLAB>();
+  const int nk = g.K / BK;  // even, at least 4
+  // B stage of the slab being multiplied (rotates 0, 1, 2 with the global slab index)
+  int rb = 0;
+  auto bst = [&](int r) { return sB + r * TILE_BYTES; };
+  auto nxt3 = [](int r) { return r == 2 ? 0 : r + 1; };
+  dma_operand<AK>(a0, cur.A, cur.offa, g.a_ld, 0, wave);
+  dma_operand<BKM>(bst(0), cur.B, cur.offb, g.b_ld, 0, wave);
+  dma_operand<AK>(a1, cur.A, cur.offa, g.a_ld, 1, wave);
+  dma_operand<BKM>(bst(1), cur.B, cur.offb, g.b_ld, 1, wave);
+  dma_operand<BKM>(bst(2), cur.B, cur.offb, g.b_ld, 2, wave);
+  sync_slab<3 * DMA_PER_OPERAND>();
   Frags f0, f1;
-  read_frags<AK, BKM>(f0, a0, b0, wm, wn, 0, lane);
+  read_frags<AK, BKM>(f0, a0, bst(0), wm, wn, 0, lane);
 
   f32x16_t acc[4][4];
   bool first = true;
-  for (int it = 0;; ++it) {
+  for (;;) {
     const int next = tile + nslots;
     const bool has_next = next < hi;
     const Tile nt = tile_of(has_next ? next : tile, tiles_m, per_t);
     Src nxt;
-    tile_src<AK, BKM>(nxt, g, nt, wave, lane);
-    char* nbias = sbias[(it + 1) & 1];
+    tile_src<AK, BKM>(nxt, g, nt, wave, lane, has_next);  // extent 0 without a next tile
 
-    // steps 0 .. nk-3 copy this tile's slabs 2 .. nk-1
-    slab_step<ST, AK, BKM, true, 1, BIAS>(acc, f0, f1, a0, b0, a1, b1, 2, !first, has_next, g, cur, nt, nbias, wm, wn, wave,
-                                lane);
-    slab_step<ST, AK, BKM, false, 1, BIAS>(acc, f0, f1, a1, b1, a0, b0, 3, false, has_next, g, cur, nt, nbias, wm, wn, wave,
-                                 lane);
-    for (int k = 2; k < nk - 2; k += 2) {
-      slab_step<ST, AK, BKM, false, 1, BIAS>(acc, f0, f1, a0, b0, a1, b1, k + 2, false, has_next, g, cur, nt, nbias, wm, wn,
-                                   wave, lane);
-      slab_step<ST, AK, BKM, false, 1, BIAS>(acc, f0, f1, a1, b1, a0, b0, k + 3, false, has_next, g, cur, nt, nbias, wm, wn,
-                                   wave, lane);
+    // step 0 (accumulators start from zero); for nk == 4 it is also step nk-4
+    {
+      char* sb = bst(rb);
+      const char* nb = bst(nxt3(rb));
+      slab_step<ST, AK, BKM, true, FROM_CUR, FROM_CUR>(acc, f0, f1, a0, sb, a1, nb, 0, nk,
+                                                      first ? WAIT_STEADY : WAIT_AFTER_EPILOGUE, g, cur, nxt, wm, wn,
+                                                      wave, lane);
+      rb = nxt3(rb);
     }
-    // steps nk-2, nk-1 copy the next tile's slabs 0, 1 (if any; without a next
-    // tile the last step copies nothing and its fragment reads of stage 0 are
-    // stale and unused: the same code on both paths keeps the accumulators in
-    // AGPRs)
-    slab_step<ST, AK, BKM, false, 2, BIAS>(acc, f0, f1, a0, b0, a1, b1, 0, false, has_next, g, nxt, nt, nbias, wm, wn, wave,
-                                 lane);
-    slab_step<ST, AK, BKM, false, 2, BIAS>(acc, f0, f1, a1, b1, a0, b0, 1, false, has_next, g, nxt, nt, nbias, wm, wn, wave,
-                                 lane);
+    // steps 1 .. nk-4 in pairs (A stages 1, 0): every copy from this tile
+    for (int k = 1; k + 1 <= nk - 4; k += 2) {
+      {
+        char* sb = bst(rb);
+        const char* nb = bst(nxt3(rb));
+        slab_step<ST, AK, BKM, false, FROM_CUR, FROM_CUR>(acc, f0, f1, a1, sb, a0, nb, k, nk, WAIT_STEADY, g, cur, nxt,
+                                                         wm, wn, wave, lane);
+        rb = nxt3(rb);
+      }
+      {
+        char* sb = bst(rb);
+        const char* nb = bst(nxt3(rb));
+        slab_step<ST, AK, BKM, false, FROM_CUR, FROM_CUR>(acc, f0, f1, a0, sb, a1, nb, k + 1, nk, WAIT_STEADY, g, cur,
+                                                         nxt, wm, wn, wave, lane);
+        rb = nxt3(rb);
+      }
+    }
+    // step nk-3 (A stage 1): A slab nk-1 of this tile, B slab 0 of the next
+    {
+      char* sb = bst(rb);
+      const char* nb = bst(nxt3(rb));
+      slab_step<ST, AK, BKM, false, FROM_CUR, FROM_NXT>(acc, f0, f1, a1, sb, a0, nb, nk - 3, nk, WAIT_STEADY, g, cur,
+                                                       nxt, wm, wn, wave, lane);
+      rb = nxt3(rb);
+    }
+    // steps nk-2 (A stage 0) and nk-1 (A stage 1): the next tile's A slabs 0, 1 and B slabs 1, 2.
+    // Without a next tile these copies read nothing (extent 0) and fill freed stages with
+    // zeros, and the last step's fragment reads of the next stages are unused: the same code
+    // on both paths keeps the accumulators in AGPRs.
+    {
+      char* sb = bst(rb);
+      const char* nb = bst(nxt3(rb));
+      slab_step<ST, AK, BKM, false, FROM_NXT, FROM_NXT>(acc, f0, f1, a0, sb, a1, nb, nk - 2, nk, WAIT_STEADY, g, cur,
+                                                       nxt, wm, wn, wave, lane);
+      rb = nxt3(rb);
+    }
+    {
+      char* sb = bst(rb);
+      const char* nb = bst(nxt3(rb));
+      slab_step<ST, AK, BKM, false, FROM_NXT, FROM_NXT>(acc, f0, f1, a1, sb, a0, nb, nk - 1, nk, WAIT_STEADY, g, cur,
+                                                       nxt, wm, wn, wave, lane);
+      rb = nxt3(rb);
+    }
 
-    epilogue<ST, BIAS, RES>(acc, g, ct, sbias[it & 1], wm, wn, lane);
+    epilogue<ST, BIAS, RES>(acc, g, ct, wm, wn, lane);
     if (!has_next) break;
     tile = next;
     ct = nt;
     cur = nxt;
     first = false;
   }
+  // the last tile's empty copies still write LDS: let every copy land before the workgroup ends
+  __builtin_amdgcn_s_waitcnt(0x0F70);  // vmcnt(0)
 }
 
 
