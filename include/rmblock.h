@@ -62,7 +62,8 @@ typedef enum {
   RM_E_WORKSPACE = 4,  /* ws_bytes < rm_workspace_bytes(dims)                  */
   RM_E_DTYPE = 5,      /* dtype is not RM_F32, RM_BF16 or RM_F16               */
   RM_E_HIP = 6,        /* a HIP launch or runtime call failed                  */
-  RM_E_ARG = 7         /* any other invalid argument                            */
+  RM_E_ARG = 7,        /* any other invalid argument                            */
+  RM_E_SCRATCH = 8     /* rm_block_bwd_static: scratch beyond its static buffer */
 } rm_status;
 
 /* Kernel-set choice, per call (rm_dims.flags).  By default (0) shapes with
@@ -117,6 +118,27 @@ rm_status rm_block_fwd(const rm_dims* dims, const rm_params* p, const void* x, v
  * again with the same ws.  Calls on one ws must not overlap in time. */
 rm_status rm_block_bwd(const rm_dims* dims, const rm_params* p, const void* x, const void* dy,
                        void* ws, size_t ws_bytes, void* dx, const rm_grads* g, void* stream);
+
+/* Backward for callers that cannot allocate device memory (code under HIP
+ * graph capture, tight serving loops, harnesses that forbid hipMalloc): the
+ * same computation and results as rm_block_bwd, with the backward's scratch
+ * (d out2, d hidden, dZ, d out1, d r1, gradient partials) in a static device
+ * array of RM_STATIC_SCRATCH_BYTES that the library holds on each GPU it runs
+ * on until the process ends, instead of in the caller's workspace.
+ *   - ws needs to hold only the regions the forward saves: ws_bytes >= offset
+ *     + bytes of region RM_WS_STATS (rm_ws_region), the start of a workspace
+ *     that rm_block_fwd filled (a full rm_workspace_bytes() one is fine).
+ *   - Shapes whose scratch exceeds RM_STATIC_SCRATCH_BYTES get RM_E_SCRATCH
+ *     and nothing is launched (the small workloads of the pages fit; the
+ *     production shape B1024 T64 D1280 needs rm_block_bwd).
+ *   - Allocates nothing (no hipMalloc, hipFree or allocating library call;
+ *     the instrumentation rm_prof_* must be off).
+ *   - Every call on one GPU shares that GPU's array, which keeps the last
+ *     call's contents (nothing in it needs to start at zero): calls that
+ *     overlap in time on one GPU race and give undefined results. */
+#define RM_STATIC_SCRATCH_BYTES (256u << 20)
+rm_status rm_block_bwd_static(const rm_dims* dims, const rm_params* p, const void* x, const void* dy,
+                              void* ws, size_t ws_bytes, void* dx, const rm_grads* g, void* stream);
 
 /* Token mixing alone (page 1, "Exact computation", token mixing paragraph):
  * out[b,i,j*S+s] = in[b,j,i*S+s], S = D/T.  A pure permutation of element bits

@@ -166,3 +166,21 @@ def test_no_oracle_or_fallback_in_product_path():
                 text = open(os.path.join(dirpath, f)).read()
                 assert "import oracle" not in text and "from oracle" not in text, f
                 assert "numpy" not in text, f
+
+
+def test_static_backward_checks_before_any_launch(rb):
+    """rm_block_bwd_static (no allocation; scratch in a static per-GPU buffer) rejects a scratch
+    larger than RM_STATIC_SCRATCH_BYTES and a workspace smaller than the forward's saved regions,
+    before any HIP call."""
+    lib = rb.library()
+    by = ctypes.byref
+    params = rb.rmblock.CParams(*([256] * 14))
+    grads = rb.rmblock.CGrads(*([512] * 14))
+    big = rb.dims(1024, 64, 1280, 2, "bf16")
+    assert lib.rm_block_bwd_static(by(big), by(params), 1024, 1024, 4096, 1 << 40, 2048, by(grads), None) == 8
+    assert lib.rm_status_string(8)
+    small = rb.dims(256, 16, 256, 3, "f32")
+    off, nb = rb.ws_region(small, 4)
+    assert lib.rm_block_bwd_static(by(small), by(params), 1024, 1024, 4096, off + nb - 1, 2048, by(grads), None) == 4
+    # the scratch of the fp32 B256 T16 D256 k3 workload fits the static buffer
+    assert rb.workspace_bytes(small) - (off + nb) <= rb.rmblock.RM_STATIC_SCRATCH_BYTES

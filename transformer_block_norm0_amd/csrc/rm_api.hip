@@ -18,6 +18,7 @@
 //   ln1 bwd    norm1 backward (r1 recomputed via the token-mix gather) => dr1 (+ dgamma1, dbeta1)
 //   ln0 bwd    token-mix adjoint as a gather, norm0 backward, + dr1   => dx (+ dgamma0, dbeta0)
 //   finalize   fixed-order sums of every partial              => parameter gradients
+#include <atomic>
 #include <mutex>
 #include <vector>
 
@@ -60,6 +61,9 @@ WsLayout ws_layout(const rm_dims& d) {
   L.hid = take(N * H * sz);
   L.r2 = take(N * D * sz);
   L.stats = take(ST_COUNT * N * 4);
+  // the backward's scratch: offsets from its own (256-byte aligned) start
+  L.scratch_off = align256(off);
+  off = 0;
   L.do2 = take(N * D * sz);
   L.dhid = take(N * H * sz);
   L.dz = take(N * 2 * H * sz);
@@ -69,7 +73,8 @@ WsLayout ws_layout(const rm_dims& d) {
   L.p_gate = take((4 * nb * T * H + nb * T * 2 * H) * 4);
   // tail partials per (row group, token), or per sample when the tail runs one sample per workgroup
   L.p_tail = take(4 * (sample_in_lds(d) ? (size_t)d.B : nb * T) * D * 4);
-  L.total = align256(off);
+  L.scratch_bytes = align256(off);
+  L.total = L.scratch_off + L.scratch_bytes;
   return L;
 }
 
@@ -142,7 +147,10 @@ namespace {
 
 bool aligned(const void* p, size_t a) { return (reinterpret_cast<uintptr_t>(p) % a) == 0; }
 
-rm_status check_common(const rm_dims* dims, const rm_params* p, const void* ws, size_t ws_bytes) {
+// need_saved_only: the workspace has to hold the forward's saved regions only
+// (rm_block_bwd_static), not the backward's scratch as well.
+rm_status check_common(const rm_dims* dims, const rm_params* p, const void* ws, size_t ws_bytes,
+                       bool need_saved_only = false) {
   if (!dims || !p) return RM_E_NULL;
   if (dims->dtype != RM_F32 && dims->dtype != RM_BF16 && dims->dtype != RM_F16) return RM_E_DTYPE;
   if (!dims_valid(*dims)) return RM_E_DIMS;
@@ -156,7 +164,9 @@ rm_status check_common(const rm_dims* dims, const rm_params* p, const void* ws, 
   }
   if (!ws) return RM_E_NULL;
   if (!aligned(ws, 256)) return RM_E_ALIGN;
-  if (ws_bytes < ws_layout(*dims).total) return RM_E_WORKSPACE;
+  const WsLayout L = ws_layout(*dims);
+  const size_t saved_end = L.stats + (size_t)ST_COUNT * dims->B * dims->T * 4;  // end of the last saved region
+  if (ws_bytes < (need_saved_only ? saved_end : L.total)) return RM_E_WORKSPACE;
   return RM_OK;
 }
 
@@ -164,6 +174,97 @@ rm_status hip_status(hipError_t e) { return e == hipSuccess ? RM_OK : RM_E_HIP; 
 
 // The small-batch kernels run this call: its shape fits them and the caller did not ask for the main kernels.
 bool use_small(const rm_dims& d) { return !(d.flags & RM_FLAG_MAIN_KERNELS) && small_supported(d); }
+
+// Scratch of rm_block_bwd_static: the backward's scratch regions (d out2,
+// d hidden, dZ, d out1, d r1 and the parameter-gradient partials) for shapes
+// whose scratch fits.  One array per GPU the library runs on, held until the
+// process ends.  In host code `scratch` is a stand-in, not a device address:
+// host code uses only the per-device address that static_scratch() obtains.
+__device__ __align__(256) char scratch[RM_STATIC_SCRATCH_BYTES];
+
+// Per-device address of `scratch`, looked up once per device (with that
+// device current) and kept.
+std::atomic<void*> g_scratch_ptr[64];
+std::mutex g_scratch_mu;
+
+rm_status static_scratch(void** out) {
+  int dev = 0;
+  if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= 64) return RM_E_HIP;
+  void* ptr = g_scratch_ptr[dev].load(std::memory_order_acquire);
+  if (!ptr) {
+    std::lock_guard<std::mutex> lk(g_scratch_mu);
+    ptr = g_scratch_ptr[dev].load(std::memory_order_relaxed);
+    if (!ptr) {
+      if (hipGetSymbolAddress(&ptr, HIP_SYMBOL(scratch)) != hipSuccess || !ptr) return RM_E_HIP;
+      g_scratch_ptr[dev].store(ptr, std::memory_order_release);
+    }
+  }
+  *out = ptr;
+  return RM_OK;
+}
+
+// Checks of the backward's arguments other than the workspace size.
+rm_status check_bwd_args(const rm_dims* dims, const void* x, const void* dy, void* dx, const rm_grads* g) {
+  if (!x || !dy || !dx || !g) return RM_E_NULL;
+  const size_t es = dims->dtype == RM_F32 ? 4 : 2;
+  if (!aligned(x, es) || !aligned(dy, es) || !aligned(dx, es)) return RM_E_ALIGN;
+  const void* gptrs[] = {g->w1, g->b1, g->wout, g->bout, g->lnx_g, g->lnx_b, g->lng_g,
+                         g->lng_b, g->ln0_g, g->ln0_b, g->ln1_g, g->ln1_b, g->ln2_g, g->ln2_b};
+  for (const void* q : gptrs) {
+    if (!q) return RM_E_NULL;
+    if (!aligned(q, es)) return RM_E_ALIGN;
+  }
+  return RM_OK;
+}
+
+// The backward's launch sequence: the forward's saved regions in ws, the
+// scratch regions (layout offsets from the scratch start) at sc.
+rm_status backward(const rm_dims& d, const rm_params* p, const void* x, const void* dy, void* ws, void* sc,
+                   void* dx, const rm_grads* g, hipStream_t s) {
+  const WsLayout L = ws_layout(d);
+  char* w = reinterpret_cast<char*>(ws);
+  char* c = reinterpret_cast<char*>(sc);
+  const long T = d.T, D = d.D, H = (long)d.k * d.D;
+  hipError_t e;
+  if (use_small(d)) return hip_status(launch_small_bwd(d, *p, x, dy, ws, sc, L, dx, *g, s));
+
+  if ((e = launch_ln2_bwd(d, *p, dy, ws, sc, L, s)) != hipSuccess) return hip_status(e);
+
+  GemmArgs a{};
+  a.M = d.B; a.N = H; a.K = D; a.batch = T;
+  a.A = c + L.do2; a.a_bs = D; a.a_ld = T * D;
+  a.B = p->wout; a.b_bs = H * D; a.b_ld = D;
+  a.C = c + L.dhid; a.c_bs = H; a.c_ld = T * H; a.c_f32 = 0;
+  if ((e = launch_gemm(d.dtype, true, true, a, KID_GEMM_DHID, s)) != hipSuccess) return hip_status(e);
+
+  if ((e = launch_gate_bwd(d, *p, ws, sc, L, s)) != hipSuccess) return hip_status(e);
+
+  GemmArgs wo{};
+  wo.M = H; wo.N = D; wo.K = d.B; wo.batch = T;
+  wo.A = w + L.hid; wo.a_bs = H; wo.a_ld = T * H;
+  wo.B = c + L.do2; wo.b_bs = D; wo.b_ld = T * D;
+  wo.C = g->wout; wo.c_bs = H * D; wo.c_ld = D; wo.c_f32 = 0;
+  if ((e = launch_gemm(d.dtype, false, false, wo, KID_GEMM_DWOUT, s)) != hipSuccess) return hip_status(e);
+
+  GemmArgs w1g{};
+  w1g.M = D; w1g.N = 2 * H; w1g.K = d.B; w1g.batch = T;
+  w1g.A = w + L.h1; w1g.a_bs = D; w1g.a_ld = T * D;
+  w1g.B = c + L.dz; w1g.b_bs = 2 * H; w1g.b_ld = T * 2 * H;
+  w1g.C = g->w1; w1g.c_bs = D * 2 * H; w1g.c_ld = 2 * H; w1g.c_f32 = 0;
+  if ((e = launch_gemm(d.dtype, false, false, w1g, KID_GEMM_DW1, s)) != hipSuccess) return hip_status(e);
+
+  GemmArgs dh{};
+  dh.M = d.B; dh.N = D; dh.K = 2 * H; dh.batch = T;
+  dh.A = c + L.dz; dh.a_bs = 2 * H; dh.a_ld = T * 2 * H;
+  dh.B = p->w1; dh.b_bs = D * 2 * H; dh.b_ld = 2 * H;
+  dh.C = c + L.dh1; dh.c_bs = D; dh.c_ld = T * D; dh.c_f32 = d.dtype == RM_F32;
+  dh.res = c + L.do2; dh.res_bs = D; dh.res_ld = T * D; dh.res_f32 = 0;
+  if ((e = launch_gemm(d.dtype, true, true, dh, KID_GEMM_DH1, s)) != hipSuccess) return hip_status(e);
+
+  if ((e = launch_tail_bwd(d, *p, x, dx, ws, sc, L, s)) != hipSuccess) return hip_status(e);
+  if ((e = launch_finalize(d, *g, sc, L, s)) != hipSuccess) return hip_status(e);
+  return RM_OK;
+}
 
 }  // namespace
 
@@ -181,6 +282,9 @@ const char* rm_status_string(int s) {
     case RM_E_DTYPE: return "dtype must be RM_F32, RM_BF16 or RM_F16";
     case RM_E_HIP: return "HIP launch or runtime error";
     case RM_E_ARG: return "invalid argument";
+    case RM_E_SCRATCH:
+      return "backward scratch larger than RM_STATIC_SCRATCH_BYTES (rm_block_bwd_static); use rm_block_bwd with a "
+             "workspace of rm_workspace_bytes()";
     default: return "unknown status";
   }
 }
@@ -247,63 +351,28 @@ rm_status rm_block_fwd(const rm_dims* dims, const rm_params* p, const void* x, v
   return RM_OK;
 }
 
+
+
 rm_status rm_block_bwd(const rm_dims* dims, const rm_params* p, const void* x, const void* dy, void* ws,
                        size_t ws_bytes, void* dx, const rm_grads* g, void* stream) {
   rm_status st = check_common(dims, p, ws, ws_bytes);
   if (st != RM_OK) return st;
-  if (!x || !dy || !dx || !g) return RM_E_NULL;
-  const size_t es = dims->dtype == RM_F32 ? 4 : 2;
-  if (!aligned(x, es) || !aligned(dy, es) || !aligned(dx, es)) return RM_E_ALIGN;
-  const void* gptrs[] = {g->w1, g->b1, g->wout, g->bout, g->lnx_g, g->lnx_b, g->lng_g,
-                         g->lng_b, g->ln0_g, g->ln0_b, g->ln1_g, g->ln1_b, g->ln2_g, g->ln2_b};
-  for (const void* q : gptrs) {
-    if (!q) return RM_E_NULL;
-    if (!aligned(q, es)) return RM_E_ALIGN;
-  }
-  const rm_dims d = *dims;
-  const WsLayout L = ws_layout(d);
-  hipStream_t s = reinterpret_cast<hipStream_t>(stream);
-  char* w = reinterpret_cast<char*>(ws);
-  const long T = d.T, D = d.D, H = (long)d.k * d.D;
-  hipError_t e;
-  if (use_small(d)) return hip_status(launch_small_bwd(d, *p, x, dy, ws, L, dx, *g, s));
+  if ((st = check_bwd_args(dims, x, dy, dx, g)) != RM_OK) return st;
+  const WsLayout L = ws_layout(*dims);
+  return backward(*dims, p, x, dy, ws, reinterpret_cast<char*>(ws) + L.scratch_off, dx, g,
+                  reinterpret_cast<hipStream_t>(stream));
+}
 
-  if ((e = launch_ln2_bwd(d, *p, dy, ws, L, s)) != hipSuccess) return hip_status(e);
-
-  GemmArgs a{};
-  a.M = d.B; a.N = H; a.K = D; a.batch = T;
-  a.A = w + L.do2; a.a_bs = D; a.a_ld = T * D;
-  a.B = p->wout; a.b_bs = H * D; a.b_ld = D;
-  a.C = w + L.dhid; a.c_bs = H; a.c_ld = T * H; a.c_f32 = 0;
-  if ((e = launch_gemm(d.dtype, true, true, a, KID_GEMM_DHID, s)) != hipSuccess) return hip_status(e);
-
-  if ((e = launch_gate_bwd(d, *p, ws, L, s)) != hipSuccess) return hip_status(e);
-
-  GemmArgs wo{};
-  wo.M = H; wo.N = D; wo.K = d.B; wo.batch = T;
-  wo.A = w + L.hid; wo.a_bs = H; wo.a_ld = T * H;
-  wo.B = w + L.do2; wo.b_bs = D; wo.b_ld = T * D;
-  wo.C = g->wout; wo.c_bs = H * D; wo.c_ld = D; wo.c_f32 = 0;
-  if ((e = launch_gemm(d.dtype, false, false, wo, KID_GEMM_DWOUT, s)) != hipSuccess) return hip_status(e);
-
-  GemmArgs w1g{};
-  w1g.M = D; w1g.N = 2 * H; w1g.K = d.B; w1g.batch = T;
-  w1g.A = w + L.h1; w1g.a_bs = D; w1g.a_ld = T * D;
-  w1g.B = w + L.dz; w1g.b_bs = 2 * H; w1g.b_ld = T * 2 * H;
-  w1g.C = g->w1; w1g.c_bs = D * 2 * H; w1g.c_ld = 2 * H; w1g.c_f32 = 0;
-  if ((e = launch_gemm(d.dtype, false, false, w1g, KID_GEMM_DW1, s)) != hipSuccess) return hip_status(e);
-
-  GemmArgs dh{};
-  dh.M = d.B; dh.N = D; dh.K = 2 * H; dh.batch = T;
-  dh.A = w + L.dz; dh.a_bs = 2 * H; dh.a_ld = T * 2 * H;
-  dh.B = p->w1; dh.b_bs = D * 2 * H; dh.b_ld = 2 * H;
-  dh.C = w + L.dh1; dh.c_bs = D; dh.c_ld = T * D; dh.c_f32 = d.dtype == RM_F32;
-  dh.res = w + L.do2; dh.res_bs = D; dh.res_ld = T * D; dh.res_f32 = 0;
-  if ((e = launch_gemm(d.dtype, true, true, dh, KID_GEMM_DH1, s)) != hipSuccess) return hip_status(e);
-
-  if ((e = launch_tail_bwd(d, *p, x, dx, ws, L, s)) != hipSuccess) return hip_status(e);
-  if ((e = launch_finalize(d, *g, ws, L, s)) != hipSuccess) return hip_status(e);
-  return RM_OK;
+rm_status rm_block_bwd_static(const rm_dims* dims, const rm_params* p, const void* x, const void* dy, void* ws,
+                              size_t ws_bytes, void* dx, const rm_grads* g, void* stream) {
+  rm_status st = check_common(dims, p, ws, ws_bytes, true);
+  if (st != RM_OK) return st;
+  if ((st = check_bwd_args(dims, x, dy, dx, g)) != RM_OK) return st;
+  const WsLayout L = ws_layout(*dims);
+  if (L.scratch_bytes > RM_STATIC_SCRATCH_BYTES) return RM_E_SCRATCH;
+  void* sc = nullptr;
+  if ((st = static_scratch(&sc)) != RM_OK) return st;
+  return backward(*dims, p, x, dy, ws, sc, dx, g, reinterpret_cast<hipStream_t>(stream));
 }
 
 rm_status rm_token_mix(const rm_dims* dims, const void* in, void* out, void* stream) {

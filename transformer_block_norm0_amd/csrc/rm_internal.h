@@ -37,12 +37,16 @@ enum KernelId {
 
 extern const char* const kKernelNames[KID_COUNT];
 
-// Byte offsets into the caller's workspace.
+// Workspace layout.  The regions the forward saves for the backward come
+// first, at byte offsets from the workspace's start; the backward's scratch
+// follows at scratch_off, its regions at byte offsets from the scratch start
+// (so the scratch may also live elsewhere: rm_block_bwd_static).
 struct WsLayout {
-  size_t h1, z, hid, r2, stats;            // written by the forward, read by the backward
-  size_t do2, dhid, dz, dh1, dr1;          // backward scratch
-  size_t p_ln2, p_gate, p_tail;            // backward partial sums (fp32)
-  size_t total;
+  size_t h1, z, hid, r2, stats;            // saved by the forward: offsets from the workspace start
+  size_t do2, dhid, dz, dh1, dr1;          // backward scratch: offsets from the scratch start
+  size_t p_ln2, p_gate, p_tail;            // backward partial sums (fp32): offsets from the scratch start
+  size_t scratch_off, scratch_bytes;       // where the scratch starts in the workspace, its size
+  size_t total;                            // scratch_off + scratch_bytes
   int nb;                                  // row groups per token: ceil(B / ROWS_PER_GROUP)
 };
 
@@ -98,13 +102,14 @@ hipError_t launch_gate_fwd(const rm_dims& d, const rm_params& p, void* ws, const
                            hipStream_t s);
 hipError_t launch_ln2_fwd(const rm_dims& d, const rm_params& p, void* y, void* ws,
                           const WsLayout& L, hipStream_t s);
-hipError_t launch_ln2_bwd(const rm_dims& d, const rm_params& p, const void* dy, void* ws,
+// Backward launchers: ws holds the forward's saved regions, sc the scratch.
+hipError_t launch_ln2_bwd(const rm_dims& d, const rm_params& p, const void* dy, void* ws, void* sc,
                           const WsLayout& L, hipStream_t s);
-hipError_t launch_gate_bwd(const rm_dims& d, const rm_params& p, void* ws, const WsLayout& L,
+hipError_t launch_gate_bwd(const rm_dims& d, const rm_params& p, void* ws, void* sc, const WsLayout& L,
                            hipStream_t s);
-hipError_t launch_tail_bwd(const rm_dims& d, const rm_params& p, const void* x, void* dx, void* ws,
+hipError_t launch_tail_bwd(const rm_dims& d, const rm_params& p, const void* x, void* dx, void* ws, void* sc,
                            const WsLayout& L, hipStream_t s);
-hipError_t launch_finalize(const rm_dims& d, const rm_grads& g, void* ws, const WsLayout& L,
+hipError_t launch_finalize(const rm_dims& d, const rm_grads& g, void* sc, const WsLayout& L,
                            hipStream_t s);
 hipError_t launch_token_mix(const rm_dims& d, const void* in, void* out, hipStream_t s);
 
@@ -117,7 +122,7 @@ constexpr int SMALL_MAX_B = 8, SMALL_MAX_D = 128, SMALL_MAX_H = 256;
 bool small_supported(const rm_dims& d);
 hipError_t launch_small_fwd(const rm_dims& d, const rm_params& p, const void* x, void* y, void* ws,
                             const WsLayout& L, hipStream_t s);
-hipError_t launch_small_bwd(const rm_dims& d, const rm_params& p, const void* x, const void* dy, void* ws,
+hipError_t launch_small_bwd(const rm_dims& d, const rm_params& p, const void* x, const void* dy, void* ws, void* sc,
                             const WsLayout& L, void* dx, const rm_grads& g, hipStream_t s);
 
 }  // namespace rm

@@ -1601,27 +1601,27 @@ hipError_t ln2_fwd_t(const rm_dims& d, const rm_params& p, void* y, void* ws, co
 }
 
 template <typename ST>
-hipError_t ln2_bwd_t(const rm_dims& d, const rm_params& p, const void* dy, void* ws, const WsLayout& L,
+hipError_t ln2_bwd_t(const rm_dims& d, const rm_params& p, const void* dy, void* ws, void* sc, const WsLayout& L,
                      hipStream_t s) {
   const dim3 grid(d.T, L.nb);
   prof_begin(KID_LN2_BWD, s);
   if (d.D % 4 == 0)
     hipLaunchKernelGGL((k_ln2_bwd<ST, 4, MAXD / 256>), grid, dim3(256), 0, s, wsp<ST>(ws, L.r2), cptr<ST>(dy),
-                       cptr<ST>(p.ln2_g), wsp<float>(ws, L.stats), wsp<ST>(ws, L.do2), wsp<float>(ws, L.p_ln2), d.B,
+                       cptr<ST>(p.ln2_g), wsp<float>(ws, L.stats), wsp<ST>(sc, L.do2), wsp<float>(sc, L.p_ln2), d.B,
                        d.T, d.D, L.nb);
   else
     hipLaunchKernelGGL((k_ln2_bwd<ST, 1, MAXD / 64>), grid, dim3(256), 0, s, wsp<ST>(ws, L.r2), cptr<ST>(dy),
-                       cptr<ST>(p.ln2_g), wsp<float>(ws, L.stats), wsp<ST>(ws, L.do2), wsp<float>(ws, L.p_ln2), d.B,
+                       cptr<ST>(p.ln2_g), wsp<float>(ws, L.stats), wsp<ST>(sc, L.do2), wsp<float>(sc, L.p_ln2), d.B,
                        d.T, d.D, L.nb);
   prof_end(KID_LN2_BWD, s);
   return hipGetLastError();
 }
 
 template <typename ST>
-hipError_t gate_bwd_t(const rm_dims& d, const rm_params& p, void* ws, const WsLayout& L, hipStream_t s) {
+hipError_t gate_bwd_t(const rm_dims& d, const rm_params& p, void* ws, void* sc, const WsLayout& L, hipStream_t s) {
   const int H = d.k * d.D;
   constexpr int NV = 16 / sizeof(ST);
-  float* pg = wsp<float>(ws, L.p_gate);
+  float* pg = wsp<float>(sc, L.p_gate);
   float* pb1 = pg + 4L * L.nb * d.T * H;
   const dim3 grid(d.T, L.nb);
   prof_begin(KID_GATE_BWD, s);
@@ -1629,65 +1629,66 @@ hipError_t gate_bwd_t(const rm_dims& d, const rm_params& p, void* ws, const WsLa
   // one workgroup of H/4 threads per row group (up to 640: 10 waves, room for the prefetch ring)
   if (H % 4 == 0 && H <= 2560 && 2L * d.B * d.T * H * (long)sizeof(ST) <= 0x7fffffffL)
     hipLaunchKernelGGL((k_gate_bwd_ring<ST, 640>), grid, dim3(round64(H / 4)), 0, s, wsp<ST>(ws, L.z),
-                       wsp<ST>(ws, L.dhid), cptr<ST>(p.lnx_g), cptr<ST>(p.lnx_b), cptr<ST>(p.lng_g),
-                       cptr<ST>(p.lng_b), wsp<float>(ws, L.stats), wsp<ST>(ws, L.dz), pg, pb1, d.B, d.T, H, L.nb);
+                       wsp<ST>(sc, L.dhid), cptr<ST>(p.lnx_g), cptr<ST>(p.lnx_b), cptr<ST>(p.lng_g),
+                       cptr<ST>(p.lng_b), wsp<float>(ws, L.stats), wsp<ST>(sc, L.dz), pg, pb1, d.B, d.T, H, L.nb);
   else if (H % 4 == 0)
     hipLaunchKernelGGL((k_gate_bwd<ST, 4, 1, 1024, 2>), grid, dim3(round64(H / 4)), 0, s, wsp<ST>(ws, L.z),
-                       wsp<ST>(ws, L.dhid), cptr<ST>(p.lnx_g), cptr<ST>(p.lnx_b), cptr<ST>(p.lng_g),
-                       cptr<ST>(p.lng_b), wsp<float>(ws, L.stats), wsp<ST>(ws, L.dz), pg, pb1, d.B, d.T, H, L.nb);
+                       wsp<ST>(sc, L.dhid), cptr<ST>(p.lnx_g), cptr<ST>(p.lnx_b), cptr<ST>(p.lng_g),
+                       cptr<ST>(p.lng_b), wsp<float>(ws, L.stats), wsp<ST>(sc, L.dz), pg, pb1, d.B, d.T, H, L.nb);
   else
     hipLaunchKernelGGL((k_gate_bwd<ST, 1, 8, 512, 1>), grid, dim3(round64((H + 7) / 8)), 0, s, wsp<ST>(ws, L.z),
-                       wsp<ST>(ws, L.dhid), cptr<ST>(p.lnx_g), cptr<ST>(p.lnx_b), cptr<ST>(p.lng_g),
-                       cptr<ST>(p.lng_b), wsp<float>(ws, L.stats), wsp<ST>(ws, L.dz), pg, pb1, d.B, d.T, H, L.nb);
+                       wsp<ST>(sc, L.dhid), cptr<ST>(p.lnx_g), cptr<ST>(p.lnx_b), cptr<ST>(p.lng_g),
+                       cptr<ST>(p.lng_b), wsp<float>(ws, L.stats), wsp<ST>(sc, L.dz), pg, pb1, d.B, d.T, H, L.nb);
   prof_end(KID_GATE_BWD, s);
   return hipGetLastError();
 }
 
 template <typename ST>
-hipError_t tail_bwd_t(const rm_dims& d, const rm_params& p, const void* x, void* dx, void* ws, const WsLayout& L,
+hipError_t tail_bwd_t(const rm_dims& d, const rm_params& p, const void* x, void* dx, void* ws, void* sc,
+                      const WsLayout& L,
                       hipStream_t s) {
   const dim3 grid(d.T, L.nb);
   hipError_t e;
   if constexpr (sizeof(ST) == 2) {
     if (sample_in_lds(d)) {
       prof_begin(KID_TAIL_BWD, s);
-      hipLaunchKernelGGL(k_tail_bwd_lds<ST>, dim3(d.B), dim3(512), 0, s, cptr<ST>(x), wsp<ST>(ws, L.dh1),
+      hipLaunchKernelGGL(k_tail_bwd_lds<ST>, dim3(d.B), dim3(512), 0, s, cptr<ST>(x), wsp<ST>(sc, L.dh1),
                          cptr<ST>(p.ln0_g), cptr<ST>(p.ln0_b), cptr<ST>(p.ln1_g), wsp<float>(ws, L.stats),
-                         reinterpret_cast<ST*>(dx), wsp<float>(ws, L.p_tail), d.B, d.T, d.D);
+                         reinterpret_cast<ST*>(dx), wsp<float>(sc, L.p_tail), d.B, d.T, d.D);
       prof_end(KID_TAIL_BWD, s);
       return hipGetLastError();
     }
   }
   prof_begin(KID_LN1_BWD, s);
   if (vec4_rows(d))
-    hipLaunchKernelGGL((k_ln1_bwd<ST, 4, MAXD / 256>), grid, dim3(256), 0, s, cptr<ST>(x), wsp<ST>(ws, L.dh1),
+    hipLaunchKernelGGL((k_ln1_bwd<ST, 4, MAXD / 256>), grid, dim3(256), 0, s, cptr<ST>(x), wsp<ST>(sc, L.dh1),
                        cptr<ST>(p.ln0_g), cptr<ST>(p.ln0_b), cptr<ST>(p.ln1_g), wsp<float>(ws, L.stats),
-                       wsp<ST>(ws, L.dr1), wsp<float>(ws, L.p_tail), d.B, d.T, d.D, L.nb);
+                       wsp<ST>(sc, L.dr1), wsp<float>(sc, L.p_tail), d.B, d.T, d.D, L.nb);
   else
-    hipLaunchKernelGGL((k_ln1_bwd<ST, 1, MAXD / 64>), grid, dim3(256), 0, s, cptr<ST>(x), wsp<ST>(ws, L.dh1),
+    hipLaunchKernelGGL((k_ln1_bwd<ST, 1, MAXD / 64>), grid, dim3(256), 0, s, cptr<ST>(x), wsp<ST>(sc, L.dh1),
                        cptr<ST>(p.ln0_g), cptr<ST>(p.ln0_b), cptr<ST>(p.ln1_g), wsp<float>(ws, L.stats),
-                       wsp<ST>(ws, L.dr1), wsp<float>(ws, L.p_tail), d.B, d.T, d.D, L.nb);
+                       wsp<ST>(sc, L.dr1), wsp<float>(sc, L.p_tail), d.B, d.T, d.D, L.nb);
   prof_end(KID_LN1_BWD, s);
   if ((e = hipGetLastError()) != hipSuccess) return e;
   prof_begin(KID_LN0_BWD, s);
   if (vec4_rows(d))
-    hipLaunchKernelGGL((k_ln0_bwd<ST, 4, MAXD / 256>), grid, dim3(256), 0, s, cptr<ST>(x), wsp<ST>(ws, L.dr1),
+    hipLaunchKernelGGL((k_ln0_bwd<ST, 4, MAXD / 256>), grid, dim3(256), 0, s, cptr<ST>(x), wsp<ST>(sc, L.dr1),
                        cptr<ST>(p.ln0_g), wsp<float>(ws, L.stats), reinterpret_cast<ST*>(dx),
-                       wsp<float>(ws, L.p_tail), d.B, d.T, d.D, L.nb);
+                       wsp<float>(sc, L.p_tail), d.B, d.T, d.D, L.nb);
   else
-    hipLaunchKernelGGL((k_ln0_bwd<ST, 1, MAXD / 64>), grid, dim3(256), 0, s, cptr<ST>(x), wsp<ST>(ws, L.dr1),
+    hipLaunchKernelGGL((k_ln0_bwd<ST, 1, MAXD / 64>), grid, dim3(256), 0, s, cptr<ST>(x), wsp<ST>(sc, L.dr1),
                        cptr<ST>(p.ln0_g), wsp<float>(ws, L.stats), reinterpret_cast<ST*>(dx),
-                       wsp<float>(ws, L.p_tail), d.B, d.T, d.D, L.nb);
+                       wsp<float>(sc, L.p_tail), d.B, d.T, d.D, L.nb);
   prof_end(KID_LN0_BWD, s);
   return hipGetLastError();
 }
 
 template <typename ST>
-hipError_t finalize_t(const rm_dims& d, const rm_grads& g, void* ws, const WsLayout& L, hipStream_t s) {
+hipError_t finalize_t(const rm_dims& d, const rm_grads& g, void* sc, const WsLayout& L, hipStream_t s) {
   const int T = d.T, D = d.D, H = d.k * d.D, nb = L.nb;
-  const float* pl = wsp<float>(ws, L.p_ln2);
-  const float* pg = wsp<float>(ws, L.p_gate);
-  const float* pt = wsp<float>(ws, L.p_tail);
+  const float* pl = wsp<float>(sc, L.p_ln2);
+  const float* pg = wsp<float>(sc, L.p_gate);
+  const float* pt = wsp<float>(sc, L.p_tail);
   const long bl = (long)nb * T * D, bg = (long)nb * T * H;
   RedJobs J;
   J.j[0] = {pl + 0 * bl, D, nb * T, D, g.ln2_g, 0};
@@ -1732,19 +1733,19 @@ hipError_t launch_ln2_fwd(const rm_dims& d, const rm_params& p, void* y, void* w
                           hipStream_t s) {
   return RM_DISPATCH(ln2_fwd_t, d, p, y, ws, L, s);
 }
-hipError_t launch_ln2_bwd(const rm_dims& d, const rm_params& p, const void* dy, void* ws, const WsLayout& L,
+hipError_t launch_ln2_bwd(const rm_dims& d, const rm_params& p, const void* dy, void* ws, void* sc, const WsLayout& L,
                           hipStream_t s) {
-  return RM_DISPATCH(ln2_bwd_t, d, p, dy, ws, L, s);
+  return RM_DISPATCH(ln2_bwd_t, d, p, dy, ws, sc, L, s);
 }
-hipError_t launch_gate_bwd(const rm_dims& d, const rm_params& p, void* ws, const WsLayout& L, hipStream_t s) {
-  return RM_DISPATCH(gate_bwd_t, d, p, ws, L, s);
+hipError_t launch_gate_bwd(const rm_dims& d, const rm_params& p, void* ws, void* sc, const WsLayout& L, hipStream_t s) {
+  return RM_DISPATCH(gate_bwd_t, d, p, ws, sc, L, s);
 }
-hipError_t launch_tail_bwd(const rm_dims& d, const rm_params& p, const void* x, void* dx, void* ws,
+hipError_t launch_tail_bwd(const rm_dims& d, const rm_params& p, const void* x, void* dx, void* ws, void* sc,
                            const WsLayout& L, hipStream_t s) {
-  return RM_DISPATCH(tail_bwd_t, d, p, x, dx, ws, L, s);
+  return RM_DISPATCH(tail_bwd_t, d, p, x, dx, ws, sc, L, s);
 }
-hipError_t launch_finalize(const rm_dims& d, const rm_grads& g, void* ws, const WsLayout& L, hipStream_t s) {
-  return RM_DISPATCH(finalize_t, d, g, ws, L, s);
+hipError_t launch_finalize(const rm_dims& d, const rm_grads& g, void* sc, const WsLayout& L, hipStream_t s) {
+  return RM_DISPATCH(finalize_t, d, g, sc, L, s);
 }
 hipError_t launch_token_mix(const rm_dims& d, const void* in, void* out, hipStream_t s) {
   const long rows = (long)d.B * d.T;

@@ -45,7 +45,8 @@ struct SmallArgs {
   rm_params p;
   rm_grads g;
   void *y, *dx;
-  char* ws;
+  char* ws;  // the forward's saved regions (layout offsets from ws)
+  char* sc;  // the backward's scratch (layout offsets from sc)
   WsLayout L;
   int B, T, D, H;
 };
@@ -351,11 +352,11 @@ __global__ __launch_bounds__(FWD_THREADS) void k_small_bwd_tok(SmallArgs a) {
   const auto P = [&](const void* q) { return reinterpret_cast<const ST*>(q); };
   const ST* x = P(a.x);
   const float* stats = reinterpret_cast<const float*>(a.ws + a.L.stats);
-  float* p_ln2 = reinterpret_cast<float*>(a.ws + a.L.p_ln2);    // [2][T][D]: dgamma2, dbeta2
-  float* p_gate = reinterpret_cast<float*>(a.ws + a.L.p_gate);  // [4][T][H]: dgamma_x, dbeta_x, dgamma_g, dbeta_g
+  float* p_ln2 = reinterpret_cast<float*>(a.sc + a.L.p_ln2);    // [2][T][D]: dgamma2, dbeta2
+  float* p_gate = reinterpret_cast<float*>(a.sc + a.L.p_gate);  // [4][T][H]: dgamma_x, dbeta_x, dgamma_g, dbeta_g
   // [2][T][D]: dgamma1, dbeta1, in the dZ region (dZ stays in LDS here; its
   // B*T*2H storage elements hold 2*T*D floats for every B >= 1, k >= 2)
-  float* p_ln1 = reinterpret_cast<float*>(a.ws + a.L.dz);
+  float* p_ln1 = reinterpret_cast<float*>(a.sc + a.L.dz);
   const int b = wave;
   const long row = (long)b * T + t;
 
@@ -564,7 +565,7 @@ __global__ __launch_bounds__(FWD_THREADS) void k_small_bwd_tok(SmallArgs a) {
       s2 += dn[q] * n1[q];
     }
     const float m1 = wave_sum(s1) / (float)D, m2 = wave_sum(s2) / (float)D;
-    ST* dr1 = reinterpret_cast<ST*>(a.ws + a.L.dr1);
+    ST* dr1 = reinterpret_cast<ST*>(a.sc + a.L.dr1);
     float pa[QD];
 #pragma unroll
     for (int q = 0; q < QD; ++q) {
@@ -589,7 +590,7 @@ __global__ __launch_bounds__(FIN_THREADS) void k_small_bwd_fin(SmallArgs a) {
   const long NR = (long)B * T;
   const auto P = [&](const void* q) { return reinterpret_cast<const ST*>(q); };
   const ST* x = P(a.x);
-  const ST* dr1 = P(a.ws + a.L.dr1);
+  const ST* dr1 = P(a.sc + a.L.dr1);
   const float* stats = reinterpret_cast<const float*>(a.ws + a.L.stats);
   ST* dx = reinterpret_cast<ST*>(a.dx);
 
@@ -642,9 +643,9 @@ __global__ __launch_bounds__(FIN_THREADS) void k_small_bwd_fin(SmallArgs a) {
   }
 
   // per-token partials summed over t in order
-  const float* p_ln2 = reinterpret_cast<const float*>(a.ws + a.L.p_ln2);
-  const float* p_gate = reinterpret_cast<const float*>(a.ws + a.L.p_gate);
-  const float* p_ln1 = reinterpret_cast<const float*>(a.ws + a.L.dz);
+  const float* p_ln2 = reinterpret_cast<const float*>(a.sc + a.L.p_ln2);
+  const float* p_gate = reinterpret_cast<const float*>(a.sc + a.L.p_gate);
+  const float* p_ln1 = reinterpret_cast<const float*>(a.sc + a.L.dz);
   // every (job, column) pair on its own thread; the token rows are loaded
   // eight at a time before they are added in order
   const int ncol = 4 * D + 4 * H;
@@ -737,9 +738,10 @@ hipError_t launch_small_fwd(const rm_dims& d, const rm_params& p, const void* x,
   return small_fwd_t<float>(a, s);
 }
 
-hipError_t launch_small_bwd(const rm_dims& d, const rm_params& p, const void* x, const void* dy, void* ws,
+hipError_t launch_small_bwd(const rm_dims& d, const rm_params& p, const void* x, const void* dy, void* ws, void* sc,
                             const WsLayout& L, void* dx, const rm_grads& g, hipStream_t s) {
   SmallArgs a = small_args(d, p, x, ws, L);
+  a.sc = reinterpret_cast<char*>(sc);
   a.dy = dy;
   a.dx = dx;
   a.g = g;

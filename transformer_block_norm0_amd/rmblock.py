@@ -24,7 +24,8 @@ PARAM_NAMES = ("w1", "b1", "wout", "bout", "lnx_g", "lnx_b", "lng_g", "lng_b",
                "ln0_g", "ln0_b", "ln1_g", "ln1_b", "ln2_g", "ln2_b")
 
 STATUS = {0: "RM_OK", 1: "RM_E_DIMS", 2: "RM_E_NULL", 3: "RM_E_ALIGN", 4: "RM_E_WORKSPACE",
-          5: "RM_E_DTYPE", 6: "RM_E_HIP", 7: "RM_E_ARG"}
+          5: "RM_E_DTYPE", 6: "RM_E_HIP", 7: "RM_E_ARG", 8: "RM_E_SCRATCH"}
+RM_STATIC_SCRATCH_BYTES = 256 << 20
 
 
 class RmError(RuntimeError):
@@ -69,6 +70,8 @@ def _lib():
                                      ctypes.c_void_p, ctypes.c_size_t, ctypes.c_void_p, P(CGrads),
                                      ctypes.c_void_p]
         lib.rm_block_bwd.restype = ctypes.c_int
+        lib.rm_block_bwd_static.argtypes = lib.rm_block_bwd.argtypes
+        lib.rm_block_bwd_static.restype = ctypes.c_int
         lib.rm_token_mix.argtypes = [P(CDims), ctypes.c_void_p, ctypes.c_void_p, ctypes.c_void_p]
         lib.rm_token_mix.restype = ctypes.c_int
         lib.rm_ws_region.argtypes = [P(CDims), ctypes.c_int, P(ctypes.c_size_t), P(ctypes.c_size_t)]
@@ -191,6 +194,23 @@ def block_bwd(d: CDims, params: dict, x, dy, ws, dx, grads: dict, ws_bytes: int 
                              _ptr(dx), ctypes.byref(cg), _stream(stream))
     if st:
         raise RmError(st, "rm_block_bwd")
+
+
+def block_bwd_static(d: CDims, params: dict, x, dy, ws, dx, grads: dict, ws_bytes: int | None = None, stream=None,
+                     check=True):
+    """rm_block_bwd_static: rm_block_bwd with the backward's scratch in the library's static
+    per-GPU buffer (allocates nothing); ws needs only the forward's saved regions."""
+    if check:
+        for t, n in ((x, "x"), (dy, "dy"), (dx, "dx")):
+            _check(t, d, (d.B, d.T, d.D), n)
+    if ws_bytes is None:
+        ws_bytes = ws.numel() * ws.element_size()
+    cp = _cparams(d, params, CParams, check)
+    cg = _cparams(d, grads, CGrads, check)
+    st = _lib().rm_block_bwd_static(ctypes.byref(d), ctypes.byref(cp), _ptr(x), _ptr(dy), _ptr(ws), ws_bytes,
+                                    _ptr(dx), ctypes.byref(cg), _stream(stream))
+    if st:
+        raise RmError(st, "rm_block_bwd_static")
 
 
 def token_mix(d: CDims, inp, out, stream=None):
