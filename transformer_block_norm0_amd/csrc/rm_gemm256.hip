@@ -363,9 +363,11 @@ __device__ __forceinline__ void load_row4x16(v2u32 (&r)[16], const GemmArgs& g, 
 // bf16.  Lane l holds, per (m block i, n block j, v/4 group q), 4 consecutive
 // columns n = 32j + 8q + 4(l/32) of row m = 32i + l%32.  Lanes l and l+32
 // exchange halves (v_permlane32_swap) so that each lane holds 8 consecutive
-// columns (lane l < 32: 8q..8q+7, lane l+32: 8(q+1)..8(q+1)+7, q = 0, 2) for
-// one 16-byte buffer store: EPI_STORES per wave, every one issued (rows past
-// M or columns past N get an out-of-range offset that the buffer unit drops).
+// columns (lane l < 32: 8q..8q+7, lane l+32: 8(q+1)..8(q+1)+7, q = 0, 2), and
+// the odd and even 16-lane rows exchange the q = 0 and q = 2 sets
+// (v_permlane16_swap), so that each 16-byte buffer store covers 16 rows x 64
+// contiguous bytes: EPI_STORES per wave, every one issued (rows past M or
+// columns past N get an out-of-range offset that the buffer unit drops).
 // BIAS / RES are compile-time, so the epilogue has no branches.  The bias
 // (64 values per lane) is loaded from the token's bias row once per tile, or
 // once per m block next to a residual (which needs the registers); the
@@ -406,6 +408,8 @@ __device__ __forceinline__ void epilogue(const f32x16_t (&acc)[4][4], const Gemm
     }
 #pragma unroll
     for (int j = 0; j < 4; ++j) {
+      // the 16-byte chunks 4j + q/2*2 + h of row m (q = 0, 2), packed
+      v4u32 chunk[2];
 #pragma unroll
       for (int q = 0; q < 4; q += 2) {
         float v0[4], v1[4];
@@ -422,18 +426,31 @@ __device__ __forceinline__ void epilogue(const f32x16_t (&acc)[4][4], const Gemm
           add16x4<ST>(v0, res[i & 1][4 * j + q]);
           add16x4<ST>(v1, res[i & 1][4 * j + q + 1]);
         }
-        uint32_t a0 = pair16<ST>(v0[0], v0[1]), a1 = pair16<ST>(v0[2], v0[3]);
-        uint32_t b0 = pair16<ST>(v1[0], v1[1]), b1 = pair16<ST>(v1[2], v1[3]);
+        const uint32_t a0 = pair16<ST>(v0[0], v0[1]), a1 = pair16<ST>(v0[2], v0[3]);
+        const uint32_t b0 = pair16<ST>(v1[0], v1[1]), b1 = pair16<ST>(v1[2], v1[3]);
         const auto s0 = __builtin_amdgcn_permlane32_swap(a0, b0, false, false);
         const auto s1 = __builtin_amdgcn_permlane32_swap(a1, b1, false, false);
-        a0 = s0[0]; b0 = s0[1];
-        a1 = s1[0]; b1 = s1[1];
-        // now lane < 32 holds (a0 a1 | b0 b1) = columns 8q..8q+7, lane >= 32 (a0 a1 | b0 b1) = 8(q+1)..
-        const int ns = c.n0 + wn * 128 + 32 * j + 8 * (q + h);
-        const bool ok = mok && ns < g.N;
-        const uint32_t co = ok ? (uint32_t)m * cld + (uint32_t)ns * 2 : OUT_OF_RANGE;
-        const v4u32 d = {a0, a1, b0, b1};
-        __builtin_amdgcn_raw_buffer_store_b128(d, crs, co, 0, 0);
+        // lane l < 32: columns 8q..8q+7 of row l (chunk 4j + q); lane l >= 32: 8(q+1).. (chunk 4j + q + 1)
+        chunk[q >> 1] = v4u32{s0[0], s1[0], s0[1], s1[1]};
+      }
+      // Odd 16-lane rows swap with even ones (partner l ^ 16): afterwards store
+      // s (0, 1) holds, in lane l, row 16s + l%16 of the block and its chunk
+      // 4j + 2((l/16)%2) + l/32: 16 rows x 64 contiguous bytes per store.
+      v4u32 st[2];
+#pragma unroll
+      for (int k = 0; k < 4; ++k) {
+        const auto sw = __builtin_amdgcn_permlane16_swap(chunk[0][k], chunk[1][k], false, false);
+        st[0][k] = sw[0];
+        st[1][k] = sw[1];
+      }
+      const int cpos = 2 * ((lane >> 4) & 1) + h;  // chunk within the 32-column block
+      const int ns = c.n0 + wn * 128 + 32 * j + 8 * cpos;
+#pragma unroll
+      for (int sidx = 0; sidx < 2; ++sidx) {
+        const int ms = c.m0 + wm * 128 + 32 * i + (lane & 15) + 16 * sidx;
+        const bool ok = ms < g.M && ns < g.N;
+        const uint32_t co = ok ? (uint32_t)ms * cld + (uint32_t)ns * 2 : OUT_OF_RANGE;
+        __builtin_amdgcn_raw_buffer_store_b128(st[sidx], crs, co, 0, 0);
       }
     }
   }
