@@ -187,11 +187,12 @@ def check_epilogue(g, m0, n0, written, sizes):
     for wave in range(4):
         wm, wn = wave >> 1, wave & 1
         mb = m0 + wm * 128 + r
-        # after the lane-half and 16-lane-row swaps: store s of block (i, j) holds, in lane l,
-        # row 32i + 16s + l%16 and the 16-byte chunk 2((l/16)%2) + l/32 of the 32-column block j
-        for i, j, sidx in itertools.product(range(4), range(4), range(2)):
-            m = m0 + wm * 128 + 32 * i + (lane & 15) + 16 * sidx
-            ns = n0 + wn * 128 + 32 * j + 8 * (2 * ((lane >> 4) & 1) + h)
+        # after the lane-half, 16-lane-row and 8-lane swaps: store (s, u) of block i and column
+        # pair jj holds, in lane l, row 32i + 16s + 8u + l%8 and the 16-byte chunk
+        # 4((l/8)%2) + 2((l/16)%2) + l/32 of the 64 columns 64jj .. 64jj + 63
+        for i, jj, sidx, u in itertools.product(range(4), range(2), range(2), range(2)):
+            m = m0 + wm * 128 + 32 * i + 16 * sidx + 8 * u + (lane & 7)
+            ns = n0 + wn * 128 + 64 * jj + 8 * (4 * ((lane >> 3) & 1) + 2 * ((lane >> 4) & 1) + h)
             ok = (m < M) & (ns < N)
             co = m * g["c_ld"] * 2 + ns * 2
             assert np.all(co[ok] + 16 <= c_ext)

@@ -365,9 +365,11 @@ __device__ __forceinline__ void load_row4x16(v2u32 (&r)[16], const GemmArgs& g, 
 // exchange halves (v_permlane32_swap) so that each lane holds 8 consecutive
 // columns (lane l < 32: 8q..8q+7, lane l+32: 8(q+1)..8(q+1)+7, q = 0, 2), and
 // the odd and even 16-lane rows exchange the q = 0 and q = 2 sets
-// (v_permlane16_swap), so that each 16-byte buffer store covers 16 rows x 64
-// contiguous bytes: EPI_STORES per wave, every one issued (rows past M or
-// columns past N get an out-of-range offset that the buffer unit drops).
+// (v_permlane16_swap), and the halves of each 16-lane row exchange rows of
+// two neighbouring 32-column blocks (DPP rotation by 8), so that each 16-byte
+// buffer store covers 8 rows x 128 contiguous bytes (whole cache lines):
+// EPI_STORES per wave, every one issued (rows past M or columns past N get an
+// out-of-range offset that the buffer unit drops).
 // BIAS / RES are compile-time, so the epilogue has no branches.  The bias
 // (64 values per lane) is loaded from the token's bias row once per tile, or
 // once per m block next to a residual (which needs the registers); the
@@ -406,6 +408,9 @@ __device__ __forceinline__ void epilogue(const f32x16_t (&acc)[4][4], const Gemm
     if constexpr (RES) {
       if (i < 3) load_row4x16(res[(i + 1) & 1], g, rrs, (uint32_t)(m + 32) * rld, c.n0 + nb, m + 32 < g.M);
     }
+    // rows 32i + 16s + l%16 (s = 0, 1) of the 32-column blocks j = 2jj, 2jj + 1,
+    // each lane one 16-byte chunk 2((l/16)%2) + l/32 of its block
+    v4u32 blk[2][2];
 #pragma unroll
     for (int j = 0; j < 4; ++j) {
       // the 16-byte chunks 4j + q/2*2 + h of row m (q = 0, 2), packed
@@ -433,24 +438,44 @@ __device__ __forceinline__ void epilogue(const f32x16_t (&acc)[4][4], const Gemm
         // lane l < 32: columns 8q..8q+7 of row l (chunk 4j + q); lane l >= 32: 8(q+1).. (chunk 4j + q + 1)
         chunk[q >> 1] = v4u32{s0[0], s1[0], s0[1], s1[1]};
       }
-      // Odd 16-lane rows swap with even ones (partner l ^ 16): afterwards store
+      // Odd 16-lane rows swap with even ones (partner l ^ 16): afterwards set
       // s (0, 1) holds, in lane l, row 16s + l%16 of the block and its chunk
-      // 4j + 2((l/16)%2) + l/32: 16 rows x 64 contiguous bytes per store.
-      v4u32 st[2];
+      // 2((l/16)%2) + l/32.
 #pragma unroll
       for (int k = 0; k < 4; ++k) {
         const auto sw = __builtin_amdgcn_permlane16_swap(chunk[0][k], chunk[1][k], false, false);
-        st[0][k] = sw[0];
-        st[1][k] = sw[1];
+        blk[j & 1][0][k] = sw[0];
+        blk[j & 1][1][k] = sw[1];
       }
-      const int cpos = 2 * ((lane >> 4) & 1) + h;  // chunk within the 32-column block
-      const int ns = c.n0 + wn * 128 + 32 * j + 8 * cpos;
+      if (j & 1) {
+        // The two 8-lane halves of each 16-lane row exchange the blocks' rows
+        // 8..15 and 0..7 (rotation by 8 within the row): store 2s + u then
+        // holds, in lane l, row 16s + 8u + l%8 and the 16-byte chunk
+        // 4((l/8)%2) + 2((l/16)%2) + l/32 of the 64 columns 64(j/2) .. +63:
+        // 8 rows x 128 bytes (whole cache lines) per store.
+        const int jj = j >> 1;
+        const bool lo8 = (lane & 8) == 0;
+        const int cpos = 4 * ((lane >> 3) & 1) + 2 * ((lane >> 4) & 1) + h;
+        const int ns = c.n0 + wn * 128 + 64 * jj + 8 * cpos;
 #pragma unroll
-      for (int sidx = 0; sidx < 2; ++sidx) {
-        const int ms = c.m0 + wm * 128 + 32 * i + (lane & 15) + 16 * sidx;
-        const bool ok = ms < g.M && ns < g.N;
-        const uint32_t co = ok ? (uint32_t)ms * cld + (uint32_t)ns * 2 : OUT_OF_RANGE;
-        __builtin_amdgcn_raw_buffer_store_b128(st[sidx], crs, co, 0, 0);
+        for (int sidx = 0; sidx < 2; ++sidx) {
+          v4u32 x, y;
+#pragma unroll
+          for (int k = 0; k < 4; ++k) {
+            const uint32_t p0 = blk[0][sidx][k], p1 = blk[1][sidx][k];
+            const uint32_t r0 = (uint32_t)__builtin_amdgcn_update_dpp(0, (int)p0, 0x128, 0xF, 0xF, false);  // row_ror:8
+            const uint32_t r1 = (uint32_t)__builtin_amdgcn_update_dpp(0, (int)p1, 0x128, 0xF, 0xF, false);
+            x[k] = lo8 ? p0 : r1;
+            y[k] = lo8 ? r0 : p1;
+          }
+#pragma unroll
+          for (int u = 0; u < 2; ++u) {
+            const int ms = c.m0 + wm * 128 + 32 * i + 16 * sidx + 8 * u + (lane & 7);
+            const bool ok = ms < g.M && ns < g.N;
+            const uint32_t co = ok ? (uint32_t)ms * cld + (uint32_t)ns * 2 : OUT_OF_RANGE;
+            __builtin_amdgcn_raw_buffer_store_b128(u == 0 ? x : y, crs, co, 0, 0);
+          }
+        }
       }
     }
   }
