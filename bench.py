@@ -107,6 +107,30 @@ def step_flops(d):
     return 18.0 * d.B * d.T * d.D * d.k * d.D
 
 
+def host_cpu():
+    """CPU model and physical core count of the host, as /proc/cpuinfo states them."""
+    model, cores = "unknown", set()
+    phys = core = None
+    try:
+        for line in open("/proc/cpuinfo"):
+            k, _, v = line.partition(":")
+            k, v = k.strip(), v.strip()
+            if k == "model name" and model == "unknown":
+                model = v
+            elif k == "physical id":
+                phys = v
+            elif k == "core id":
+                core = v
+            elif not k and phys is not None and core is not None:
+                cores.add((phys, core))
+                phys = core = None
+        if phys is not None and core is not None:
+            cores.add((phys, core))
+    except OSError:
+        pass
+    return model, len(cores) or None
+
+
 def cpu_baseline(name, batch, min_seconds):
     """The float64 oracle (unchanged) on the first `batch` samples of the workload."""
     import oracle
@@ -128,9 +152,42 @@ def cpu_baseline(name, batch, min_seconds):
         if el >= min_seconds:
             break
     tokens = reps * d.B * d.T
+    model, physical = host_cpu()
     return {"value": tokens / el, "unit": "tokens/s", "cores": cores, "kind": "oracle",
+            "cpu_model": model, "physical_cores": physical, "threads_available": len(os.sched_getaffinity(0)),
             "sample": f"first {batch} of {WORKLOADS[name].dims.B} samples of {name} "
                       f"(all parameters), float64 fwd+bwd x{reps} in {el:.1f} s"}
+
+
+def library_gemms(d, dtype, reps=10):
+    """The block's six per-token GEMM shapes through torch.bmm (hipBLASLt on this stack), for
+    comparison with the library's kernels: every operand a dense contiguous [T, rows, cols]
+    tensor (no transposed views), so the strides differ from the library's [B, T, .] operands."""
+    import torch
+    B, T, D, H = d.B, d.T, d.D, d.k * d.D
+    tdt = {"bf16": torch.bfloat16, "f16": torch.float16, "f32": torch.float32}[dtype]
+    shapes = {"gemm_up": (B, D, 2 * H), "gemm_down": (B, H, D), "gemm_dhid": (B, D, H),
+              "gemm_dwout": (H, B, D), "gemm_dw1": (D, B, 2 * H), "gemm_dh1": (B, 2 * H, D)}
+    out = {}
+    for name, (m, k, n) in shapes.items():
+        a = torch.randn(T, m, k, device="cuda").to(tdt).contiguous()
+        b = torch.randn(T, k, n, device="cuda").to(tdt).contiguous()
+        c = torch.empty(T, m, n, device="cuda", dtype=tdt)
+        for _ in range(3):
+            torch.bmm(a, b, out=c)
+        torch.cuda.synchronize()
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        e0.record()
+        for _ in range(reps):
+            torch.bmm(a, b, out=c)
+        e1.record()
+        torch.cuda.synchronize()
+        ms = e0.elapsed_time(e1) / reps
+        out[name] = {"avg_ms": round(ms, 5), "tflops": round(2.0 * T * m * k * n / (ms / 1e3) / 1e12, 2)}
+        log(f"  torch.bmm {name} [{T} x {m}x{k} @ {k}x{n}]: {ms:.4f} ms, {out[name]['tflops']} TFLOP/s")
+        del a, b, c
+    torch.cuda.empty_cache()
+    return out
 
 
 def main():
@@ -149,6 +206,8 @@ def main():
     ap.add_argument("--kernels", choices=["auto", "main"], default="auto",
                     help="auto: B<=8, D<=128, H<=256 shapes take the small-batch kernels (3 launches per step); "
                          "main: every shape takes the main kernel set")
+    ap.add_argument("--library-gemms", action="store_true",
+                    help="also time the six GEMM shapes through torch.bmm (hipBLASLt) for comparison")
     ap.add_argument("--copy-calibration-mib", type=int, default=0,
                     help="run one plain device-to-device copy of this many MiB first (reference for HBM counters)")
     args = ap.parse_args()
@@ -373,6 +432,9 @@ def main():
         "graph_replay": graph,
         "kernels": kernels,
     }
+    if args.library_gemms:
+        log("library GEMMs (torch.bmm) on the same shapes:")
+        out["library_gemms"] = library_gemms(d, w.dtype)
     print(json.dumps(out), flush=True)
 
 
