@@ -320,9 +320,19 @@ hipError_t run(const GemmArgs& g, bool vec, hipStream_t s) {
 
 template <typename ST, bool AK, bool BKM>
 hipError_t run_shape(const GemmArgs& g, bool vec, hipStream_t s) {
-  // the larger of M and N gets the 256-wide side of the tile
-  if (g.M >= g.N) return run<ST, AK, BKM, 256, 128>(g, vec, s);
-  return run<ST, AK, BKM, 128, 256>(g, vec, s);
+  const long cus = device_cu_count();
+  auto tiles = [&](int bm, int bn) { return (long)((g.M + bm - 1) / bm) * ((g.N + bn - 1) / bn) * g.batch; };
+  // the larger of M and N gets the 256-wide side of the tile, while that leaves no compute unit idle
+  if (g.M >= g.N && tiles(256, 128) >= cus) return run<ST, AK, BKM, 256, 128>(g, vec, s);
+  if (g.M < g.N && tiles(128, 256) >= cus) return run<ST, AK, BKM, 128, 256>(g, vec, s);
+  // few tiles (small B or few tokens): smaller tiles spread the work over more compute units.  A
+  // 64-wide side needs a K-major operand on it (the M/N-major loader covers 128 rows at least).
+  if (tiles(128, 128) >= cus) return run<ST, AK, BKM, 128, 128>(g, vec, s);
+  if constexpr (AK) {
+    if (!BKM || g.M >= g.N) return run<ST, AK, BKM, 64, 128>(g, vec, s);
+  }
+  if constexpr (BKM) return run<ST, AK, BKM, 128, 64>(g, vec, s);
+  return run<ST, AK, BKM, 128, 128>(g, vec, s);
 }
 
 template <typename ST>
