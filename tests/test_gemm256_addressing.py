@@ -275,29 +275,61 @@ def test_replica_catches_a_planted_slip():
 
 DMA_PER_OPERAND = 8
 EPI_STORES = 32
+# B pieces of a slab issued in the last k step of the step that frees its stage; the
+# rest follow, spread over the first three k steps of the next step
+B_LATE = 0
+
+
+# A pieces of the last k step after MFMAs A_STRIDE * x; late B pieces in the other slots
+A_STRIDE = 2
+
+
+def b_early_begin(ks):
+    return B_LATE + ((DMA_PER_OPERAND - B_LATE) * ks) // 3
+
+
+def last_kstep_slots():
+    """Operand of the copy issued after each of the last k step's 16 MFMAs (or None)."""
+    slots = []
+    for x in range(16):
+        if x % A_STRIDE == 0 and x // A_STRIDE < DMA_PER_OPERAND:
+            slots.append("A")
+        elif (A_STRIDE == 1 and DMA_PER_OPERAND <= x < DMA_PER_OPERAND + B_LATE) or \
+                (A_STRIDE == 2 and x % 2 == 1 and x // 2 < B_LATE):
+            slots.append("B")
+        else:
+            slots.append(None)
+    return slots
+
+
 WAIT_STEADY = DMA_PER_OPERAND
 WAIT_AFTER_EPILOGUE = DMA_PER_OPERAND + EPI_STORES
 
 
 def simulate_pipeline(nk, ntiles, epilogue_extra=0):
     """Replays the kernel's per-wave event sequence for `ntiles` tiles of `nk` slabs: copy issues
-    (A ring of 2 stages, B ring of 3; the last tile's next-tile copies are issued too, through a
-    resource of extent 0), the epilogue's vector-memory operations, waits (vmcnt N + barrier)
-    and the fragment reads of each slab.  Vector-memory operations complete in issue order, so
-    after a wait with count N every operation but the newest N is complete.  Checks that every
-    slab's copies are complete before its first read, that no copy targets a stage whose
-    previous slab may still be read, and that no copy is in flight at the end."""
+    piece by piece (A ring of 2 stages, B ring of 3; A slab k+2 and the first B_LATE pieces of
+    B slab k+3 in step k's last k step, the other B pieces of slab k+2 in the first k steps of
+    step k; the last tile's next-tile copies are issued too, through a resource of extent 0),
+    the epilogue's vector-memory operations, waits (vmcnt N + barrier) and the fragment reads of
+    each slab.  Vector-memory operations complete in issue order, so after a wait with count N
+    every operation but the newest N is complete.  Checks that every slab's copies are all
+    issued and complete before its first read, that no copy targets a stage whose previous slab
+    may still be read, and that no copy is in flight at the end."""
     ops = []               # ("A"|"B"|"E", slab)
     done = 0               # ops[:done] complete
     stage_of = {}          # (operand, global slab) -> stage
+    pieces = {}            # (operand, global slab) -> pieces issued
     reading = {}           # (operand, stage) -> global slab whose reads are not yet fenced
 
-    def issue(op, slab):
+    def issue(op, slab, n):
         ring = 2 if op == "A" else 3
         st = slab % ring
         assert (op, st) not in reading or reading[(op, st)] is None, f"{op} stage {st} overwritten while read"
         stage_of[(op, slab)] = st
-        ops.extend([(op, slab)] * DMA_PER_OPERAND)   # one 16-byte copy per lane and instruction
+        pieces[(op, slab)] = pieces.get((op, slab), 0) + n
+        assert pieces[(op, slab)] <= DMA_PER_OPERAND
+        ops.extend([(op, slab)] * n)   # one 16-byte copy per lane and instruction
 
     def wait(n):
         nonlocal done
@@ -307,27 +339,33 @@ def simulate_pipeline(nk, ntiles, epilogue_extra=0):
 
     def read(slab):
         for op in ("A", "B"):
-            assert (op, slab) in stage_of, f"slab {slab} {op} never copied"
+            assert pieces.get((op, slab), 0) == DMA_PER_OPERAND, f"slab {slab} {op} not fully copied"
             last = len(ops) - 1 - ops[::-1].index((op, slab))
             assert last < done, f"slab {slab} {op} read before its copy completed"
             reading[(op, stage_of[(op, slab)])] = slab
 
     S = lambda t, k: t * nk + k          # global slab index
     # prologue
-    for op, k in (("A", 0), ("B", 0), ("A", 1), ("B", 1), ("B", 2)):
-        issue(op, S(0, k))
-    wait(3 * DMA_PER_OPERAND)
+    issue("A", S(0, 0), DMA_PER_OPERAND)
+    issue("B", S(0, 0), DMA_PER_OPERAND)
+    issue("A", S(0, 1), DMA_PER_OPERAND)
+    issue("B", S(0, 1), DMA_PER_OPERAND)
+    issue("B", S(0, 2), B_LATE)
+    wait(2 * DMA_PER_OPERAND + B_LATE)
     read(S(0, 0))                          # first k step's fragments
     for t in range(ntiles):
         has_next = t + 1 < ntiles
         for k in range(nk):
-            read(S(t, k))                  # k steps 1..3 of slab k
+            # k steps 0..2: the rest of B slab k+2, then k steps 1..3's fragments of slab k
+            for ks in range(3):
+                issue("B", S(t, k + 2), b_early_begin(ks + 1) - b_early_begin(ks))
+            read(S(t, k))
             wait(WAIT_AFTER_EPILOGUE if (k == 0 and t > 0) else WAIT_STEADY)
-            ka, kb = k + 2, k + 3
             # copies of the next tile are issued even without one (slab indices past the last
             # tile: empty copies into freed stages)
-            issue("A", S(t, ka))
-            issue("B", S(t, kb))
+            for op in last_kstep_slots():
+                if op is not None:
+                    issue(op, S(t, k + 2) if op == "A" else S(t, k + 3), 1)
             if k + 1 < nk:
                 read(S(t, k + 1))          # next slab's first fragments
             elif has_next:
@@ -343,6 +381,19 @@ def simulate_pipeline(nk, ntiles, epilogue_extra=0):
 def test_gemm256_pipeline_waits(nk, ntiles):
     simulate_pipeline(nk, ntiles)
     simulate_pipeline(nk, ntiles, epilogue_extra=64 + 64)   # residual and bias loads in the epilogue
+
+
+def test_pipeline_replica_catches_late_b_between_a_pieces():
+    """Late B pieces interleaved with A's leave fewer than DMA_PER_OPERAND copies after A's
+    last piece, so the steady wait would let A pieces stay in flight: the replica must say so."""
+    global A_STRIDE, B_LATE
+    saved = A_STRIDE, B_LATE
+    A_STRIDE, B_LATE = 2, 2
+    try:
+        with pytest.raises(AssertionError):
+            simulate_pipeline(20, 2)
+    finally:
+        A_STRIDE, B_LATE = saved
 
 
 def test_pipeline_replica_catches_a_short_wait():

@@ -91,6 +91,28 @@ __device__ __forceinline__ int mswz(int krow, int chunk) { return krow * 512 + (
 // k-rows 16w + 2i, +1 (lane l -> k-row +l/32, physical chunk l%32); each lane
 // fetches the logical chunk that the swizzle places there.
 constexpr int DMA_PER_OPERAND = 8;
+// B pieces of a slab issued in the last k step of the step that frees its
+// stage; the other pieces follow, spread over the starts of the next step's
+// first three k steps, so that no k step issues more than 10 copies per wave.
+constexpr int B_LATE = 0;
+static_assert(B_LATE >= 0 && B_LATE <= DMA_PER_OPERAND, "B pieces per slab");
+// first B piece issued in k step ks = 0..3 of the following step (3: none left)
+constexpr int b_early_begin(int ks) { return B_LATE + ((DMA_PER_OPERAND - B_LATE) * ks) / 3; }
+// Slots of the last k step (after MFMA x = 0..15): the A piece or the late B
+// piece issued there, or -1.  A_STRIDE 1: A after MFMAs 0..7, late B after
+// 8..; A_STRIDE 2: A after the even MFMAs, late B after the odd ones.
+constexpr int A_STRIDE = 2;
+static_assert(A_STRIDE == 1 || A_STRIDE == 2, "A slot spacing");
+// the waits count DMA_PER_OPERAND B pieces after A's last piece: late B pieces
+// may only follow every A piece
+static_assert(A_STRIDE == 1 || B_LATE == 0, "late B pieces between A pieces");
+constexpr int a_slot_piece(int x) {
+  return (x % A_STRIDE == 0 && x / A_STRIDE < DMA_PER_OPERAND) ? x / A_STRIDE : -1;
+}
+constexpr int b_slot_piece(int x) {
+  return A_STRIDE == 1 ? ((x >= DMA_PER_OPERAND && x - DMA_PER_OPERAND < B_LATE) ? x - DMA_PER_OPERAND : -1)
+                       : ((x % 2 == 1 && x / 2 < B_LATE) ? x / 2 : -1);
+}
 constexpr int DMA_PER_SLAB = 2 * DMA_PER_OPERAND;  // per wave, A and B
 template <bool KMAJ>
 __device__ __forceinline__ void slab_offsets(uint32_t (&off)[DMA_PER_OPERAND], long ld, int mn0, int MN, int wave,
@@ -303,12 +325,24 @@ __device__ __forceinline__ uint32_t slab_koff(long ld, int kslab) {
   return (uint32_t)(KMAJ ? (long)kslab * BK * 2 : (long)kslab * BK * ld * 2);
 }
 
+// B pieces b_early_begin(ks) .. b_early_begin(ks + 1) - 1 of a slab into its
+// stage (k step ks = 0, 1, 2 of the step after the one that issued the slab's
+// first pieces), fenced from the surrounding schedule.
+template <bool KMAJ, int KS>
+__device__ __forceinline__ void early_b(char* stage, __amdgpu_buffer_rsrc_t rs, const uint32_t (&off)[DMA_PER_OPERAND],
+                                        uint32_t koff, int wave) {
+  __builtin_amdgcn_sched_barrier(0);
+#pragma unroll
+  for (int i = b_early_begin(KS); i < b_early_begin(KS + 1); ++i) dma_piece<KMAJ>(stage, rs, off[i], koff, i, wave);
+  __builtin_amdgcn_sched_barrier(0);
+}
+
 // The last k step of a slab: its 16 MFMAs, with the copies of the freed
-// stages (8 A pieces, then 8 B pieces) issued one after each MFMA and the
-// next slab's first-k-step fragments read after MFMAs 8..15.  Each group is
-// fenced (sched_barrier), so the copies issue in the shadow of the MFMAs
-// instead of as a burst while the matrix pipe waits.  There are no branches:
-// copies that have no source go through a resource of extent 0.
+// stages (8 A pieces, then the first B_LATE B pieces) issued one after each
+// MFMA and the next slab's first-k-step fragments read after MFMAs 8..15.
+// Each group is fenced (sched_barrier), so the copies issue in the shadow of
+// the MFMAs instead of as a burst while the matrix pipe waits.  There are no
+// branches: copies that have no source go through a resource of extent 0.
 template <typename ST, bool AK, bool BKM>
 __device__ __forceinline__ void last_kstep(f32x16_t (&acc)[4][4], const Frags& f1, Frags& f0, const char* na,
                                            const char* nb, char* sa, char* sb, __amdgpu_buffer_rsrc_t rsa,
@@ -324,10 +358,9 @@ __device__ __forceinline__ void last_kstep(f32x16_t (&acc)[4][4], const Frags& f
     else
       acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(__builtin_bit_cast(bf16x8_t, f1.b[j]),
                                                           __builtin_bit_cast(bf16x8_t, f1.a[i]), acc[i][j], 0, 0, 0);
-    if (x < 8) {
-      dma_piece<AK>(sa, rsa, offa[x], koffa, x, wave);
-    } else {
-      dma_piece<BKM>(sb, rsb, offb[x - 8], koffb, x - 8, wave);
+    if (a_slot_piece(x) >= 0) dma_piece<AK>(sa, rsa, offa[a_slot_piece(x)], koffa, a_slot_piece(x), wave);
+    if (b_slot_piece(x) >= 0) dma_piece<BKM>(sb, rsb, offb[b_slot_piece(x)], koffb, b_slot_piece(x), wave);
+    if (x >= 8) {
       const int r = x - 8;
       if (r < 4) f0.a[r] = read_frag<AK>(na, wm * 128 + 32 * r, 0, lane);
       else f0.b[r - 4] = read_frag<BKM>(nb, wn * 128 + 32 * (r - 4), 0, lane);
@@ -502,25 +535,31 @@ enum { FROM_CUR = 0, FROM_NXT = 1 };
 // first fragments are read during the last k step's MFMAs.
 template <typename ST, bool AK, bool BKM, bool ZERO, int SRC_A, int SRC_B>
 __device__ __forceinline__ void slab_step(f32x16_t (&acc)[4][4], Frags& f0, Frags& f1, char* sa, char* sb,
-                                          const char* na, const char* nb, int k, int nk, int wait,
+                                          const char* na, const char* nb, char* eb, int k, int nk, int wait,
                                           const GemmArgs& g, const Src& cur, const Src& nxt, int wm, int wn, int wave,
                                           int lane) {
   constexpr int NR = (AK ? 4 : 8) + (BKM ? 4 : 8);
+  // B slab k+2 (stage eb, freed by the previous step) comes from where A slab k+2 does
+  const Src& srca = SRC_A == FROM_CUR ? cur : nxt;
+  const uint32_t koffe = slab_koff<BKM>(g.b_ld, SRC_A == FROM_CUR ? k + 2 : k + 2 - nk);
+  early_b<BKM, 0>(eb, srca.B, srca.offb, koffe, wave);
   read_frags<AK, BKM>(f1, sa, sb, wm, wn, 1, lane);
   mfma16<ST, ZERO>(acc, f0);
   interleave<NR>();
   __builtin_amdgcn_sched_barrier(0);
+  early_b<BKM, 1>(eb, srca.B, srca.offb, koffe, wave);
   read_frags<AK, BKM>(f0, sa, sb, wm, wn, 2, lane);
   mfma16<ST, false>(acc, f1);
   interleave<NR>();
   __builtin_amdgcn_sched_barrier(0);
+  early_b<BKM, 2>(eb, srca.B, srca.offb, koffe, wave);
   read_frags<AK, BKM>(f1, sa, sb, wm, wn, 3, lane);
   mfma16<ST, false>(acc, f0);
   interleave<NR>();
   if (wait == WAIT_AFTER_EPILOGUE) sync_slab<WAIT_AFTER_EPILOGUE>();
   else sync_slab<WAIT_STEADY>();
-  // copies into the freed stages: A slab k+2 and B slab k+3, from this tile or the next one
-  const Src& srca = SRC_A == FROM_CUR ? cur : nxt;
+  // copies into the freed stages: A slab k+2 and the first B pieces of slab k+3,
+  // from this tile or the next one
   const Src& srcb = SRC_B == FROM_CUR ? cur : nxt;
   const uint32_t koffa = slab_koff<AK>(g.a_ld, SRC_A == FROM_CUR ? k + 2 : k + 2 - nk);
   const uint32_t koffb = slab_koff<BKM>(g.b_ld, SRC_B == FROM_CUR ? k + 3 : k + 3 - nk);
@@ -536,24 +575,28 @@ __device__ __forceinline__ void slab_step(f32x16_t (&acc)[4][4], Frags& f0, Frag
 // Pipeline.  Slab index s runs on across tiles (nk, the slabs per tile, is
 // even).  A slabs use a ring of 2 LDS stages (s % 2), B slabs a ring of 3
 // (rotating at run time): the whole 160 KB of LDS.  Step k, once slab k is
-// fully read, copies A slab k+2 and then B slab k+3 into the stages it frees,
-// so one A slab and two B slabs are in flight while a slab is multiplied
-// (B, the operand with more misses in L2, runs one slab further ahead: a
-// copy-only run of these operand streams delivers 15-20 % more bytes per
-// clock with B two slabs ahead than with both one ahead).  The copies of the
-// last three steps of a tile come from the next tile (if any).
+// fully read, copies A slab k+2 and the first B_LATE pieces of B slab k+3
+// into the stages it frees; the other B pieces of slab k+3 follow in the
+// first three k steps of step k+1, so no k step issues more than ten copies
+// per wave.  One A slab and about two B slabs are in flight while a slab is
+// multiplied (B, the operand with more misses in L2, runs one slab further
+// ahead: a copy-only run of these operand streams delivers 15-20 % more bytes
+// per clock with B two slabs ahead than with both one ahead).  The copies of
+// the last three steps of a tile come from the next tile (if any).
 //
 // Wait counts (vector-memory operations complete in issue order; every wave
 // issues DMA_PER_OPERAND copies per operand and slab, on every step, also
 // when they have no source).  Step k waits for slab k+1, whose last copy is
-// A(k+1), issued at step k-1 just before B(k+2):
+// A(k+1), issued in step k-1's last k step; after it come the DMA_PER_OPERAND
+// pieces of B(k+2) (B_LATE in step k-1, the rest in step k before the wait):
 //   * steady state: B(k+2) may stay in flight: WAIT_STEADY = DMA_PER_OPERAND;
 //   * a tile's first step (not the first tile): the previous tile's epilogue
-//     (EPI_STORES stores, every one issued) follows B(k+2):
+//     (EPI_STORES stores, every one issued) lies between B(k+2)'s pieces:
 //     WAIT_AFTER_EPILOGUE = DMA_PER_OPERAND + EPI_STORES.
-// The first tile's prologue issues A(0) B(0) A(1) B(1) B(2), waits for slab
-// 0 with the last three in flight, and its first step keeps B(2) in flight.
-// The kernel ends with a wait for every copy.
+// The first tile's prologue issues A(0) B(0) A(1) B(1) and B(2)'s first
+// B_LATE pieces and waits for slab 0 with the last of them in flight; its
+// first step issues the rest of B(2) and keeps B(2) in flight.  The kernel
+// ends with a wait for every copy.
 
 template <typename ST, bool AK, bool BKM, bool BIAS, bool RES>
 __device__ __forceinline__ void gemm256_body(const GemmArgs& g) {
@@ -588,8 +631,9 @@ __device__ __forceinline__ void gemm256_body(const GemmArgs& g) {
   dma_operand<BKM>(bst(0), cur.B, cur.offb, g.b_ld, 0, wave);
   dma_operand<AK>(a1, cur.A, cur.offa, g.a_ld, 1, wave);
   dma_operand<BKM>(bst(1), cur.B, cur.offb, g.b_ld, 1, wave);
-  dma_operand<BKM>(bst(2), cur.B, cur.offb, g.b_ld, 2, wave);
-  sync_slab<3 * DMA_PER_OPERAND>();
+#pragma unroll
+  for (int i = 0; i < B_LATE; ++i) dma_piece<BKM>(bst(2), cur.B, cur.offb[i], slab_koff<BKM>(g.b_ld, 2), i, wave);
+  sync_slab<2 * DMA_PER_OPERAND + B_LATE>();
   Frags f0, f1;
   read_frags<AK, BKM>(f0, a0, bst(0), wm, wn, 0, lane);
 
@@ -606,7 +650,8 @@ __device__ __forceinline__ void gemm256_body(const GemmArgs& g) {
     {
       char* sb = bst(rb);
       const char* nb = bst(nxt3(rb));
-      slab_step<ST, AK, BKM, true, FROM_CUR, FROM_CUR>(acc, f0, f1, a0, sb, a1, nb, 0, nk,
+      char* eb = bst(nxt3(nxt3(rb)));
+      slab_step<ST, AK, BKM, true, FROM_CUR, FROM_CUR>(acc, f0, f1, a0, sb, a1, nb, eb, 0, nk,
                                                       first ? WAIT_STEADY : WAIT_AFTER_EPILOGUE, g, cur, nxt, wm, wn,
                                                       wave, lane);
       rb = nxt3(rb);
@@ -616,14 +661,16 @@ __device__ __forceinline__ void gemm256_body(const GemmArgs& g) {
       {
         char* sb = bst(rb);
         const char* nb = bst(nxt3(rb));
-        slab_step<ST, AK, BKM, false, FROM_CUR, FROM_CUR>(acc, f0, f1, a1, sb, a0, nb, k, nk, WAIT_STEADY, g, cur, nxt,
+        char* eb = bst(nxt3(nxt3(rb)));
+        slab_step<ST, AK, BKM, false, FROM_CUR, FROM_CUR>(acc, f0, f1, a1, sb, a0, nb, eb, k, nk, WAIT_STEADY, g, cur, nxt,
                                                          wm, wn, wave, lane);
         rb = nxt3(rb);
       }
       {
         char* sb = bst(rb);
         const char* nb = bst(nxt3(rb));
-        slab_step<ST, AK, BKM, false, FROM_CUR, FROM_CUR>(acc, f0, f1, a0, sb, a1, nb, k + 1, nk, WAIT_STEADY, g, cur,
+        char* eb = bst(nxt3(nxt3(rb)));
+        slab_step<ST, AK, BKM, false, FROM_CUR, FROM_CUR>(acc, f0, f1, a0, sb, a1, nb, eb, k + 1, nk, WAIT_STEADY, g, cur,
                                                          nxt, wm, wn, wave, lane);
         rb = nxt3(rb);
       }
@@ -632,7 +679,8 @@ __device__ __forceinline__ void gemm256_body(const GemmArgs& g) {
     {
       char* sb = bst(rb);
       const char* nb = bst(nxt3(rb));
-      slab_step<ST, AK, BKM, false, FROM_CUR, FROM_NXT>(acc, f0, f1, a1, sb, a0, nb, nk - 3, nk, WAIT_STEADY, g, cur,
+      char* eb = bst(nxt3(nxt3(rb)));
+      slab_step<ST, AK, BKM, false, FROM_CUR, FROM_NXT>(acc, f0, f1, a1, sb, a0, nb, eb, nk - 3, nk, WAIT_STEADY, g, cur,
                                                        nxt, wm, wn, wave, lane);
       rb = nxt3(rb);
     }
@@ -643,14 +691,16 @@ __device__ __forceinline__ void gemm256_body(const GemmArgs& g) {
     {
       char* sb = bst(rb);
       const char* nb = bst(nxt3(rb));
-      slab_step<ST, AK, BKM, false, FROM_NXT, FROM_NXT>(acc, f0, f1, a0, sb, a1, nb, nk - 2, nk, WAIT_STEADY, g, cur,
+      char* eb = bst(nxt3(nxt3(rb)));
+      slab_step<ST, AK, BKM, false, FROM_NXT, FROM_NXT>(acc, f0, f1, a0, sb, a1, nb, eb, nk - 2, nk, WAIT_STEADY, g, cur,
                                                        nxt, wm, wn, wave, lane);
       rb = nxt3(rb);
     }
     {
       char* sb = bst(rb);
       const char* nb = bst(nxt3(rb));
-      slab_step<ST, AK, BKM, false, FROM_NXT, FROM_NXT>(acc, f0, f1, a1, sb, a0, nb, nk - 1, nk, WAIT_STEADY, g, cur,
+      char* eb = bst(nxt3(nxt3(rb)));
+      slab_step<ST, AK, BKM, false, FROM_NXT, FROM_NXT>(acc, f0, f1, a1, sb, a0, nb, eb, nk - 1, nk, WAIT_STEADY, g, cur,
                                                        nxt, wm, wn, wave, lane);
       rb = nxt3(rb);
     }
