@@ -228,6 +228,34 @@ __device__ __forceinline__ void mfma16(f32x16_t (&acc)[4][4], const Frags& f) {
     }
 }
 
+// The bias enters as the accumulators' starting value: one MFMA per block
+// with a rank-1 product, first operand = the bias column of the block (k = 0:
+// lane l < 32 holds bias[n = l] in element 0, everything else 0), second
+// operand = ones (lane l < 32 holds 1.0 in element 0), so that block (i, j)
+// starts at bias[n] in every row m; the products are exact in fp32.  This
+// replaces a bias load and add in the epilogue.
+template <typename ST>
+constexpr uint32_t ONE_BITS = std::is_same<ST, f16_t>::value ? 0x3C00u : 0x3F80u;
+
+template <typename ST>
+__device__ __forceinline__ void bias_init(f32x16_t (&acc)[4][4], const uint16_t (&bf)[4], uint32_t ones) {
+  const f32x16_t zero = {};
+  const short8_t one8 = __builtin_bit_cast(short8_t, v4u32{ones, 0u, 0u, 0u});
+#pragma unroll
+  for (int j = 0; j < 4; ++j) {
+    const short8_t b8 = __builtin_bit_cast(short8_t, v4u32{(uint32_t)bf[j], 0u, 0u, 0u});
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      if constexpr (std::is_same<ST, f16_t>::value)
+        acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_f16(__builtin_bit_cast(f16x8_t, b8),
+                                                           __builtin_bit_cast(f16x8_t, one8), zero, 0, 0, 0);
+      else
+        acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(__builtin_bit_cast(bf16x8_t, b8),
+                                                            __builtin_bit_cast(bf16x8_t, one8), zero, 0, 0, 0);
+    }
+  }
+}
+
 // Scheduling pattern for 16 MFMAs whose fragments are already in registers,
 // issued together with NREAD LDS reads for a later k step: one MFMA, one
 // read, alternately, then the remaining MFMAs.
@@ -392,7 +420,7 @@ __device__ __forceinline__ void load_row4x16(v2u32 (&r)[16], const GemmArgs& g, 
     }
 }
 
-// Tile epilogue straight from the accumulators: C = acc (+ bias) (+ residual),
+// Tile epilogue straight from the accumulators: C = acc (+ residual),
 // bf16.  Lane l holds, per (m block i, n block j, v/4 group q), 4 consecutive
 // columns n = 32j + 8q + 4(l/32) of row m = 32i + l%32.  Lanes l and l+32
 // exchange halves (v_permlane32_swap) so that each lane holds 8 consecutive
@@ -403,11 +431,10 @@ __device__ __forceinline__ void load_row4x16(v2u32 (&r)[16], const GemmArgs& g, 
 // buffer store covers 8 rows x 128 contiguous bytes (whole cache lines):
 // EPI_STORES per wave, every one issued (rows past M or columns past N get an
 // out-of-range offset that the buffer unit drops).
-// BIAS / RES are compile-time, so the epilogue has no branches.  The bias
-// (64 values per lane) is loaded from the token's bias row once per tile, or
-// once per m block next to a residual (which needs the registers); the
-// residual of m block i+1 is loaded while block i is computed and stored.
-template <typename ST, bool BIAS, bool RES>
+// RES is compile-time, so the epilogue has no branches (a bias is already in
+// the accumulators, see bias_init); the residual of m block i+1 is loaded
+// while block i is computed and stored.
+template <typename ST, bool RES>
 __device__ __forceinline__ void epilogue(const f32x16_t (&acc)[4][4], const GemmArgs& g, const Tile& c, int wm, int wn,
                                          int lane) {
   const int r = lane & 31, h = lane >> 5;
@@ -417,12 +444,6 @@ __device__ __forceinline__ void epilogue(const f32x16_t (&acc)[4][4], const Gemm
   const __amdgpu_buffer_rsrc_t crs = make_rsrc(cbase, (long)g.M * g.c_ld * 2);
   // byte strides (uniform; every per-token offset is below 2^31)
   const uint32_t cld = (uint32_t)(g.c_ld * 2);
-  v2u32 bias[16];
-  __amdgpu_buffer_rsrc_t brs;
-  if constexpr (BIAS) {
-    brs = make_rsrc(reinterpret_cast<const char*>(g.bias) + (long)c.t * g.bias_bs * 2, (long)g.N * 2);
-    if constexpr (!RES) load_row4x16(bias, g, brs, 0u, c.n0 + nb, true);
-  }
   v2u32 res[2][16];
   __amdgpu_buffer_rsrc_t rrs;
   uint32_t rld = 0;
@@ -437,7 +458,6 @@ __device__ __forceinline__ void epilogue(const f32x16_t (&acc)[4][4], const Gemm
     __builtin_amdgcn_sched_barrier(0);
     const int m = mb + 32 * i;
     const bool mok = m < g.M;
-    if constexpr (BIAS && RES) load_row4x16(bias, g, brs, 0u, c.n0 + nb, true);
     if constexpr (RES) {
       if (i < 3) load_row4x16(res[(i + 1) & 1], g, rrs, (uint32_t)(m + 32) * rld, c.n0 + nb, m + 32 < g.M);
     }
@@ -455,10 +475,6 @@ __device__ __forceinline__ void epilogue(const f32x16_t (&acc)[4][4], const Gemm
         for (int e = 0; e < 4; ++e) {
           v0[e] = acc[i][j][4 * q + e];
           v1[e] = acc[i][j][4 * q + 4 + e];
-        }
-        if constexpr (BIAS) {
-          add16x4<ST>(v0, bias[4 * j + q]);
-          add16x4<ST>(v1, bias[4 * j + q + 1]);
         }
         if constexpr (RES) {
           add16x4<ST>(v0, res[i & 1][4 * j + q]);
@@ -533,18 +549,23 @@ enum { FROM_CUR = 0, FROM_NXT = 1 };
 // just freed receive A slab k+2 (sa) and B slab k+3 (sb): from this tile
 // (k+2 < nk, k+3 < nk) or the next one (when there is one).  The next slab's
 // first fragments are read during the last k step's MFMAs.
-template <typename ST, bool AK, bool BKM, bool ZERO, int SRC_A, int SRC_B>
+template <typename ST, bool AK, bool BKM, bool ZERO, int SRC_A, int SRC_B, bool BIAS = false>
 __device__ __forceinline__ void slab_step(f32x16_t (&acc)[4][4], Frags& f0, Frags& f1, char* sa, char* sb,
                                           const char* na, const char* nb, char* eb, int k, int nk, int wait,
                                           const GemmArgs& g, const Src& cur, const Src& nxt, int wm, int wn, int wave,
-                                          int lane) {
+                                          int lane, const uint16_t (&bf)[4], uint32_t ones) {
   constexpr int NR = (AK ? 4 : 8) + (BKM ? 4 : 8);
   // B slab k+2 (stage eb, freed by the previous step) comes from where A slab k+2 does
   const Src& srca = SRC_A == FROM_CUR ? cur : nxt;
   const uint32_t koffe = slab_koff<BKM>(g.b_ld, SRC_A == FROM_CUR ? k + 2 : k + 2 - nk);
   early_b<BKM, 0>(eb, srca.B, srca.offb, koffe, wave);
   read_frags<AK, BKM>(f1, sa, sb, wm, wn, 1, lane);
-  mfma16<ST, ZERO>(acc, f0);
+  if constexpr (ZERO && BIAS) {
+    bias_init<ST>(acc, bf, ones);
+    mfma16<ST, false>(acc, f0);
+  } else {
+    mfma16<ST, ZERO>(acc, f0);
+  }
   interleave<NR>();
   __builtin_amdgcn_sched_barrier(0);
   early_b<BKM, 1>(eb, srca.B, srca.offb, koffe, wave);
@@ -565,6 +586,28 @@ __device__ __forceinline__ void slab_step(f32x16_t (&acc)[4][4], Frags& f0, Frag
   const uint32_t koffb = slab_koff<BKM>(g.b_ld, SRC_B == FROM_CUR ? k + 3 : k + 3 - nk);
   last_kstep<ST, AK, BKM>(acc, f1, f0, na, nb, sa, sb, srca.A, srca.offa, koffa, srcb.B, srcb.offb, koffb, wm, wn,
                           wave, lane);
+}
+
+// Bias fragment of a tile for bias_init: lane l < 32 loads bias[n0 + 128 wn +
+// 32 j + l] (zero past N, for lanes l >= 32 and without a tile).
+__device__ __forceinline__ void load_bias_frag(uint16_t (&bf)[4], const GemmArgs& g, const Tile& c, int wn, int lane,
+                                               bool active) {
+  const __amdgpu_buffer_rsrc_t rs =
+      make_rsrc(reinterpret_cast<const char*>(g.bias) + (long)c.t * g.bias_bs * 2, active ? (long)g.N * 2 : 0L);
+#pragma unroll
+  for (int j = 0; j < 4; ++j) {
+    const int n = c.n0 + wn * 128 + 32 * j + lane;
+    const uint32_t off = (lane < 32 && n < g.N) ? (uint32_t)n * 2 : OUT_OF_RANGE;
+    bf[j] = __builtin_amdgcn_raw_buffer_load_b16(rs, off, 0, 0);
+  }
+}
+
+// Marks the loaded bias fragment as used here, so that the compiler's wait
+// for the load lands at this point (it counts only its own memory operations,
+// not the copies, so a wait placed anywhere else could also wait for copies
+// still in flight).
+__device__ __forceinline__ void settle(uint16_t (&bf)[4]) {
+  asm volatile("" : "+v"(bf[0]), "+v"(bf[1]), "+v"(bf[2]), "+v"(bf[3]));
 }
 
 // Persistent kernel: one workgroup per CU.  Workgroup w runs on XCD w % 8;
@@ -622,6 +665,13 @@ __device__ __forceinline__ void gemm256_body(const GemmArgs& g) {
   Tile ct = tile_of(tile, tiles_m, per_t);
   Src cur;
   tile_src<AK, BKM>(cur, g, ct, wave, lane);
+  // bias fragments of the current and the next tile (the next one's is loaded a tile ahead)
+  uint16_t bias_cur[4] = {0, 0, 0, 0}, bias_nxt[4] = {0, 0, 0, 0};
+  const uint32_t ones = lane < 32 ? ONE_BITS<ST> : 0u;
+  if constexpr (BIAS) {
+    load_bias_frag(bias_cur, g, ct, wn, lane, true);
+    settle(bias_cur);  // before any copy is issued
+  }
   const int nk = g.K / BK;  // even, at least 4
   // B stage of the slab being multiplied (rotates 0, 1, 2 with the global slab index)
   int rb = 0;
@@ -645,15 +695,16 @@ __device__ __forceinline__ void gemm256_body(const GemmArgs& g) {
     const Tile nt = tile_of(has_next ? next : tile, tiles_m, per_t);
     Src nxt;
     tile_src<AK, BKM>(nxt, g, nt, wave, lane, has_next);  // extent 0 without a next tile
+    if constexpr (BIAS) load_bias_frag(bias_nxt, g, nt, wn, lane, has_next);
 
     // step 0 (accumulators start from zero); for nk == 4 it is also step nk-4
     {
       char* sb = bst(rb);
       const char* nb = bst(nxt3(rb));
       char* eb = bst(nxt3(nxt3(rb)));
-      slab_step<ST, AK, BKM, true, FROM_CUR, FROM_CUR>(acc, f0, f1, a0, sb, a1, nb, eb, 0, nk,
-                                                      first ? WAIT_STEADY : WAIT_AFTER_EPILOGUE, g, cur, nxt, wm, wn,
-                                                      wave, lane);
+      slab_step<ST, AK, BKM, true, FROM_CUR, FROM_CUR, BIAS>(acc, f0, f1, a0, sb, a1, nb, eb, 0, nk,
+                                                            first ? WAIT_STEADY : WAIT_AFTER_EPILOGUE, g, cur, nxt, wm,
+                                                            wn, wave, lane, bias_cur, ones);
       rb = nxt3(rb);
     }
     // steps 1 .. nk-4 in pairs (A stages 1, 0): every copy from this tile
@@ -663,7 +714,7 @@ __device__ __forceinline__ void gemm256_body(const GemmArgs& g) {
         const char* nb = bst(nxt3(rb));
         char* eb = bst(nxt3(nxt3(rb)));
         slab_step<ST, AK, BKM, false, FROM_CUR, FROM_CUR>(acc, f0, f1, a1, sb, a0, nb, eb, k, nk, WAIT_STEADY, g, cur, nxt,
-                                                         wm, wn, wave, lane);
+                                                         wm, wn, wave, lane, bias_cur, ones);
         rb = nxt3(rb);
       }
       {
@@ -671,7 +722,7 @@ __device__ __forceinline__ void gemm256_body(const GemmArgs& g) {
         const char* nb = bst(nxt3(rb));
         char* eb = bst(nxt3(nxt3(rb)));
         slab_step<ST, AK, BKM, false, FROM_CUR, FROM_CUR>(acc, f0, f1, a0, sb, a1, nb, eb, k + 1, nk, WAIT_STEADY, g, cur,
-                                                         nxt, wm, wn, wave, lane);
+                                                         nxt, wm, wn, wave, lane, bias_cur, ones);
         rb = nxt3(rb);
       }
     }
@@ -681,7 +732,7 @@ __device__ __forceinline__ void gemm256_body(const GemmArgs& g) {
       const char* nb = bst(nxt3(rb));
       char* eb = bst(nxt3(nxt3(rb)));
       slab_step<ST, AK, BKM, false, FROM_CUR, FROM_NXT>(acc, f0, f1, a1, sb, a0, nb, eb, nk - 3, nk, WAIT_STEADY, g, cur,
-                                                       nxt, wm, wn, wave, lane);
+                                                       nxt, wm, wn, wave, lane, bias_cur, ones);
       rb = nxt3(rb);
     }
     // steps nk-2 (A stage 0) and nk-1 (A stage 1): the next tile's A slabs 0, 1 and B slabs 1, 2.
@@ -693,7 +744,7 @@ __device__ __forceinline__ void gemm256_body(const GemmArgs& g) {
       const char* nb = bst(nxt3(rb));
       char* eb = bst(nxt3(nxt3(rb)));
       slab_step<ST, AK, BKM, false, FROM_NXT, FROM_NXT>(acc, f0, f1, a0, sb, a1, nb, eb, nk - 2, nk, WAIT_STEADY, g, cur,
-                                                       nxt, wm, wn, wave, lane);
+                                                       nxt, wm, wn, wave, lane, bias_cur, ones);
       rb = nxt3(rb);
     }
     {
@@ -701,15 +752,19 @@ __device__ __forceinline__ void gemm256_body(const GemmArgs& g) {
       const char* nb = bst(nxt3(rb));
       char* eb = bst(nxt3(nxt3(rb)));
       slab_step<ST, AK, BKM, false, FROM_NXT, FROM_NXT>(acc, f0, f1, a1, sb, a0, nb, eb, nk - 1, nk, WAIT_STEADY, g, cur,
-                                                       nxt, wm, wn, wave, lane);
+                                                       nxt, wm, wn, wave, lane, bias_cur, ones);
       rb = nxt3(rb);
     }
 
-    epilogue<ST, BIAS, RES>(acc, g, ct, wm, wn, lane);
+    epilogue<ST, RES>(acc, g, ct, wm, wn, lane);
+    // after the epilogue's stores: the wait leaves them in flight
+    if constexpr (BIAS) settle(bias_nxt);
     if (!has_next) break;
     tile = next;
     ct = nt;
     cur = nxt;
+#pragma unroll
+    for (int j = 0; j < 4; ++j) bias_cur[j] = bias_nxt[j];
     first = false;
   }
   // the last tile's empty copies still write LDS: let every copy land before the workgroup ends
@@ -797,9 +852,8 @@ bool gemm256_supported(int dtype, bool a_kmajor, bool b_kmajor, const GemmArgs& 
   // per-token operand byte offsets fit the 32-bit copy offsets
   const long a_rows = a_kmajor ? g.M : g.K, b_rows = b_kmajor ? g.N : g.K;
   if (a_rows * g.a_ld * 2 > 0xffffffffL || b_rows * g.b_ld * 2 > 0xffffffffL) return false;
-  // the epilogue stores 8 columns per lane pair; a bias tile is copied in 16-byte pieces
+  // the epilogue stores 8 columns per lane pair (the bias is read element by element)
   if (g.N % 8 || g.c_ld % 4 || g.c_bs % 4 || (reinterpret_cast<uintptr_t>(g.C) & 15)) return false;
-  if (g.bias && (g.bias_bs % 8 || (reinterpret_cast<uintptr_t>(g.bias) & 15))) return false;
   if (g.res && (g.res_f32 || g.res_ld % 4 || g.res_bs % 4 || (reinterpret_cast<uintptr_t>(g.res) & 15)))
     return false;  // the residual is bf16
   // per-token byte offsets of C and the residual fit the 31-bit buffer range
