@@ -198,20 +198,58 @@ def check_epilogue(g, m0, n0, written, sizes):
             assert np.all(co[ok] + 16 <= c_ext)
             np.add.at(written, (m[ok][:, None], ns[ok][:, None] + np.arange(8)), 1)
         if g["res"]:
-            r_ext = M * g["res_ld"] * 2
-            for i, j, q in itertools.product(range(4), range(4), range(4)):
-                m = mb + 32 * i
-                n = n0 + wn * 128 + 4 * h + 32 * j + 8 * q
-                ok = (m < M) & (n < N)
-                ro = m * g["res_ld"] * 2 + n * 2
-                assert np.all(n[ok] + 3 < N) and np.all(ro[ok] + 8 <= r_ext)
+            check_residual_copy(g, m0, n0, wm, wn)
     if g["bias"]:
-        # the epilogue's bias loads: 4 consecutive values at columns n0 + wn*128 + 4h + 32j + 8q
+        # the bias fragment: lane l < 32 reads the one value at column n0 + wn*128 + 32j + l
         for wn in range(2):
-            for j, q in itertools.product(range(4), range(4)):
-                n = n0 + wn * 128 + 4 * h + 32 * j + 8 * q
-                ok = n < N
-                assert np.all(n[ok] + 3 < N) and np.all(n[ok] * 2 + 8 <= N * 2)
+            for j in range(4):
+                n = n0 + wn * 128 + 32 * j + lane
+                ok = (lane < 32) & (n < N)
+                assert np.all(n[ok] * 2 + 2 <= N * 2)
+
+
+OUT_OF_RANGE = 0x80000000
+
+
+def check_residual_copy(g, m0, n0, wm, wn, read_swizzle=15):
+    """The residual's way through LDS for one wave: the copies' source offsets (res_offsets,
+    res_piece) stay inside the token's residual or read zero (rows past M lie beyond the
+    extent, columns past N get OUT_OF_RANGE), and the epilogue's reads (lane l: row l%32 of
+    block i, 8 bytes h = l/32 of logical chunk 4j + q) find exactly the elements of the rows
+    and columns the accumulators hold."""
+    M, N, rld = g["M"], g["N"], g["res_ld"] * 2
+    r_ext = min(M * rld, 0x7FFFFFFF)
+    lane = np.arange(64)
+    row = np.array([4 * p + (lane >> 4) for p in range(8)])          # [piece, lane]
+    lc = (lane & 15) ^ (row & 15)
+    m = m0 + wm * 128 + row
+    n = n0 + wn * 128 + 8 * lc
+    off = np.where(n < N, m * rld + n * 2, OUT_OF_RANGE)
+    for blk in range(4):
+        o = np.where(off == OUT_OF_RANGE, OUT_OF_RANGE, off + blk * 32 * rld)
+        mb = m + 32 * blk
+        valid = (o != OUT_OF_RANGE) & (mb < M)
+        assert np.all(o[valid] + 16 <= r_ext)                          # whole 16 bytes inside
+        assert np.all((o[(o != OUT_OF_RANGE) & (mb >= M)]) >= r_ext)   # rows past M read zero
+        assert np.all(o < 2 ** 32)
+        # LDS image of the region: byte p*1024 + 16*lane holds the 8 columns from n, row mb
+        region = {}
+        for p_, l_ in itertools.product(range(8), range(64)):
+            pos = p_ * 1024 + 16 * l_
+            assert 0 <= pos and pos + 16 <= 8192
+            region[pos] = (int(mb[p_, l_]), int(n[p_, l_])) if valid[p_, l_] else None
+        r, h = lane & 31, lane >> 5
+        for x in range(16):                  # logical chunk 4j + q
+            addr = r * 256 + ((x ^ (r & read_swizzle)) << 4) + 8 * h
+            assert np.all(addr + 8 <= 8192)
+            for l_ in range(64):
+                want_m = m0 + wm * 128 + 32 * blk + int(r[l_])
+                want_n = n0 + wn * 128 + 8 * x + 4 * int(h[l_])
+                got = region[int(addr[l_]) - 8 * int(h[l_])]
+                if want_m < M and want_n < N:
+                    assert got == (want_m, want_n - 4 * int(h[l_])), (blk, x, l_, got)
+                else:
+                    assert got is None or got[0] >= M or got[1] >= N
 
 
 def check_gemm(name, g, sizes):
@@ -256,6 +294,16 @@ def test_gemm256_addresses_stay_in_bounds(shape):
             taken += 1
     if shape in ((1024, 64, 1280, 2), (1024, 32, 512, 2)):
         assert taken == 6
+
+
+def test_residual_copy_checked_and_a_planted_swizzle_slip_caught():
+    gemms, _ = gemms_of_block(1024, 64, 1280, 2)
+    for name in ("down", "dh1"):
+        g = gemms[name]
+        assert supported(g) and g["res"]
+        check_residual_copy(g, 768, 1024, 1, 1)
+        with pytest.raises(AssertionError):
+            check_residual_copy(g, 768, 1024, 1, 1, read_swizzle=7)
 
 
 def test_replica_catches_a_planted_slip():
@@ -304,9 +352,11 @@ def last_kstep_slots():
 
 WAIT_STEADY = DMA_PER_OPERAND
 WAIT_AFTER_EPILOGUE = DMA_PER_OPERAND + EPI_STORES
+RES_INTERLEAVED = False
+RES_WAIT = [DMA_PER_OPERAND, EPI_STORES // 4 + DMA_PER_OPERAND, EPI_STORES // 4 + DMA_PER_OPERAND, EPI_STORES // 4]
 
 
-def simulate_pipeline(nk, ntiles, epilogue_extra=0):
+def simulate_pipeline(nk, ntiles, epilogue_extra=0, res=False):
     """Replays the kernel's per-wave event sequence for `ntiles` tiles of `nk` slabs: copy issues
     piece by piece (A ring of 2 stages, B ring of 3; A slab k+2 and the first B_LATE pieces of
     B slab k+3 in step k's last k step, the other B pieces of slab k+2 in the first k steps of
@@ -315,7 +365,13 @@ def simulate_pipeline(nk, ntiles, epilogue_extra=0):
     each slab.  Vector-memory operations complete in issue order, so after a wait with count N
     every operation but the newest N is complete.  Checks that every slab's copies are all
     issued and complete before its first read, that no copy targets a stage whose previous slab
-    may still be read, and that no copy is in flight at the end."""
+    may still be read, and that no copy is in flight at the end.
+
+    res: the kernels with a residual.  The tile's last step copies residual blocks 0 and 1
+    (this wave's rows) into the two stages its last slab leaves, instead of the next tile's A
+    slab 1; the epilogue waits for block i with the count RES_WAIT[i], reads it, stores its 8
+    rows and copies block i+2 into the same region (i < 2); the next tile's A slab 1 follows
+    the epilogue, and the next tile's first step waits with the steady count."""
     ops = []               # ("A"|"B"|"E", slab)
     done = 0               # ops[:done] complete
     stage_of = {}          # (operand, global slab) -> stage
@@ -344,6 +400,26 @@ def simulate_pipeline(nk, ntiles, epilogue_extra=0):
             assert last < done, f"slab {slab} {op} read before its copy completed"
             reading[(op, stage_of[(op, slab)])] = slab
 
+    res_region = {}        # (tile, block) -> (operand, stage) holding it
+    res_read_done = set()
+
+    def res_issue(t, i, region):
+        # a wave overwrites only its own region, after its reads of the block there
+        for (tt, ii), reg in res_region.items():
+            if reg == region and (tt, ii) not in res_read_done:
+                raise AssertionError(f"residual block {ii} overwritten before it was read")
+        res_region[(t, i)] = region
+        ops.extend([("R", (t, i))] * DMA_PER_OPERAND)
+
+    def res_read(t, i):
+        last = len(ops) - 1 - ops[::-1].index(("R", (t, i)))
+        assert last < done, f"residual block {i} of tile {t} read before its copy completed"
+        res_read_done.add((t, i))
+
+    def wait_vm(n):        # a wave's own wait, no barrier
+        nonlocal done
+        done = max(done, len(ops) - n)
+
     S = lambda t, k: t * nk + k          # global slab index
     # prologue
     issue("A", S(0, 0), DMA_PER_OPERAND)
@@ -360,18 +436,43 @@ def simulate_pipeline(nk, ntiles, epilogue_extra=0):
             for ks in range(3):
                 issue("B", S(t, k + 2), b_early_begin(ks + 1) - b_early_begin(ks))
             read(S(t, k))
-            wait(WAIT_AFTER_EPILOGUE if (k == 0 and t > 0) else WAIT_STEADY)
+            wait(WAIT_AFTER_EPILOGUE if (k == 0 and t > 0 and not res) else WAIT_STEADY)
             # copies of the next tile are issued even without one (slab indices past the last
             # tile: empty copies into freed stages)
-            for op in last_kstep_slots():
-                if op is not None:
-                    issue(op, S(t, k + 2) if op == "A" else S(t, k + 3), 1)
+            if res and k == nk - 1:
+                assert B_LATE == 0
+                xb, ya = ("B", S(t, k) % 3), ("A", S(t, k) % 2)   # stages of the last slab
+                for region in (xb, ya):
+                    assert reading.get(region) is None, "residual copied over a slab still read"
+                if RES_INTERLEAVED:        # a planted mistake: blocks 0 and 1 slot by slot
+                    res_region[(t, 0)], res_region[(t, 1)] = xb, ya
+                    for _ in range(DMA_PER_OPERAND):
+                        ops.extend([("R", (t, 0)), ("R", (t, 1))])
+                else:
+                    res_issue(t, 0, xb)
+                    res_issue(t, 1, ya)
+            else:
+                for op in last_kstep_slots():
+                    if op is not None:
+                        issue(op, S(t, k + 2) if op == "A" else S(t, k + 3), 1)
             if k + 1 < nk:
                 read(S(t, k + 1))          # next slab's first fragments
             elif has_next:
                 read(S(t + 1, 0))
-        for e in range(EPI_STORES + epilogue_extra):
-            ops.append(("E", (t, e)))
+        if res:
+            for i in range(4):
+                wait_vm(RES_WAIT[i])
+                res_read(t, i)
+                for e in range(EPI_STORES // 4):
+                    ops.append(("E", (t, i, e)))
+                if i < 2:
+                    res_issue(t, i + 2, res_region[(t, i)])
+            for e in range(epilogue_extra):
+                ops.append(("E", (t, "x", e)))
+            issue("A", S(t, nk + 1), DMA_PER_OPERAND)   # the next tile's A slab 1
+        else:
+            for e in range(EPI_STORES + epilogue_extra):
+                ops.append(("E", (t, e)))
     wait(0)                                # the kernel's final wait
     assert done == len(ops)
 
@@ -380,7 +481,30 @@ def simulate_pipeline(nk, ntiles, epilogue_extra=0):
 @pytest.mark.parametrize("ntiles", [1, 2, 3, 7])
 def test_gemm256_pipeline_waits(nk, ntiles):
     simulate_pipeline(nk, ntiles)
-    simulate_pipeline(nk, ntiles, epilogue_extra=64 + 64)   # residual and bias loads in the epilogue
+    simulate_pipeline(nk, ntiles, res=True)
+
+
+def test_pipeline_replica_catches_interleaved_residual_blocks():
+    """Blocks 0 and 1 copied slot by slot leave one copy after block 0's last piece, not
+    DMA_PER_OPERAND: the first epilogue wait would not cover block 0."""
+    global RES_INTERLEAVED
+    RES_INTERLEAVED = True
+    try:
+        with pytest.raises(AssertionError):
+            simulate_pipeline(20, 2, res=True)
+    finally:
+        RES_INTERLEAVED = False
+
+
+def test_pipeline_replica_catches_a_short_residual_wait():
+    """The epilogue's second wait one block too loose (block 1 could still be in flight)."""
+    saved = RES_WAIT[1]
+    RES_WAIT[1] = saved + DMA_PER_OPERAND
+    try:
+        with pytest.raises(AssertionError):
+            simulate_pipeline(20, 2, res=True)
+    finally:
+        RES_WAIT[1] = saved
 
 
 def test_pipeline_replica_catches_late_b_between_a_pieces():

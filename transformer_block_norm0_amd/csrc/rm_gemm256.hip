@@ -365,18 +365,60 @@ __device__ __forceinline__ void early_b(char* stage, __amdgpu_buffer_rsrc_t rs, 
   __builtin_amdgcn_sched_barrier(0);
 }
 
+// Residual of a tile's epilogue, copied into LDS like the operand slabs.
+// During the epilogue two stages are free: the B stage and the A stage of the
+// tile's last slab (the next tile's B slab 2 and A slab 1 go there only
+// afterwards).  Each wave copies the 32 x 128 residual block of its m block i
+// into its own 8 KB of one of them (i even: the B stage, i odd: the A stage),
+// so a wave reads only data it copied itself and needs no barrier: row r of a
+// block is 256 bytes whose 16-byte chunks are XOR-swizzled by r % 16, piece p
+// (one copy per lane) holds rows 4p .. 4p+3.
+struct ResDma {
+  __amdgpu_buffer_rsrc_t rs;          // the token's residual rows
+  uint32_t off[DMA_PER_OPERAND];      // block 0 source offsets per piece (OUT_OF_RANGE past N)
+  uint32_t step;                      // bytes from one block to the next (32 rows)
+  char* xb;                           // this wave's 8 KB of the free B stage (blocks 0, 2)
+  char* ya;                           // this wave's 8 KB of the free A stage (blocks 1, 3)
+};
+constexpr int RES_REGION = 8192;      // bytes of one wave's block: 32 rows x 256 bytes
+
+__device__ __forceinline__ void res_offsets(ResDma& r, const GemmArgs& g, const Tile& c, int wm, int wn, int lane) {
+  const uint32_t rld = (uint32_t)(g.res_ld * 2);
+  r.rs = make_rsrc(reinterpret_cast<const char*>(g.res) + (long)c.t * g.res_bs * 2, (long)g.M * g.res_ld * 2);
+  r.step = 32u * rld;
+#pragma unroll
+  for (int p = 0; p < DMA_PER_OPERAND; ++p) {
+    const int row = 4 * p + (lane >> 4);
+    const int lc = (lane & 15) ^ (row & 15);
+    const int m = c.m0 + wm * 128 + row;  // rows past M read zero (offset beyond the extent)
+    const int n = c.n0 + wn * 128 + 8 * lc;
+    r.off[p] = n < g.N ? (uint32_t)m * rld + (uint32_t)n * 2 : OUT_OF_RANGE;
+  }
+}
+
+// Piece p of residual block blk into a wave region.
+__device__ __forceinline__ void res_piece(const ResDma& r, char* region, int blk, int p) {
+  const uint32_t o = r.off[p];
+  dma16(o == OUT_OF_RANGE ? OUT_OF_RANGE : o + (uint32_t)blk * r.step, r.rs, lds_addr(region + p * 1024));
+}
+
 // The last k step of a slab: its 16 MFMAs, with the copies of the freed
 // stages (8 A pieces, then the first B_LATE B pieces) issued one after each
 // MFMA and the next slab's first-k-step fragments read after MFMAs 8..15.
 // Each group is fenced (sched_barrier), so the copies issue in the shadow of
 // the MFMAs instead of as a burst while the matrix pipe waits.  There are no
 // branches: copies that have no source go through a resource of extent 0.
-template <typename ST, bool AK, bool BKM>
+// RDMA (the last step of a tile with a residual): the slots carry residual
+// block 0 (slots 0..7), then block 1 (slots 8..15), instead of the A pieces,
+// whose copy follows the epilogue; block 1 after all of block 0 leaves exactly
+// DMA_PER_OPERAND copies after block 0 for the epilogue's first wait.
+template <typename ST, bool AK, bool BKM, bool RDMA = false>
 __device__ __forceinline__ void last_kstep(f32x16_t (&acc)[4][4], const Frags& f1, Frags& f0, const char* na,
                                            const char* nb, char* sa, char* sb, __amdgpu_buffer_rsrc_t rsa,
                                            const uint32_t (&offa)[DMA_PER_OPERAND], uint32_t koffa,
                                            __amdgpu_buffer_rsrc_t rsb, const uint32_t (&offb)[DMA_PER_OPERAND],
-                                           uint32_t koffb, int wm, int wn, int wave, int lane) {
+                                           uint32_t koffb, int wm, int wn, int wave, int lane, const ResDma* rd) {
+  static_assert(!RDMA || B_LATE == 0, "residual slots leave no room for late B pieces");
 #pragma unroll
   for (int x = 0; x < 16; ++x) {
     const int i = x >> 2, j = x & 3;
@@ -386,8 +428,12 @@ __device__ __forceinline__ void last_kstep(f32x16_t (&acc)[4][4], const Frags& f
     else
       acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(__builtin_bit_cast(bf16x8_t, f1.b[j]),
                                                           __builtin_bit_cast(bf16x8_t, f1.a[i]), acc[i][j], 0, 0, 0);
-    if (a_slot_piece(x) >= 0) dma_piece<AK>(sa, rsa, offa[a_slot_piece(x)], koffa, a_slot_piece(x), wave);
-    if (b_slot_piece(x) >= 0) dma_piece<BKM>(sb, rsb, offb[b_slot_piece(x)], koffb, b_slot_piece(x), wave);
+    if constexpr (RDMA) {
+      res_piece(*rd, x < DMA_PER_OPERAND ? rd->xb : rd->ya, x < DMA_PER_OPERAND ? 0 : 1, x % DMA_PER_OPERAND);
+    } else {
+      if (a_slot_piece(x) >= 0) dma_piece<AK>(sa, rsa, offa[a_slot_piece(x)], koffa, a_slot_piece(x), wave);
+      if (b_slot_piece(x) >= 0) dma_piece<BKM>(sb, rsb, offb[b_slot_piece(x)], koffb, b_slot_piece(x), wave);
+    }
     if (x >= 8) {
       const int r = x - 8;
       if (r < 4) f0.a[r] = read_frag<AK>(na, wm * 128 + 32 * r, 0, lane);
@@ -406,20 +452,6 @@ __device__ __forceinline__ void add16x4(float (&v)[4], v2u32 w) {
   v[3] += hi16<ST>(w.y);
 }
 
-// 16 loads of 4 consecutive storage values of one row of a [., ld] tensor:
-// columns nbase + 32j + 8q (zero where the row or the column is out of range).
-__device__ __forceinline__ void load_row4x16(v2u32 (&r)[16], const GemmArgs& g, __amdgpu_buffer_rsrc_t rs, uint32_t row_off,
-                                             int nbase, bool mok) {
-#pragma unroll
-  for (int j = 0; j < 4; ++j)
-#pragma unroll
-    for (int q = 0; q < 4; ++q) {
-      const int n = nbase + 32 * j + 8 * q;
-      const uint32_t ro = (mok && n < g.N) ? row_off + (uint32_t)n * 2 : OUT_OF_RANGE;
-      r[4 * j + q] = __builtin_bit_cast(v2u32, __builtin_amdgcn_raw_buffer_load_b64(rs, ro, 0, 0));
-    }
-}
-
 // Tile epilogue straight from the accumulators: C = acc (+ residual),
 // bf16.  Lane l holds, per (m block i, n block j, v/4 group q), 4 consecutive
 // columns n = 32j + 8q + 4(l/32) of row m = 32i + l%32.  Lanes l and l+32
@@ -432,34 +464,42 @@ __device__ __forceinline__ void load_row4x16(v2u32 (&r)[16], const GemmArgs& g, 
 // EPI_STORES per wave, every one issued (rows past M or columns past N get an
 // out-of-range offset that the buffer unit drops).
 // RES is compile-time, so the epilogue has no branches (a bias is already in
-// the accumulators, see bias_init); the residual of m block i+1 is loaded
-// while block i is computed and stored.
+// the accumulators, see bias_init).  The residual blocks 0 and 1 were copied
+// into LDS during the tile's last k step (ResDma); block i is waited for with
+// an exact count (RES_WAIT: the copies and stores this wave issued after it),
+// read from LDS, and block i+2 is copied into the region block i leaves.
+template <int N>
+__device__ __forceinline__ void vm_wait() {
+  static_assert(N >= 0 && N <= 63, "vmcnt range");
+  asm volatile("s_waitcnt vmcnt(%0)" ::"n"(N) : "memory");
+}
+constexpr int EPI_STORES_PER_BLOCK = EPI_STORES / 4;
+// vector-memory operations issued after residual block i's copy when the epilogue waits for it
+constexpr int RES_WAIT[4] = {DMA_PER_OPERAND, EPI_STORES_PER_BLOCK + DMA_PER_OPERAND,
+                             EPI_STORES_PER_BLOCK + DMA_PER_OPERAND, EPI_STORES_PER_BLOCK};
+
 template <typename ST, bool RES>
 __device__ __forceinline__ void epilogue(const f32x16_t (&acc)[4][4], const GemmArgs& g, const Tile& c, int wm, int wn,
-                                         int lane) {
+                                         int lane, const ResDma* rd) {
   const int r = lane & 31, h = lane >> 5;
-  const int mb = c.m0 + wm * 128 + r;  // + 32 i
-  const int nb = wn * 128 + 4 * h;     // + 32 j + 8 q (tile-local)
   char* cbase = reinterpret_cast<char*>(g.C) + (long)c.t * g.c_bs * 2;
   const __amdgpu_buffer_rsrc_t crs = make_rsrc(cbase, (long)g.M * g.c_ld * 2);
   // byte strides (uniform; every per-token offset is below 2^31)
   const uint32_t cld = (uint32_t)(g.c_ld * 2);
-  v2u32 res[2][16];
-  __amdgpu_buffer_rsrc_t rrs;
-  uint32_t rld = 0;
-  if constexpr (RES) {
-    const char* rbase = reinterpret_cast<const char*>(g.res) + (long)c.t * g.res_bs * 2;
-    rrs = make_rsrc(rbase, (long)g.M * g.res_ld * 2);
-    rld = (uint32_t)(g.res_ld * 2);
-    load_row4x16(res[0], g, rrs, (uint32_t)mb * rld, c.n0 + nb, mb < g.M);
-  }
 #pragma unroll
   for (int i = 0; i < 4; ++i) {
     __builtin_amdgcn_sched_barrier(0);
-    const int m = mb + 32 * i;
-    const bool mok = m < g.M;
+    v2u32 res[16];
     if constexpr (RES) {
-      if (i < 3) load_row4x16(res[(i + 1) & 1], g, rrs, (uint32_t)(m + 32) * rld, c.n0 + nb, m + 32 < g.M);
+      // lane l: row r of block i, the 8 bytes h of logical chunk 4j + q (columns 32j + 8q + 4h ..)
+      if (i == 0) vm_wait<RES_WAIT[0]>();  // i is a constant once the loop is unrolled
+      else if (i == 1) vm_wait<RES_WAIT[1]>();
+      else if (i == 2) vm_wait<RES_WAIT[2]>();
+      else vm_wait<RES_WAIT[3]>();
+      const char* reg = (i & 1) ? rd->ya : rd->xb;
+#pragma unroll
+      for (int x = 0; x < 16; ++x)
+        res[x] = *reinterpret_cast<const v2u32*>(reg + r * 256 + ((x ^ (r & 15)) << 4) + 8 * h);
     }
     // rows 32i + 16s + l%16 (s = 0, 1) of the 32-column blocks j = 2jj, 2jj + 1,
     // each lane one 16-byte chunk 2((l/16)%2) + l/32 of its block
@@ -477,8 +517,8 @@ __device__ __forceinline__ void epilogue(const f32x16_t (&acc)[4][4], const Gemm
           v1[e] = acc[i][j][4 * q + 4 + e];
         }
         if constexpr (RES) {
-          add16x4<ST>(v0, res[i & 1][4 * j + q]);
-          add16x4<ST>(v1, res[i & 1][4 * j + q + 1]);
+          add16x4<ST>(v0, res[4 * j + q]);
+          add16x4<ST>(v1, res[4 * j + q + 1]);
         }
         const uint32_t a0 = pair16<ST>(v0[0], v0[1]), a1 = pair16<ST>(v0[2], v0[3]);
         const uint32_t b0 = pair16<ST>(v1[0], v1[1]), b1 = pair16<ST>(v1[2], v1[3]);
@@ -527,6 +567,15 @@ __device__ __forceinline__ void epilogue(const f32x16_t (&acc)[4][4], const Gemm
         }
       }
     }
+    if constexpr (RES) {
+      if (i < 2) {
+        // this wave's reads of block i are complete: block i+2 into the same region
+        asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");
+        char* reg = (i & 1) ? rd->ya : rd->xb;
+#pragma unroll
+        for (int p = 0; p < DMA_PER_OPERAND; ++p) res_piece(*rd, reg, i + 2, p);
+      }
+    }
   }
   __builtin_amdgcn_sched_barrier(0);
 }
@@ -549,11 +598,11 @@ enum { FROM_CUR = 0, FROM_NXT = 1 };
 // just freed receive A slab k+2 (sa) and B slab k+3 (sb): from this tile
 // (k+2 < nk, k+3 < nk) or the next one (when there is one).  The next slab's
 // first fragments are read during the last k step's MFMAs.
-template <typename ST, bool AK, bool BKM, bool ZERO, int SRC_A, int SRC_B, bool BIAS = false>
+template <typename ST, bool AK, bool BKM, bool ZERO, int SRC_A, int SRC_B, bool BIAS = false, bool RDMA = false>
 __device__ __forceinline__ void slab_step(f32x16_t (&acc)[4][4], Frags& f0, Frags& f1, char* sa, char* sb,
                                           const char* na, const char* nb, char* eb, int k, int nk, int wait,
                                           const GemmArgs& g, const Src& cur, const Src& nxt, int wm, int wn, int wave,
-                                          int lane, const uint16_t (&bf)[4], uint32_t ones) {
+                                          int lane, const uint16_t (&bf)[4], uint32_t ones, const ResDma* rd = nullptr) {
   constexpr int NR = (AK ? 4 : 8) + (BKM ? 4 : 8);
   // B slab k+2 (stage eb, freed by the previous step) comes from where A slab k+2 does
   const Src& srca = SRC_A == FROM_CUR ? cur : nxt;
@@ -584,8 +633,8 @@ __device__ __forceinline__ void slab_step(f32x16_t (&acc)[4][4], Frags& f0, Frag
   const Src& srcb = SRC_B == FROM_CUR ? cur : nxt;
   const uint32_t koffa = slab_koff<AK>(g.a_ld, SRC_A == FROM_CUR ? k + 2 : k + 2 - nk);
   const uint32_t koffb = slab_koff<BKM>(g.b_ld, SRC_B == FROM_CUR ? k + 3 : k + 3 - nk);
-  last_kstep<ST, AK, BKM>(acc, f1, f0, na, nb, sa, sb, srca.A, srca.offa, koffa, srcb.B, srcb.offb, koffb, wm, wn,
-                          wave, lane);
+  last_kstep<ST, AK, BKM, RDMA>(acc, f1, f0, na, nb, sa, sb, srca.A, srca.offa, koffa, srcb.B, srcb.offb, koffb, wm,
+                                wn, wave, lane, rd);
 }
 
 // Bias fragment of a tile for bias_init: lane l < 32 loads bias[n0 + 128 wn +
@@ -703,7 +752,8 @@ __device__ __forceinline__ void gemm256_body(const GemmArgs& g) {
       const char* nb = bst(nxt3(rb));
       char* eb = bst(nxt3(nxt3(rb)));
       slab_step<ST, AK, BKM, true, FROM_CUR, FROM_CUR, BIAS>(acc, f0, f1, a0, sb, a1, nb, eb, 0, nk,
-                                                            first ? WAIT_STEADY : WAIT_AFTER_EPILOGUE, g, cur, nxt, wm,
+                                                            (first || RES) ? WAIT_STEADY : WAIT_AFTER_EPILOGUE, g, cur,
+                                                            nxt, wm,
                                                             wn, wave, lane, bias_cur, ones);
       rb = nxt3(rb);
     }
@@ -735,7 +785,9 @@ __device__ __forceinline__ void gemm256_body(const GemmArgs& g) {
                                                        nxt, wm, wn, wave, lane, bias_cur, ones);
       rb = nxt3(rb);
     }
-    // steps nk-2 (A stage 0) and nk-1 (A stage 1): the next tile's A slabs 0, 1 and B slabs 1, 2.
+    // steps nk-2 (A stage 0) and nk-1 (A stage 1): the next tile's A slabs 0, 1 and B slabs 1, 2
+    // (with a residual, step nk-1 copies residual blocks 0, 1 instead and A slab 1 follows the
+    // epilogue).
     // Without a next tile these copies read nothing (extent 0) and fill freed stages with
     // zeros, and the last step's fragment reads of the next stages are unused: the same code
     // on both paths keeps the accumulators in AGPRs.
@@ -747,18 +799,32 @@ __device__ __forceinline__ void gemm256_body(const GemmArgs& g) {
                                                        nxt, wm, wn, wave, lane, bias_cur, ones);
       rb = nxt3(rb);
     }
+    ResDma rdm;
     {
       char* sb = bst(rb);
       const char* nb = bst(nxt3(rb));
       char* eb = bst(nxt3(nxt3(rb)));
-      slab_step<ST, AK, BKM, false, FROM_NXT, FROM_NXT>(acc, f0, f1, a1, sb, a0, nb, eb, nk - 1, nk, WAIT_STEADY, g, cur,
-                                                       nxt, wm, wn, wave, lane, bias_cur, ones);
+      if constexpr (RES) {
+        res_offsets(rdm, g, ct, wm, wn, lane);
+        rdm.xb = sb + wave * RES_REGION;  // stage of this tile's last B slab
+        rdm.ya = a1 + wave * RES_REGION;  // stage of this tile's last A slab
+      }
+      slab_step<ST, AK, BKM, false, FROM_NXT, FROM_NXT, false, RES>(acc, f0, f1, a1, sb, a0, nb, eb, nk - 1, nk,
+                                                                    WAIT_STEADY, g, cur, nxt, wm, wn, wave, lane,
+                                                                    bias_cur, ones, &rdm);
       rb = nxt3(rb);
     }
 
-    epilogue<ST, RES>(acc, g, ct, wm, wn, lane);
+    epilogue<ST, RES>(acc, g, ct, wm, wn, lane, &rdm);
     // after the epilogue's stores: the wait leaves them in flight
     if constexpr (BIAS) settle(bias_nxt);
+    if constexpr (RES) {
+      // the next tile's A slab 1 into the stage residual blocks 1 and 3 leave (this wave's reads done)
+      asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");
+#pragma unroll
+      for (int i = 0; i < DMA_PER_OPERAND; ++i)
+        dma_piece<AK>(a1, nxt.A, nxt.offa[i], slab_koff<AK>(g.a_ld, 1), i, wave);
+    }
     if (!has_next) break;
     tile = next;
     ct = nt;
