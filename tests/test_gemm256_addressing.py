@@ -187,12 +187,12 @@ def check_epilogue(g, m0, n0, written, sizes):
     for wave in range(4):
         wm, wn = wave >> 1, wave & 1
         mb = m0 + wm * 128 + r
-        # after the lane-half, 16-lane-row and 8-lane swaps: store (s, u) of block i and column
-        # pair jj holds, in lane l, row 32i + 16s + 8u + l%8 and the 16-byte chunk
-        # 4((l/8)%2) + 2((l/16)%2) + l/32 of the 64 columns 64jj .. 64jj + 63
-        for i, jj, sidx, u in itertools.product(range(4), range(2), range(2), range(2)):
-            m = m0 + wm * 128 + 32 * i + 16 * sidx + 8 * u + (lane & 7)
-            ns = n0 + wn * 128 + 64 * jj + 8 * (4 * ((lane >> 3) & 1) + 2 * ((lane >> 4) & 1) + h)
+        # staged through LDS (check_output_staging): store s of block i holds, in lane l,
+        # row 32i + 4s + l/16 and columns 8(l%16) .. + 7 of the wave's 128
+        stores = [(m0 + wm * 128 + 32 * i + 4 * s8 + (lane >> 4), n0 + wn * 128 + 8 * (lane & 15))
+                  for i in range(4) for s8 in range(8)]
+        assert len(stores) == 32      # EPI_STORES, every one issued
+        for m, ns in stores:
             ok = (m < M) & (ns < N)
             co = m * g["c_ld"] * 2 + ns * 2
             assert np.all(co[ok] + 16 <= c_ext)
@@ -211,6 +211,32 @@ def check_epilogue(g, m0, n0, written, sizes):
 OUT_OF_RANGE = 0x80000000
 
 
+def check_output_staging(read_swizzle=15):
+    """The LDS pass of the epilogue without a residual, for one wave's 32 x 128 block: lane l
+    writes the 4 columns 32j + 8q + 4h .. + 3 of row l%32 (h = l/32) at byte
+    r*256 + 16((4j + q) ^ (r % 16)) + 8h, then reads 16 bytes of row 4s + l/16 at logical chunk
+    l%16; every read must return the 8 columns 8(l%16) .. + 7 of that row, in order."""
+    lane = np.arange(64)
+    r, h = lane & 31, lane >> 5
+    region = {}
+    for j, q in itertools.product(range(4), range(4)):
+        addr = r * 256 + (((4 * j + q) ^ (r & 15)) << 4) + 8 * h
+        assert np.all(addr + 8 <= 8192)
+        for l_ in range(64):
+            for e in range(4):
+                pos = int(addr[l_]) + 2 * e
+                assert pos not in region, "two lanes write one element"
+                region[pos] = (int(r[l_]), 32 * j + 8 * q + 4 * int(h[l_]) + e)
+    assert len(region) == 32 * 128
+    rr0, ch = lane >> 4, lane & 15
+    for s8 in range(8):
+        rr = 4 * s8 + rr0
+        addr = rr * 256 + ((ch ^ (rr & read_swizzle)) << 4)
+        for l_ in range(64):
+            got = [region[int(addr[l_]) + 2 * e] for e in range(8)]
+            assert got == [(int(rr[l_]), 8 * int(ch[l_]) + e) for e in range(8)], (s8, l_, got)
+
+
 def check_residual_copy(g, m0, n0, wm, wn, read_swizzle=15):
     """The residual's way through LDS for one wave: the copies' source offsets (res_offsets,
     res_piece) stay inside the token's residual or read zero (rows past M lie beyond the
@@ -220,13 +246,20 @@ def check_residual_copy(g, m0, n0, wm, wn, read_swizzle=15):
     M, N, rld = g["M"], g["N"], g["res_ld"] * 2
     r_ext = min(M * rld, 0x7FFFFFFF)
     lane = np.arange(64)
-    row = np.array([4 * p + (lane >> 4) for p in range(8)])          # [piece, lane]
-    lc = (lane & 15) ^ (row & 15)
+    # the kernel keeps the offsets of pieces 0..3 (res_offsets); piece p + 4 is 16 rows on
+    row4 = np.array([4 * p + (lane >> 4) for p in range(4)])          # [piece, lane]
+    lc4 = (lane & 15) ^ (row4 & 15)
+    off4 = np.where(n0 + wn * 128 + 8 * lc4 < N, (m0 + wm * 128 + row4) * rld + (n0 + wn * 128 + 8 * lc4) * 2,
+                    OUT_OF_RANGE)
+    row = np.concatenate([row4, row4 + 16])
+    lc = np.concatenate([lc4, lc4])
     m = m0 + wm * 128 + row
     n = n0 + wn * 128 + 8 * lc
-    off = np.where(n < N, m * rld + n * 2, OUT_OF_RANGE)
     for blk in range(4):
-        o = np.where(off == OUT_OF_RANGE, OUT_OF_RANGE, off + blk * 32 * rld)
+        o = np.array([np.where(off4[p & 3] == OUT_OF_RANGE, OUT_OF_RANGE,
+                               off4[p & 3] + blk * 32 * rld + (16 * rld if p >= 4 else 0)) for p in range(8)])
+        # the same element the row formula names
+        assert np.all((o == OUT_OF_RANGE) | (o == (m + 32 * blk) * rld + n * 2))
         mb = m + 32 * blk
         valid = (o != OUT_OF_RANGE) & (mb < M)
         assert np.all(o[valid] + 16 <= r_ext)                          # whole 16 bytes inside
@@ -294,6 +327,12 @@ def test_gemm256_addresses_stay_in_bounds(shape):
             taken += 1
     if shape in ((1024, 64, 1280, 2), (1024, 32, 512, 2)):
         assert taken == 6
+
+
+def test_output_staging_planted_swizzle_slip_caught():
+    check_output_staging()
+    with pytest.raises(AssertionError):
+        check_output_staging(read_swizzle=7)
 
 
 def test_residual_copy_checked_and_a_planted_swizzle_slip_caught():

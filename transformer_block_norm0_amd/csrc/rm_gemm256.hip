@@ -375,7 +375,8 @@ __device__ __forceinline__ void early_b(char* stage, __amdgpu_buffer_rsrc_t rs, 
 // (one copy per lane) holds rows 4p .. 4p+3.
 struct ResDma {
   __amdgpu_buffer_rsrc_t rs;          // the token's residual rows
-  uint32_t off[DMA_PER_OPERAND];      // block 0 source offsets per piece (OUT_OF_RANGE past N)
+  uint32_t off[4];                    // block 0 source offsets of pieces 0..3 (OUT_OF_RANGE past N);
+                                      // piece p + 4 is 16 rows further on, same columns
   uint32_t step;                      // bytes from one block to the next (32 rows)
   char* xb;                           // this wave's 8 KB of the free B stage (blocks 0, 2)
   char* ya;                           // this wave's 8 KB of the free A stage (blocks 1, 3)
@@ -387,7 +388,7 @@ __device__ __forceinline__ void res_offsets(ResDma& r, const GemmArgs& g, const 
   r.rs = make_rsrc(reinterpret_cast<const char*>(g.res) + (long)c.t * g.res_bs * 2, (long)g.M * g.res_ld * 2);
   r.step = 32u * rld;
 #pragma unroll
-  for (int p = 0; p < DMA_PER_OPERAND; ++p) {
+  for (int p = 0; p < 4; ++p) {
     const int row = 4 * p + (lane >> 4);
     const int lc = (lane & 15) ^ (row & 15);
     const int m = c.m0 + wm * 128 + row;  // rows past M read zero (offset beyond the extent)
@@ -398,8 +399,9 @@ __device__ __forceinline__ void res_offsets(ResDma& r, const GemmArgs& g, const 
 
 // Piece p of residual block blk into a wave region.
 __device__ __forceinline__ void res_piece(const ResDma& r, char* region, int blk, int p) {
-  const uint32_t o = r.off[p];
-  dma16(o == OUT_OF_RANGE ? OUT_OF_RANGE : o + (uint32_t)blk * r.step, r.rs, lds_addr(region + p * 1024));
+  const uint32_t o = r.off[p & 3];
+  const uint32_t rows = (uint32_t)blk * r.step + (p >= 4 ? r.step / 2 : 0u);  // 32 rows per block, 16 per half
+  dma16(o == OUT_OF_RANGE ? OUT_OF_RANGE : o + rows, r.rs, lds_addr(region + p * 1024));
 }
 
 // The last k step of a slab: its 16 MFMAs, with the copies of the freed
@@ -452,22 +454,22 @@ __device__ __forceinline__ void add16x4(float (&v)[4], v2u32 w) {
   v[3] += hi16<ST>(w.y);
 }
 
-// Tile epilogue straight from the accumulators: C = acc (+ residual),
-// bf16.  Lane l holds, per (m block i, n block j, v/4 group q), 4 consecutive
-// columns n = 32j + 8q + 4(l/32) of row m = 32i + l%32.  Lanes l and l+32
-// exchange halves (v_permlane32_swap) so that each lane holds 8 consecutive
-// columns (lane l < 32: 8q..8q+7, lane l+32: 8(q+1)..8(q+1)+7, q = 0, 2), and
-// the odd and even 16-lane rows exchange the q = 0 and q = 2 sets
-// (v_permlane16_swap), and the halves of each 16-lane row exchange rows of
-// two neighbouring 32-column blocks (DPP rotation by 8), so that each 16-byte
-// buffer store covers 8 rows x 128 contiguous bytes (whole cache lines):
-// EPI_STORES per wave, every one issued (rows past M or columns past N get an
-// out-of-range offset that the buffer unit drops).
-// RES is compile-time, so the epilogue has no branches (a bias is already in
-// the accumulators, see bias_init).  The residual blocks 0 and 1 were copied
-// into LDS during the tile's last k step (ResDma); block i is waited for with
-// an exact count (RES_WAIT: the copies and stores this wave issued after it),
-// read from LDS, and block i+2 is copied into the region block i leaves.
+// Tile epilogue straight from the accumulators: C = acc (+ residual), bf16
+// (a bias is already in the accumulators, see bias_init).  Each wave's 32 x
+// 128 block i passes through 8 KB of LDS: lane l holds, per (n block j, group
+// q), the 4 columns 32j + 8q + 4(l/32) .. + 3 of row l%32 and writes them
+// (8 bytes) at row r, logical 16-byte chunk 4j + q of 256-byte rows whose
+// chunks are XOR-swizzled by row % 16; it then reads back 16 bytes of a row,
+// so each store covers 4 rows x 256 contiguous bytes (whole cache lines),
+// with no lane exchanges.  Every store is issued (rows past M or columns past
+// N get an out-of-range offset, which the buffer unit drops): EPI_STORES per
+// wave.
+//   Without a residual, block i uses this wave's part of the free B stage
+// (ResDma::xb).  With one (RES), block i's residual is already in that place
+// (blocks 0, 2 in xb, 1, 3 in ya, copied by ResDma): the epilogue waits for it
+// with an exact count (RES_WAIT: the copies and stores this wave issued after
+// it), reads each 8-byte piece, adds it in fp32 and writes the sum over it,
+// and after block i's stores copies block i+2 into the same place.
 template <int N>
 __device__ __forceinline__ void vm_wait() {
   static_assert(N >= 0 && N <= 63, "vmcnt range");
@@ -480,100 +482,53 @@ constexpr int RES_WAIT[4] = {DMA_PER_OPERAND, EPI_STORES_PER_BLOCK + DMA_PER_OPE
 
 template <typename ST, bool RES>
 __device__ __forceinline__ void epilogue(const f32x16_t (&acc)[4][4], const GemmArgs& g, const Tile& c, int wm, int wn,
-                                         int lane, const ResDma* rd) {
+                                         int lane, const ResDma& rd) {
   const int r = lane & 31, h = lane >> 5;
   char* cbase = reinterpret_cast<char*>(g.C) + (long)c.t * g.c_bs * 2;
   const __amdgpu_buffer_rsrc_t crs = make_rsrc(cbase, (long)g.M * g.c_ld * 2);
-  // byte strides (uniform; every per-token offset is below 2^31)
   const uint32_t cld = (uint32_t)(g.c_ld * 2);
+  const int rr0 = lane >> 4, ch = lane & 15;  // read-back: row 4s + rr0, logical chunk ch
+  const int ns = c.n0 + wn * 128 + 8 * ch;
 #pragma unroll
   for (int i = 0; i < 4; ++i) {
     __builtin_amdgcn_sched_barrier(0);
-    v2u32 res[16];
+    char* stg = (RES && (i & 1)) ? rd.ya : rd.xb;
     if constexpr (RES) {
-      // lane l: row r of block i, the 8 bytes h of logical chunk 4j + q (columns 32j + 8q + 4h ..)
       if (i == 0) vm_wait<RES_WAIT[0]>();  // i is a constant once the loop is unrolled
       else if (i == 1) vm_wait<RES_WAIT[1]>();
       else if (i == 2) vm_wait<RES_WAIT[2]>();
       else vm_wait<RES_WAIT[3]>();
-      const char* reg = (i & 1) ? rd->ya : rd->xb;
-#pragma unroll
-      for (int x = 0; x < 16; ++x)
-        res[x] = *reinterpret_cast<const v2u32*>(reg + r * 256 + ((x ^ (r & 15)) << 4) + 8 * h);
     }
-    // rows 32i + 16s + l%16 (s = 0, 1) of the 32-column blocks j = 2jj, 2jj + 1,
-    // each lane one 16-byte chunk 2((l/16)%2) + l/32 of its block
-    v4u32 blk[2][2];
 #pragma unroll
     for (int j = 0; j < 4; ++j) {
-      // the 16-byte chunks 4j + q/2*2 + h of row m (q = 0, 2), packed
-      v4u32 chunk[2];
+      // one n block at a time keeps few registers live (the residual kernels are at the limit)
+      if constexpr (RES) __builtin_amdgcn_sched_barrier(0);
 #pragma unroll
-      for (int q = 0; q < 4; q += 2) {
-        float v0[4], v1[4];
+      for (int q = 0; q < 4; ++q) {
+        v2u32* piece = reinterpret_cast<v2u32*>(stg + r * 256 + (((4 * j + q) ^ (r & 15)) << 4) + 8 * h);
+        float v[4];
 #pragma unroll
-        for (int e = 0; e < 4; ++e) {
-          v0[e] = acc[i][j][4 * q + e];
-          v1[e] = acc[i][j][4 * q + 4 + e];
-        }
-        if constexpr (RES) {
-          add16x4<ST>(v0, res[4 * j + q]);
-          add16x4<ST>(v1, res[4 * j + q + 1]);
-        }
-        const uint32_t a0 = pair16<ST>(v0[0], v0[1]), a1 = pair16<ST>(v0[2], v0[3]);
-        const uint32_t b0 = pair16<ST>(v1[0], v1[1]), b1 = pair16<ST>(v1[2], v1[3]);
-        const auto s0 = __builtin_amdgcn_permlane32_swap(a0, b0, false, false);
-        const auto s1 = __builtin_amdgcn_permlane32_swap(a1, b1, false, false);
-        // lane l < 32: columns 8q..8q+7 of row l (chunk 4j + q); lane l >= 32: 8(q+1).. (chunk 4j + q + 1)
-        chunk[q >> 1] = v4u32{s0[0], s1[0], s0[1], s1[1]};
+        for (int e = 0; e < 4; ++e) v[e] = acc[i][j][4 * q + e];
+        if constexpr (RES) add16x4<ST>(v, *piece);
+        *piece = v2u32{pair16<ST>(v[0], v[1]), pair16<ST>(v[2], v[3])};
       }
-      // Odd 16-lane rows swap with even ones (partner l ^ 16): afterwards set
-      // s (0, 1) holds, in lane l, row 16s + l%16 of the block and its chunk
-      // 2((l/16)%2) + l/32.
+    }
 #pragma unroll
-      for (int k = 0; k < 4; ++k) {
-        const auto sw = __builtin_amdgcn_permlane16_swap(chunk[0][k], chunk[1][k], false, false);
-        blk[j & 1][0][k] = sw[0];
-        blk[j & 1][1][k] = sw[1];
-      }
-      if (j & 1) {
-        // The two 8-lane halves of each 16-lane row exchange the blocks' rows
-        // 8..15 and 0..7 (rotation by 8 within the row): store 2s + u then
-        // holds, in lane l, row 16s + 8u + l%8 and the 16-byte chunk
-        // 4((l/8)%2) + 2((l/16)%2) + l/32 of the 64 columns 64(j/2) .. +63:
-        // 8 rows x 128 bytes (whole cache lines) per store.
-        const int jj = j >> 1;
-        const bool lo8 = (lane & 8) == 0;
-        const int cpos = 4 * ((lane >> 3) & 1) + 2 * ((lane >> 4) & 1) + h;
-        const int ns = c.n0 + wn * 128 + 64 * jj + 8 * cpos;
-#pragma unroll
-        for (int sidx = 0; sidx < 2; ++sidx) {
-          v4u32 x, y;
-#pragma unroll
-          for (int k = 0; k < 4; ++k) {
-            const uint32_t p0 = blk[0][sidx][k], p1 = blk[1][sidx][k];
-            const uint32_t r0 = (uint32_t)__builtin_amdgcn_update_dpp(0, (int)p0, 0x128, 0xF, 0xF, false);  // row_ror:8
-            const uint32_t r1 = (uint32_t)__builtin_amdgcn_update_dpp(0, (int)p1, 0x128, 0xF, 0xF, false);
-            x[k] = lo8 ? p0 : r1;
-            y[k] = lo8 ? r0 : p1;
-          }
-#pragma unroll
-          for (int u = 0; u < 2; ++u) {
-            const int ms = c.m0 + wm * 128 + 32 * i + 16 * sidx + 8 * u + (lane & 7);
-            const bool ok = ms < g.M && ns < g.N;
-            const uint32_t co = ok ? (uint32_t)ms * cld + (uint32_t)ns * 2 : OUT_OF_RANGE;
-            __builtin_amdgcn_raw_buffer_store_b128(u == 0 ? x : y, crs, co, 0, 0);
-          }
-        }
-      }
+    for (int s8 = 0; s8 < 8; ++s8) {
+      if (RES && s8 == 4) __builtin_amdgcn_sched_barrier(0);  // four read-backs in flight at a time
+      const int rr = 4 * s8 + rr0;
+      const v4u32 val = *reinterpret_cast<const v4u32*>(stg + rr * 256 + ((ch ^ (rr & 15)) << 4));
+      const int ms = c.m0 + wm * 128 + 32 * i + rr;
+      const bool ok = ms < g.M && ns < g.N;
+      const uint32_t co = ok ? (uint32_t)ms * cld + (uint32_t)ns * 2 : OUT_OF_RANGE;
+      __builtin_amdgcn_raw_buffer_store_b128(val, crs, co, 0, 0);
     }
     if constexpr (RES) {
       if (i < 2) {
-        // this wave's reads of block i are complete: block i+2 into the same region
+        // this wave's reads of the place are complete: residual block i+2 into it
         asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");
-        char* reg = (i & 1) ? rd->ya : rd->xb;
 #pragma unroll
-        for (int p = 0; p < DMA_PER_OPERAND; ++p) res_piece(*rd, reg, i + 2, p);
+        for (int p = 0; p < DMA_PER_OPERAND; ++p) res_piece(rd, stg, i + 2, p);
       }
     }
   }
@@ -804,18 +759,16 @@ __device__ __forceinline__ void gemm256_body(const GemmArgs& g) {
       char* sb = bst(rb);
       const char* nb = bst(nxt3(rb));
       char* eb = bst(nxt3(nxt3(rb)));
-      if constexpr (RES) {
-        res_offsets(rdm, g, ct, wm, wn, lane);
-        rdm.xb = sb + wave * RES_REGION;  // stage of this tile's last B slab
-        rdm.ya = a1 + wave * RES_REGION;  // stage of this tile's last A slab
-      }
+      rdm.xb = sb + wave * RES_REGION;  // stage of this tile's last B slab
+      rdm.ya = a1 + wave * RES_REGION;  // stage of this tile's last A slab
+      if constexpr (RES) res_offsets(rdm, g, ct, wm, wn, lane);
       slab_step<ST, AK, BKM, false, FROM_NXT, FROM_NXT, false, RES>(acc, f0, f1, a1, sb, a0, nb, eb, nk - 1, nk,
                                                                     WAIT_STEADY, g, cur, nxt, wm, wn, wave, lane,
                                                                     bias_cur, ones, &rdm);
       rb = nxt3(rb);
     }
 
-    epilogue<ST, RES>(acc, g, ct, wm, wn, lane, &rdm);
+    epilogue<ST, RES>(acc, g, ct, wm, wn, lane, rdm);
     // after the epilogue's stores: the wait leaves them in flight
     if constexpr (BIAS) settle(bias_nxt);
     if constexpr (RES) {
