@@ -15,6 +15,7 @@
 //     (b, t) of one group of samples at one token t, with block reductions:
 //     the backward kernels, whose per-column parameter-gradient partial sums
 //     then stay in a few registers per thread.
+#include <atomic>
 #include "rm_common.h"
 #include "rm_internal.h"
 #include "rm_vec.h"
@@ -212,16 +213,17 @@ __device__ __forceinline__ void bstv(__amdgpu_buffer_rsrc_t rs, uint32_t voff, u
   }
 }
 
-// Resident blocks per compute unit of a kernel at a block size (cached).
-template <typename K>
-int resident_blocks(K kernel, int threads) {
-  static int cached = 0;
-  if (cached == 0) {
-    int n = 0;
-    if (hipOccupancyMaxActiveBlocksPerMultiprocessor(&n, kernel, threads, 0) != hipSuccess || n <= 0) n = 1;
-    cached = n;
+// Resident blocks per compute unit of a kernel at a block size (cached per
+// kernel; concurrent first calls store the same value).
+template <auto KERNEL>
+int resident_blocks(int threads) {
+  static std::atomic<int> cached{0};
+  int n = cached.load(std::memory_order_relaxed);
+  if (n == 0) {
+    if (hipOccupancyMaxActiveBlocksPerMultiprocessor(&n, KERNEL, threads, 0) != hipSuccess || n <= 0) n = 1;
+    cached.store(n, std::memory_order_relaxed);
   }
-  return cached;
+  return n;
 }
 
 // ---------------------------------------------------------------------------
@@ -1587,7 +1589,7 @@ template <typename ST>
 hipError_t ln2_fwd_t(const rm_dims& d, const rm_params& p, void* y, void* ws, const WsLayout& L, hipStream_t s) {
   const long NR = (long)d.B * d.T;
   // persistent: as many four-wave blocks as stay resident
-  const int rb = d.D % 4 == 0 ? resident_blocks(k_ln2_fwd<ST, 4>, 256) : resident_blocks(k_ln2_fwd<ST, 1>, 256);
+  const int rb = d.D % 4 == 0 ? resident_blocks<k_ln2_fwd<ST, 4>>(256) : resident_blocks<k_ln2_fwd<ST, 1>>(256);
   const dim3 grid((unsigned)std::min<long>((NR + 3) / 4, (long)rb * device_cu_count()));
   prof_begin(KID_LN2_FWD, s);
   if (d.D % 4 == 0)
