@@ -489,6 +489,11 @@ __device__ __forceinline__ void epilogue(const f32x16_t (&acc)[4][4], const Gemm
   const uint32_t cld = (uint32_t)(g.c_ld * 2);
   const int rr0 = lane >> 4, ch = lane & 15;  // read-back: row 4s + rr0, logical chunk ch
   const int ns = c.n0 + wn * 128 + 8 * ch;
+  // store s of block i: row m0 + 128 wm + rr0 + (32 i + 4 s), so its offset is this lane's
+  // base plus a uniform multiple of the row pitch; rows_left = rows from the lane's first on
+  const int m_first = c.m0 + wm * 128 + rr0;
+  const int rows_left = ns < g.N ? g.M - m_first : 0;
+  const uint32_t off_first = (uint32_t)m_first * cld + (uint32_t)ns * 2;
 #pragma unroll
   for (int i = 0; i < 4; ++i) {
     __builtin_amdgcn_sched_barrier(0);
@@ -518,9 +523,8 @@ __device__ __forceinline__ void epilogue(const f32x16_t (&acc)[4][4], const Gemm
       if (RES && s8 == 4) __builtin_amdgcn_sched_barrier(0);  // four read-backs in flight at a time
       const int rr = 4 * s8 + rr0;
       const v4u32 val = *reinterpret_cast<const v4u32*>(stg + rr * 256 + ((ch ^ (rr & 15)) << 4));
-      const int ms = c.m0 + wm * 128 + 32 * i + rr;
-      const bool ok = ms < g.M && ns < g.N;
-      const uint32_t co = ok ? (uint32_t)ms * cld + (uint32_t)ns * 2 : OUT_OF_RANGE;
+      const int dr = 32 * i + 4 * s8;  // rr - rr0
+      const uint32_t co = dr < rows_left ? off_first + (uint32_t)dr * cld : OUT_OF_RANGE;
       __builtin_amdgcn_raw_buffer_store_b128(val, crs, co, 0, 0);
     }
     if constexpr (RES) {
