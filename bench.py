@@ -61,12 +61,23 @@ def small_flops(d):
     return {"small_fwd": f, "small_bwd": 2.0 * f}
 
 
+# samples per group of the backward's parameter-gradient partials (the library's row groups)
+ROWS_PER_GROUP = 128
+
+
+def tail_per_sample(d, sz):
+    """The backward tail runs one sample per workgroup in LDS (16-bit samples of at most 160 KB with
+    16-byte rows and 4-element token-mix chunks) and writes per-sample partials."""
+    return sz == 2 and d.D % 8 == 0 and (d.D // d.T) % 4 == 0 and d.T * d.D * 2 <= 64 * 1280 * 2
+
+
 def row_bytes(d, sz):
     """Algorithmic HBM bytes of each row-kernel launch: its inputs read once, outputs written once."""
     B, T, D, H = d.B, d.T, d.D, d.k * d.D
     N = B * T
-    nb = (B + 63) // 64
-    p_ln2, p_gate, p_tail = 3 * nb * T * D * 4, (4 * nb * T * H + nb * T * 2 * H) * 4, 4 * nb * T * D * 4
+    nb = (B + ROWS_PER_GROUP - 1) // ROWS_PER_GROUP
+    p_ln2, p_gate = 3 * nb * T * D * 4, (4 * nb * T * H + nb * T * 2 * H) * 4
+    p_tail = 4 * (B if tail_per_sample(d, sz) else nb * T) * D * 4
     return {
         "prologue": N * D * sz * 2 + N * 16,                              # x -> out1, 4 stats
         "gate_fwd": N * 2 * H * sz + N * H * sz + N * 16,                 # Z -> hidden, 4 stats

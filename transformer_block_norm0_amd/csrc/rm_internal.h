@@ -10,7 +10,7 @@
 namespace rm {
 
 // Rows (b) per workgroup in the per-token row-group kernels of the backward.
-constexpr int ROWS_PER_GROUP = 64;
+constexpr int ROWS_PER_GROUP = 128;
 
 enum KernelId {
   KID_PROLOGUE = 0,   // norm0 -> token mix -> +x -> norm1
