@@ -239,6 +239,23 @@ int resident_blocks(int threads) {
 //      norm1 in registers and one store of out1.
 constexpr int PRO_LDS_BYTES = (int)SAMPLE_LDS_BYTES;  // 160 KB: T*D bf16 for T <= 64, D <= 1280
 
+// Copy nbytes (a multiple of 16) from global src to LDS dst with 16-byte
+// buffer loads that write LDS directly, range-checked against [src, src +
+// nbytes) (an offset outside reads zeros): the wave's pieces first, first +
+// stride, ... (first and stride uniform multiples of 64 pieces; piece p is
+// bytes 16p .. 16p + 15 of both).  Inline assembly, so the compiler does not
+// count these loads: the caller waits (vmcnt(0)) before reading the data.
+__device__ __forceinline__ void copy_to_lds(const void* src, void* dst, int nbytes, int first, int stride, int lane) {
+  const int np = nbytes >> 4;
+  const __amdgpu_buffer_rsrc_t rs = row_rsrc(src, (long)nbytes);
+  const char* d = reinterpret_cast<const char*>(dst);
+  for (int p0 = first; p0 < np; p0 += stride) {
+    const int p = p0 + lane;
+    const uint32_t lds = lds_byte_addr(d + (long)p0 * 16);
+    if (p < np) asm volatile("buffer_load_dwordx4 %0, %1, 0 offen lds" ::"v"((uint32_t)p * 16), "s"(rs), "{m0}"(lds) : "memory");
+  }
+}
+
 __device__ __forceinline__ float load_bypass_l1(const float* p) {
   return __hip_atomic_load(p, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
 }

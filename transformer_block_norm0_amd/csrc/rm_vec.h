@@ -258,35 +258,15 @@ __device__ __forceinline__ void block_sum8(float (&v)[8], float* red, int parity
   }
 }
 
-// floor(c / S) for 0 <= c < 2^16, 1 <= S <= 1280 (exact: the quotient's
-// fractional part is at least 0.5/S away from an integer).
-// 16-byte direct global -> LDS copy: lane l's 16 bytes (uniform base sbase
-// plus its byte offset voff) land at LDS byte address lds + 16 * l, so one
-// instruction fills a contiguous run of LDS per wave.  Inline assembly: the
-// compiler does not count it, so wait_vm_all() must precede any read of the
-// data.  Addresses must be 16-byte aligned.
-__device__ __forceinline__ void copy16_to_lds(uint32_t voff, const void* sbase, uint32_t lds) {
-  asm volatile("global_load_lds_dwordx4 %0, %1" ::"v"(voff), "s"(sbase), "{m0}"(lds) : "memory");
-}
 // Wait until every vector-memory operation of this wave has completed.
 __device__ __forceinline__ void wait_vm_all() { asm volatile("s_waitcnt vmcnt(0)" ::: "memory"); }
 // LDS byte address of a pointer into a __shared__ object.
 __device__ __forceinline__ uint32_t lds_byte_addr(const void* p) {
   return (uint32_t)(uintptr_t)((__attribute__((address_space(3))) const char*)p);
 }
-// Copy nbytes (a multiple of 16) from global src to LDS dst, the wave's
-// pieces first..first+stride-1, first+stride*... (src, dst, first and stride
-// uniform per wave; first and stride multiples of 64 pieces).
-__device__ __forceinline__ void copy_to_lds(const void* src, void* dst, int nbytes, int first, int stride,
-                                            int lane) {
-  const int np = nbytes >> 4;
-  const char* d = reinterpret_cast<const char*>(dst);
-  for (int p0 = first; p0 < np; p0 += stride) {
-    const int p = p0 + lane;
-    if (p < np) copy16_to_lds((uint32_t)p * 16, src, lds_byte_addr(d + (long)p0 * 16));
-  }
-}
 
+// floor(c / S) for 0 <= c < 2^16, 1 <= S <= 1280 (exact: the quotient's
+// fractional part is at least 0.5/S away from an integer).
 __device__ __forceinline__ int div_small(int c, float invS) { return (int)(((float)c + 0.5f) * invS); }
 
 }  // namespace rm
