@@ -25,6 +25,7 @@ from __future__ import annotations
 import argparse
 import json
 import os
+import subprocess
 import sys
 import time
 
@@ -201,6 +202,45 @@ def library_gemms(d, dtype, reps=10):
     return out
 
 
+def power_sampler(path, max_seconds=900.0):
+    """Child process: socket power (W) and gfx clock (MHz) of GPU 0 every 20 ms into a csv, until
+    terminated (or max_seconds).  Reads the SMI counters only; never touches HIP."""
+    import amdsmi
+    amdsmi.amdsmi_init()
+    h = amdsmi.amdsmi_get_processor_handles()[0]
+    t_end = time.time() + max_seconds
+    with open(path, "w") as f:
+        cap = amdsmi.amdsmi_get_power_cap_info(h).get("power_cap")
+        f.write(f"# power_cap_uw {cap}\n")
+        while time.time() < t_end:
+            p = amdsmi.amdsmi_get_power_info(h).get("current_socket_power")
+            c = amdsmi.amdsmi_get_clock_info(h, amdsmi.AmdSmiClkType.GFX).get("clk")
+            f.write(f"{time.time():.3f},{p},{c}\n")
+            f.flush()
+            time.sleep(0.02)
+
+
+def power_summary(path, t0, t1):
+    """Mean / max socket power and mean gfx clock over the samples taken in [t0, t1]."""
+    cap, pw, ck = None, [], []
+    for line in open(path):
+        if line.startswith("# power_cap_uw"):
+            v = line.split()[-1]
+            cap = float(v) / 1e6 if v.replace(".", "").isdigit() else None
+            continue
+        t, p, c = line.strip().split(",")
+        if t0 <= float(t) <= t1:
+            if p.replace(".", "").isdigit():
+                pw.append(float(p))
+            if c.replace(".", "").isdigit():
+                ck.append(float(c))
+    if not pw:
+        return {"error": "no power samples in the timed region"}
+    return {"avg_w": round(sum(pw) / len(pw), 1), "max_w": max(pw), "cap_w": cap,
+            "gfx_mhz_avg": round(sum(ck) / len(ck), 1) if ck else None, "samples": len(pw),
+            "window": "timed region"}
+
+
 def main():
     ap = argparse.ArgumentParser(description=__doc__, formatter_class=argparse.RawDescriptionHelpFormatter)
     ap.add_argument("--gpus", type=int, default=1)
@@ -219,6 +259,12 @@ def main():
                          "main: every shape takes the main kernel set")
     ap.add_argument("--library-gemms", action="store_true",
                     help="also time the six GEMM shapes through torch.bmm (hipBLASLt) for comparison")
+    ap.add_argument("--power-log", default=None, metavar="CSV",
+                    help="sample socket power and gfx clock (child process, SMI counters) into CSV and report "
+                         "their means over the timed region")
+    ap.add_argument("--zero-operands", action="store_true",
+                    help="zero x, dy, w1, b1, wout and bout before timing: the same kernels and schedule on "
+                         "operands that barely toggle (a power-dependence measurement, not a throughput claim)")
     ap.add_argument("--copy-calibration-mib", type=int, default=0,
                     help="run one plain device-to-device copy of this many MiB first (reference for HBM counters)")
     args = ap.parse_args()
@@ -227,6 +273,10 @@ def main():
         print(f"bench.py: this build runs on one GPU only (asked for --gpus {args.gpus}); "
               "multi-GPU sharding is not built", file=sys.stderr)
         sys.exit(2)
+
+    sampler = None
+    if args.power_log:
+        sampler = subprocess.Popen([sys.executable, os.path.abspath(__file__), "--power-sampler", args.power_log])
 
     import torch
     import transformer_block_norm0_amd as rb
@@ -243,6 +293,9 @@ def main():
     from rm_gpu import DeviceCase  # noqa: E402  (moves the case to the device, calls the C ABI)
     dc = DeviceCase(case, kernels=args.kernels)
     del case
+    if args.zero_operands:
+        for t in (dc.x, dc.dy, dc.params["w1"], dc.params["b1"], dc.params["wout"], dc.params["bout"]):
+            t.zero_()
     torch.cuda.synchronize()
     stream = torch.cuda.current_stream()
     if args.copy_calibration_mib:
@@ -270,12 +323,14 @@ def main():
     ev0, ev1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
     torch.cuda.synchronize()
     h0 = time.perf_counter()
+    wall0 = time.time()
     ev0.record(stream)
     for _ in range(args.steps):
         step()
     ev1.record(stream)
     torch.cuda.synchronize()
     host_s = time.perf_counter() - h0
+    wall1 = time.time()
     ms_total = ev0.elapsed_time(ev1)
     ms_step = ms_total / args.steps
     peak_mem = torch.cuda.max_memory_allocated()
@@ -417,6 +472,13 @@ def main():
         cpu = cpu_baseline(w.name, args.cpu_batch, args.cpu_seconds)
         log(f"  {cpu['value']:.4g} tokens/s on {cpu['cores']} threads")
 
+    power = None
+    if sampler is not None:
+        sampler.terminate()
+        sampler.wait(timeout=30)
+        power = power_summary(args.power_log, wall0, wall1)
+        log(f"power over the timed region: {power}")
+
     out = {
         "metric": ("fwd+bwd tokens/s and % MFMA peak, B1024 T64 D1280 k2 bf16, 1 GPU" if w.name == PRODUCTION
                    else f"fwd+bwd tokens/s and % MFMA peak, {w.name}, 1 GPU"),
@@ -430,7 +492,8 @@ def main():
         "scaling": "weak",
         "vs_baseline": None,
         "dtype": w.dtype,
-        "data": "synthetic (seeded N(0,1) inputs and upstream grad, he-uniform weights)",
+        "data": ("synthetic, x dy w1 b1 wout bout all zero (power-dependence measurement)" if args.zero_operands
+                 else "synthetic (seeded N(0,1) inputs and upstream grad, he-uniform weights)"),
         "config": {"workload": w.name, "B": d.B, "T": d.T, "D": d.D, "k": d.k, "H": d.H,
                    "tokens_per_step": tokens, "parallelism": "single GPU", "kernels": args.kernels},
         "tflops": round(tflops, 2),
@@ -442,6 +505,7 @@ def main():
         "pages_protocol": protocol,
         "graph_replay": graph,
         "kernels": kernels,
+        "power": power,
     }
     if args.library_gemms:
         log("library GEMMs (torch.bmm) on the same shapes:")
@@ -473,4 +537,7 @@ def load_traffic(kernel, workload):
 
 
 if __name__ == "__main__":
-    main()
+    if len(sys.argv) == 3 and sys.argv[1] == "--power-sampler":
+        power_sampler(sys.argv[2])
+    else:
+        main()
