@@ -21,13 +21,16 @@
 //     compiler neither waits for them at every LDS read nor reorders them.
 //   * One barrier per slab, before its last k step: the fragments of k steps
 //     2..4 are read during the MFMAs of the step before, then the barrier
-//     (next slab landed, this slab fully read), the copies of A slab k+2 and
-//     B slab k+3 into the stages just freed, and the next slab's first
-//     fragments are read during the last k step's MFMAs.  No LDS latency is
-//     exposed inside a tile.
+//     (next slab landed, this slab fully read); A slab k+2 is copied into the
+//     stage just freed between the last k step's MFMAs, B slab k+3 at the
+//     starts of the next slab's first three k steps, and the next slab's
+//     first fragments are read during the last k step's MFMAs, so every
+//     fragment read is issued a k step before its MFMAs.
 //   * Persistent: one workgroup per CU walks a range of tiles; the copy
-//     stream continues into the next tile and a tile's results are stored
-//     straight from the accumulators while the next tile's copies land.
+//     stream continues into the next tile, and a tile's results go through
+//     LDS (freed operand stages) to whole-cache-line stores while the next
+//     tile's copies land.  The bias is the accumulators' starting value (a
+//     rank-1 MFMA); a residual is copied into LDS like an operand slab.
 //   * K-major operands (row = m or n, 128 contiguous bytes of K: one whole
 //     cache line per row and slab) live in LDS as 128-byte rows whose 16-byte
 //     chunks are XOR-swizzled by (row/2)%8; an MFMA fragment is one 16-byte
@@ -454,7 +457,7 @@ __device__ __forceinline__ void add16x4(float (&v)[4], v2u32 w) {
   v[3] += hi16<ST>(w.y);
 }
 
-// Tile epilogue straight from the accumulators: C = acc (+ residual), bf16
+// Tile epilogue: C = acc (+ residual), bf16
 // (a bias is already in the accumulators, see bias_init).  Each wave's 32 x
 // 128 block i passes through 8 KB of LDS: lane l holds, per (n block j, group
 // q), the 4 columns 32j + 8q + 4(l/32) .. + 3 of row l%32 and writes them
