@@ -62,8 +62,13 @@ def small_flops(d):
     return {"small_fwd": f, "small_bwd": 2.0 * f}
 
 
-# samples per group of the backward's parameter-gradient partials (the library's row groups)
-ROWS_PER_GROUP = 128
+def rows_per_group(B, T):
+    """Samples per group of the backward's parameter-gradient partials (the library's row groups):
+    128, halved down to 16 while T * ceil(B / rows) < 512 workgroups."""
+    r = 128
+    while r > 16 and T * -(-B // r) < 512:
+        r //= 2
+    return r
 
 
 def tail_per_sample(d, sz):
@@ -76,7 +81,7 @@ def row_bytes(d, sz):
     """Algorithmic HBM bytes of each row-kernel launch: its inputs read once, outputs written once."""
     B, T, D, H = d.B, d.T, d.D, d.k * d.D
     N = B * T
-    nb = (B + ROWS_PER_GROUP - 1) // ROWS_PER_GROUP
+    nb = -(-B // rows_per_group(B, T))
     p_ln2, p_gate = 3 * nb * T * D * 4, (4 * nb * T * H + nb * T * 2 * H) * 4
     p_tail = 4 * (B if tail_per_sample(d, sz) else nb * T) * D * 4
     return {

@@ -44,8 +44,13 @@ def tail_per_sample(B, T, D, dtype):
     return dtype in ("bf16", "f16") and D % 8 == 0 and (D // T) % 4 == 0 and T * D * 2 <= 64 * 1280 * 2
 
 
-# samples per group of the backward's parameter-gradient partials (rm_internal.h)
-ROWS_PER_GROUP = 128
+def rows_per_group(B, T):
+    """Samples per group of the backward's parameter-gradient partials (the library's row groups):
+    128, halved down to 16 while T * ceil(B / rows) < 512 workgroups."""
+    r = 128
+    while r > 16 and T * -(-B // r) < 512:
+        r //= 2
+    return r
 
 
 def expected_workspace_bytes(B, T, D, k, dtype):
@@ -53,7 +58,7 @@ def expected_workspace_bytes(B, T, D, k, dtype):
     al = lambda v: (v + 255) // 256 * 256
     N, H = B * T, k * D
     sz = 4 if dtype == "f32" else 2
-    nb = (B + ROWS_PER_GROUP - 1) // ROWS_PER_GROUP
+    nb = -(-B // rows_per_group(B, T))
     sizes = [N * D * sz, N * 2 * H * sz, N * H * sz, N * D * sz, 10 * N * 4,     # saved by the forward
              N * D * sz, N * H * sz, N * 2 * H * sz, N * D * sz, N * D * sz,     # backward scratch
              3 * nb * T * D * 4, (4 * nb * T * H + nb * T * 2 * H) * 4,                        # partials

@@ -54,7 +54,8 @@ WsLayout ws_layout(const rm_dims& d) {
     off += bytes;
     return r;
   };
-  L.nb = (d.B + ROWS_PER_GROUP - 1) / ROWS_PER_GROUP;
+  L.rpg = rows_per_group(d.B, d.T);
+  L.nb = (d.B + L.rpg - 1) / L.rpg;
   const size_t nb = L.nb;
   L.h1 = take(N * D * sz);
   L.z = take(N * 2 * H * sz);

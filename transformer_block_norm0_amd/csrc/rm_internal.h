@@ -9,8 +9,17 @@
 
 namespace rm {
 
-// Rows (b) per workgroup in the per-token row-group kernels of the backward.
-constexpr int ROWS_PER_GROUP = 128;
+// Rows (b) per workgroup in the per-token row-group kernels of the backward:
+// 128, halved (down to 16) while the T x ceil(B / rows) workgroups of those
+// kernels would number fewer than 512 (two per compute unit), so that small
+// batches still spread over the chip.  Always a power of two.
+constexpr int MAX_ROWS_PER_GROUP = 128;
+constexpr int MIN_ROWS_PER_GROUP = 16;
+inline int rows_per_group(int B, int T) {
+  int r = MAX_ROWS_PER_GROUP;
+  while (r > MIN_ROWS_PER_GROUP && (long)T * ((B + r - 1) / r) < 512) r >>= 1;
+  return r;
+}
 
 enum KernelId {
   KID_PROLOGUE = 0,   // norm0 -> token mix -> +x -> norm1
@@ -47,7 +56,8 @@ struct WsLayout {
   size_t p_ln2, p_gate, p_tail;            // backward partial sums (fp32): offsets from the scratch start
   size_t scratch_off, scratch_bytes;       // where the scratch starts in the workspace, its size
   size_t total;                            // scratch_off + scratch_bytes
-  int nb;                                  // row groups per token: ceil(B / ROWS_PER_GROUP)
+  int rpg;                                 // rows per group: rows_per_group(B, T)
+  int nb;                                  // row groups per token: ceil(B / rpg)
 };
 
 bool dims_valid(const rm_dims& d);

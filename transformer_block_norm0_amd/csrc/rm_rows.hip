@@ -575,7 +575,7 @@ __global__ __launch_bounds__(256) void k_ln2_fwd(const ST* __restrict__ r2, cons
 
 // ---------------------------------------------------------------------------
 // Backward row-group kernels: blockIdx.x = token t, blockIdx.y = group of
-// ROWS_PER_GROUP samples; thread k owns the N-element chunks k, k + blockDim,
+// rpg samples; thread k owns the N-element chunks k, k + blockDim,
 // ... (QC of them) of every row it visits.  Partial sums of parameter
 // gradients over the group's rows are written to part[.][group][t][col].
 
@@ -607,7 +607,7 @@ template <typename ST, int N, int Q>
 __global__ __launch_bounds__(256) void k_ln2_bwd(const ST* __restrict__ r2, const ST* __restrict__ dy,
                                                  const ST* __restrict__ g2, const float* __restrict__ stats,
                                                  ST* __restrict__ do2, float* __restrict__ part, int B, int T,
-                                                 int D, int nb) {
+                                                 int D, int nb, int rpg) {
   __shared__ float lds[4 * MAXD];
   const int t = blockIdx.x, grp = blockIdx.y;
   const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
@@ -618,8 +618,8 @@ __global__ __launch_bounds__(256) void k_ln2_bwd(const ST* __restrict__ r2, cons
   for (int q = 0; q < Q; ++q)
 #pragma unroll
     for (int e = 0; e < N; ++e) pg[q][e] = pb[q][e] = po[q][e] = 0.f;
-  const int b_end = min(B, (grp + 1) * ROWS_PER_GROUP);
-  for (int b = grp * ROWS_PER_GROUP + wave; b < b_end; b += 4) {
+  const int b_end = min(B, (grp + 1) * rpg);
+  for (int b = grp * rpg + wave; b < b_end; b += 4) {
     const long row = (long)b * T + t;
     const float mu = stats[ST_MU2 * NR + row], rs = stats[ST_RS2 * NR + row];
     Raw<ST, N> rr[Q];
@@ -727,7 +727,7 @@ __global__ __launch_bounds__(MAXT) void k_gate_bwd(const ST* __restrict__ Z, con
                                                    const ST* __restrict__ gg, const ST* __restrict__ bg,
                                                    const float* __restrict__ stats, ST* __restrict__ dZ,
                                                    float* __restrict__ pgate, float* __restrict__ pb1, int B,
-                                                   int T, int H, int nb) {
+                                                   int T, int H, int nb, int rpg) {
   __shared__ float red[2 * 4 * RPI * 16];
   const int t = blockIdx.x, grp = blockIdx.y;
   const int nw = blockDim.x >> 6;
@@ -748,7 +748,7 @@ __global__ __launch_bounds__(MAXT) void k_gate_bwd(const ST* __restrict__ Z, con
     ldr(gg + c, rgg[k]);
     ldr(bg + c, rbg[k]);
   }
-  const int b_begin = grp * ROWS_PER_GROUP, b_end = min(B, (grp + 1) * ROWS_PER_GROUP);
+  const int b_begin = grp * rpg, b_end = min(B, (grp + 1) * rpg);
   int parity = 0;
   for (int b0 = b_begin; b0 < b_end; b0 += RPI) {
     GateBwdSlot<ST, N, QC> cur[RPI];
@@ -862,7 +862,7 @@ __global__ __launch_bounds__(MAXT) void k_gate_bwd(const ST* __restrict__ Z, con
 
 // Gate / SiLU / inner LayerNorm backward for H % 4 == 0: one thread per
 // 4-column chunk of U (and the matching chunk of G and d hidden), one
-// workgroup walking the ROWS_PER_GROUP rows (b, t) of one sample group at one
+// workgroup walking the rpg rows (b, t) of one sample group at one
 // token t.  Rows go two at a time: the pair's u, g, d hidden sit in a
 // two-slot register ring, refilled with the next pair (unconditional loads
 // from clamped rows) before the pair's one block reduction of eight sums, so
@@ -881,9 +881,9 @@ __global__ __launch_bounds__(MAXT) void k_gate_bwd_ring(const ST* __restrict__ Z
                                                         const ST* __restrict__ gg, const ST* __restrict__ bg,
                                                         const float* __restrict__ stats, ST* __restrict__ dZ,
                                                         float* __restrict__ pgate, float* __restrict__ pb1, int B,
-                                                        int T, int H, int nb) {
+                                                        int T, int H, int nb, int rpg) {
   __shared__ float red8[2 * 16 * 8];
-  __shared__ float4 sst[ROWS_PER_GROUP];
+  __shared__ float4 sst[MAX_ROWS_PER_GROUP];
   constexpr int SZ = (int)sizeof(ST);
   const int t = blockIdx.x, grp = blockIdx.y;
   const int nw = blockDim.x >> 6;
@@ -900,7 +900,7 @@ __global__ __launch_bounds__(MAXT) void k_gate_bwd_ring(const ST* __restrict__ Z
 #pragma unroll
   for (int e = 0; e < 4; ++e) agx[e] = abx[e] = agg[e] = abg[e] = au[e] = ag[e] = 0.f;
 
-  const int b0 = grp * ROWS_PER_GROUP, bl = min(B, b0 + ROWS_PER_GROUP) - 1;
+  const int b0 = grp * rpg, bl = min(B, b0 + rpg) - 1;
   // every row access: uniform row offset (scalar) + this thread's column offset
   const __amdgpu_buffer_rsrc_t zrs = row_rsrc(Z, NR * 2 * H * SZ);
   const __amdgpu_buffer_rsrc_t hrs = row_rsrc(dhid, NR * H * SZ);
@@ -910,7 +910,7 @@ __global__ __launch_bounds__(MAXT) void k_gate_bwd_ring(const ST* __restrict__ Z
 
   zero_red(red8);
   // the group's inner-LN statistics (mux, rsx, mug, rsg per row) staged in LDS once
-  for (int i = threadIdx.x; i < 4 * ROWS_PER_GROUP; i += blockDim.x) {
+  for (int i = threadIdx.x; i < 4 * rpg; i += blockDim.x) {
     const int r = i >> 2, q = i & 3;
     const long row = (long)min(b0 + r, bl) * T + t;
     reinterpret_cast<float*>(sst)[i] = stats[(ST_MUX + q) * NR + row];
@@ -1007,10 +1007,11 @@ __global__ __launch_bounds__(MAXT) void k_gate_bwd_ring(const ST* __restrict__ Z
       bst4<ST>(drs, sok ? vg : 0x80000000u, rowk[k] * zrow, dg);
     }
   };
-  static_assert(ROWS_PER_GROUP % RING == 0, "the ring slots are consumed together");
+  // rpg is a power of two of at least MIN_ROWS_PER_GROUP: the ring slots are consumed together
+  static_assert(MIN_ROWS_PER_GROUP % RING == 0, "whole ring steps per group");
 #pragma unroll 1
-  for (int r0 = 0; r0 < ROWS_PER_GROUP - RING; r0 += RING) pair_step(r0, std::true_type{});
-  pair_step(ROWS_PER_GROUP - RING, std::false_type{});
+  for (int r0 = 0; r0 < rpg - RING; r0 += RING) pair_step(r0, std::true_type{});
+  pair_step(rpg - RING, std::false_type{});
   if (craw < H) {
     const long blk = (long)nb * T * H;
     const long o = ((long)grp * T + t) * H;
@@ -1285,7 +1286,7 @@ __global__ __launch_bounds__(256) void k_ln1_bwd(const ST* __restrict__ x, const
                                                  const ST* __restrict__ g0, const ST* __restrict__ be0,
                                                  const ST* __restrict__ g1, const float* __restrict__ stats,
                                                  ST* __restrict__ dr1, float* __restrict__ part, int B, int T,
-                                                 int D, int nb) {
+                                                 int D, int nb, int rpg) {
   __shared__ float lds[4 * MAXD];
   const int i = blockIdx.x, grp = blockIdx.y;
   const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
@@ -1303,8 +1304,8 @@ __global__ __launch_bounds__(256) void k_ln1_bwd(const ST* __restrict__ x, const
 #pragma unroll
     for (int e = 0; e < N; ++e) pg[q][e] = pb[q][e] = 0.f;
   }
-  const int b_end = min(B, (grp + 1) * ROWS_PER_GROUP);
-  for (int b = grp * ROWS_PER_GROUP + wave; b < b_end; b += 4) {
+  const int b_end = min(B, (grp + 1) * rpg);
+  for (int b = grp * rpg + wave; b < b_end; b += 4) {
     const long row = (long)b * T + i;
     const long base = (long)b * T * D;
     const float mu1 = stats[ST_MU1 * NR + row], rs1 = stats[ST_RS1 * NR + row];
@@ -1373,7 +1374,7 @@ template <typename ST, int N, int Q>
 __global__ __launch_bounds__(256) void k_ln0_bwd(const ST* __restrict__ x, const ST* __restrict__ dr1,
                                                  const ST* __restrict__ g0, const float* __restrict__ stats,
                                                  ST* __restrict__ dx, float* __restrict__ part, int B, int T, int D,
-                                                 int nb) {
+                                                 int nb, int rpg) {
   __shared__ float lds[4 * MAXD];
   const int j = blockIdx.x, grp = blockIdx.y;
   const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
@@ -1391,8 +1392,8 @@ __global__ __launch_bounds__(256) void k_ln0_bwd(const ST* __restrict__ x, const
 #pragma unroll
     for (int e = 0; e < N; ++e) pg[q][e] = pb[q][e] = 0.f;
   }
-  const int b_end = min(B, (grp + 1) * ROWS_PER_GROUP);
-  for (int b = grp * ROWS_PER_GROUP + wave; b < b_end; b += 4) {
+  const int b_end = min(B, (grp + 1) * rpg);
+  for (int b = grp * rpg + wave; b < b_end; b += 4) {
     const long row = (long)b * T + j;
     const long base = (long)b * T * D;
     const float mu0 = stats[ST_MU0 * NR + row], rs0 = stats[ST_RS0 * NR + row];
@@ -1627,11 +1628,11 @@ hipError_t ln2_bwd_t(const rm_dims& d, const rm_params& p, const void* dy, void*
   if (d.D % 4 == 0)
     hipLaunchKernelGGL((k_ln2_bwd<ST, 4, MAXD / 256>), grid, dim3(256), 0, s, wsp<ST>(ws, L.r2), cptr<ST>(dy),
                        cptr<ST>(p.ln2_g), wsp<float>(ws, L.stats), wsp<ST>(sc, L.do2), wsp<float>(sc, L.p_ln2), d.B,
-                       d.T, d.D, L.nb);
+                       d.T, d.D, L.nb, L.rpg);
   else
     hipLaunchKernelGGL((k_ln2_bwd<ST, 1, MAXD / 64>), grid, dim3(256), 0, s, wsp<ST>(ws, L.r2), cptr<ST>(dy),
                        cptr<ST>(p.ln2_g), wsp<float>(ws, L.stats), wsp<ST>(sc, L.do2), wsp<float>(sc, L.p_ln2), d.B,
-                       d.T, d.D, L.nb);
+                       d.T, d.D, L.nb, L.rpg);
   prof_end(KID_LN2_BWD, s);
   return hipGetLastError();
 }
@@ -1649,15 +1650,15 @@ hipError_t gate_bwd_t(const rm_dims& d, const rm_params& p, void* ws, void* sc, 
   if (H % 4 == 0 && H <= 2560 && 2L * d.B * d.T * H * (long)sizeof(ST) <= 0x7fffffffL)
     hipLaunchKernelGGL((k_gate_bwd_ring<ST, 640>), grid, dim3(round64(H / 4)), 0, s, wsp<ST>(ws, L.z),
                        wsp<ST>(sc, L.dhid), cptr<ST>(p.lnx_g), cptr<ST>(p.lnx_b), cptr<ST>(p.lng_g),
-                       cptr<ST>(p.lng_b), wsp<float>(ws, L.stats), wsp<ST>(sc, L.dz), pg, pb1, d.B, d.T, H, L.nb);
+                       cptr<ST>(p.lng_b), wsp<float>(ws, L.stats), wsp<ST>(sc, L.dz), pg, pb1, d.B, d.T, H, L.nb, L.rpg);
   else if (H % 4 == 0)
     hipLaunchKernelGGL((k_gate_bwd<ST, 4, 1, 1024, 2>), grid, dim3(round64(H / 4)), 0, s, wsp<ST>(ws, L.z),
                        wsp<ST>(sc, L.dhid), cptr<ST>(p.lnx_g), cptr<ST>(p.lnx_b), cptr<ST>(p.lng_g),
-                       cptr<ST>(p.lng_b), wsp<float>(ws, L.stats), wsp<ST>(sc, L.dz), pg, pb1, d.B, d.T, H, L.nb);
+                       cptr<ST>(p.lng_b), wsp<float>(ws, L.stats), wsp<ST>(sc, L.dz), pg, pb1, d.B, d.T, H, L.nb, L.rpg);
   else
     hipLaunchKernelGGL((k_gate_bwd<ST, 1, 8, 512, 1>), grid, dim3(round64((H + 7) / 8)), 0, s, wsp<ST>(ws, L.z),
                        wsp<ST>(sc, L.dhid), cptr<ST>(p.lnx_g), cptr<ST>(p.lnx_b), cptr<ST>(p.lng_g),
-                       cptr<ST>(p.lng_b), wsp<float>(ws, L.stats), wsp<ST>(sc, L.dz), pg, pb1, d.B, d.T, H, L.nb);
+                       cptr<ST>(p.lng_b), wsp<float>(ws, L.stats), wsp<ST>(sc, L.dz), pg, pb1, d.B, d.T, H, L.nb, L.rpg);
   prof_end(KID_GATE_BWD, s);
   return hipGetLastError();
 }
@@ -1682,22 +1683,22 @@ hipError_t tail_bwd_t(const rm_dims& d, const rm_params& p, const void* x, void*
   if (vec4_rows(d))
     hipLaunchKernelGGL((k_ln1_bwd<ST, 4, MAXD / 256>), grid, dim3(256), 0, s, cptr<ST>(x), wsp<ST>(sc, L.dh1),
                        cptr<ST>(p.ln0_g), cptr<ST>(p.ln0_b), cptr<ST>(p.ln1_g), wsp<float>(ws, L.stats),
-                       wsp<ST>(sc, L.dr1), wsp<float>(sc, L.p_tail), d.B, d.T, d.D, L.nb);
+                       wsp<ST>(sc, L.dr1), wsp<float>(sc, L.p_tail), d.B, d.T, d.D, L.nb, L.rpg);
   else
     hipLaunchKernelGGL((k_ln1_bwd<ST, 1, MAXD / 64>), grid, dim3(256), 0, s, cptr<ST>(x), wsp<ST>(sc, L.dh1),
                        cptr<ST>(p.ln0_g), cptr<ST>(p.ln0_b), cptr<ST>(p.ln1_g), wsp<float>(ws, L.stats),
-                       wsp<ST>(sc, L.dr1), wsp<float>(sc, L.p_tail), d.B, d.T, d.D, L.nb);
+                       wsp<ST>(sc, L.dr1), wsp<float>(sc, L.p_tail), d.B, d.T, d.D, L.nb, L.rpg);
   prof_end(KID_LN1_BWD, s);
   if ((e = hipGetLastError()) != hipSuccess) return e;
   prof_begin(KID_LN0_BWD, s);
   if (vec4_rows(d))
     hipLaunchKernelGGL((k_ln0_bwd<ST, 4, MAXD / 256>), grid, dim3(256), 0, s, cptr<ST>(x), wsp<ST>(sc, L.dr1),
                        cptr<ST>(p.ln0_g), wsp<float>(ws, L.stats), reinterpret_cast<ST*>(dx),
-                       wsp<float>(sc, L.p_tail), d.B, d.T, d.D, L.nb);
+                       wsp<float>(sc, L.p_tail), d.B, d.T, d.D, L.nb, L.rpg);
   else
     hipLaunchKernelGGL((k_ln0_bwd<ST, 1, MAXD / 64>), grid, dim3(256), 0, s, cptr<ST>(x), wsp<ST>(sc, L.dr1),
                        cptr<ST>(p.ln0_g), wsp<float>(ws, L.stats), reinterpret_cast<ST*>(dx),
-                       wsp<float>(sc, L.p_tail), d.B, d.T, d.D, L.nb);
+                       wsp<float>(sc, L.p_tail), d.B, d.T, d.D, L.nb, L.rpg);
   prof_end(KID_LN0_BWD, s);
   return hipGetLastError();
 }
