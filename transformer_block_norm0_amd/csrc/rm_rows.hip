@@ -238,6 +238,18 @@ int resident_blocks(int threads) {
 //   3. output row i: the token-mix gather and the residual read LDS, then
 //      norm1 in registers and one store of out1.
 constexpr int PRO_LDS_BYTES = (int)SAMPLE_LDS_BYTES;  // 160 KB: T*D bf16 for T <= 64, D <= 1280
+// LDS tiers of the sample kernels: a workgroup declares the smallest tier
+// that holds its sample (T*D*2 bytes) and runs as many threads as leave the
+// LDS and the register file room for 160 KB / tier workgroups per CU, so a
+// small sample's load, compute and store overlap with other samples'.
+constexpr int lds_tier(long sample_bytes) {
+  return sample_bytes <= PRO_LDS_BYTES / 4 ? PRO_LDS_BYTES / 4
+         : sample_bytes <= PRO_LDS_BYTES / 2 ? PRO_LDS_BYTES / 2 : PRO_LDS_BYTES;
+}
+// prologue: 16 waves per CU in all (at most 128 VGPRs each)
+constexpr int pro_threads(int tier) { return 1024 * tier / PRO_LDS_BYTES; }
+// tail: 8 waves per CU in all (at most 256 VGPRs each), at least 4 per workgroup
+constexpr int tail_threads(int tier) { return tier == PRO_LDS_BYTES ? 512 : 256; }
 
 // Copy nbytes (a multiple of 16) from global src to LDS dst with 16-byte
 // buffer loads that write LDS directly, range-checked against [src, src +
@@ -260,14 +272,14 @@ __device__ __forceinline__ float load_bypass_l1(const float* p) {
   return __hip_atomic_load(p, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
 }
 
-template <typename ST>
-__global__ __launch_bounds__(1024) void k_prologue_lds(const ST* __restrict__ x, const ST* __restrict__ g0,
+template <typename ST, int LDSB>
+__global__ __launch_bounds__(pro_threads(LDSB), 4) void k_prologue_lds(const ST* __restrict__ x, const ST* __restrict__ g0,
                                                        const ST* __restrict__ be0, const ST* __restrict__ g1,
                                                        const ST* __restrict__ be1, ST* __restrict__ h1,
                                                        float* __restrict__ stats, int B, int T, int D) {
   constexpr int N = 4;
   constexpr int Q = MAXD / (64 * N);
-  __shared__ __attribute__((aligned(16))) char sx[PRO_LDS_BYTES];
+  __shared__ __attribute__((aligned(16))) char sx[LDSB];
   const int b = blockIdx.x;
   const int lane = threadIdx.x & 63;
   const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
@@ -1065,15 +1077,15 @@ __device__ __forceinline__ void sum_wave_rows(const float* lds, float* __restric
   }
 }
 
-template <typename ST>
-__global__ __launch_bounds__(512) void k_tail_bwd_lds(const ST* __restrict__ x, const ST* __restrict__ dh1,
+template <typename ST, int LDSB>
+__global__ __launch_bounds__(tail_threads(LDSB), 2) void k_tail_bwd_lds(const ST* __restrict__ x, const ST* __restrict__ dh1,
                                                        const ST* __restrict__ g0, const ST* __restrict__ be0,
                                                        const ST* __restrict__ g1, const float* __restrict__ stats,
                                                        ST* __restrict__ dx, float* __restrict__ part, int B, int T,
                                                        int D) {
   constexpr int N = 4;
   constexpr int Q = MAXD / (64 * N);
-  __shared__ __attribute__((aligned(16))) char sx[PRO_LDS_BYTES];
+  __shared__ __attribute__((aligned(16))) char sx[LDSB];
   float* const lf = reinterpret_cast<float*>(sx);
   const int b = blockIdx.x;
   const int lane = threadIdx.x & 63;
@@ -1552,9 +1564,16 @@ hipError_t prologue_t(const rm_dims& d, const rm_params& p, const void* x, void*
   prof_begin(KID_PROLOGUE, s);
   if constexpr (sizeof(ST) == 2) {
     if (sample_in_lds(d)) {
-      hipLaunchKernelGGL(k_prologue_lds<ST>, dim3(d.B), dim3(1024), 0, s, cptr<ST>(x), cptr<ST>(p.ln0_g),
-                         cptr<ST>(p.ln0_b), cptr<ST>(p.ln1_g), cptr<ST>(p.ln1_b), wsp<ST>(ws, L.h1),
-                         wsp<float>(ws, L.stats), d.B, d.T, d.D);
+      const int tier = lds_tier((long)d.T * d.D * 2);
+      auto launch = [&](auto kernel, int threads) {
+        hipLaunchKernelGGL(kernel, dim3(d.B), dim3(threads), 0, s, cptr<ST>(x), cptr<ST>(p.ln0_g),
+                           cptr<ST>(p.ln0_b), cptr<ST>(p.ln1_g), cptr<ST>(p.ln1_b), wsp<ST>(ws, L.h1),
+                           wsp<float>(ws, L.stats), d.B, d.T, d.D);
+      };
+      constexpr int T1 = PRO_LDS_BYTES, T2 = PRO_LDS_BYTES / 2, T4 = PRO_LDS_BYTES / 4;
+      if (tier == T4) launch(k_prologue_lds<ST, T4>, pro_threads(T4));
+      else if (tier == T2) launch(k_prologue_lds<ST, T2>, pro_threads(T2));
+      else launch(k_prologue_lds<ST, T1>, pro_threads(T1));
       prof_end(KID_PROLOGUE, s);
       return hipGetLastError();
     }
@@ -1672,9 +1691,16 @@ hipError_t tail_bwd_t(const rm_dims& d, const rm_params& p, const void* x, void*
   if constexpr (sizeof(ST) == 2) {
     if (sample_in_lds(d)) {
       prof_begin(KID_TAIL_BWD, s);
-      hipLaunchKernelGGL(k_tail_bwd_lds<ST>, dim3(d.B), dim3(512), 0, s, cptr<ST>(x), wsp<ST>(sc, L.dh1),
-                         cptr<ST>(p.ln0_g), cptr<ST>(p.ln0_b), cptr<ST>(p.ln1_g), wsp<float>(ws, L.stats),
-                         reinterpret_cast<ST*>(dx), wsp<float>(sc, L.p_tail), d.B, d.T, d.D);
+      const int tier = lds_tier((long)d.T * d.D * 2);
+      auto launch = [&](auto kernel, int threads) {
+        hipLaunchKernelGGL(kernel, dim3(d.B), dim3(threads), 0, s, cptr<ST>(x), wsp<ST>(sc, L.dh1),
+                           cptr<ST>(p.ln0_g), cptr<ST>(p.ln0_b), cptr<ST>(p.ln1_g), wsp<float>(ws, L.stats),
+                           reinterpret_cast<ST*>(dx), wsp<float>(sc, L.p_tail), d.B, d.T, d.D);
+      };
+      constexpr int T1 = PRO_LDS_BYTES, T2 = PRO_LDS_BYTES / 2, T4 = PRO_LDS_BYTES / 4;
+      if (tier == T4) launch(k_tail_bwd_lds<ST, T4>, tail_threads(T4));
+      else if (tier == T2) launch(k_tail_bwd_lds<ST, T2>, tail_threads(T2));
+      else launch(k_tail_bwd_lds<ST, T1>, tail_threads(T1));
       prof_end(KID_TAIL_BWD, s);
       return hipGetLastError();
     }
