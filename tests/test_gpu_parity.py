@@ -77,9 +77,10 @@ SMALL = [
     ("B256_T16_D256_k3_f16_lnrand", None),
 ]
 EDGE = [  # (B, T, D, k): B=1 minimum dims; S=1; odd D (unaligned bf16 rows); S=160 and H=3840;
-    # ragged tiles; the small-batch envelope's maximum (B*T = 512 rows, D = 128, H = 256)
+    # ragged tiles; the small-batch envelope's maximum (B*T = 512 rows, D = 128, H = 256); an
+    # 80 KB 16-bit sample (the middle LDS tier of the sample-in-LDS prologue and tail)
     (1, 8, 64, 2), (2, 64, 64, 3), (3, 13, 65, 3), (5, 8, 1280, 3), (67, 16, 256, 2), (130, 8, 96, 3),
-    (8, 64, 128, 2)]
+    (8, 64, 128, 2), (6, 32, 1280, 2)]
 
 
 def check_case(case, intermediates=True, kernels="auto"):
