@@ -228,8 +228,9 @@ int resident_blocks(int threads) {
 
 // ---------------------------------------------------------------------------
 // Forward prologue for 16-bit storage with the whole sample staged in LDS (T*D*2 bytes,
-// at most 160 KB), so x is read from HBM once.  One workgroup (16 waves) per
-// sample b, one wave per row, 4-element chunks (D % 4 == 0, S % 4 == 0):
+// at most 160 KB), so x is read from HBM once.  One workgroup (16 waves for
+// the 160 KB LDS tier, fewer for smaller samples, see lds_tier) per sample b,
+// one wave per row, 4-element chunks (D % 4 == 0, S % 4 == 0):
 //   1. each wave loads its rows of x[b] once, computes norm0's statistics in
 //      registers, writes the raw row to LDS and the statistics to `stats`;
 //   2. after the barrier each lane fetches the statistics of the (at most
@@ -1037,10 +1038,11 @@ __global__ __launch_bounds__(MAXT) void k_gate_bwd_ring(const ST* __restrict__ Z
   }
 }
 
-// Backward tail for 16-bit storage, one workgroup (8 waves) per sample b with
-// the sample staged in LDS (at most 160 KB), so the token-mix gathers read LDS
-// instead of 40-byte pieces of HBM lines.  Wave w owns the contiguous rows
-// R*w .. R*w+R-1 (R = ceil(T / 8)) in both row phases.
+// Backward tail for 16-bit storage, one workgroup (8 waves for the 160 KB LDS
+// tier, 4 for the smaller ones) per sample b with the sample staged in LDS
+// (at most 160 KB), so the token-mix gathers read LDS instead of 40-byte
+// pieces of HBM lines.  Wave w of nw owns the contiguous rows R*w .. R*w+R-1
+// (R = ceil(T / nw)) in both row phases.
 //   1. x[b] -> LDS by direct 16-byte copies, all in flight together (plain
 //      loads when x is not 16-byte aligned);
 //   2. norm1 backward per row i: r1 = token_mix(norm0(x)) + x, the mixed term
@@ -1054,7 +1056,7 @@ __global__ __launch_bounds__(MAXT) void k_gate_bwd_ring(const ST* __restrict__ Z
 //      LDS, n0 from x[j] (global, next row prefetched) and the saved
 //      statistics; dx = dr1 + rstd0 (dn - mean(dn) - n0 mean(dn n0)),
 //      dn = da0 gamma0;
-//   4. the 8 waves' column partials of both phases added through LDS in a
+//   4. the waves' column partials of both phases added through LDS in a
 //      fixed order and stored.
 // The next row's global operands are loaded while the current row is
 // computed; row statistics are read once per wave, one row per lane.
