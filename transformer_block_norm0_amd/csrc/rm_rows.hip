@@ -888,15 +888,18 @@ __global__ __launch_bounds__(MAXT) void k_gate_bwd(const ST* __restrict__ Z, con
 //   dU  = rsx (dux gx - mean(dux gx) - nx mean(dux gx nx)), same for dG.
 constexpr int RING = 2;
 
-template <typename ST, int MAXT>
+template <typename ST, int MAXT, int RPG>
 __global__ __launch_bounds__(MAXT) void k_gate_bwd_ring(const ST* __restrict__ Z, const ST* __restrict__ dhid,
                                                         const ST* __restrict__ gx, const ST* __restrict__ bx,
                                                         const ST* __restrict__ gg, const ST* __restrict__ bg,
                                                         const float* __restrict__ stats, ST* __restrict__ dZ,
                                                         float* __restrict__ pgate, float* __restrict__ pb1, int B,
-                                                        int T, int H, int nb, int rpg) {
+                                                        int T, int H, int nb) {
   __shared__ float red8[2 * 16 * 8];
   __shared__ float4 sst[MAX_ROWS_PER_GROUP];
+  // the group size is a compile-time constant: the row loop keeps a static trip count
+  static_assert(RPG >= MIN_ROWS_PER_GROUP && RPG <= MAX_ROWS_PER_GROUP && (RPG & (RPG - 1)) == 0, "group size");
+  constexpr int rpg = RPG;
   constexpr int SZ = (int)sizeof(ST);
   const int t = blockIdx.x, grp = blockIdx.y;
   const int nw = blockDim.x >> 6;
@@ -1669,9 +1672,18 @@ hipError_t gate_bwd_t(const rm_dims& d, const rm_params& p, void* ws, void* sc, 
   // 8-byte chunks (4 elements) keep the per-thread partial sums small
   // one workgroup of H/4 threads per row group (up to 640: 10 waves, room for the prefetch ring)
   if (H % 4 == 0 && H <= 2560 && 2L * d.B * d.T * H * (long)sizeof(ST) <= 0x7fffffffL)
-    hipLaunchKernelGGL((k_gate_bwd_ring<ST, 640>), grid, dim3(round64(H / 4)), 0, s, wsp<ST>(ws, L.z),
-                       wsp<ST>(sc, L.dhid), cptr<ST>(p.lnx_g), cptr<ST>(p.lnx_b), cptr<ST>(p.lng_g),
-                       cptr<ST>(p.lng_b), wsp<float>(ws, L.stats), wsp<ST>(sc, L.dz), pg, pb1, d.B, d.T, H, L.nb, L.rpg);
+  {
+    auto ring = [&](auto kernel) {
+      hipLaunchKernelGGL(kernel, grid, dim3(round64(H / 4)), 0, s, wsp<ST>(ws, L.z), wsp<ST>(sc, L.dhid),
+                         cptr<ST>(p.lnx_g), cptr<ST>(p.lnx_b), cptr<ST>(p.lng_g), cptr<ST>(p.lng_b),
+                         wsp<float>(ws, L.stats), wsp<ST>(sc, L.dz), pg, pb1, d.B, d.T, H, L.nb);
+    };
+    static_assert(MIN_ROWS_PER_GROUP == 16 && MAX_ROWS_PER_GROUP == 128, "one instantiation per group size");
+    if (L.rpg == 16) ring(k_gate_bwd_ring<ST, 640, 16>);
+    else if (L.rpg == 32) ring(k_gate_bwd_ring<ST, 640, 32>);
+    else if (L.rpg == 64) ring(k_gate_bwd_ring<ST, 640, 64>);
+    else ring(k_gate_bwd_ring<ST, 640, 128>);
+  }
   else if (H % 4 == 0)
     hipLaunchKernelGGL((k_gate_bwd<ST, 4, 1, 1024, 2>), grid, dim3(round64(H / 4)), 0, s, wsp<ST>(ws, L.z),
                        wsp<ST>(sc, L.dhid), cptr<ST>(p.lnx_g), cptr<ST>(p.lnx_b), cptr<ST>(p.lng_g),
